@@ -1,0 +1,453 @@
+// CPU oracle for the fully-INT8 FlashAttention-style attention forward.
+//
+// TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously-correct
+// statement of what the GPU library computes. Only the tests, the smoke check
+// and the CPU-baseline leg of the benchmark load it. It shares no code, header,
+// table or helper with the HIP library, and the HIP library never calls it.
+//
+// Sources (the method is stated in the pages listed here; every step below
+// names the passage it follows):
+//  [IFA]  "INT-FlashAttention: Enabling Flash Attention for INT8 Quantization",
+//         abstract: FlashAttention forward with fully INT8 Q/K/V input and
+//         token-level (one scale per row) post-training quantization.
+//  [IA]   "IntAttention: A Fully Integer Attention Pipeline for Efficient Edge
+//         Inference", §2.1 (standard scaled-dot-product attention; symmetric
+//         INT8 quantization with zero point 0 and scale absmax/127, Eq. 3;
+//         integer logits with INT32 accumulation; output O ~ s_V * P * V_hat),
+//         §2.2 (max-subtracted stable softmax), §3.1 (logit rescale factor
+//         alpha = s_Q s_K / sqrt(d), Eq. 4), §3.2 (prior methods quantize the
+//         probabilities as signed INT8 with a multiplier of 127).
+//  [FA3]  "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
+//         Low-precision", abstract: tiled attention with the softmax fused
+//         block by block (online softmax).
+//  [LLMI8] "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale",
+//         abstract: vector-wise quantization, i.e. one scale per row of the
+//         left operand times one scale per column of the right operand.
+//
+// Readings of points the pages leave open (each is also listed in the design
+// notes of the repository):
+//  * quantizer: q = clamp(rne(x * r), -127, 127) with r = 127/a and s = a/127,
+//    a = absmax of the group; x*r is one rounded fp32 multiply; an all-zero
+//    group gets s = 0 and q = 0.
+//  * per-token V inside the INT8 P.V product: the scale of tile t is
+//    s_t = max of s_V over the tile's in-range keys; key j's probability is
+//    quantized with multiplier w_j = (127 * s_V[j]) / s_t.
+//  * P_hat = rne(P_tilde * w) of the exact product (at most 48 significant
+//    bits, so exact in double); w = 127 for per-tensor V.
+//  * the running max used to quantize a tile is the max after that tile (m').
+//  * rowsum l accumulates the fp32 P_tilde before quantization.
+//  * INT32 accumulation inside a tile, fp32 across tiles.
+//  * causal mask is bottom-right aligned: query i sees key j iff
+//    j <= i + (Lkv - Lq).
+//  * GQA: query head h reads kv head h / (H / Hkv).
+//  * 1/sqrt(d) is the fp32 rounding of the double value.
+//
+// Build: g++ -std=c++17 -O2 -fno-fast-math -ffp-contract=off -fPIC -shared
+//        -pthread (see oracle/build.py). -ffp-contract=off keeps every fp32
+//        multiply and add separately rounded, as the steps below state them.
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <thread>
+#include <vector>
+
+#ifdef ORACLE_PLANT
+// A planted mistake (compiled only into throw-away test builds, never into the
+// oracle the tests compare against) to show that the pins catch it.
+#define PLANT(name) (std::strcmp(ORACLE_PLANT, name) == 0)
+#else
+#define PLANT(name) false
+#endif
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// IEEE binary16 codec, written from the format's definition (1 sign bit,
+// 5 exponent bits with bias 15, 10 fraction bits, subnormals at exponent 0).
+// ---------------------------------------------------------------------------
+float half_bits_to_float(uint16_t h) {
+  const uint32_t sign = h >> 15;
+  const uint32_t e = (h >> 10) & 0x1fu;
+  const uint32_t f = h & 0x3ffu;
+  float mag;
+  if (e == 0) {
+    mag = std::ldexp(static_cast<float>(f), -24);  // f * 2^-24, exact
+  } else if (e == 31) {
+    mag = f ? std::numeric_limits<float>::quiet_NaN()
+            : std::numeric_limits<float>::infinity();
+  } else {
+    mag = std::ldexp(static_cast<float>(f | 0x400u), static_cast<int>(e) - 25);
+  }
+  return sign ? -mag : mag;
+}
+
+// Round-to-nearest-even encoding of an fp32 value as binary16.
+uint16_t float_to_half_bits(float x) {
+  uint32_t bits;
+  std::memcpy(&bits, &x, 4);
+  const uint16_t sign = static_cast<uint16_t>((bits >> 16) & 0x8000u);
+  const double a = std::fabs(static_cast<double>(x));
+  if (std::isnan(x)) return sign | 0x7e00u;
+  if (a >= 65520.0) return sign | 0x7c00u;  // rounds to infinity
+  if (a < std::ldexp(1.0, -14)) {
+    // subnormal grid: multiples of 2^-24
+    const double n = std::nearbyint(a * std::ldexp(1.0, 24));  // exact scaling
+    return sign | static_cast<uint16_t>(n);  // n == 1024 encodes 2^-14 exactly
+  }
+  int e2;
+  std::frexp(a, &e2);     // a = m * 2^e2 with m in [0.5, 1)
+  int E = e2 - 1;         // a in [2^E, 2^(E+1))
+  double n = std::nearbyint(std::ldexp(a, 10 - E));  // in [1024, 2048]
+  if (n >= 2048.0) { n = 1024.0; ++E; }
+  if (E + 15 >= 31) return sign | 0x7c00u;
+  return sign | static_cast<uint16_t>(((E + 15) << 10) | (static_cast<int>(n) - 1024));
+}
+
+// ---------------------------------------------------------------------------
+// Symmetric INT8 quantization of one group (IA §2.1, Eq. 3; IFA abstract for
+// the token-level granularity).
+// ---------------------------------------------------------------------------
+void quantize_group(const float* x, int64_t n, int8_t* q, float* s_out) {
+  float a = 0.0f;
+  for (int64_t i = 0; i < n; ++i) a = std::max(a, std::fabs(x[i]));
+  if (a == 0.0f) {
+    *s_out = 0.0f;
+    for (int64_t i = 0; i < n; ++i) q[i] = 0;
+    return;
+  }
+  const float s = a / 127.0f;   // stored scale: X ~ s * X_hat
+  const float r = 127.0f / a;   // multiplier applied to every element
+  *s_out = s;
+  for (int64_t i = 0; i < n; ++i) {
+    const float y = x[i] * r;                  // one rounded fp32 multiply
+    float t = PLANT("quant_round_away") ? std::round(y) : std::nearbyint(y);
+    t = std::min(127.0f, std::max(-127.0f, t));
+    q[i] = static_cast<int8_t>(t);
+  }
+}
+
+// Exact integer dot product of two int8 rows (IA §2.1: INT8 x INT8 products
+// accumulated in 32-bit integers).
+int32_t dot_i8(const int8_t* a, const int8_t* b, int d) {
+  int32_t acc = 0;
+  for (int c = 0; c < d; ++c) acc += static_cast<int32_t>(a[c]) * static_cast<int32_t>(b[c]);
+  return acc;
+}
+
+struct Problem {
+  const int8_t* q; const float* s_q;
+  const int8_t* k; const float* s_k;
+  const int8_t* v; const float* s_v;
+  int v_per_token;
+  int B, H, Hkv, Lq, Lkv, d, causal;
+  int kv_tile, kv_split_len;
+};
+
+// Per-key trace of one row, for the invariant tests.
+struct RowTrace {
+  float* S;        // [Lkv] dequantized logit (-inf if masked)
+  float* m_tile;   // [Lkv] running max m' used for the key's tile
+  float* p_tilde;  // [Lkv] exp(S - m')
+  int32_t* p_hat;  // [Lkv] quantized probability
+  float* w;        // [Lkv] quantization multiplier of the key
+  float* split_m;  // [Lkv] final running max of the key's split
+};
+
+// One query row, step by step. Returns O[d] (fp32) and lse.
+void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, RowTrace* tr) {
+  const int d = P.d;
+  const int group = P.H / P.Hkv;
+  const int hk = PLANT("gqa_wrong_head") ? (h % P.Hkv) : (h / group);  // GQA mapping
+  const int64_t qrow = (static_cast<int64_t>(b) * P.H + h) * P.Lq + i;
+  const int8_t* qv = P.q + qrow * d;
+  const float sq = P.s_q[qrow];
+  const int64_t kv_base = (static_cast<int64_t>(b) * P.Hkv + hk) * P.Lkv;
+  const int8_t* kmat = P.k + kv_base * d;
+  const int8_t* vmat = P.v + kv_base * d;
+  const float* sk = P.s_k + kv_base;
+  const float* sv = P.v_per_token ? (P.s_v + kv_base) : P.s_v;
+
+  // Bottom-right aligned causal mask: last visible key of this row.
+  int64_t last = P.Lkv - 1;
+  if (P.causal) {
+    last = static_cast<int64_t>(i) + (P.Lkv - P.Lq);
+    if (PLANT("causal_off_by_one")) last -= 1;
+  }
+  const float inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+  const float NEG_INF = -std::numeric_limits<float>::infinity();
+
+  const int Bc = P.kv_tile;
+  const int split_len = P.kv_split_len > 0 ? P.kv_split_len : P.Lkv;
+  const int n_splits = (P.Lkv + split_len - 1) / split_len;
+
+  std::vector<float> acc(d), S(Bc), pt(Bc), w(Bc);
+  std::vector<int32_t> ph(Bc), T(d);
+  std::vector<float> sm(n_splits), sl(n_splits), sacc(static_cast<size_t>(n_splits) * d);
+
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const int s0 = sp * split_len;
+    const int s1 = std::min(P.Lkv, s0 + split_len);
+    // Online softmax state of this split (FA3 abstract: softmax fused tile by
+    // tile; IA §2.2: max-subtracted stable softmax).
+    float m = NEG_INF, l = 0.0f;
+    std::fill(acc.begin(), acc.end(), 0.0f);
+    for (int t0 = s0; t0 < s1; t0 += Bc) {         // ascending tile order
+      const int t1 = std::min(s1, t0 + Bc);
+      const int n = t1 - t0;
+      // Dequantized logits: S = S_int * s_Q[i] * s_K[j] / sqrt(d)
+      // (IA §2.1 integer logits; IA §3.1 Eq. 4 for the rescale factor; the
+      // per-row x per-column scale product is LLM.int8()'s vector-wise form).
+      float mt = NEG_INF;
+      for (int jj = 0; jj < n; ++jj) {
+        const int j = t0 + jj;
+        if (j > last) { S[jj] = NEG_INF; continue; }
+        const int32_t s_int = dot_i8(qv, kmat + static_cast<int64_t>(j) * d, d);
+        float x = static_cast<float>(s_int) * sq;
+        if (!PLANT("drop_sk")) x = x * sk[j];
+        x = x * inv_sqrt_d;
+        S[jj] = x;
+        mt = std::max(mt, x);
+      }
+      const float m_new = std::max(m, mt);
+      if (m_new == NEG_INF) continue;                // nothing visible yet
+      float alpha = (m == NEG_INF) ? 0.0f : std::exp(m - m_new);
+      if (PLANT("alpha_sign")) alpha = (m == NEG_INF) ? 0.0f : std::exp(m_new - m);
+      if (PLANT("no_alpha")) alpha = (m == NEG_INF) ? 0.0f : 1.0f;
+      // Scale of this tile's V contribution and per-key P multipliers.
+      float st;
+      if (P.v_per_token) {
+        st = 0.0f;
+        for (int jj = 0; jj < n; ++jj) st = std::max(st, sv[t0 + jj]);
+      } else {
+        st = sv[0];
+      }
+      float lsum = 0.0f;
+      for (int jj = 0; jj < n; ++jj) {
+        const float p = (S[jj] == NEG_INF) ? 0.0f : std::exp(S[jj] - m_new);
+        pt[jj] = p;
+        lsum += p;
+        float wj;
+        if (P.v_per_token) wj = (st > 0.0f) ? (127.0f * sv[t0 + jj]) / st : 0.0f;
+        else wj = 127.0f;
+        w[jj] = wj;
+        // P_hat = rne(P_tilde * w): signed INT8 probabilities with multiplier
+        // 127 (IA §3.2 describes this as the prior methods' choice).
+        ph[jj] = static_cast<int32_t>(std::nearbyint(static_cast<double>(p) * static_cast<double>(wj)));
+      }
+      l = PLANT("l_no_rescale") ? (l + lsum) : (alpha * l + lsum);
+      // T = P_hat . V_hat over this tile, exact in INT32.
+      for (int c = 0; c < d; ++c) T[c] = 0;
+      for (int jj = 0; jj < n; ++jj) {
+        if (ph[jj] == 0) continue;
+        const int8_t* vr = vmat + static_cast<int64_t>(t0 + jj) * d;
+        for (int c = 0; c < d; ++c) {
+          const int8_t vv = PLANT("transpose_v") ? vmat[static_cast<int64_t>(c % P.Lkv) * d + ((t0 + jj) % d)] : vr[c];
+          T[c] += ph[jj] * static_cast<int32_t>(vv);
+        }
+      }
+      // fp32 accumulation across tiles: acc = alpha * acc + s_t * T
+      // (IA §2.1: O ~ s_V * P * V_hat).
+      for (int c = 0; c < d; ++c) acc[c] = alpha * acc[c] + st * static_cast<float>(T[c]);
+      m = m_new;
+      if (tr) {
+        for (int jj = 0; jj < n; ++jj) {
+          const int j = t0 + jj;
+          tr->S[j] = S[jj]; tr->m_tile[j] = m_new; tr->p_tilde[j] = pt[jj];
+          tr->p_hat[j] = ph[jj]; tr->w[j] = w[jj];
+        }
+      }
+    }
+    sm[sp] = m; sl[sp] = l;
+    std::copy(acc.begin(), acc.end(), sacc.begin() + static_cast<size_t>(sp) * d);
+    if (tr) for (int j = s0; j < s1; ++j) tr->split_m[j] = m;
+  }
+
+  // Merge the splits by their maxima (same identity as the tile rescale).
+  float M = NEG_INF;
+  for (int sp = 0; sp < n_splits; ++sp) M = std::max(M, sm[sp]);
+  float L = 0.0f;
+  std::fill(acc.begin(), acc.end(), 0.0f);
+  for (int sp = 0; sp < n_splits; ++sp) {
+    if (sm[sp] == NEG_INF) continue;
+    const float f = std::exp(sm[sp] - M);
+    L += f * sl[sp];
+    for (int c = 0; c < d; ++c) acc[c] += f * sacc[static_cast<size_t>(sp) * d + c];
+  }
+  // Output: O = acc / (127 * l); s_V is already inside acc.
+  for (int c = 0; c < d; ++c) o[c] = acc[c] / (127.0f * L);
+  if (lse) *lse = M + std::log(L);
+}
+
+template <class F>
+void parallel_for(int64_t n, int nthreads, F f) {
+  if (nthreads <= 0) nthreads = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
+  nthreads = static_cast<int>(std::min<int64_t>(nthreads, std::max<int64_t>(1, n)));
+  std::atomic<int64_t> next{0};
+  auto worker = [&]() {
+    for (;;) {
+      const int64_t i0 = next.fetch_add(16);
+      if (i0 >= n) break;
+      const int64_t i1 = std::min(n, i0 + 16);
+      for (int64_t i = i0; i < i1; ++i) f(i);
+    }
+  };
+  std::vector<std::thread> th;
+  for (int t = 1; t < nthreads; ++t) th.emplace_back(worker);
+  worker();
+  for (auto& t : th) t.join();
+}
+
+bool problem_ok(const Problem& P) {
+  if (P.B < 1 || P.H < 1 || P.Hkv < 1 || P.Lq < 1 || P.Lkv < 1 || P.d < 1) return false;
+  if (P.H % P.Hkv) return false;
+  if (P.kv_tile < 1) return false;
+  if (P.kv_split_len < 0 || (P.kv_split_len > 0 && P.kv_split_len % P.kv_tile)) return false;
+  if (P.causal && P.Lq > P.Lkv) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_half_to_float(const uint16_t* h, float* f, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) f[i] = half_bits_to_float(h[i]);
+  return 0;
+}
+
+int oracle_float_to_half(const float* f, uint16_t* h, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) h[i] = float_to_half_bits(f[i]);
+  return 0;
+}
+
+// x: fp32 [n_rows, n_cols] (x_is_half = 0) or binary16 bits (x_is_half = 1).
+// Groups of rows_per_scale consecutive rows share one scale.
+int oracle_quantize_rows(const void* x, int x_is_half, int64_t n_rows, int32_t n_cols,
+                         int64_t rows_per_scale, int8_t* q, float* scales) {
+  if (n_rows < 1 || n_cols < 1 || rows_per_scale < 1 || n_rows % rows_per_scale) return 1;
+  const int64_t n_groups = n_rows / rows_per_scale;
+  const int64_t gsize = rows_per_scale * n_cols;
+  std::vector<float> buf(static_cast<size_t>(gsize));
+  for (int64_t g = 0; g < n_groups; ++g) {
+    const int64_t off = g * gsize;
+    if (x_is_half) {
+      const uint16_t* hx = static_cast<const uint16_t*>(x) + off;
+      for (int64_t i = 0; i < gsize; ++i) buf[i] = half_bits_to_float(hx[i]);
+    } else {
+      const float* fx = static_cast<const float*>(x) + off;
+      std::copy(fx, fx + gsize, buf.begin());
+    }
+    quantize_group(buf.data(), gsize, q + off, scales + g);
+  }
+  return 0;
+}
+
+// S_int[b,h,i,j] = sum_c Q_hat[b,h,i,c] * K_hat[b,h/(H/Hkv),j,c] for every pair
+// (mask not applied; the caller compares the visible pairs).
+int oracle_logits_i32(const int8_t* q, const int8_t* k, int32_t B, int32_t H, int32_t Hkv,
+                      int32_t Lq, int32_t Lkv, int32_t d, int32_t* s_out, int nthreads) {
+  if (B < 1 || H < 1 || Hkv < 1 || Lq < 1 || Lkv < 1 || d < 1 || H % Hkv) return 1;
+  const int group = H / Hkv;
+  parallel_for(static_cast<int64_t>(B) * H * Lq, nthreads, [&](int64_t r) {
+    const int64_t bh = r / Lq;
+    const int b = static_cast<int>(bh / H), h = static_cast<int>(bh % H);
+    const int64_t kv_base = (static_cast<int64_t>(b) * Hkv + h / group) * Lkv;
+    for (int j = 0; j < Lkv; ++j)
+      s_out[r * Lkv + j] = dot_i8(q + r * d, k + (kv_base + j) * d, d);
+  });
+  return 0;
+}
+
+// INT8 attention forward, step by step, with the KV schedule as parameters.
+// rows == NULL: every (b,h,i) row; o is [B,H,Lq,d], lse is [B,H,Lq].
+// rows != NULL: n_rows flat row ids (b*H + h)*Lq + i; o is [n_rows,d], lse [n_rows].
+int oracle_attn_int8(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                     const int8_t* v, const float* s_v, int32_t v_per_token,
+                     int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                     int32_t causal, int32_t kv_tile, int32_t kv_split_len,
+                     const int64_t* rows, int64_t n_rows, float* o, float* lse, int nthreads) {
+  Problem P{q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
+  if (!problem_ok(P)) return 1;
+  const int64_t total = static_cast<int64_t>(B) * H * Lq;
+  const int64_t n = rows ? n_rows : total;
+  for (int64_t r = 0; rows && r < n; ++r)
+    if (rows[r] < 0 || rows[r] >= total) return 1;
+  parallel_for(n, nthreads, [&](int64_t r) {
+    const int64_t id = rows ? rows[r] : r;
+    const int i = static_cast<int>(id % Lq);
+    const int64_t bh = id / Lq;
+    attend_row(P, static_cast<int>(bh / H), static_cast<int>(bh % H), i, o + r * d,
+               lse ? lse + r : nullptr, nullptr);
+  });
+  return 0;
+}
+
+// Same as oracle_attn_int8 for one row, also returning the per-key trace
+// (each array has Lkv entries; masked keys keep S = -inf and P = 0).
+int oracle_attn_int8_trace(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                           const int8_t* v, const float* s_v, int32_t v_per_token,
+                           int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                           int32_t causal, int32_t kv_tile, int32_t kv_split_len,
+                           int32_t b, int32_t h, int32_t i, float* o, float* lse,
+                           float* S, float* m_tile, float* p_tilde, int32_t* p_hat, float* w,
+                           float* split_m) {
+  Problem P{q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
+  if (!problem_ok(P) || b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Lq) return 1;
+  const float NEG_INF = -std::numeric_limits<float>::infinity();
+  for (int j = 0; j < Lkv; ++j) {
+    S[j] = NEG_INF; m_tile[j] = NEG_INF; p_tilde[j] = 0.0f; p_hat[j] = 0; w[j] = 0.0f; split_m[j] = NEG_INF;
+  }
+  RowTrace tr{S, m_tile, p_tilde, p_hat, w, split_m};
+  attend_row(P, b, h, i, o, lse, &tr);
+  return 0;
+}
+
+// Exact scaled-dot-product attention in fp64 on un-quantized fp32 inputs
+// (IA §2.1: A = Q K^T, P = softmax(A / sqrt(d)), O = P V), same mask and GQA
+// mapping. rows/n_rows as in oracle_attn_int8.
+int oracle_attn_ref_f64(const float* q, const float* k, const float* v,
+                        int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                        int32_t causal, const int64_t* rows, int64_t n_rows, double* o, int nthreads) {
+  if (B < 1 || H < 1 || Hkv < 1 || Lq < 1 || Lkv < 1 || d < 1 || H % Hkv) return 1;
+  if (causal && Lq > Lkv) return 1;
+  const int group = H / Hkv;
+  const int64_t total = static_cast<int64_t>(B) * H * Lq;
+  const int64_t n = rows ? n_rows : total;
+  for (int64_t r = 0; rows && r < n; ++r)
+    if (rows[r] < 0 || rows[r] >= total) return 1;
+  parallel_for(n, nthreads, [&](int64_t r) {
+    const int64_t id = rows ? rows[r] : r;
+    const int i = static_cast<int>(id % Lq);
+    const int64_t bh = id / Lq;
+    const int b = static_cast<int>(bh / H), h = static_cast<int>(bh % H);
+    const int64_t kv_base = (static_cast<int64_t>(b) * Hkv + h / group) * Lkv;
+    const float* qv = q + id * d;
+    const int64_t last = causal ? static_cast<int64_t>(i) + (Lkv - Lq) : Lkv - 1;
+    std::vector<double> a(static_cast<size_t>(last + 1));
+    double mx = -std::numeric_limits<double>::infinity();
+    const double scale = 1.0 / std::sqrt(static_cast<double>(d));
+    for (int64_t j = 0; j <= last; ++j) {
+      const float* kv = k + (kv_base + j) * d;
+      double dot = 0.0;
+      for (int c = 0; c < d; ++c) dot += static_cast<double>(qv[c]) * static_cast<double>(kv[c]);
+      a[j] = dot * scale;
+      mx = std::max(mx, a[j]);
+    }
+    double den = 0.0;
+    for (int64_t j = 0; j <= last; ++j) { a[j] = std::exp(a[j] - mx); den += a[j]; }
+    double* orow = o + r * d;
+    for (int c = 0; c < d; ++c) orow[c] = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+      const float* vv = v + (kv_base + j) * d;
+      const double p = a[j] / den;
+      for (int c = 0; c < d; ++c) orow[c] += p * static_cast<double>(vv[c]);
+    }
+  });
+  return 0;
+}
+
+}  // extern "C"
