@@ -1,0 +1,200 @@
+"""Benchmark of the INT8 attention forward hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that is
+already resident in HBM: per-token INT8 quantization of Q and K, INT8
+quantization of V (per tensor or per token, as the workload says), and the
+fused attention forward. `value` is algorithmic INT8 ops (4 d per visible
+query-key pair) per second of step time, in TOPS.
+
+Also reported on the same JSON line:
+  roofline      the fused attention kernel alone: its average duration from HIP
+                events around each launch in the timed region, against the
+                dense INT8 MFMA peak (5.0 POP/s)
+  cpu_baseline  the oracle (plain C++, all host threads given to it) timed on
+                a bounded, seeded sample of the workload's query rows
+  kernels       per-kernel averages (quantize passes, attention) in the timed region
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import WORKLOADS  # noqa: E402
+
+METRIC = "INT8 attention fwd TOPS & % INT8 MFMA peak (B4 H32 L4096 d128, causal)"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="l4096_outlier", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="time only the fused attention launches (for profiling runs)")
+    return ap.parse_args()
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, q, k, v, target_s):
+    """Time the oracle's INT8 attention on a seeded sample of rows, scaled so
+    the timed call lasts about target_s seconds."""
+    import oracle
+    rps_v = 1 if w.v_per_token else v.size // w.d
+    qh, sq = oracle.quantize_rows(q, 1)
+    kh, sk = oracle.quantize_rows(k, 1)
+    vh, sv = oracle.quantize_rows(v, rps_v)
+    import int8_quantized_flashattention_amd as m
+    tile, split = m.attn_int8_fwd_schedule(w.B, w.H, w.Hkv, w.Lq, w.Lkv, w.d, w.causal)
+    nth = host_threads()
+    total_rows = w.B * w.H * w.Lq
+    rng = np.random.Generator(np.random.PCG64(12345))
+
+    def ops_of(rows):
+        i = rows % w.Lq
+        keys = np.minimum(w.Lkv, i + (w.Lkv - w.Lq) + 1) if w.causal else np.full(rows.shape, w.Lkv)
+        return float(4 * w.d * keys.sum())
+
+    n = min(total_rows, 64 * nth)
+    while True:
+        rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_int8(qh, sq, kh, sk, vh, sv, w.v_per_token, w.B, w.H, w.Hkv, w.Lq, w.Lkv, w.d,
+                         w.causal, tile, split, rows=rows, nthreads=nth)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= total_rows:
+            break
+        n = int(min(total_rows, max(2 * n, n * target_s / max(dt, 1e-3))))
+    return {"value": ops_of(rows) / dt / 1e12, "unit": "TOPS", "cores": nth, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "%d of %d query rows (seeded uniform sample), INT8 attention step only "
+                      "(quantization excluded), %d host threads" % (rows.size, total_rows, nth)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_quantized_flashattention_amd as m
+
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    q, k, v = w.inputs()
+    dq, dk, dv = (torch.from_numpy(a).cuda() for a in (q, k, v))
+    d = w.d
+    rps_v = 1 if w.v_per_token else v.size // d
+    # outputs and quantized buffers allocated once, outside the timed region
+    qh = torch.empty(dq.shape, dtype=torch.int8, device="cuda")
+    kh = torch.empty(dk.shape, dtype=torch.int8, device="cuda")
+    vh = torch.empty(dv.shape, dtype=torch.int8, device="cuda")
+    sq = torch.empty(dq.numel() // d, dtype=torch.float32, device="cuda")
+    sk = torch.empty(dk.numel() // d, dtype=torch.float32, device="cuda")
+    sv = torch.empty(dv.numel() // d // rps_v, dtype=torch.float32, device="cuda")
+    odt = torch.float16 if w.o_dtype == "f16" else torch.float32
+    o = torch.empty((w.B, w.H, w.Lq, d), dtype=odt, device="cuda")
+    ws_n = m.attn_int8_fwd_workspace_size(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda") if ws_n else None
+    stream = torch.cuda.current_stream()
+
+    def quantize():
+        m.attn_quantize_rows(dq, 1, qh, sq)
+        m.attn_quantize_rows(dk, 1, kh, sk)
+        m.attn_quantize_rows(dv, rps_v, vh, sv)
+
+    def attend():
+        m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        if not args.attn_only:
+            quantize()
+        attend()
+    quantize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        if not args.attn_only:
+            quantize()
+        e1.record(stream)
+        attend()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = wall * 1e3 / args.steps
+    attn_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    quant_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+
+    ops = float(w.ops())
+    value = ops / (step_ms * 1e-3) / 1e12
+    kernel_tops = ops / (attn_ms * 1e-3) / 1e12
+    tile, split = m.attn_int8_fwd_schedule(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
+    kv_bytes = 2 * w.B * w.Hkv * w.Lkv * d + 4 * (2 * w.B * w.Hkv * w.Lkv + w.B * w.H * w.Lq)
+    o_bytes = w.B * w.H * w.Lq * d * (2 if w.o_dtype == "f16" else 4)
+    attn_bytes = w.B * w.H * w.Lq * d + kv_bytes + o_bytes      # compulsory HBM bytes
+    in_bytes = (q.nbytes + k.nbytes + v.nbytes)
+    quant_bytes = (in_bytes if w.v_per_token else in_bytes + v.nbytes) + q.size + k.size + v.size
+
+    bound_mfma = ops / attn_bytes > PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if bound_mfma:
+        roof = {"bound": "mfma", "achieved": round(kernel_tops, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(kernel_tops / PEAK_INT8_TOPS, 4), "traffic": None}
+    else:
+        gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = "attn_fwd_kernel"
+    roof["kernel_ms"] = round(attn_ms, 4)
+    roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
+                   "d": d, "causal": bool(w.causal),
+                   "v_scale": "per_token" if w.v_per_token else "per_tensor",
+                   "inputs": "%s N(0,1)%s" % (w.in_dtype, ", 1%% of head-dim channels x20 in Q and K"
+                                              if w.outlier_seed is not None else ""),
+                   "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
+                   "step": "attention only" if args.attn_only else
+                           "quantize Q,K,V + fused attention"},
+        "roofline": roof,
+        "kernels": {"attention_ms": round(attn_ms, 4), "quantize_ms": round(quant_ms, 4),
+                    "attention_tops": round(kernel_tops, 2),
+                    "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1)
+                    if quant_ms > 0 and not args.attn_only else None},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

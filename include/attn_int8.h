@@ -1,0 +1,156 @@
+/*
+ * attn_int8.h — C ABI of the INT8 FlashAttention-style attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (see the pages cited on each entry point):
+ *   1. per-row symmetric INT8 quantization of Q and K, and of V per tensor or
+ *      per row: s = absmax / 127, zero point 0
+ *      ("IntAttention: A Fully Integer Attention Pipeline for Efficient Edge
+ *      Inference", §2.1 Eq. 3; token-level granularity from
+ *      "INT-FlashAttention: Enabling Flash Attention for INT8 Quantization",
+ *      abstract);
+ *   2. a fused tiled forward: INT8 x INT8 -> INT32 logits, dequantized by
+ *      s_Q[i] s_K[j] / sqrt(d) (IntAttention §2.1 and §3.1 Eq. 4; the
+ *      row-scale x column-scale form is the vector-wise scheme of
+ *      "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale",
+ *      abstract), an fp32 online softmax over KV tiles (max subtraction as in
+ *      IntAttention §2.2; tile-wise fusion as in "FlashAttention-3",
+ *      abstract), probabilities quantized to INT8 with multiplier 127
+ *      (IntAttention §3.2, the prior-methods scheme), INT8 P.V into INT32 per
+ *      tile, and the final rescale O = acc / (127 l) (IntAttention §2.1,
+ *      O ~ s_V P V_hat).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except the
+ *    two output pointers of attn_int8_fwd_schedule (host). The library never
+ *    allocates, frees, copies between host and device, or synchronizes.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it and the call returns at once.
+ *  - All arguments are checked on the host before anything is launched. On any
+ *    error nothing is launched, no output is touched, and the status says why.
+ *    A launch failure reported by the HIP runtime returns ATTN_ERR_HIP.
+ *  - Tensors are dense and row-major with the last dimension innermost:
+ *    q [B, H, Lq, d], k and v [B, Hkv, Lkv, d], o [B, H, Lq, d].
+ *  - Inputs must be finite; NaN and Inf are outside the contract.
+ *  - The functions keep no global mutable state and are reentrant; calls that
+ *    run on different streams over disjoint outputs do not interact.
+ */
+#ifndef ATTN_INT8_H
+#define ATTN_INT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment, bad flag   */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request outside what is implemented       */
+  ATTN_ERR_HIP = 3          /* the HIP runtime reported an error at launch     */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1 } attn_dtype;
+
+typedef enum { ATTN_VSCALE_PER_TENSOR = 0, ATTN_VSCALE_PER_TOKEN = 1 } attn_vscale;
+
+/*
+ * attn_quantize_rows — symmetric INT8 quantization of groups of rows
+ * (IntAttention §2.1 Eq. 3; token-level groups from the INT-FlashAttention
+ * abstract).
+ *
+ *   x       [n_rows, n_cols] of x_dt (fp32 or fp16), device, 16-byte aligned.
+ *   q       [n_rows, n_cols] int8 output, device, 8-byte aligned.
+ *   scales  [n_rows / rows_per_scale] fp32 output, device, 4-byte aligned.
+ *   rows_per_scale: consecutive rows sharing one scale. 1 = per token;
+ *           n_rows = one scale for the whole tensor; any divisor of n_rows.
+ *   n_cols  must be a multiple of 8 (else ATTN_ERR_UNSUPPORTED).
+ *
+ * For each group with absmax a: if a == 0 then s = 0 and every code is 0;
+ * otherwise s = a / 127 and r = 127 / a (each a correctly rounded fp32
+ * division) and q = clamp(rne(x * r), -127, 127), where x * r is one rounded
+ * fp32 multiply and rne rounds to nearest, ties to even. Codes are in
+ * [-127, 127]; -128 is never produced.
+ * While the call runs, `scales` is also used as scratch for the group maxima.
+ */
+attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols,
+                               int64_t rows_per_scale, int8_t* q, float* scales, void* stream);
+
+/*
+ * attn_int8_fwd — fused INT8 attention forward (INT-FlashAttention abstract:
+ * FlashAttention forward with fully INT8 inputs; formulas as listed at the top
+ * of this header).
+ *
+ *   q    int8 [B, H, Lq, d]      s_q fp32 [B, H, Lq]       (per-token scales)
+ *   k    int8 [B, Hkv, Lkv, d]   s_k fp32 [B, Hkv, Lkv]    (per-token scales)
+ *   v    int8 [B, Hkv, Lkv, d]   s_v fp32 [1] (ATTN_VSCALE_PER_TENSOR) or
+ *                                    [B, Hkv, Lkv] (ATTN_VSCALE_PER_TOKEN)
+ *   o    [B, H, Lq, d] of o_dt (fp32 or fp16, rounded to nearest even)
+ *   lse  fp32 [B, H, Lq] natural-log log-sum-exp of the scaled logits, or NULL
+ *   d    64 or 128 (else ATTN_ERR_UNSUPPORTED)
+ *   H % Hkv == 0; query head h reads KV head h / (H / Hkv).
+ *   causal 0 or 1. Causal masking is bottom-right aligned: query i sees key j
+ *        iff j <= i + (Lkv - Lq); causal requires Lq <= Lkv.
+ *   workspace, workspace_bytes: device scratch of at least
+ *        attn_int8_fwd_workspace_size(...) bytes, 256-byte aligned (may be
+ *        NULL when that size is 0).
+ *   int8 tensors and o must be 16-byte aligned, scales 4-byte aligned; each
+ *   tensor must have fewer than 2^31 elements.
+ *
+ * Per row the kernel visits the KV tiles reported by attn_int8_fwd_schedule
+ * in ascending order. For tile t with running max m' (after the tile):
+ * P_tilde = exp(S - m'), l = alpha l + sum P_tilde, P_hat = rne(P_tilde w_j)
+ * with w_j = 127 (per-tensor V) or 127 s_V[j] / s_t (per-token V, s_t = the
+ * largest s_V of the tile's keys), acc = alpha acc + s_t * (P_hat . V_hat)
+ * (s_t = s_V for per-tensor V), and finally O = acc / (127 l). Because P_hat
+ * follows the running max, O depends on the tile size and split points; they
+ * are part of the result's definition and are reported by the schedule query.
+ */
+attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                          const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                          attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv,
+                          int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * attn_int8_fwd_workspace_size — bytes of device workspace attn_int8_fwd needs
+ * for this problem (0 when it needs none; split-KV decode shapes need room for
+ * the per-split partial results). Returns 0 for invalid problems as well;
+ * attn_int8_fwd then reports the error.
+ */
+size_t attn_int8_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                                    int32_t d, int32_t causal);
+
+/*
+ * attn_int8_fwd_schedule — the schedule facts that change attn_int8_fwd's
+ * result (the probability grid follows the running max, so the result depends
+ * on where tiles and splits start): *kv_tile = keys per KV tile (tiles start at
+ * multiples of it), *kv_split_len = keys per KV split (splits start at
+ * multiples of it and are merged by their maxima), or 0 when the KV range is
+ * not split. Host pointers. Same argument checks as attn_int8_fwd.
+ */
+attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                                   int32_t d, int32_t causal, int32_t* kv_tile,
+                                   int32_t* kv_split_len);
+
+/*
+ * attn_int8_debug_logits — test entry point: runs the INT8 Q.K^T tile code of
+ * the fused prefill kernel (IntAttention §2.1: INT8 products with INT32
+ * accumulation) and writes the exact INT32 logit of every visible pair to
+ * s_out [B, H, Lq, Lkv] (int32, device, 16-byte aligned). Pairs masked by the
+ * causal rule are not written. Same shape rules as attn_int8_fwd.
+ */
+attn_status attn_int8_debug_logits(const int8_t* q, const int8_t* k, int32_t B, int32_t H,
+                                   int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,
+                                   int32_t* s_out, void* stream);
+
+/* attn_status_str — static, NUL-terminated description of a status code. */
+const char* attn_status_str(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_INT8_H */

@@ -1,0 +1,186 @@
+"""Python binding of libattn_int8 (INT8 FlashAttention-style forward, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn_int8.so``; PyTorch supplies device memory and the stream.
+The functions carry the names of the C ABI in ``include/attn_int8.h``.
+
+Importing this package loads the library and raises ImportError when it has
+not been built (``python int8_quantized_flashattention_amd/build.py``): there
+is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_int8.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_F16 = 0, 1
+ATTN_VSCALE_PER_TENSOR, ATTN_VSCALE_PER_TOKEN = 0, 1
+
+# every function the C header declares, with its ctypes signature
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "attn_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
+    "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
+                                     _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "attn_int8_fwd_workspace_size": (_SZ, [_I32] * 7),
+    "attn_int8_fwd_schedule": (ctypes.c_int, [_I32] * 7 + [_P, _P]),
+    "attn_int8_debug_logits": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _P, _P]),
+    "attn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libattn_int8.so is not built (%s); run "
+                          "`python int8_quantized_flashattention_amd/build.py`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %s (status %d)" % (fn, attn_status_str(status), status))
+        self.status = status
+
+
+def attn_status_str(status):
+    return _lib.attn_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != ATTN_OK:
+        raise AttnError(fn, status)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def attn_quantize_rows(x, rows_per_scale=1, q=None, scales=None, stream=None):
+    """Symmetric INT8 quantization of groups of `rows_per_scale` rows of x
+    (fp16 or fp32, last axis = row). Returns (q int8 like x, scales fp32)."""
+    _dev(x, "x")
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    n_cols = x.shape[-1]
+    n_rows = x.numel() // n_cols
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scales is None:
+        n = n_rows // rows_per_scale if rows_per_scale > 0 else 0
+        scales = torch.empty(max(n, 1), dtype=torch.float32, device=x.device)
+    _dev(q, "q", torch.int8)
+    _dev(scales, "scales", torch.float32)
+    st = _lib.attn_quantize_rows(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32,
+                                 n_rows, n_cols, rows_per_scale, _ptr(q), _ptr(scales), _stream(stream))
+    _check("attn_quantize_rows", st)
+    return q, scales
+
+
+def attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal):
+    return int(_lib.attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, int(causal)))
+
+
+def attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal):
+    """(kv_tile, kv_split_len) the forward uses for this shape; 0 = no split."""
+    t, s = ctypes.c_int32(), ctypes.c_int32()
+    _check("attn_int8_fwd_schedule",
+           _lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, int(causal), ctypes.byref(t),
+                                       ctypes.byref(s)))
+    return t.value, s.value
+
+
+def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
+                  return_lse=False, out=None, lse=None, workspace=None, stream=None):
+    """Fused INT8 attention forward. q [B,H,Lq,d] int8, k/v [B,Hkv,Lkv,d] int8,
+    s_q [B*H*Lq], s_k [B*Hkv*Lkv], s_v [1] or [B*Hkv*Lkv] (fp32).
+    Returns O (and lse when return_lse)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, torch.int8)
+    for t, n in ((s_q, "s_q"), (s_k, "s_k"), (s_v, "s_v")):
+        _dev(t, n, torch.float32)
+    B, H, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Lkv, d) or tuple(v.shape) != (B, Hkv, Lkv, d):
+        raise ValueError("k and v must be [B, Hkv, Lkv, d] matching q")
+    if s_q.numel() != B * H * Lq or s_k.numel() != B * Hkv * Lkv:
+        raise ValueError("s_q / s_k sizes do not match q / k")
+    if s_v.numel() != (B * Hkv * Lkv if v_per_token else 1):
+        raise ValueError("s_v size does not match v_per_token")
+    if o_dtype not in (torch.float16, torch.float32):
+        raise TypeError("o_dtype must be float16 or float32")
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=o_dtype, device=q.device)
+    _dev(out, "out", o_dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    need = attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.attn_int8_fwd(_ptr(q), _ptr(s_q), _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
+                            ATTN_VSCALE_PER_TOKEN if v_per_token else ATTN_VSCALE_PER_TENSOR,
+                            _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32, _ptr(lse),
+                            B, H, Hkv, Lq, Lkv, d, int(causal), _ptr(workspace), ws_bytes,
+                            _stream(stream))
+    _check("attn_int8_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_int8_debug_logits(q, k, causal, out=None, stream=None):
+    """INT32 logits of every visible pair from the prefill kernel's tile code;
+    masked pairs keep out's previous contents (out defaults to zeros)."""
+    _dev(q, "q", torch.int8)
+    _dev(k, "k", torch.int8)
+    B, H, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.zeros((B, H, Lq, Lkv), dtype=torch.int32, device=q.device)
+    _dev(out, "out", torch.int32)
+    st = _lib.attn_int8_debug_logits(_ptr(q), _ptr(k), B, H, Hkv, Lq, Lkv, d, int(causal), _ptr(out),
+                                     _stream(stream))
+    _check("attn_int8_debug_logits", st)
+    return out
+
+
+def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, return_lse=False):
+    """The whole path from fp16/fp32 Q, K, V: per-token quantization of Q and K,
+    per-tensor or per-token quantization of V, then the fused forward."""
+    B, H, Lq, d = q.shape
+    qh, sq = attn_quantize_rows(q, 1)
+    kh, sk = attn_quantize_rows(k, 1)
+    vh, sv = attn_quantize_rows(v, 1 if v_per_token else v.numel() // d)
+    return attn_int8_fwd(qh, sq, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
+
+
+__all__ = ["attn_quantize_rows", "attn_int8_fwd", "attn_int8_fwd_workspace_size",
+           "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
+           "AttnError", "LIB_PATH", "SIGNATURES"]

@@ -1,0 +1,147 @@
+// Host side of the C ABI declared in include/attn_int8.h: argument checks,
+// schedule selection and kernel dispatch. Nothing here allocates, copies or
+// synchronizes; every check happens before the first launch.
+#include <stdint.h>
+
+#include "attn_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+attn_status check_shape(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                        int32_t causal) {
+  if (B < 1 || H < 1 || Hkv < 1 || Lq < 1 || Lkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (causal && Lq > Lkv) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int64_t nq = int64_t{B} * H * Lq * d;
+  const int64_t nk = int64_t{B} * Hkv * Lkv * d;
+  if (nq > kMaxElems || nk > kMaxElems) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t{B} * H > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+namespace attn {
+
+// Decode-shaped problems (few query rows per KV head) take the split-KV
+// kernel; everything else the prefill kernel with one KV pass per row block.
+void fwd_schedule(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal, int* kv_tile,
+                  int* kv_split_len, int* use_decode) {
+  (void)B; (void)H; (void)Hkv; (void)Lq; (void)Lkv; (void)d; (void)causal;
+  *kv_tile = kPrefillBN;
+  *kv_split_len = 0;
+  *use_decode = 0;
+}
+
+size_t fwd_workspace_bytes(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal) {
+  int tile, split, dec;
+  fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
+  if (!dec || split == 0) return 0;
+  const int64_t n_splits = (Lkv + split - 1) / split;
+  // per (query row, split): running max, row sum, d accumulators (fp32)
+  const int64_t rows = int64_t{B} * H * Lq;
+  const int64_t bytes = rows * n_splits * (2 + d) * 4;
+  return static_cast<size_t>((bytes + 255) / 256 * 256);
+}
+
+}  // namespace attn
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols,
+                               int64_t rows_per_scale, int8_t* q, float* scales, void* stream) {
+  if (!x || !q || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (n_rows < 1 || n_cols < 1 || rows_per_scale < 1 || n_rows % rows_per_scale != 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
+  if (n_cols % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (n_rows / rows_per_scale > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_quantize(x, x_dt == ATTN_F16, n_rows, n_cols, rows_per_scale, q,
+                                             scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_int8_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                                    int32_t d, int32_t causal) {
+  if (check_shape(B, H, Hkv, Lq, Lkv, d, causal) != ATTN_OK) return 0;
+  return attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
+}
+
+attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                                   int32_t d, int32_t causal, int32_t* kv_tile,
+                                   int32_t* kv_split_len) {
+  if (!kv_tile || !kv_split_len) return ATTN_ERR_INVALID_ARG;
+  const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
+  if (s != ATTN_OK) return s;
+  int tile, split, dec;
+  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
+  *kv_tile = tile;
+  *kv_split_len = split;
+  return ATTN_OK;
+}
+
+attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                          const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                          attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv,
+                          int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !s_q || !k || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
+  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN) return ATTN_ERR_INVALID_ARG;
+  if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
+  if (s != ATTN_OK) return s;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned(s_q, 4) || !aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4)))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return ATTN_ERR_INVALID_ARG;
+
+  attn::FwdArgs a{};
+  a.q = q; a.s_q = s_q; a.k = k; a.s_k = s_k; a.v = v; a.s_v = s_v;
+  a.o = o; a.lse = lse; a.s_dump = nullptr;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
+  a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN); a.o_f16 = (o_dt == ATTN_F16);
+  a.workspace = workspace;
+  int tile, split, dec;
+  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = dec ? attn::launch_decode(a, split, st) : attn::launch_prefill(a, st);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_int8_debug_logits(const int8_t* q, const int8_t* k, int32_t B, int32_t H,
+                                   int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,
+                                   int32_t* s_out, void* stream) {
+  if (!q || !k || !s_out) return ATTN_ERR_INVALID_ARG;
+  const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
+  if (s != ATTN_OK) return s;
+  if (int64_t{B} * H * Lq * Lkv > kMaxElems) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(s_out, 16)) return ATTN_ERR_INVALID_ARG;
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.s_dump = s_out;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d; a.causal = causal;
+  const hipError_t e = attn::launch_debug_logits(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

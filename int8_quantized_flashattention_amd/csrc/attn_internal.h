@@ -1,0 +1,43 @@
+// Internal declarations shared by the HIP sources of libattn_int8.
+// Not part of the public ABI (include/attn_int8.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_int8.h"
+
+namespace attn {
+
+// Problem description after host-side validation.
+struct FwdArgs {
+  const int8_t* q; const float* s_q;
+  const int8_t* k; const float* s_k;
+  const int8_t* v; const float* s_v;
+  void* o; float* lse;
+  int32_t* s_dump;          // debug logits output (dump variant only)
+  int B, H, Hkv, Lq, Lkv, d;
+  int causal, v_per_token, o_f16;
+  void* workspace;
+};
+
+// Prefill kernel geometry: BM query rows per workgroup, BN keys per KV tile.
+constexpr int kPrefillBM = 128;
+constexpr int kPrefillBN = 64;
+
+// Decode (split-KV) geometry.
+constexpr int kDecodeBN = 64;           // keys per tile
+constexpr int kDecodeMaxGroup = 8;      // query heads per KV head handled by one workgroup
+
+// Schedule the fused forward uses for this problem (what changes the result).
+void fwd_schedule(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal, int* kv_tile,
+                  int* kv_split_len, int* use_decode);
+size_t fwd_workspace_bytes(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal);
+
+hipError_t launch_quantize(const void* x, int x_f16, int64_t n_rows, int n_cols,
+                           int64_t rows_per_scale, int8_t* q, float* scales, hipStream_t st);
+hipError_t launch_prefill(const FwdArgs& a, hipStream_t st);
+hipError_t launch_debug_logits(const FwdArgs& a, hipStream_t st);
+hipError_t launch_decode(const FwdArgs& a, int split_len, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,216 @@
+// Symmetric INT8 quantization of row groups for gfx950.
+//
+// Operation ("IntAttention: A Fully Integer Attention Pipeline for Efficient
+// Edge Inference", §2.1 Eq. 3, zero point 0; one scale per token as in the
+// "INT-FlashAttention" abstract, or one per larger group of rows):
+//   a = max |x| over the group; a == 0 -> s = 0, q = 0;
+//   else s = a / 127, r = 127 / a (correctly rounded fp32 divisions) and
+//   q = clamp(rne(x * r), -127, 127) with x * r one rounded fp32 multiply.
+//
+// The pass is HBM-bound (2 or 4 bytes in, 1 byte out per element), so the
+// design is about streaming: every lane moves one 16-byte (fp16) or 32-byte
+// (fp32) chunk of 8 elements per load, a group small enough for one wavefront
+// (per-token rows) is reduced with cross-lane max inside the wavefront and
+// quantized from registers in the same pass, and large groups (per-tensor or
+// per-head scales) take two passes: an order-free maximum through atomicMax on
+// the bit pattern of |x| (non-negative floats order like their bits), then the
+// quantizing pass, whose re-read mostly hits the 256 MB last-level cache.
+#include "attn_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace attn {
+namespace {
+
+constexpr int kChunk = 8;          // elements per lane per load
+constexpr int kThreads = 256;
+
+struct Chunk8 { float x[kChunk]; };
+
+template <bool F16>
+__device__ __forceinline__ Chunk8 load_chunk(const void* base, int64_t elem) {
+  Chunk8 c;
+  if constexpr (F16) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const __half*>(base) + elem);
+    const __half2* h = reinterpret_cast<const __half2*>(&raw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 f = __half22float2(h[i]);
+      c.x[2 * i] = f.x;
+      c.x[2 * i + 1] = f.y;
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    const float4 a = p[0], b = p[1];
+    c.x[0] = a.x; c.x[1] = a.y; c.x[2] = a.z; c.x[3] = a.w;
+    c.x[4] = b.x; c.x[5] = b.y; c.x[6] = b.z; c.x[7] = b.w;
+  }
+  return c;
+}
+
+__device__ __forceinline__ float chunk_absmax(const Chunk8& c) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) m = fmaxf(m, fabsf(c.x[i]));
+  return m;
+}
+
+// q = clamp(rne(x * r)); the multiply is kept separate from the rounding (no
+// contraction) so the code is the RNE of the rounded product.
+__device__ __forceinline__ int quant1(float x, float r) {
+  float t = __builtin_rintf(__fmul_rn(x, r));
+  t = fminf(127.0f, fmaxf(-127.0f, t));
+  return static_cast<int>(t);
+}
+
+__device__ __forceinline__ void store_codes(int8_t* q, int64_t elem, const Chunk8& c, float r, bool zero) {
+  uint32_t w0 = 0, w1 = 0;
+  if (!zero) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0 |= (static_cast<uint32_t>(quant1(c.x[i], r)) & 0xffu) << (8 * i);
+      w1 |= (static_cast<uint32_t>(quant1(c.x[4 + i], r)) & 0xffu) << (8 * i);
+    }
+  }
+  *reinterpret_cast<uint2*>(q + elem) = make_uint2(w0, w1);
+}
+
+// ---------------------------------------------------------------------------
+// Small groups: a team of T lanes (a power of two <= 64) owns one group and
+// each lane holds up to CH chunks in registers.
+// ---------------------------------------------------------------------------
+template <bool F16, int T, int CH>
+__global__ __launch_bounds__(kThreads) void quantize_small_groups(
+    const void* __restrict__ x, int64_t n_groups, int64_t group_elems, int8_t* __restrict__ q,
+    float* __restrict__ scales) {
+  constexpr int kTeams = kThreads / T;
+  const int team = threadIdx.x / T;
+  const int tl = threadIdx.x % T;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kTeams + team;
+  const bool live = g < n_groups;
+  const int64_t base = g * group_elems;
+  const int n_chunks = static_cast<int>(group_elems / kChunk);
+
+  Chunk8 c[CH];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ci = tl + i * T;
+    if (live && ci < n_chunks) {
+      c[i] = load_chunk<F16>(x, base + static_cast<int64_t>(ci) * kChunk);
+      a = fmaxf(a, chunk_absmax(c[i]));
+    }
+  }
+  // team-wide maximum (exact: max is order-free)
+#pragma unroll
+  for (int off = T / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, T));
+  if (!live) return;
+  const bool zero = (a == 0.0f);
+  const float r = zero ? 0.0f : __fdiv_rn(127.0f, a);
+  if (tl == 0) scales[g] = zero ? 0.0f : __fdiv_rn(a, 127.0f);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ci = tl + i * T;
+    if (ci < n_chunks) store_codes(q, base + static_cast<int64_t>(ci) * kChunk, c[i], r, zero);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large groups: grid (n_groups, blocks_per_group); each block strides over its
+// group's chunks.
+// ---------------------------------------------------------------------------
+__global__ void zero_bits(uint32_t* bits, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) bits[i] = 0u;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void absmax_large_groups(const void* __restrict__ x,
+                                                                int64_t group_elems,
+                                                                uint32_t* __restrict__ bits) {
+  const int64_t g = blockIdx.x;
+  const int64_t base = g * group_elems;
+  const int64_t n_chunks = group_elems / kChunk;
+  float a = 0.0f;
+  for (int64_t ci = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x; ci < n_chunks;
+       ci += static_cast<int64_t>(gridDim.y) * kThreads)
+    a = fmaxf(a, chunk_absmax(load_chunk<F16>(x, base + ci * kChunk)));
+  for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  __shared__ float wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = wmax[0];
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, wmax[w]);
+    atomicMax(bits + g, __float_as_uint(m));  // |x| >= 0: float order == bit order
+  }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void quantize_large_groups(const void* __restrict__ x,
+                                                                  int64_t group_elems,
+                                                                  const uint32_t* __restrict__ bits,
+                                                                  int8_t* __restrict__ q) {
+  const int64_t g = blockIdx.x;
+  const int64_t base = g * group_elems;
+  const int64_t n_chunks = group_elems / kChunk;
+  const float a = __uint_as_float(bits[g]);
+  const bool zero = (a == 0.0f);
+  const float r = zero ? 0.0f : __fdiv_rn(127.0f, a);
+  for (int64_t ci = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x; ci < n_chunks;
+       ci += static_cast<int64_t>(gridDim.y) * kThreads)
+    store_codes(q, base + ci * kChunk, load_chunk<F16>(x, base + ci * kChunk), r, zero);
+}
+
+__global__ void finalize_scales(float* scales, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float a = __uint_as_float(reinterpret_cast<const uint32_t*>(scales)[i]);
+    scales[i] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, 127.0f);
+  }
+}
+
+template <bool F16, int T, int CH>
+hipError_t run_small(const void* x, int64_t n_groups, int64_t ge, int8_t* q, float* s, hipStream_t st) {
+  constexpr int kTeams = kThreads / T;
+  const int64_t blocks = (n_groups + kTeams - 1) / kTeams;
+  hipLaunchKernelGGL((quantize_small_groups<F16, T, CH>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), 0, st, x, n_groups, ge, q, s);
+  return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t run(const void* x, int64_t n_rows, int n_cols, int64_t rps, int8_t* q, float* s,
+               hipStream_t st) {
+  const int64_t ge = rps * static_cast<int64_t>(n_cols);
+  const int64_t n_groups = n_rows / rps;
+  const int64_t n_chunks = ge / kChunk;
+  if (n_chunks <= 8) return run_small<F16, 8, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 16) return run_small<F16, 16, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 32) return run_small<F16, 32, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 64) return run_small<F16, 64, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 256) return run_small<F16, 64, 4>(x, n_groups, ge, q, s, st);
+  // large groups: zero the maxima, atomic max, quantize, turn maxima into scales
+  uint32_t* bits = reinterpret_cast<uint32_t*>(s);
+  const unsigned zb = static_cast<unsigned>((n_groups + 255) / 256);
+  hipLaunchKernelGGL(zero_bits, dim3(zb), dim3(256), 0, st, bits, n_groups);
+  const int64_t per_block = static_cast<int64_t>(kThreads) * 4;   // chunks per block per pass
+  int64_t bpg = (n_chunks + per_block - 1) / per_block;
+  if (bpg > 2048) bpg = 2048;
+  const dim3 grid(static_cast<unsigned>(n_groups), static_cast<unsigned>(bpg));
+  hipLaunchKernelGGL(absmax_large_groups<F16>, grid, dim3(kThreads), 0, st, x, ge, bits);
+  hipLaunchKernelGGL(quantize_large_groups<F16>, grid, dim3(kThreads), 0, st, x, ge,
+                     static_cast<const uint32_t*>(bits), q);
+  hipLaunchKernelGGL(finalize_scales, dim3(zb), dim3(256), 0, st, s, n_groups);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int x_f16, int64_t n_rows, int n_cols, int64_t rps,
+                           int8_t* q, float* scales, hipStream_t st) {
+  return x_f16 ? run<true>(x, n_rows, n_cols, rps, q, scales, st)
+               : run<false>(x, n_rows, n_cols, rps, q, scales, st);
+}
+
+}  // namespace attn

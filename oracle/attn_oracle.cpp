@@ -70,19 +70,24 @@ namespace {
 // 5 exponent bits with bias 15, 10 fraction bits, subnormals at exponent 0).
 // ---------------------------------------------------------------------------
 float half_bits_to_float(uint16_t h) {
-  const uint32_t sign = h >> 15;
+  const uint32_t sign = static_cast<uint32_t>(h >> 15) << 31;
   const uint32_t e = (h >> 10) & 0x1fu;
   const uint32_t f = h & 0x3ffu;
-  float mag;
+  uint32_t bits;
   if (e == 0) {
-    mag = std::ldexp(static_cast<float>(f), -24);  // f * 2^-24, exact
+    // subnormal or zero: f * 2^-24, exact in fp32 (f < 2^10, power-of-two factor)
+    const float mag = static_cast<float>(f) * 5.9604644775390625e-8f;
+    std::memcpy(&bits, &mag, 4);
+    bits |= sign;
   } else if (e == 31) {
-    mag = f ? std::numeric_limits<float>::quiet_NaN()
-            : std::numeric_limits<float>::infinity();
+    bits = sign | 0x7f800000u | (f << 13);     // infinity or NaN
   } else {
-    mag = std::ldexp(static_cast<float>(f | 0x400u), static_cast<int>(e) - 25);
+    // normal: same value with the exponent re-biased from 15 to 127
+    bits = sign | ((e + 112u) << 23) | (f << 13);
   }
-  return sign ? -mag : mag;
+  float out;
+  std::memcpy(&out, &bits, 4);
+  return out;
 }
 
 // Round-to-nearest-even encoding of an fp32 value as binary16.

@@ -1,0 +1,111 @@
+"""Helpers of the GPU parity tests: run one problem through the HIP path and
+through the oracle on the same bytes, and compare.
+
+Tolerance for O (fp32 or fp16 output): max-abs error <= 2e-2 and relative
+Frobenius error <= 1e-2 against the oracle run with the GPU's KV schedule.
+The quantized tensors, their scales and the INT32 logits must be bit-exact.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+O_MAX_ABS = 2e-2
+O_REL_FRO = 1e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def quantize_both(lib, x, rows_per_scale):
+    """Quantize host array x on the GPU and with the oracle; assert bit-exact.
+    Returns the (shared) host codes and scales plus the device copies."""
+    qd, sd = lib.attn_quantize_rows(dev(x), rows_per_scale)
+    qg, sg = host(qd), host(sd)
+    qo, so = oracle.quantize_rows(x, rows_per_scale)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32)), "scales differ"
+    if not np.array_equal(qg, qo):
+        bad = np.argwhere(qg != qo)[:5]
+        raise AssertionError("codes differ at %s" % bad.tolist())
+    return qo, so, qd, sd
+
+
+def compare_o(o_gpu, o_ref, what=""):
+    o_gpu = np.asarray(o_gpu, np.float32)
+    o_ref = np.asarray(o_ref, np.float32)
+    assert o_gpu.shape == o_ref.shape
+    assert np.all(np.isfinite(o_gpu)), "non-finite output " + what
+    diff = o_gpu.astype(np.float64) - o_ref.astype(np.float64)
+    max_abs = float(np.abs(diff).max())
+    den = float(np.linalg.norm(o_ref.astype(np.float64)))
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    log("  %s max_abs=%.3e rel_fro=%.3e" % (what, max_abs, rel))
+    assert max_abs <= O_MAX_ABS and rel <= O_REL_FRO, (what, max_abs, rel)
+    return max_abs, rel
+
+
+def quantize_subset(lib, x, batches):
+    """Per-token quantization on the GPU over all of x; the oracle quantizes the
+    selected batch entries, which must match bit for bit."""
+    qd, sd = lib.attn_quantize_rows(dev(x), 1)
+    qo, so = oracle.quantize_rows(np.ascontiguousarray(x[batches]), 1)
+    qg = host(qd)[batches]
+    sg = host(sd).reshape(x.shape[:-1])[batches].reshape(-1)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32)), "scales differ"
+    assert np.array_equal(qg, qo), "codes differ"
+    return qo, so, qd, sd
+
+
+def run_problem(lib, q, k, v, causal, v_per_token, o_dtype, rows=None, check_lse=True, tag="",
+                batches=None):
+    """Full path on the GPU vs the oracle. q/k/v are host fp16/fp32 arrays.
+    rows: optional flat row ids to compare (default: every row).
+    batches: optional batch indices; the oracle then quantizes and attends only
+    those entries (per-token V only, where batch entries are independent)."""
+    B, H, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    log("[%s] B=%d H=%d Hkv=%d Lq=%d Lkv=%d d=%d causal=%d vpt=%d o=%s" %
+        (tag, B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o_dtype))
+    if batches is None:
+        qh, sq, qd, sqd = quantize_both(lib, q, 1)
+        kh, sk, kd, skd = quantize_both(lib, k, 1)
+        vh, sv, vd, svd = quantize_both(lib, v, 1 if v_per_token else v.size // d)
+    else:
+        assert v_per_token and rows is None
+        batches = np.asarray(batches)
+        qh, sq, qd, sqd = quantize_subset(lib, q, batches)
+        kh, sk, kd, skd = quantize_subset(lib, k, batches)
+        vh, sv, vd, svd = quantize_subset(lib, v, batches)
+    tdt = torch.float16 if o_dtype == "f16" else torch.float32
+    o, lse = lib.attn_int8_fwd(qd, sqd, kd, skd, vd, svd, v_per_token, causal, tdt, return_lse=True)
+    og = host(o).astype(np.float32)
+    lg = host(lse)
+    tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
+    if batches is not None:
+        og, lg, B = og[batches], lg[batches], len(batches)
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, v_per_token, B, H, Hkv, Lq, Lkv, d, causal,
+                              tile, split, rows=rows)
+    if rows is None:
+        compare_o(og, oo, tag)
+        lg_sel = lg.reshape(-1)
+    else:
+        compare_o(og.reshape(-1, d)[rows], oo, tag)
+        lg_sel = lg.reshape(-1)[rows]
+    if check_lse:
+        lo_f = lo.reshape(-1)
+        err = np.abs(lg_sel - lo_f) / np.maximum(1.0, np.abs(lo_f))
+        assert float(err.max()) <= 1e-4, ("lse", float(err.max()))
+    return og, oo

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every function include/attn_int8.h declares,
+and rejects every invalid request on the host before any launch (no GPU needed:
+the rejected calls never reach the HIP runtime, so fake addresses are safe)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_int8.h")
+
+import int8_quantized_flashattention_amd as m  # noqa: E402
+
+OK, INVALID, UNSUPPORTED = m.ATTN_OK, m.ATTN_ERR_INVALID_ARG, m.ATTN_ERR_UNSUPPORTED
+L = m._lib
+A = 0x100000  # a 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(m.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in (OK, INVALID, UNSUPPORTED, m.ATTN_ERR_HIP):
+        assert m.attn_status_str(s) and m.attn_status_str(s) != "unknown status"
+    assert m.attn_status_str(99) == "unknown status"
+
+
+def fwd(**kw):
+    args = dict(q=A, s_q=A, k=A, s_k=A, v=A, s_v=A, v_mode=0, o=A, o_dt=1, lse=None, B=1, H=2, Hkv=1,
+                Lq=8, Lkv=8, d=64, causal=0, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return L.attn_int8_fwd(p(args["q"]), p(args["s_q"]), p(args["k"]), p(args["s_k"]), p(args["v"]),
+                           p(args["s_v"]), args["v_mode"], p(args["o"]), args["o_dt"], p(args["lse"]),
+                           args["B"], args["H"], args["Hkv"], args["Lq"], args["Lkv"], args["d"],
+                           args["causal"], p(args["ws"]), args["ws_bytes"], p(args["stream"]))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(s_q=None), INVALID), (dict(k=None), INVALID),
+    (dict(s_k=None), INVALID), (dict(v=None), INVALID), (dict(s_v=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(v_mode=2), INVALID), (dict(o_dt=5), INVALID),
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Hkv=0), INVALID), (dict(Lq=0), INVALID),
+    (dict(Lkv=-3), INVALID), (dict(d=0), INVALID),
+    (dict(H=3, Hkv=2), INVALID), (dict(causal=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(q=A + 8), INVALID), (dict(k=A + 4), INVALID), (dict(v=A + 1), INVALID),
+    (dict(o=A + 2), INVALID), (dict(s_q=A + 2), INVALID), (dict(lse=A + 1), INVALID),
+    (dict(B=1024, H=64, Hkv=64, Lq=4096, Lkv=4096, d=128), UNSUPPORTED),
+])
+def test_fwd_rejects_before_launch(kw, expect):
+    assert fwd(**kw) == expect
+
+
+def test_quantize_rejects_before_launch():
+    p = ctypes.c_void_p
+    q = lambda **kw: L.attn_quantize_rows(
+        p(kw.get("x", A)), kw.get("dt", 1), kw.get("n_rows", 16), kw.get("n_cols", 64),
+        kw.get("rps", 1), p(kw.get("q", A)), p(kw.get("s", A)), None)
+    assert q(x=None) == INVALID
+    assert q(q=None) == INVALID
+    assert q(s=None) == INVALID
+    assert q(dt=7) == INVALID
+    assert q(n_rows=0) == INVALID
+    assert q(n_cols=0) == INVALID
+    assert q(rps=0) == INVALID
+    assert q(rps=5) == INVALID          # 16 rows not divisible by 5
+    assert q(n_cols=60) == UNSUPPORTED  # not a multiple of 8
+    assert q(x=A + 8) == INVALID
+    assert q(q=A + 4) == INVALID
+    assert q(s=A + 2) == INVALID
+
+
+def test_debug_logits_rejects_before_launch():
+    p = ctypes.c_void_p
+    f = lambda **kw: L.attn_int8_debug_logits(
+        p(kw.get("q", A)), p(kw.get("k", A)), kw.get("B", 1), kw.get("H", 1), kw.get("Hkv", 1),
+        kw.get("Lq", 8), kw.get("Lkv", 8), kw.get("d", 64), kw.get("causal", 0),
+        p(kw.get("s", A)), None)
+    assert f(q=None) == INVALID
+    assert f(s=None) == INVALID
+    assert f(d=32) == UNSUPPORTED
+    assert f(causal=1, Lq=9) == INVALID
+    assert f(s=A + 4) == INVALID
+    assert f(B=64, H=64, Hkv=64, Lq=1024, Lkv=1024) == UNSUPPORTED
+
+
+def test_schedule_and_workspace_queries():
+    t, s = m.attn_int8_fwd_schedule(4, 32, 32, 4096, 4096, 128, 1)
+    assert t > 0 and t % 32 == 0 and s >= 0 and (s == 0 or s % t == 0)
+    assert m.attn_int8_fwd_workspace_size(1, 3, 2, 8, 8, 64, 0) == 0   # invalid -> 0
+    with pytest.raises(m.AttnError):
+        m.attn_int8_fwd_schedule(1, 1, 1, 8, 8, 48, 0)
+    assert L.attn_int8_fwd_schedule(1, 1, 1, 8, 8, 64, 0, None, None) == INVALID

@@ -1,0 +1,97 @@
+"""Fused INT8 attention on the GPU vs the oracle run with the GPU's schedule.
+
+Small workloads compare every output row; the full-size workloads (the sizes
+the benchmark times) compare seeded samples of rows that include the first and
+last rows of their heads. Quantized tensors and scales are compared bit for bit
+on the full tensors along the way.
+"""
+import numpy as np
+import pytest
+
+from gpu_parity import log, run_problem
+from workloads import WORKLOADS, gaussian
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import int8_quantized_flashattention_amd as m
+    return m
+
+
+def _sample_rows(w, n_heads=4, per_head=512, seed=0):
+    """Flat row ids (b*H + h)*Lq + i over a few heads: first rows, last rows
+    and a seeded random middle."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    BH = w.B * w.H
+    heads = np.unique(np.concatenate([[0, BH - 1], r.choice(BH, size=n_heads, replace=False)]))
+    rows = []
+    for bh in heads:
+        n = min(w.Lq, per_head)
+        fixed = np.unique(np.concatenate([np.arange(min(16, w.Lq)), np.arange(max(0, w.Lq - 64), w.Lq)]))
+        rest = r.choice(w.Lq, size=max(0, n - fixed.size), replace=False) if w.Lq > n else np.arange(w.Lq)
+        ids = np.unique(np.concatenate([fixed, rest]))
+        rows.append(bh * w.Lq + ids)
+    return np.concatenate(rows).astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny", "l1024", "l1024_causal"])
+def test_small_workloads_all_rows(lib, name):
+    w = WORKLOADS[name]
+    q, k, v = w.inputs()
+    for odt in ({w.o_dtype} | {"f32"}):
+        run_problem(lib, q, k, v, w.causal, w.v_per_token, odt, tag="%s/%s" % (name, odt))
+
+
+@pytest.mark.parametrize("name", ["l4096_outlier", "l4096_gauss", "l16384"])
+def test_full_size_workloads_sampled_rows(lib, name):
+    w = WORKLOADS[name]
+    q, k, v = w.inputs()
+    run_problem(lib, q, k, v, w.causal, w.v_per_token, w.o_dtype, rows=_sample_rows(w), tag=name)
+
+
+@pytest.mark.timeout(400)
+def test_decode_workload_sampled_batches(lib):
+    # the full 1 GB KV cache goes through the GPU path; the oracle checks a
+    # seeded set of batch entries (every head and row of each)
+    w = WORKLOADS["decode"]
+    q, k, v = w.inputs()
+    batches = np.array([0, 17, 42, 63])
+    run_problem(lib, q, k, v, w.causal, w.v_per_token, w.o_dtype, tag="decode", batches=batches)
+
+
+# ragged and degenerate shapes: Lq/Lkv not multiples of the tiles, Lq != Lkv,
+# GQA ratios, single rows/keys
+SWEEP = [  # B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o
+    (1, 1, 1, 1, 1, 64, 0, 0, "f32"), (1, 1, 1, 1, 1, 128, 1, 1, "f16"),
+    (2, 4, 2, 77, 130, 128, 1, 0, "f16"), (1, 2, 1, 1, 200, 128, 0, 1, "f32"),
+    (1, 3, 3, 300, 300, 64, 1, 1, "f32"), (1, 2, 2, 50, 190, 64, 1, 0, "f16"),
+    (3, 8, 1, 129, 65, 128, 0, 0, "f16"), (1, 8, 2, 257, 1000, 128, 1, 1, "f16"),
+    (2, 16, 4, 16, 700, 128, 0, 1, "f16"), (1, 4, 4, 640, 640, 128, 1, 0, "f32"),
+    (1, 32, 8, 3, 333, 64, 0, 1, "f32"), (2, 2, 2, 1000, 1001, 64, 1, 0, "f16"),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt", SWEEP)
+def test_shape_sweep(lib, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt):
+    seed = (B * 7 + H) * 1000003 + Lq * 1009 + Lkv
+    q = gaussian((B, H, Lq, d), seed, np.float16)
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    run_problem(lib, q, k, v, causal, vpt, odt, tag="sweep")
+
+
+def test_degenerate_inputs(lib):
+    r = np.random.Generator(np.random.PCG64(9))
+    B, H, L, d = 1, 2, 200, 128
+    base = [gaussian((B, H, L, d), 900 + i, np.float16) for i in range(3)]
+    q0 = np.zeros_like(base[0])                     # zero queries: uniform weights
+    run_problem(lib, q0, base[1], base[2], True, False, "f32", tag="zero-q")
+    v0 = np.zeros_like(base[2])                     # zero values: s_V = 0, O = 0
+    og, _ = run_problem(lib, base[0], base[1], v0, False, False, "f32", tag="zero-v")
+    assert np.all(og == 0)
+    keq = np.repeat(base[1][:, :, :1], L, axis=2)   # identical keys
+    run_problem(lib, base[0], keq, base[2], False, True, "f32", tag="equal-k")
+    big = (r.standard_normal((B, H, L, d)) * 60).astype(np.float16)  # peaked softmax
+    run_problem(lib, big, big, base[2], True, False, "f16", tag="peaked")

@@ -1,0 +1,57 @@
+"""GPU quantizer == oracle quantizer, bit for bit (codes and scales)."""
+import numpy as np
+import pytest
+
+from gpu_parity import log, quantize_both
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import int8_quantized_flashattention_amd as m
+    return m
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# (rows, cols, rows_per_scale, dtype): covers every team width, the
+# register-chunk variant, the two-pass large-group path and ragged grids
+CASES = [
+    (1, 8, 1, np.float32), (7, 64, 1, np.float16), (1000, 128, 1, np.float16),
+    (257, 64, 1, np.float32), (33, 256, 1, np.float16), (12, 128, 4, np.float32),
+    (100, 128, 10, np.float16), (3, 2048, 1, np.float16), (2, 4096, 1, np.float32),
+    (64, 128, 64, np.float16), (4096, 64, 4096, np.float32), (6, 24, 3, np.float16),
+    (4 * 1024, 64, 1024, np.float16),
+]
+
+
+@pytest.mark.parametrize("rows,cols,rps,dt", CASES)
+def test_quantize_matches_oracle(lib, rows, cols, rps, dt):
+    log("quantize rows=%d cols=%d rps=%d %s" % (rows, cols, rps, np.dtype(dt).name))
+    r = _rng(rows * 31 + cols)
+    x = (r.standard_normal((rows, cols)) * r.uniform(0.01, 30)).astype(dt)
+    if rows > 2:
+        x[1] = 0                      # an all-zero row
+    quantize_both(lib, x, rps)
+
+
+def test_quantize_ties_and_integers(lib):
+    r = _rng(5)
+    x = r.integers(-127, 128, size=(64, 64)).astype(np.float32)
+    x[:, 0] = 127.0
+    x[::2, 1:9] += 0.5                # exact half-way cases (scale 1)
+    x = np.clip(x, -127, 127)
+    q, s, _, _ = quantize_both(lib, x, 1)
+    assert np.all(s == 1.0)
+    x2 = (r.integers(-254, 255, size=(32, 128)) / 2.0).astype(np.float16)
+    quantize_both(lib, x2, 1)
+    quantize_both(lib, x2, 32)
+
+
+def test_quantize_all_zero_tensor(lib):
+    x = np.zeros((16, 128), np.float16)
+    q, s, _, _ = quantize_both(lib, x, 16)
+    assert np.all(q == 0) and np.all(s == 0)
