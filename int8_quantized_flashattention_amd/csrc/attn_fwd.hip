@@ -99,7 +99,10 @@ struct Smem {
   float st;
 };
 
-template <int D, bool VPT>
+// Stages the K tile (and, unless LOGITS_ONLY, the V^T tile and the per-key
+// scales). The logits-only variant is given no V or scale pointers and must
+// not touch them.
+template <int D, bool VPT, bool LOGITS_ONLY>
 __device__ __forceinline__ void stage_tile(Smem& sm, const FwdArgs& a, int64_t kv_base, int k0) {
   using G = Geo<D>;
   const int tid = threadIdx.x;
@@ -115,6 +118,7 @@ __device__ __forceinline__ void stage_tile(Smem& sm, const FwdArgs& a, int64_t k
       val = *reinterpret_cast<const v4i*>(a.k + (kv_base + k0 + row) * D + cc * 16);
     *reinterpret_cast<v4i*>(sm.k + row * G::KSTR + cc * 16) = val;
   }
+  if constexpr (LOGITS_ONLY) return;
   // V: lanes run along the head dim (4 channels each), 4 keys per lane,
   // transposed in registers and written as V^T.
   constexpr int kNDQ = D / 4;                        // channel quads
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     qf[c] = v4i{0, 0, 0, 0};
     if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
   }
-  const float sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
+  const float sq = (qvalid && !DUMP) ? a.s_q[q_base + qi] : 0.0f;
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
   const float c2 = sq * inv_sqrt_d * kLog2e;          // base-2 logit per unit of S_int * s_K
   const int lim = CAUSAL ? qi + shift : a.Lkv - 1;  // last visible key of this row
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * BN;
     __syncthreads();                 // previous tile fully consumed
-    stage_tile<D, VPT>(sm, a, kv_base, k0);
+    stage_tile<D, VPT, DUMP>(sm, a, kv_base, k0);
     __syncthreads();
     if (!wave_live || k0 > wave_lim) continue;   // every key of the tile is masked for this wave
 

@@ -1,0 +1,98 @@
+// Runs libattn_int8's C ABI on the CPU emulation of HIP (test infrastructure).
+// Every "device" buffer is a host allocation of exactly the size the ABI
+// documents, so AddressSanitizer reports any access outside it.
+//
+//   emu_driver quant  x.bin dt n_rows n_cols rps  q.out s.out
+//   emu_driver fwd    q.bin sq.bin k.bin sk.bin v.bin sv.bin vmode odt
+//                     B H Hkv Lq Lkv d causal  o.out lse.out
+//   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "attn_int8.h"
+
+namespace {
+
+void* read_file(const char* path, size_t expect) {
+  FILE* f = std::fopen(path, "rb");
+  if (!f) { std::fprintf(stderr, "cannot open %s\n", path); std::exit(3); }
+  void* q = std::malloc(expect ? expect : 1);   // exact size, so ASan sees overruns
+  if (std::fread(q, 1, expect, f) != expect) { std::fprintf(stderr, "short read %s\n", path); std::exit(3); }
+  std::fclose(f);
+  return q;
+}
+
+void write_file(const char* path, const void* p, size_t n) {
+  FILE* f = std::fopen(path, "wb");
+  std::fwrite(p, 1, n, f);
+  std::fclose(f);
+}
+
+// malloc'd memory is 16-byte aligned on glibc x86-64; the ABI wants 16 bytes
+// for tensors, which the exact-size allocation satisfies.
+void* alloc(size_t n) { return std::malloc(n ? n : 1); }
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc < 2) return 2;
+  const std::string mode = argv[1];
+  attn_status st;
+  if (mode == "quant" && argc == 9) {
+    const int dt = std::atoi(argv[3]);
+    const int64_t n_rows = std::atoll(argv[4]);
+    const int32_t n_cols = std::atoi(argv[5]);
+    const int64_t rps = std::atoll(argv[6]);
+    const size_t esz = dt == ATTN_F16 ? 2 : 4;
+    void* x = read_file(argv[2], n_rows * n_cols * esz);
+    int8_t* q = static_cast<int8_t*>(alloc(n_rows * n_cols));
+    float* s = static_cast<float*>(alloc(sizeof(float) * (n_rows / rps)));
+    st = attn_quantize_rows(x, static_cast<attn_dtype>(dt), n_rows, n_cols, rps, q, s, nullptr);
+    write_file(argv[7], q, n_rows * n_cols);
+    write_file(argv[8], s, sizeof(float) * (n_rows / rps));
+  } else if (mode == "fwd" && argc == 19) {
+    const int vmode = std::atoi(argv[8]), odt = std::atoi(argv[9]);
+    const int B = std::atoi(argv[10]), H = std::atoi(argv[11]), Hkv = std::atoi(argv[12]);
+    const int Lq = std::atoi(argv[13]), Lkv = std::atoi(argv[14]), d = std::atoi(argv[15]);
+    const int causal = std::atoi(argv[16]);
+    const size_t nq = size_t(B) * H * Lq, nk = size_t(B) * Hkv * Lkv;
+    auto* q = static_cast<int8_t*>(read_file(argv[2], nq * d));
+    auto* sq = static_cast<float*>(read_file(argv[3], nq * 4));
+    auto* k = static_cast<int8_t*>(read_file(argv[4], nk * d));
+    auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
+    auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode ? nk : 1) * 4));
+    const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
+    void* o = alloc(osz);
+    float* lse = static_cast<float*>(alloc(nq * 4));
+    const size_t ws_n = attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
+    void* ws = ws_n ? std::aligned_alloc(256, (ws_n + 255) / 256 * 256) : nullptr;
+    st = attn_int8_fwd(q, sq, k, sk, v, sv, static_cast<attn_vscale>(vmode), o,
+                       static_cast<attn_dtype>(odt), lse, B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n,
+                       nullptr);
+    write_file(argv[17], o, osz);
+    write_file(argv[18], lse, nq * 4);
+  } else if (mode == "logits" && argc == 12) {
+    const int B = std::atoi(argv[4]), H = std::atoi(argv[5]), Hkv = std::atoi(argv[6]);
+    const int Lq = std::atoi(argv[7]), Lkv = std::atoi(argv[8]), d = std::atoi(argv[9]);
+    const int causal = std::atoi(argv[10]);
+    const size_t nq = size_t(B) * H * Lq, nk = size_t(B) * Hkv * Lkv;
+    auto* q = static_cast<int8_t*>(read_file(argv[2], nq * d));
+    auto* k = static_cast<int8_t*>(read_file(argv[3], nk * d));
+    auto* s = static_cast<int32_t*>(alloc(nq * Lkv * 4));
+    for (size_t i = 0; i < nq * Lkv; ++i) s[i] = INT32_MIN;
+    st = attn_int8_debug_logits(q, k, B, H, Hkv, Lq, Lkv, d, causal, s, nullptr);
+    write_file(argv[11], s, nq * Lkv * 4);
+  } else {
+    std::fprintf(stderr, "bad arguments\n");
+    return 2;
+  }
+  if (st != ATTN_OK) {
+    std::fprintf(stderr, "status %d: %s\n", st, attn_status_str(st));
+    return 4;
+  }
+  return 0;
+}

@@ -1,0 +1,206 @@
+// CPU stand-in for the subset of HIP that libattn_int8's sources use.
+//
+// TEST INFRASTRUCTURE: the unchanged kernel sources are compiled for the host
+// against this header (it sits first on the include path) and run on small
+// problems under AddressSanitizer/UBSan, so that an out-of-bounds or
+// misaligned access shows up on the CPU, with a stack trace, instead of as a
+// GPU memory fault. Every lane is a host thread; __syncthreads is a block-wide
+// barrier; cross-lane operations (shuffles, MFMA) exchange operands through a
+// per-wavefront buffer between two wavefront barriers. Blocks run one after
+// another, so a function-local __shared__ variable (made static here) behaves
+// as the block's LDS.
+//
+// The MFMA operand/result layouts encoded below are the documented CDNA ones
+// (32x32: result element (i, j) in lane j + 32 * ((i / 4) % 2), register
+// (i % 4) + 4 * (i / 8); 16x16: lane j + 16 * (i / 4), register i % 4;
+// operand element (row r, k) in lane r + (lanes per block) * (k / kpl), byte
+// k % kpl with kpl int8 values per lane). The GPU parity tests check them on
+// the hardware.
+#pragma once
+
+#include <algorithm>
+#include <barrier>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <memory>
+#include <thread>
+#include <type_traits>
+#include <vector>
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __launch_bounds__(...)
+#define __shared__ static
+
+typedef int hipError_t;
+enum { hipSuccess = 0, hipErrorNotSupported = 801 };
+typedef struct ihipStream_t* hipStream_t;
+inline hipError_t hipGetLastError() { return hipSuccess; }
+
+struct dim3 {
+  unsigned x, y, z;
+  dim3(unsigned x_ = 1, unsigned y_ = 1, unsigned z_ = 1) : x(x_), y(y_), z(z_) {}
+};
+struct emu_uint3 { unsigned x, y, z; };
+
+struct alignas(8) float2 { float x, y; };
+struct alignas(16) float4 { float x, y, z, w; };
+struct alignas(8) uint2 { unsigned x, y; };
+struct alignas(16) uint4 { unsigned x, y, z, w; };
+inline float4 make_float4(float a, float b, float c, float d) { return {a, b, c, d}; }
+inline uint2 make_uint2(unsigned a, unsigned b) { return {a, b}; }
+
+namespace emu {
+
+struct Wave {
+  explicit Wave(int n) : bar(n) {}
+  std::barrier<> bar;
+  alignas(16) unsigned char slot[64][64];
+};
+
+struct Ctx {
+  emu_uint3 tid, bid;
+  Wave* wave;
+  int lane;
+};
+inline thread_local Ctx ctx;
+inline dim3 g_grid, g_block;
+inline std::barrier<>* g_block_bar = nullptr;
+
+template <class F>
+void launch(dim3 grid, dim3 block, F&& body) {
+  g_grid = grid;
+  g_block = block;
+  const int nthreads = static_cast<int>(block.x * block.y * block.z);
+  const int nwaves = (nthreads + 63) / 64;
+  for (unsigned bz = 0; bz < grid.z; ++bz)
+    for (unsigned by = 0; by < grid.y; ++by)
+      for (unsigned bx = 0; bx < grid.x; ++bx) {
+        std::barrier<> bbar(nthreads);
+        g_block_bar = &bbar;
+        std::vector<std::unique_ptr<Wave>> waves;
+        for (int w = 0; w < nwaves; ++w)
+          waves.emplace_back(new Wave(std::min(64, nthreads - 64 * w)));
+        std::vector<std::thread> th;
+        th.reserve(nthreads);
+        for (int t = 0; t < nthreads; ++t) {
+          th.emplace_back([&, t]() {
+            ctx.tid = {static_cast<unsigned>(t % block.x), static_cast<unsigned>((t / block.x) % block.y),
+                       static_cast<unsigned>(t / (block.x * block.y))};
+            ctx.bid = {bx, by, bz};
+            ctx.wave = waves[t / 64].get();
+            ctx.lane = t % 64;
+            body();
+            ctx.wave->bar.arrive_and_drop();
+            g_block_bar->arrive_and_drop();
+          });
+        }
+        for (auto& x : th) x.join();
+        g_block_bar = nullptr;
+      }
+}
+
+inline void syncthreads() { g_block_bar->arrive_and_wait(); }
+
+template <class T>
+T shfl_xor(T v, int mask, int width = 64) {
+  static_assert(sizeof(T) <= 64, "exchange slot too small");
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  int src = self ^ mask;
+  if (src >= ((self + width) & ~(width - 1))) src = self;
+  std::memcpy(w.slot[self], &v, sizeof(T));
+  w.bar.arrive_and_wait();
+  T r;
+  std::memcpy(&r, w.slot[src], sizeof(T));
+  w.bar.arrive_and_wait();
+  return r;
+}
+
+// result[i][j] += sum_k A[i][k] B[k][j] for int8 operands (kpl bytes per lane)
+template <int M, class VA, class VC>
+VC mfma_i8(VA a, VA b, VC c) {
+  static_assert(sizeof(VA) == 16, "16 int8 per lane");
+  constexpr int kpl = 16;
+  constexpr int K = 64 / M * kpl;          // 32 for 32x32, 64 for 16x16
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  std::memcpy(w.slot[self], &a, 16);
+  std::memcpy(w.slot[self] + 16, &b, 16);
+  w.bar.arrive_and_wait();
+  VC d = c;
+  constexpr int NREG = sizeof(VC) / 4;
+  for (int v = 0; v < NREG; ++v) {
+    int i, j;
+    if constexpr (M == 32) {
+      j = self % 32;
+      i = (v / 4) * 8 + (self / 32) * 4 + v % 4;
+    } else {
+      j = self % 16;
+      i = (self / 16) * 4 + v;
+    }
+    int32_t acc = d[v];
+    for (int k = 0; k < K; ++k) {
+      const int la = i + M * (k / kpl), lb = j + M * (k / kpl);
+      acc += static_cast<int32_t>(static_cast<int8_t>(w.slot[la][k % kpl])) *
+             static_cast<int32_t>(static_cast<int8_t>(w.slot[lb][16 + k % kpl]));
+    }
+    d[v] = acc;
+  }
+  w.bar.arrive_and_wait();
+  return d;
+}
+
+// v_perm_b32: bytes 0-3 of the 64-bit source are src1, bytes 4-7 src0.
+inline uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  const uint64_t src = (static_cast<uint64_t>(s0) << 32) | s1;
+  uint32_t out = 0;
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t s = (sel >> (8 * b)) & 0xffu;
+    uint32_t byte;
+    if (s < 8) byte = (src >> (8 * s)) & 0xffu;
+    else if (s < 12) byte = ((src >> (8 * (2 * (s - 8) + 1))) & 0x80u) ? 0xffu : 0u;
+    else if (s == 12) byte = 0u;
+    else byte = 0xffu;
+    out |= byte << (8 * b);
+  }
+  return out;
+}
+
+inline float bits_to_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
+inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+
+}  // namespace emu
+
+#define threadIdx (emu::ctx.tid)
+#define blockIdx (emu::ctx.bid)
+#define gridDim (emu::g_grid)
+#define blockDim (emu::g_block)
+#define __syncthreads() emu::syncthreads()
+#define __shfl_xor(...) emu::shfl_xor(__VA_ARGS__)
+#define __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, x, y, z) emu::mfma_i8<32>(a, b, c)
+#define __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, x, y, z) emu::mfma_i8<16>(a, b, c)
+#define __builtin_amdgcn_perm(a, b, s) emu::perm(a, b, s)
+#define __builtin_amdgcn_exp2f(x) std::exp2(static_cast<float>(x))
+#define hipLaunchKernelGGL(K, G, B, S, ST, ...) emu::launch(G, B, [&]() { K(__VA_ARGS__); })
+
+using std::max;
+using std::min;
+
+inline float __fmul_rn(float a, float b) { return a * b; }   // built with -ffp-contract=off
+inline float __fdiv_rn(float a, float b) { return a / b; }
+inline float __uint_as_float(uint32_t u) { return emu::bits_to_float(u); }
+inline uint32_t __float_as_uint(float f) { return emu::float_to_bits(f); }
+inline uint32_t atomicMax(uint32_t* p, uint32_t v) { return __atomic_fetch_max(p, v, __ATOMIC_RELAXED); }
+
+struct __half { _Float16 v; };
+struct alignas(4) __half2 { _Float16 x, y; };
+inline float2 __half22float2(__half2 h) { return {static_cast<float>(h.x), static_cast<float>(h.y)}; }
+inline __half2 __floats2half2_rn(float a, float b) {
+  return {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+}

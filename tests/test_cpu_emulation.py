@@ -1,0 +1,107 @@
+"""The library's kernels, compiled for the host against a CPU stand-in of HIP
+and run under AddressSanitizer/UBSan: no access leaves its buffer, and the
+results agree with the oracle (bit-exact codes, scales and INT32 logits; O
+within the same tolerance as on the GPU). The stand-in encodes the documented
+MFMA lane layouts; the GPU tests check those on the hardware."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.join(HERE, "cpu_emu"))
+
+import oracle  # noqa: E402
+import build_emu  # noqa: E402
+
+F16, F32 = 1, 0
+
+
+@pytest.fixture(scope="module")
+def exe():
+    return build_emu.ensure_built()
+
+
+def run(exe, tmp, args):
+    r = subprocess.run([exe] + [str(a) for a in args], capture_output=True, text=True, timeout=600,
+                       env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"))
+    assert r.returncode == 0, r.stderr[-4000:]
+
+
+def put(tmp, name, a):
+    p = os.path.join(str(tmp), name)
+    np.ascontiguousarray(a).tofile(p)
+    return p
+
+
+def emu_quantize(exe, tmp, x, rps):
+    n_cols = x.shape[-1]
+    n_rows = x.size // n_cols
+    qo, so = os.path.join(str(tmp), "q.out"), os.path.join(str(tmp), "s.out")
+    run(exe, tmp, ["quant", put(tmp, "x.bin", x), F16 if x.dtype == np.float16 else F32, n_rows, n_cols,
+                   rps, qo, so])
+    return np.fromfile(qo, np.int8).reshape(x.shape), np.fromfile(so, np.float32)
+
+
+@pytest.mark.parametrize("rows,cols,rps,dt", [
+    (7, 64, 1, np.float16), (257, 64, 1, np.float32), (33, 256, 1, np.float16), (12, 128, 4, np.float32),
+    (100, 128, 10, np.float16), (3, 2048, 1, np.float16), (64, 128, 64, np.float16), (6, 24, 3, np.float16),
+])
+def test_emulated_quantize(exe, tmp_path, rows, cols, rps, dt):
+    r = np.random.Generator(np.random.PCG64(rows + cols))
+    x = (r.standard_normal((rows, cols)) * 5).astype(dt)
+    x[min(1, rows - 1)] = 0
+    q, s = emu_quantize(exe, tmp_path, x, rps)
+    qo, so = oracle.quantize_rows(x, rps)
+    assert np.array_equal(q, qo) and np.array_equal(s.view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal", [
+    (1, 1, 1, 128, 128, 64, 0), (2, 4, 2, 77, 130, 128, 1), (1, 2, 1, 1, 200, 128, 0),
+    (1, 2, 2, 50, 190, 64, 1), (1, 1, 1, 1, 1, 64, 1), (1, 1, 1, 300, 300, 128, 1),
+])
+def test_emulated_logits(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal):
+    r = np.random.Generator(np.random.PCG64(Lq * 3 + Lkv))
+    q = r.integers(-127, 128, size=(B, H, Lq, d)).astype(np.int8)
+    k = r.integers(-127, 128, size=(B, Hkv, Lkv, d)).astype(np.int8)
+    so = os.path.join(str(tmp_path), "s.out")
+    run(exe, tmp_path, ["logits", put(tmp_path, "q.bin", q), put(tmp_path, "k.bin", k),
+                        B, H, Hkv, Lq, Lkv, d, causal, so])
+    s = np.fromfile(so, np.int32).reshape(B, H, Lq, Lkv)
+    ref = oracle.logits_i32(q, k, B, H, Hkv, Lq, Lkv, d)
+    vis = np.ones((Lq, Lkv), bool)
+    if causal:
+        vis = np.arange(Lkv)[None, :] <= (np.arange(Lq)[:, None] + (Lkv - Lq))
+    vis = np.broadcast_to(vis, s.shape)
+    assert np.array_equal(s[vis], ref[vis])
+    assert np.all(s[~vis] == np.iinfo(np.int32).min)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt", [
+    (1, 1, 1, 128, 128, 64, 0, 0, F32), (2, 4, 2, 77, 130, 128, 1, 0, F16),
+    (1, 2, 1, 1, 200, 128, 0, 1, F32), (1, 3, 3, 300, 300, 64, 1, 1, F32),
+    (3, 8, 1, 129, 65, 128, 0, 0, F16), (1, 1, 1, 1, 1, 64, 1, 1, F16),
+    (1, 2, 2, 130, 257, 128, 1, 1, F32), (1, 4, 1, 3, 333, 64, 0, 1, F32),
+])
+def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt):
+    r = np.random.Generator(np.random.PCG64(B * 100 + Lq * 7 + Lkv))
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
+    k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    qh, sq = oracle.quantize_rows(q, 1)
+    kh, sk = oracle.quantize_rows(k, 1)
+    vh, sv = oracle.quantize_rows(v, 1 if vpt else v.size // d)
+    oo_p, lo_p = os.path.join(str(tmp_path), "o.out"), os.path.join(str(tmp_path), "l.out")
+    files = [put(tmp_path, n + ".bin", a) for n, a in
+             (("q", qh), ("sq", sq), ("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
+    run(exe, tmp_path, ["fwd", *files, vpt, odt, B, H, Hkv, Lq, Lkv, d, causal, oo_p, lo_p])
+    o = np.fromfile(oo_p, np.float16 if odt == F16 else np.float32).astype(np.float32).reshape(B, H, Lq, d)
+    lse = np.fromfile(lo_p, np.float32).reshape(B, H, Lq)
+    import int8_quantized_flashattention_amd as m
+    tile, split = m.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, vpt, B, H, Hkv, Lq, Lkv, d, causal, tile, split)
+    err = np.abs(o - oo)
+    assert err.max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
+    assert np.abs(lse - lo).max() <= 1e-4 * max(1.0, np.abs(lo).max())
