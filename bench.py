@@ -180,7 +180,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
                    "d": d, "causal": bool(w.causal),
                    "v_scale": "per_token" if w.v_per_token else "per_tensor",
-                   "inputs": "%s N(0,1)%s" % (w.in_dtype, ", 1%% of head-dim channels x20 in Q and K"
+                   "inputs": "%s N(0,1)%s" % (w.in_dtype, ", 1 percent of head-dim channels x20 in Q and K"
                                               if w.outlier_seed is not None else ""),
                    "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
                    "step": "attention only" if args.attn_only else
