@@ -29,6 +29,17 @@
 // operand implies, so each operand fetch is one 16-byte LDS read.
 // The output accumulator O^T keeps the query in the lane too, so the
 // per-row rescale alpha is lane-local.
+//
+// Pipeline per KV tile: the next tile's global loads are issued before the
+// current tile's math and written to the other of two LDS stages after it,
+// so there is one barrier per tile. The softmax works in base 2 with 127
+// folded into the exponent: y = exp2(u c2 - m + log2 127) = 127 P_tilde, the
+// row sum accumulates y, and v_cvt_pk_u8_f32 (round to nearest even,
+// saturating) turns y into P_hat and packs it into the operand in one step.
+// For per-tensor V the P_hat . V_hat products keep accumulating in the INT32
+// MFMA accumulator while no row of the wavefront raises its max (alpha = 1),
+// and are converted to fp32 (and the older fp32 part rescaled) only when one
+// does; s_V is applied once in the epilogue.
 #include "attn_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -44,9 +55,6 @@ constexpr int BN = kPrefillBN;
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// fma(p, w, kMagic) = kMagic + rne(p * w) for 0 <= p * w < 2^22: the exact
-// product is rounded once at unit spacing, ties to even (kMagic is even).
-constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D>
@@ -76,13 +84,6 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
   c[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-// Byte 0 of a, b, c, d packed into one dword (a lowest).
-__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
-  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
 // Position of tile-local key j inside a V^T LDS row: the 16 keys that one lane
 // half (g) contributes to a 32-key MFMA step are stored contiguously, in the
 // order of that lane's logit accumulators.
@@ -91,72 +92,200 @@ __device__ __forceinline__ int vt_pos(int j) {
   return kb * 32 + ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }
 
+// One LDS stage of a KV tile. Two of them alternate: while the wavefronts
+// compute on one, the next tile (already loaded into registers) is written to
+// the other.
+struct Stage {
+  alignas(16) int8_t k[BN * (128 + 16)];   // K rows, padded
+  alignas(16) int8_t vt[128 * (BN + 16)];  // V^T rows (one per channel), padded
+  alignas(16) float sk[BN];                // s_K of the tile's keys
+  alignas(16) float wr[BN];                // per-token V: s_V[j] / s_t
+  float st;                                // per-token V: s_t, the largest s_V of the tile
+};
 struct Smem {
-  alignas(16) int8_t k[BN * (128 + 16)];
-  alignas(16) int8_t vt[128 * (BN + 16)];
-  alignas(16) float sk[BN];
-  alignas(16) float w[BN];
-  float st;
+  Stage stage[2];
 };
 
-// Stages the K tile (and, unless LOGITS_ONLY, the V^T tile and the per-key
-// scales). The logits-only variant is given no V or scale pointers and must
-// not touch them.
+// The next tile held in registers between its global loads and its LDS store.
+template <int D>
+struct TileRegs {
+  static constexpr int kCPR = D / 16;                 // 16-byte chunks per K row
+  static constexpr int kKIters = BN * kCPR / kThreads;
+  static constexpr int kNDQ = D / 4;                  // channel quads
+  static constexpr int kKQPerIter = kThreads / kNDQ;  // key quads per pass
+  static constexpr int kVIters = (BN / 4) / kKQPerIter;
+  v4i k[kKIters];
+  uint32_t v[kVIters][4];
+  float sk;
+  float sv;
+};
+
+// Global loads of tile k0 (out-of-range keys read as zero). The logits-only
+// variant is given no V or scale pointers and must not touch them.
 template <int D, bool VPT, bool LOGITS_ONLY>
-__device__ __forceinline__ void stage_tile(Smem& sm, const FwdArgs& a, int64_t kv_base, int k0) {
-  using G = Geo<D>;
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const FwdArgs& a, int64_t kv_base, int k0) {
+  using R = TileRegs<D>;
   const int tid = threadIdx.x;
-  // K rows: 16-byte chunks, coalesced along the row.
-  constexpr int kCPR = D / 16;                       // chunks per row
-  constexpr int kKIters = BN * kCPR / kThreads;
 #pragma unroll
-  for (int it = 0; it < kKIters; ++it) {
+  for (int it = 0; it < R::kKIters; ++it) {
     const int id = tid + it * kThreads;
-    const int row = id / kCPR, cc = id % kCPR;
-    v4i val = {0, 0, 0, 0};
-    if (k0 + row < a.Lkv)
-      val = *reinterpret_cast<const v4i*>(a.k + (kv_base + k0 + row) * D + cc * 16);
-    *reinterpret_cast<v4i*>(sm.k + row * G::KSTR + cc * 16) = val;
+    const int row = id / R::kCPR, cc = id % R::kCPR;
+    r.k[it] = v4i{0, 0, 0, 0};
+    if (k0 + row < a.Lkv) r.k[it] = *reinterpret_cast<const v4i*>(a.k + (kv_base + k0 + row) * D + cc * 16);
   }
   if constexpr (LOGITS_ONLY) return;
-  // V: lanes run along the head dim (4 channels each), 4 keys per lane,
-  // transposed in registers and written as V^T.
-  constexpr int kNDQ = D / 4;                        // channel quads
-  constexpr int kKQPerIter = kThreads / kNDQ;        // key quads per pass
-  constexpr int kVIters = (BN / 4) / kKQPerIter;
-  const int dq = tid % kNDQ;
+  const int dq = tid % R::kNDQ;
 #pragma unroll
-  for (int it = 0; it < kVIters; ++it) {
-    const int kq = tid / kNDQ + it * kKQPerIter;
-    uint32_t r[4], c[4];
+  for (int it = 0; it < R::kVIters; ++it) {
+    const int kq = tid / R::kNDQ + it * R::kKQPerIter;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = k0 + kq * 4 + i;
-      r[i] = (key < a.Lkv)
-                 ? *reinterpret_cast<const uint32_t*>(a.v + (kv_base + key) * D + dq * 4)
-                 : 0u;
+      r.v[it][i] = (key < a.Lkv) ? *reinterpret_cast<const uint32_t*>(a.v + (kv_base + key) * D + dq * 4) : 0u;
     }
-    transpose4x4(r, c);
-    const int pos = vt_pos(kq * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint32_t*>(sm.vt + (dq * 4 + j) * G::VSTR + pos) = c[j];
   }
-  // per-key logit scales, and for per-token V the tile scale and multipliers
+  r.sk = 0.0f;
+  r.sv = 0.0f;
   if (tid < BN) {
-    const int key = k0 + tid;
-    sm.sk[tid] = (key < a.Lkv) ? a.s_k[kv_base + key] : 0.0f;
+    if (k0 + tid < a.Lkv) r.sk = a.s_k[kv_base + k0 + tid];
   } else if (VPT && tid < 2 * BN) {
-    const int j = tid - BN;
-    const int key = k0 + j;
-    const float sv = (key < a.Lkv) ? a.s_v[kv_base + key] : 0.0f;
-    float st = sv;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) st = fmaxf(st, __shfl_xor(st, off, 64));
-    sm.w[j] = (st > 0.0f) ? __fdiv_rn(127.0f * sv, st) : 0.0f;
-    if (j == 0) sm.st = st;
+    if (k0 + tid - BN < a.Lkv) r.sv = a.s_v[kv_base + k0 + tid - BN];
   }
 }
+
+// LDS store of a tile held in registers: K rows as they are, V transposed
+// into V^T in the key order of the P operand, the per-key scales, and for
+// per-token V the tile scale s_t and the ratios s_V[j] / s_t.
+template <int D, bool VPT, bool LOGITS_ONLY>
+__device__ __forceinline__ void store_tile(Stage& sg, const TileRegs<D>& r) {
+  using R = TileRegs<D>;
+  using G = Geo<D>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < R::kKIters; ++it) {
+    const int id = tid + it * kThreads;
+    const int row = id / R::kCPR, cc = id % R::kCPR;
+    *reinterpret_cast<v4i*>(sg.k + row * G::KSTR + cc * 16) = r.k[it];
+  }
+  if constexpr (LOGITS_ONLY) return;
+  const int dq = tid % R::kNDQ;
+#pragma unroll
+  for (int it = 0; it < R::kVIters; ++it) {
+    const int kq = tid / R::kNDQ + it * R::kKQPerIter;
+    uint32_t c[4];
+    transpose4x4(r.v[it], c);
+    const int pos = vt_pos(kq * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(sg.vt + (dq * 4 + j) * G::VSTR + pos) = c[j];
+  }
+  if (tid < BN) {
+    sg.sk[tid] = r.sk;
+  } else if (VPT && tid < 2 * BN) {
+    // one wavefront (threads BN..2BN-1) reduces the tile's largest V scale
+    float st = r.sv;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) st = fmaxf(st, __shfl_xor(st, off, 64));
+    sg.wr[tid - BN] = (st > 0.0f) ? __fdiv_rn(r.sv, st) : 0.0f;
+    if (tid == BN) sg.st = st;
+  }
+}
+
+// max / sum of a value over the lane pair (l, l ^ 32) that holds one query
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// INT8 P_hat . V_hat for one tile: acc[c] (+)= sum over the 32-key blocks.
+template <int D, bool FROM_ZERO>
+__device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const Stage& sg, const v4i (&pv)[BN / 32], int lr, int g) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int c = 0; c < G::NC; ++c) {
+    v16i t = FROM_ZERO ? v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0} : acc[c];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      const v4i va = *reinterpret_cast<const v4i*>(sg.vt + (c * 32 + lr) * G::VSTR + kb * 32 + g * 16);
+      t = mfma_i8(va, pv[kb], t);
+    }
+    acc[c] = t;
+  }
+}
+
+// u = S_int * s_K[j] for this lane's keys of the tile (the query's factor c2
+// is applied later); masked keys get -inf. Returns the lane's max of u.
+template <int D, bool MASK>
+__device__ __forceinline__ float dequant_tile(const v16i (&s)[BN / 32], const Stage& sg, float (&u)[BN / 32][16],
+                                              int k0, int lim, int Lkv, int g) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int jl = kb * 32 + j4 * 8 + g * 4;
+      const float4 skv = *reinterpret_cast<const float4*>(sg.sk + jl);
+      const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = static_cast<float>(s[kb][j4 * 4 + e]) * skk[e];
+        if constexpr (MASK) {
+          const int key = k0 + jl + e;
+          x = (key < Lkv && key <= lim) ? x : kNegInf;
+        }
+        u[kb][j4 * 4 + e] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+  return mx;
+}
+
+// y = exp2(u c2 - bias) = 127 P_tilde; returns the lane's sum of y and packs
+// P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV operands.
+// CLAMP: when the running max is so large (|m| >= 2^15 in base-2 units) that
+// the fp32 rounding of the exponent argument could push the max key's y past
+// 127.5, y is clamped to 127 (the value the max key has exactly).
+template <bool VPT, bool MASK, bool CLAMP>
+__device__ __forceinline__ float probs_tile(const float (&u)[BN / 32][16], float c2, float bias, const Stage& sg,
+                                            v4i (&pv)[BN / 32], int g) {
+  float lsum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; ++kb) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (VPT) {
+        const float4 wv = *reinterpret_cast<const float4*>(sg.wr + kb * 32 + j4 * 8 + g * 4);
+        wr[0] = wv.x; wr[1] = wv.y; wr[2] = wv.z; wr[3] = wv.w;
+      }
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float uu = u[kb][j4 * 4 + e];
+        float y = exp2_hw(__builtin_fmaf(uu, c2, -bias));
+        if constexpr (MASK) y = (uu == kNegInf) ? 0.0f : y;
+        if constexpr (CLAMP) y = fminf(y, 127.0f);
+        lsum += y;
+        word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y * wr[e] : y, e, word);
+      }
+      pw[j4] = word;
+    }
+    pv[kb] = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]), static_cast<int>(pw[3])};
+  }
+  return lsum;
+}
+
+constexpr float kLog2_127 = 6.988684686772166f;
+// the INT32 run of P_hat . V_hat is converted to fp32 at least every this many
+// tiles, keeping |sum| <= 127 * 127 * keys below 2^31
+constexpr int kMaxIntTiles = 32768 / BN;
+// re-base the fp32 accumulator when the running max has grown by this much
+// (base 2) since its frame was set
+constexpr float kRebase = 60.0f;
 
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool DUMP>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
@@ -190,135 +319,156 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const float sq = (qvalid && !DUMP) ? a.s_q[q_base + qi] : 0.0f;
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
   const float c2 = sq * inv_sqrt_d * kLog2e;          // base-2 logit per unit of S_int * s_K
-  const int lim = CAUSAL ? qi + shift : a.Lkv - 1;  // last visible key of this row
-  const int wave_lim = CAUSAL ? min(qw0 + 31, a.Lq - 1) + shift : a.Lkv - 1;
+  const int lim = CAUSAL ? qi + shift : a.Lkv - 1;    // last visible key of this row
+  const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;                        // smallest in the wave
+  const int lim_last = CAUSAL ? min(qw0 + 31, a.Lq - 1) + shift : a.Lkv - 1;     // largest in the wave
 
   const int last_q = min(rb * BM + BM - 1, a.Lq - 1);
   const int kv_end = CAUSAL ? min(a.Lkv, last_q + shift + 1) : a.Lkv;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
+  // running max (base 2), partial row sum of 127 * P_tilde over this lane's keys
   float m = kNegInf, l = 0.0f;
-  float acc[G::NC][16];
+  float acc[G::NC][16];                // fp32 output accumulator (O^T, query in the lane)
+  v16i acc_i[G::NC];                   // INT32 run of P_hat . V_hat since the last conversion
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c)
+  for (int c = 0; c < G::NC; ++c) {
+    acc_i[c] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  }
+  int int_tiles = 0;
+  float m_f = kNegInf;                 // frame of acc (per-tensor V)
+
+  TileRegs<D> nx;
+  load_tile<D, VPT, DUMP>(nx, a, kv_base, 0);
+  store_tile<D, VPT, DUMP>(sm.stage[0], nx);
+  __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * BN;
-    __syncthreads();                 // previous tile fully consumed
-    stage_tile<D, VPT, DUMP>(sm, a, kv_base, k0);
-    __syncthreads();
-    if (!wave_live || k0 > wave_lim) continue;   // every key of the tile is masked for this wave
+    const Stage& sg = sm.stage[t & 1];
+    const bool more = t + 1 < n_tiles;
+    if (more) load_tile<D, VPT, DUMP>(nx, a, kv_base, k0 + BN);   // in flight during compute
 
-    // ---- S^T = K_hat . Q_hat^T for the two 32-key blocks (exact INT32) ----
-    v16i s[2];
+    if (wave_live && k0 <= lim_last) {
+      // ---- S^T = K_hat . Q_hat^T, exact INT32, 32 keys per block ----
+      v16i s[BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        s[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int c = 0; c < G::NC; ++c) {
-        const v4i ka = *reinterpret_cast<const v4i*>(sm.k + (kb * 32 + lr) * G::KSTR + c * 32 + g * 16);
-        s[kb] = mfma_i8(ka, qf[c], s[kb]);
-      }
-    }
-
-    if constexpr (DUMP) {
-      if (qvalid) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-            if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
-          }
-      }
-      continue;
-    }
-
-    // ---- dequantize + mask: u = S_int * s_K[j] (the row factor is c2) ----
-    float u[2][16];
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int jl = kb * 32 + j4 * 8 + g * 4;
-        const float4 skv = *reinterpret_cast<const float4*>(sm.sk + jl);
-        const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + jl + e;
-          const float x = static_cast<float>(s[kb][j4 * 4 + e]) * skk[e];
-          const bool vis = key < a.Lkv && key <= lim;
-          u[kb][j4 * 4 + e] = vis ? x : kNegInf;
-          mx = fmaxf(mx, u[kb][j4 * 4 + e]);
+        for (int c = 0; c < G::NC; ++c) {
+          const v4i ka = *reinterpret_cast<const v4i*>(sg.k + (kb * 32 + lr) * G::KSTR + c * 32 + g * 16);
+          s[kb] = mfma_i8(ka, qf[c], s[kb]);
         }
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // c2 >= 0, so max(u) * c2 == max(u * c2) under monotone rounding
-    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;
-    const float m_new = fmaxf(m, mx2);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = exp2_hw(m - m_use);           // 0 on the first visible tile
 
-    // ---- probabilities, row sum, INT8 quantization into MFMA operands ----
-    float lsum = 0.0f;
-    v4i pv[2];
+      if constexpr (DUMP) {
+        if (qvalid) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint32_t pw[4];
+          for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        float wk[4] = {127.0f, 127.0f, 127.0f, 127.0f};
+            for (int v = 0; v < 16; ++v) {
+              const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+              if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
+            }
+        }
+      } else {
+        // ---- dequantize (u = S_int * s_K[j]; the row factor is c2), mask ----
+        const bool need_mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
+        float u[BN / 32][16];
+        float mx = need_mask ? dequant_tile<D, true>(s, sg, u, k0, lim, a.Lkv, g)
+                             : dequant_tile<D, false>(s, sg, u, k0, lim, a.Lkv, g);
+        mx = pair_max(mx);
+        // c2 >= 0, so max(u) * c2 == max(u * c2) under monotone rounding
+        const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;
+        const float m_new = fmaxf(m, mx2);
+        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+        const float alpha = exp2_hw(m - m_use);        // 1 if unchanged, 0 on the first tile
+        const float bias = m_use - kLog2_127;          // exp2(u c2 - bias) = 127 P_tilde
+
+        // ---- 127 P_tilde, row sum, P_hat = rne(127 P_tilde) packed as MFMA operands ----
+        v4i pv[BN / 32];
+        const bool clamp = __any(fabsf(m_use) >= 32768.0f);
+        float lsum;
+        if (clamp)
+          lsum = need_mask ? probs_tile<VPT, true, true>(u, c2, bias, sg, pv, g)
+                           : probs_tile<VPT, false, true>(u, c2, bias, sg, pv, g);
+        else
+          lsum = need_mask ? probs_tile<VPT, true, false>(u, c2, bias, sg, pv, g)
+                           : probs_tile<VPT, false, false>(u, c2, bias, sg, pv, g);
+        l = alpha * l + lsum;
+
         if constexpr (VPT) {
-          const float4 wv = *reinterpret_cast<const float4*>(sm.w + kb * 32 + j4 * 8 + g * 4);
-          wk[0] = wv.x; wk[1] = wv.y; wk[2] = wv.z; wk[3] = wv.w;
-        }
-        uint32_t bits[4];
+          // per-token V: the tile scale s_t changes per tile, so convert every tile
+          v16i tv[G::NC];
+          pv_tile<D, true>(tv, sg, pv, lr, g);
+          const float st = sg.st;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float uu = u[kb][j4 * 4 + e];
-          const float p = (uu == kNegInf) ? 0.0f : exp2_hw(__builtin_fmaf(uu, c2, -m_use));
-          lsum += p;
-          bits[e] = __float_as_uint(__builtin_fmaf(p, wk[e], kMagic));
+          for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[c][v] = alpha * acc[c][v] + st * static_cast<float>(tv[c][v]);
+        } else {
+          // per-tensor V: keep summing P_hat . V_hat in INT32 while no row of
+          // the wavefront moves its max (alpha == 1 for all); convert to fp32
+          // when one does (same sums, fp32 rounding only)
+          // acc is kept in its own frame m_f (it holds 2^(m_f - m) times the
+          // fp32 part of the total); the INT32 run is in the frame of m, the
+          // max before this tile, and is folded in with one factor per lane.
+          const bool flush = __any(m_new > m) || int_tiles >= kMaxIntTiles;
+          if (flush) {
+            if (m_f == kNegInf) m_f = m_use;
+            float fold = exp2_hw(m - m_f);               // 0 before the first tile
+            if (__any(m_use - m_f > kRebase)) {          // keep acc far from overflow
+              const float r = exp2_hw(m_f - m_use);
+#pragma unroll
+              for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[c][v] *= r;
+              fold *= r;
+              m_f = m_use;
+            }
+#pragma unroll
+            for (int c = 0; c < G::NC; ++c) {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(fold, static_cast<float>(acc_i[c][v]), acc[c][v]);
+              acc_i[c] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            }
+            int_tiles = 0;
+          }
+          pv_tile<D, false>(acc_i, sg, pv, lr, g);
+          ++int_tiles;
         }
-        pw[j4] = pack_low_bytes(bits[0], bits[1], bits[2], bits[3]);
+        m = m_new;
       }
-      pv[kb] = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]),
-                   static_cast<int>(pw[3])};
     }
-    l = alpha * l + lsum;
-    const float st = VPT ? sm.st : a.s_v[0];
 
-    // ---- O^T += V_hat^T . P_hat^T (INT32 per tile), fp32 across tiles ----
-#pragma unroll
-    for (int c = 0; c < G::NC; ++c) {
-      v16i tacc = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v4i va = *reinterpret_cast<const v4i*>(sm.vt + (c * 32 + lr) * G::VSTR + kb * 32 + g * 16);
-        tacc = mfma_i8(va, pv[kb], tacc);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[c][v] = alpha * acc[c][v] + st * static_cast<float>(tacc[v]);
-    }
-    m = m_new;
+    if (more) store_tile<D, VPT, DUMP>(sm.stage[(t + 1) & 1], nx);
+    __syncthreads();
   }
 
   if constexpr (DUMP) return;
   if (!wave_live) return;
-  const float ltot = l + __shfl_xor(l, 32, 64);
+  if constexpr (!VPT) {
+    // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run
+    const float back = exp2_hw(m_f - m);
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(back, acc[c][v], static_cast<float>(acc_i[c][v]));
+  }
+  const float ltot = pair_sum(l);                      // 127 * l
   if (!qvalid) return;
-  const float rcp = 1.0f / (127.0f * ltot);
+  const float scale = (VPT ? 1.0f : a.s_v[0]) / ltot;
   const int64_t orow = (q_base + qi) * D;
 #pragma unroll
   for (int c = 0; c < G::NC; ++c)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = c * 32 + j4 * 8 + g * 4;
-      const float o0 = acc[c][j4 * 4 + 0] * rcp, o1 = acc[c][j4 * 4 + 1] * rcp;
-      const float o2 = acc[c][j4 * 4 + 2] * rcp, o3 = acc[c][j4 * 4 + 3] * rcp;
+      const float o0 = acc[c][j4 * 4 + 0] * scale, o1 = acc[c][j4 * 4 + 1] * scale;
+      const float o2 = acc[c][j4 * 4 + 2] * scale, o3 = acc[c][j4 * 4 + 3] * scale;
       if constexpr (OUT_F16) {
         const __half2 h01 = __floats2half2_rn(o0, o1);
         const __half2 h23 = __floats2half2_rn(o2, o3);
@@ -330,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) = make_float4(o0, o1, o2, o3);
       }
     }
-  if (a.lse && g == 0) a.lse[q_base + qi] = (m + __builtin_log2f(ltot)) * kLn2;
+  if (a.lse && g == 0) a.lse[q_base + qi] = (m + __builtin_log2f(ltot) - kLog2_127) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool DUMP>

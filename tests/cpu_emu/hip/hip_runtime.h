@@ -172,6 +172,53 @@ inline uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return out;
 }
 
+// v_permlane32_swap on (x, y) as measured on gfx950: lanes 0-31 get
+// (x[l], x[l + 32]), lanes 32-63 get (y[l - 32], y[l]).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+inline u32x2 permlane32_swap(uint32_t x, uint32_t y) {
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  std::memcpy(w.slot[self], &x, 4);
+  std::memcpy(w.slot[self] + 4, &y, 4);
+  w.bar.arrive_and_wait();
+  u32x2 r;
+  uint32_t a, b;
+  if (self < 32) {
+    std::memcpy(&a, w.slot[self], 4);
+    std::memcpy(&b, w.slot[self + 32], 4);
+  } else {
+    std::memcpy(&a, w.slot[self - 32] + 4, 4);
+    std::memcpy(&b, w.slot[self] + 4, 4);
+  }
+  w.bar.arrive_and_wait();
+  r[0] = a;
+  r[1] = b;
+  return r;
+}
+
+inline int wave_any(int p) {
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  std::memcpy(w.slot[self], &p, 4);
+  w.bar.arrive_and_wait();
+  int any = 0;
+  for (int l = 0; l < 64; ++l) {
+    int v;
+    std::memcpy(&v, w.slot[l], 4);
+    any |= (v != 0);
+  }
+  w.bar.arrive_and_wait();
+  return any;
+}
+
+// v_cvt_pk_u8_f32 as measured on gfx950: round to nearest even, saturate to [0, 255]
+inline uint32_t cvt_pk_u8_f32(float f, int byte, uint32_t old) {
+  float r = std::nearbyint(f);
+  r = std::isnan(r) ? 0.0f : std::fmin(255.0f, std::fmax(0.0f, r));
+  const uint32_t v = static_cast<uint32_t>(r);
+  return (old & ~(0xffu << (8 * byte))) | (v << (8 * byte));
+}
+
 inline float bits_to_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
 
@@ -187,6 +234,9 @@ inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); ret
 #define __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, x, y, z) emu::mfma_i8<16>(a, b, c)
 #define __builtin_amdgcn_perm(a, b, s) emu::perm(a, b, s)
 #define __builtin_amdgcn_exp2f(x) std::exp2(static_cast<float>(x))
+#define __builtin_amdgcn_permlane32_swap(x, y, fi, bc) emu::permlane32_swap(x, y)
+#define __builtin_amdgcn_cvt_pk_u8_f32(f, b, old) emu::cvt_pk_u8_f32(f, b, old)
+#define __any(p) emu::wave_any(p)
 #define hipLaunchKernelGGL(K, G, B, S, ST, ...) emu::launch(G, B, [&]() { K(__VA_ARGS__); })
 
 using std::max;

@@ -79,16 +79,20 @@ def test_emulated_logits(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal):
     assert np.all(s[~vis] == np.iinfo(np.int32).min)
 
 
-@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt", [
-    (1, 1, 1, 128, 128, 64, 0, 0, F32), (2, 4, 2, 77, 130, 128, 1, 0, F16),
-    (1, 2, 1, 1, 200, 128, 0, 1, F32), (1, 3, 3, 300, 300, 64, 1, 1, F32),
-    (3, 8, 1, 129, 65, 128, 0, 0, F16), (1, 1, 1, 1, 1, 64, 1, 1, F16),
-    (1, 2, 2, 130, 257, 128, 1, 1, F32), (1, 4, 1, 3, 333, 64, 0, 1, F32),
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt,gain", [
+    (1, 1, 1, 128, 128, 64, 0, 0, F32, 1), (2, 4, 2, 77, 130, 128, 1, 0, F16, 1),
+    (1, 2, 1, 1, 200, 128, 0, 1, F32, 1), (1, 3, 3, 300, 300, 64, 1, 1, F32, 1),
+    (3, 8, 1, 129, 65, 128, 0, 0, F16, 1), (1, 1, 1, 1, 1, 64, 1, 1, F16, 1),
+    (1, 2, 2, 130, 257, 128, 1, 1, F32, 1), (1, 4, 1, 3, 333, 64, 0, 1, F32, 1),
+    # large logits: the running max keeps growing by tens of units (re-basing path)
+    (1, 2, 2, 256, 640, 128, 1, 0, F32, 12), (1, 1, 1, 64, 500, 64, 0, 0, F32, 30),
 ])
-def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt):
+def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt, gain):
     r = np.random.Generator(np.random.PCG64(B * 100 + Lq * 7 + Lkv))
-    q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32) * np.float32(gain)
     k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    # keys whose norm grows along the sequence make late keys dominate
+    k *= np.linspace(1.0, float(gain), Lkv, dtype=np.float32)[None, None, :, None]
     v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
     qh, sq = oracle.quantize_rows(q, 1)
     kh, sk = oracle.quantize_rows(k, 1)
@@ -105,3 +109,21 @@ def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, o
     err = np.abs(o - oo)
     assert err.max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
     assert np.abs(lse - lo).max() <= 1e-4 * max(1.0, np.abs(lo).max())
+
+
+def test_emulated_attention_huge_logits(exe, tmp_path):
+    # Q = K = 60 N(0,1): logits ~5e4, where fp32 rounding of the exponent
+    # argument could otherwise push the max key's probability code past 127
+    r = np.random.Generator(np.random.PCG64(9))
+    B, H, L, d = 1, 2, 200, 128
+    big = (r.standard_normal((B, H, L, d)) * 60).astype(np.float16)
+    v = r.standard_normal((B, H, L, d)).astype(np.float16)
+    qh, sq = oracle.quantize_rows(big, 1)
+    vh, sv = oracle.quantize_rows(v, v.size // d)
+    oo_p, lo_p = os.path.join(str(tmp_path), "o.out"), os.path.join(str(tmp_path), "l.out")
+    files = [put(tmp_path, n + ".bin", a) for n, a in
+             (("q", qh), ("sq", sq), ("k", qh), ("sk", sq), ("v", vh), ("sv", sv))]
+    run(exe, tmp_path, ["fwd", *files, 0, F32, B, H, H, L, L, d, 1, oo_p, lo_p])
+    o = np.fromfile(oo_p, np.float32).reshape(B, H, L, d)
+    oo, _ = oracle.attn_int8(qh, sq, qh, sq, vh, sv, False, B, H, H, L, L, d, True, 64, 0)
+    assert np.abs(o - oo).max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
