@@ -24,13 +24,19 @@ CFLAGS = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=" + ARCH, "-I" + INCLUDE
           "-Wall", "-Wno-unused-function"]
 
 
+# Per-source code generation options. The fused attention kernel keeps its
+# MFMA results in VGPRs: its softmax reads every logit with VALU instructions,
+# and accumulator-register results would need a copy per value.
+EXTRA = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

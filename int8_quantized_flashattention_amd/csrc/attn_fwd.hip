@@ -12,34 +12,40 @@
 // Mapping onto CDNA4
 // ------------------
 // One workgroup = 4 wavefronts = kPrefillBM (128) query rows of one (b, h);
-// each wavefront owns 32 rows. K/V are streamed in tiles of kPrefillBN (64)
-// keys through LDS and shared by the 4 wavefronts.
+// each wavefront owns 32 rows. K/V stream through LDS in tiles of kPrefillBN
+// (64) keys shared by the 4 wavefronts.
 //
-// Both products use v_mfma_i32_32x32x32_i8 (32x32 output, K = 32 int8 per
-// step, 16 int8 per lane per operand). The logits are computed transposed,
-// S^T = K_hat . Q_hat^T, so that in the 32x32 INT32 result every lane holds
-// 16 keys of ONE query (lane l: query l % 32, keys (v/4)*8 + (l/32)*4 + v%4
-// for accumulator v). The softmax statistics of a query therefore live in one
-// lane pair (l, l ^ 32): row max and row sum need a single cross-half step.
-// The quantized probabilities P_hat of a lane are exactly the 16 int8 B-operand
-// values of O^T = V_hat^T . P_hat^T for the same 32-key block, so P never
-// leaves registers. The A operand V_hat^T needs, per lane, 16 keys of one
-// head-dim channel: V tiles are transposed while they are staged into LDS
-// (4x4 byte transposes with v_perm) and stored with the key order the P
-// operand implies, so each operand fetch is one 16-byte LDS read.
-// The output accumulator O^T keeps the query in the lane too, so the
-// per-row rescale alpha is lane-local.
+// Both products use v_mfma_i32_32x32x32_i8. The logits are computed
+// transposed, S^T = K_hat . Q_hat^T, so that in the 32x32 INT32 result every
+// lane holds 16 keys of ONE query (lane l: query l % 32, keys
+// (v/4)*8 + (l/32)*4 + v%4 for accumulator v): row max and row sum need one
+// cross-half step (v_permlane32_swap). The quantized probabilities of a lane
+// are exactly the 16 int8 B-operand values of O^T = V_hat^T . P_hat^T for the
+// same 32 keys, so P never leaves registers. V tiles are transposed while
+// staged (4x4 byte transposes with v_perm) and stored in the key order the P
+// operand implies, so each operand fetch is one 16-byte LDS read. O^T keeps
+// the query in the lane, so the per-row rescale is lane-local.
 //
-// Pipeline per KV tile: the next tile's global loads are issued before the
-// current tile's math and written to the other of two LDS stages after it,
-// so there is one barrier per tile. The softmax works in base 2 with 127
-// folded into the exponent: y = exp2(u c2 - m + log2 127) = 127 P_tilde, the
-// row sum accumulates y, and v_cvt_pk_u8_f32 (round to nearest even,
-// saturating) turns y into P_hat and packs it into the operand in one step.
-// For per-tensor V the P_hat . V_hat products keep accumulating in the INT32
-// MFMA accumulator while no row of the wavefront raises its max (alpha = 1),
-// and are converted to fp32 (and the older fp32 part rescaled) only when one
-// does; s_V is applied once in the epilogue.
+// Instruction budget. On gfx950 the issue time of the VALU work per
+// (query, key) pair is the first-order cost next to the pair's MFMA work, so
+// per pair the kernel spends only: one INT32->fp32 convert, one multiply by
+// s_K[j], half a v_max3, one fma for the base-2 exponent (127 folded in), one
+// v_exp_f32, one add for the row sum and one v_cvt_pk_u8_f32 (round to
+// nearest even, saturating) that quantizes P and packs it into the MFMA
+// operand. Everything else is per tile or per workgroup:
+//  - loads use raw buffer resources built once per workgroup: the tile offset
+//    is the scalar offset, per-lane offsets never change, and out-of-range
+//    keys read as zero in hardware (no compares, no 64-bit address math);
+//  - for per-tensor V the P_hat . V_hat products keep accumulating in the
+//    INT32 MFMA accumulator while no row of the wavefront raises its max and
+//    are folded into the fp32 accumulator (which keeps its own frame, and
+//    lives in LDS since only folds touch it) only when one does; s_V is
+//    applied once in the epilogue;
+//  - masking code runs only on diagonal / ragged tiles.
+// Software pipeline: iteration t issues the MFMAs of QK(t+1) and PV(t-1)
+// next to the VALU work of softmax(t) and of dequantizing S(t+1), so the
+// matrix core works while the VALU computes probabilities. K stages are
+// triple-buffered and V stages double-buffered; each tile has one barrier.
 #include "attn_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -52,182 +58,245 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
+constexpr int NKB = BN / 32;                 // 32-key blocks per tile
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2_127 = 6.988684686772166f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kBufWord3 = 0x00020000;        // raw buffer, 32-bit data format
+// the INT32 run of P_hat . V_hat is folded into fp32 at least every this many
+// tiles, keeping |sum| <= 127 * 127 * keys below 2^31
+constexpr int kMaxIntTiles = 32768 / BN;
+// re-base the fp32 accumulator when the running max has grown by this much
+// (base 2) since its frame was set
+constexpr float kRebase = 60.0f;
+// beyond this |running max| (base 2) the fp32 rounding of the exponent
+// argument could push the max key's 127 P_tilde past 127.5
+constexpr float kClampAbove = 32768.0f;
 
 template <int D>
 struct Geo {
-  static constexpr int KSTR = D + 16;     // LDS bytes per K row (padding breaks bank aliasing)
-  static constexpr int VSTR = BN + 16;    // LDS bytes per V^T row
-  static constexpr int NC = D / 32;       // 32-channel chunks of the head dim
+  static constexpr int KSTR = D + 16;             // LDS bytes per K row (padding spreads banks)
+  static constexpr int VSTR = BN + 16;            // LDS bytes per V^T row
+  static constexpr int NC = D / 32;               // 32-channel chunks of the head dim
+  static constexpr int KPT = BN * D / 16 / kThreads;            // 16-byte K chunks per thread
+  static constexpr int VITEMS = (D / 4) * (BN / 8);             // (channel quad, key octet) items
+  static constexpr int VPT_ITEMS = (VITEMS + kThreads - 1) / kThreads;
 };
 
 __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
-
+__device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transpose a 4x4 byte block: r[i] holds bytes (row i, cols 0..3); returns
 // c[j] holding bytes (rows 0..3, col j).
-__device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4]) {
-  // interleave rows 0/1 and 2/3 byte-wise
+__device__ __forceinline__ void transpose4x4(const uint32_t* r, uint32_t* c) {
   const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
   const uint32_t hi01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
   const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
   const uint32_t hi23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
   c[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);  // r0b0 r1b0 r2b0 r3b0
-  c[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);  // r0b1 r1b1 r2b1 r3b1
+  c[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
   c[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
   c[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-// Position of tile-local key j inside a V^T LDS row: the 16 keys that one lane
-// half (g) contributes to a 32-key MFMA step are stored contiguously, in the
-// order of that lane's logit accumulators.
-__device__ __forceinline__ int vt_pos(int j) {
-  const int kb = j >> 5, r = j & 31;
-  return kb * 32 + ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
-}
-
-// One LDS stage of a KV tile. Two of them alternate: while the wavefronts
-// compute on one, the next tile (already loaded into registers) is written to
-// the other.
-struct Stage {
-  alignas(16) int8_t k[BN * (128 + 16)];   // K rows, padded
-  alignas(16) int8_t vt[128 * (BN + 16)];  // V^T rows (one per channel), padded
-  alignas(16) float sk[BN];                // s_K of the tile's keys
-  alignas(16) float wr[BN];                // per-token V: s_V[j] / s_t
-  float st;                                // per-token V: s_t, the largest s_V of the tile
+// K stage: K rows (padded), per-key s_K, per-token V scales and the partial
+// maxima of those scales (one per wavefront that loaded them).
+struct KStage {
+  alignas(16) int8_t k[BN * (128 + 16)];
+  alignas(16) float sk[BN];
+  alignas(16) float sv[BN];
+  float stp[BN / 64];
 };
+// V stage: V^T rows (one per channel, padded), keys in P-operand order.
+struct VStage {
+  alignas(16) int8_t vt[128 * (BN + 16)];
+};
+// For per-tensor V the fp32 accumulator is touched only when a fold happens,
+// so it lives in LDS (16 KB per wavefront at d = 128), lane-contiguous in
+// float4 units: the accumulator values (c, 4q..4q+3) of lane l sit at float
+// offset ((wave * NC + c) * 4 + q) * 256 + 4 l, so every access is a
+// conflict-free 1 KB wavefront transfer.
+template <int D, bool LDS_ACC>
 struct Smem {
-  Stage stage[2];
+  KStage ks[3];
+  VStage vs[2];
+  alignas(16) float acc[LDS_ACC ? 4 * (D / 32) * 16 * 64 : 4];
 };
 
-// The next tile held in registers between its global loads and its LDS store.
+struct Bufs {
+  __amdgpu_buffer_rsrc_t k, v, sk, sv;
+};
+
+// Per-thread load/store offsets (fixed for the whole kernel).
 template <int D>
-struct TileRegs {
-  static constexpr int kCPR = D / 16;                 // 16-byte chunks per K row
-  static constexpr int kKIters = BN * kCPR / kThreads;
-  static constexpr int kNDQ = D / 4;                  // channel quads
-  static constexpr int kKQPerIter = kThreads / kNDQ;  // key quads per pass
-  static constexpr int kVIters = (BN / 4) / kKQPerIter;
-  v4i k[kKIters];
-  uint32_t v[kVIters][4];
-  float sk;
-  float sv;
-};
+struct Map {
+  using G = Geo<D>;
+  uint32_t k_src[G::KPT];        // byte offset of a 16-byte K chunk within a tile
+  int k_dst[G::KPT];             // its LDS offset within the K stage
+  uint32_t v_src[G::VPT_ITEMS];  // byte offset of key0's channel quad within a tile
+  int v_dst[G::VPT_ITEMS];       // LDS offset of row 4*dq, 8-byte slot of the key octet
+  bool v_live[G::VPT_ITEMS];
 
-// Global loads of tile k0 (out-of-range keys read as zero). The logits-only
-// variant is given no V or scale pointers and must not touch them.
-template <int D, bool VPT, bool LOGITS_ONLY>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const FwdArgs& a, int64_t kv_base, int k0) {
-  using R = TileRegs<D>;
-  const int tid = threadIdx.x;
+  __device__ __forceinline__ void init(int tid) {
 #pragma unroll
-  for (int it = 0; it < R::kKIters; ++it) {
-    const int id = tid + it * kThreads;
-    const int row = id / R::kCPR, cc = id % R::kCPR;
-    r.k[it] = v4i{0, 0, 0, 0};
-    if (k0 + row < a.Lkv) r.k[it] = *reinterpret_cast<const v4i*>(a.k + (kv_base + k0 + row) * D + cc * 16);
-  }
-  if constexpr (LOGITS_ONLY) return;
-  const int dq = tid % R::kNDQ;
+    for (int i = 0; i < G::KPT; ++i) {
+      const int id = tid + i * kThreads;
+      const int row = id / (D / 16), cc = id % (D / 16);
+      k_src[i] = static_cast<uint32_t>(row * D + cc * 16);
+      k_dst[i] = row * G::KSTR + cc * 16;
+    }
+    // a wavefront takes 8 channel quads x 8 key octets, so its 8-byte LDS
+    // writes spread over all banks
 #pragma unroll
-  for (int it = 0; it < R::kVIters; ++it) {
-    const int kq = tid / R::kNDQ + it * R::kKQPerIter;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k0 + kq * 4 + i;
-      r.v[it][i] = (key < a.Lkv) ? *reinterpret_cast<const uint32_t*>(a.v + (kv_base + key) * D + dq * 4) : 0u;
+    for (int i = 0; i < G::VPT_ITEMS; ++i) {
+      const int item = tid + i * kThreads;
+      v_live[i] = item < G::VITEMS;
+      const int wc = item / 64, l = item % 64;
+      const int dq = (wc % (D / 32)) * 8 + (l % 8);
+      const int ko = (wc / (D / 32)) * 8 + (l / 8);
+      const int kb = ko / 4, gq = (ko % 4) / 2, hh = ko % 2;
+      const int key0 = kb * 32 + 16 * hh + 4 * gq;     // keys key0..+3 and key0+8..+11
+      v_src[i] = static_cast<uint32_t>(key0 * D + dq * 4);
+      v_dst[i] = (dq * 4) * G::VSTR + kb * 32 + gq * 16 + 8 * hh;
     }
   }
+};
+
+// Next tiles' data between their global loads and their LDS stores.
+template <int D>
+struct KRegs {
+  v4i k[Geo<D>::KPT];
+  float sk, sv;
+};
+template <int D>
+struct VRegs {
+  uint32_t v[Geo<D>::VPT_ITEMS][8];
+};
+
+// SCALES: also load s_K (and, for per-token V, s_V); the logits-only kernel
+// has no scale pointers and must not touch them.
+template <int D, bool SCALES, bool VPT>
+__device__ __forceinline__ void load_k(KRegs<D>& r, const Bufs& bf, const Map<D>& mp, int k0) {
+  const int tid = threadIdx.x;
+  const uint32_t soff = static_cast<uint32_t>(k0) * D;
+#pragma unroll
+  for (int i = 0; i < Geo<D>::KPT; ++i) r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bf.k, mp.k_src[i], soff, 0);
   r.sk = 0.0f;
   r.sv = 0.0f;
-  if (tid < BN) {
-    if (k0 + tid < a.Lkv) r.sk = a.s_k[kv_base + k0 + tid];
-  } else if (VPT && tid < 2 * BN) {
-    if (k0 + tid - BN < a.Lkv) r.sv = a.s_v[kv_base + k0 + tid - BN];
+  if constexpr (SCALES) {
+    if (tid < BN) r.sk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bf.sk, tid * 4, k0 * 4, 0));
+    if (VPT && tid >= kThreads - BN)
+      r.sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bf.sv, (tid - (kThreads - BN)) * 4, k0 * 4, 0));
   }
 }
 
-// LDS store of a tile held in registers: K rows as they are, V transposed
-// into V^T in the key order of the P operand, the per-key scales, and for
-// per-token V the tile scale s_t and the ratios s_V[j] / s_t.
-template <int D, bool VPT, bool LOGITS_ONLY>
-__device__ __forceinline__ void store_tile(Stage& sg, const TileRegs<D>& r) {
-  using R = TileRegs<D>;
-  using G = Geo<D>;
+template <int D>
+__device__ __forceinline__ void load_v(VRegs<D>& r, const Bufs& bf, const Map<D>& mp, int k0) {
+  const uint32_t soff = static_cast<uint32_t>(k0) * D;
+#pragma unroll
+  for (int it = 0; it < Geo<D>::VPT_ITEMS; ++it) {
+    if (!mp.v_live[it]) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.v[it][i] = __builtin_amdgcn_raw_buffer_load_b32(bf.v, mp.v_src[it] + i * D, soff, 0);
+      r.v[it][4 + i] = __builtin_amdgcn_raw_buffer_load_b32(bf.v, mp.v_src[it] + (8 + i) * D, soff, 0);
+    }
+  }
+}
+
+template <int D, bool SCALES, bool VPT>
+__device__ __forceinline__ void store_k(KStage& s, const KRegs<D>& r, const Map<D>& mp) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int it = 0; it < R::kKIters; ++it) {
-    const int id = tid + it * kThreads;
-    const int row = id / R::kCPR, cc = id % R::kCPR;
-    *reinterpret_cast<v4i*>(sg.k + row * G::KSTR + cc * 16) = r.k[it];
-  }
-  if constexpr (LOGITS_ONLY) return;
-  const int dq = tid % R::kNDQ;
+  for (int i = 0; i < Geo<D>::KPT; ++i) *reinterpret_cast<v4i*>(s.k + mp.k_dst[i]) = r.k[i];
+  if constexpr (SCALES) {
+    if (tid < BN) s.sk[tid] = r.sk;
+    if (VPT && tid >= kThreads - BN) {
+      const int j = tid - (kThreads - BN);
+      s.sv[j] = r.sv;
+      float st = r.sv;
 #pragma unroll
-  for (int it = 0; it < R::kVIters; ++it) {
-    const int kq = tid / R::kNDQ + it * R::kKQPerIter;
-    uint32_t c[4];
-    transpose4x4(r.v[it], c);
-    const int pos = vt_pos(kq * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(sg.vt + (dq * 4 + j) * G::VSTR + pos) = c[j];
-  }
-  if (tid < BN) {
-    sg.sk[tid] = r.sk;
-  } else if (VPT && tid < 2 * BN) {
-    // one wavefront (threads BN..2BN-1) reduces the tile's largest V scale
-    float st = r.sv;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) st = fmaxf(st, __shfl_xor(st, off, 64));
-    sg.wr[tid - BN] = (st > 0.0f) ? __fdiv_rn(r.sv, st) : 0.0f;
-    if (tid == BN) sg.st = st;
+      for (int off = 32; off > 0; off >>= 1) st = fmaxf(st, __shfl_xor(st, off, 64));
+      if ((j & 63) == 0) s.stp[j >> 6] = st;
+    }
   }
 }
 
-// max / sum of a value over the lane pair (l, l ^ 32) that holds one query
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// INT8 P_hat . V_hat for one tile: acc[c] (+)= sum over the 32-key blocks.
-template <int D, bool FROM_ZERO>
-__device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const Stage& sg, const v4i (&pv)[BN / 32], int lr, int g) {
+template <int D>
+__device__ __forceinline__ void store_v(VStage& s, const VRegs<D>& r, const Map<D>& mp) {
   using G = Geo<D>;
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c) {
-    v16i t = FROM_ZERO ? v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0} : acc[c];
+  for (int it = 0; it < G::VPT_ITEMS; ++it) {
+    if (!mp.v_live[it]) continue;
+    uint32_t lo[4], hi[4];
+    transpose4x4(&r.v[it][0], lo);
+    transpose4x4(&r.v[it][4], hi);
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      const v4i va = *reinterpret_cast<const v4i*>(sg.vt + (c * 32 + lr) * G::VSTR + kb * 32 + g * 16);
-      t = mfma_i8(va, pv[kb], t);
-    }
-    acc[c] = t;
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint2*>(s.vt + mp.v_dst[it] + j * G::VSTR) = make_uint2(lo[j], hi[j]);
   }
 }
 
-// u = S_int * s_K[j] for this lane's keys of the tile (the query's factor c2
-// is applied later); masked keys get -inf. Returns the lane's max of u.
-template <int D, bool MASK>
-__device__ __forceinline__ float dequant_tile(const v16i (&s)[BN / 32], const Stage& sg, float (&u)[BN / 32][16],
-                                              int k0, int lim, int Lkv, int g) {
-  float mx = kNegInf;
+// Scheduling hint for the straight-line block just emitted: alternate one
+// MFMA with N_VALU VALU instructions, NM times, so the matrix core works
+// while the VALU does the softmax arithmetic.
+template <int NM, int N_VALU>
+__device__ __forceinline__ void interleave() {
 #pragma unroll
-  for (int kb = 0; kb < BN / 32; ++kb)
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, N_VALU, 0);   // VALU
+  }
+}
+
+// S^T for one tile: exact INT32 logits, 32 keys per block (shared with the
+// logits-dump kernel).
+template <int D>
+__device__ __forceinline__ void qk_tile(v16i (&s)[NKB], const KStage& ks, const v4i (&qf)[D / 32], int lr, int g) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+  for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const v4i ka = *reinterpret_cast<const v4i*>(ks.k + (kb * 32 + lr) * G::KSTR + c * 32 + g * 16);
+      s[kb] = mfma_i8(ka, qf[c], s[kb]);
+    }
+}
+
+// O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T.
+template <int D>
+__device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const VStage& vs, const v4i (&pv)[NKB], int lr, int g) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const v4i va = *reinterpret_cast<const v4i*>(vs.vt + (c * 32 + lr) * G::VSTR + kb * 32 + g * 16);
+      acc[c] = mfma_i8(va, pv[kb], acc[c]);
+    }
+}
+
+// u = S_int * s_K[j] for this lane's keys (the query's factor c2 comes
+// later); masked keys get -inf. Returns the max over the lane pair.
+template <bool MASK>
+__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage& ks, float (&u)[NKB][16], int k0,
+                                              int lim, int Lkv, int g) {
+  // the maximum is taken as a tree (independent partial maxima), so a single
+  // wavefront per SIMD is not held up by a long dependency chain
+  float gm[NKB * 4];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int jl = kb * 32 + j4 * 8 + g * 4;
-      const float4 skv = *reinterpret_cast<const float4*>(sg.sk + jl);
+      const float4 skv = *reinterpret_cast<const float4*>(ks.sk + jl);
       const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -237,60 +306,83 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[BN / 32], const St
           x = (key < Lkv && key <= lim) ? x : kNegInf;
         }
         u[kb][j4 * 4 + e] = x;
-        mx = fmaxf(mx, x);
       }
+      const float* x = &u[kb][j4 * 4];
+      gm[kb * 4 + j4] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     }
-  return mx;
+#pragma unroll
+  for (int w = NKB * 4; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) gm[i] = fmaxf(gm[i], gm[i + w / 2]);
+  const float mx = gm[0];
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// y = exp2(u c2 - bias) = 127 P_tilde; returns the lane's sum of y and packs
+// y = exp2(u c2 - bias) = 127 P_tilde; returns this lane's sum of y and packs
 // P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV operands.
-// CLAMP: when the running max is so large (|m| >= 2^15 in base-2 units) that
-// the fp32 rounding of the exponent argument could push the max key's y past
-// 127.5, y is clamped to 127 (the value the max key has exactly).
+// CLAMP: when |running max| >= kClampAbove, y is clamped to 127 (the value the
+// max key has exactly), since exponent rounding could otherwise give 128.
 template <bool VPT, bool MASK, bool CLAMP>
-__device__ __forceinline__ float probs_tile(const float (&u)[BN / 32][16], float c2, float bias, const Stage& sg,
-                                            v4i (&pv)[BN / 32], int g) {
-  float lsum = 0.0f;
+__device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2, float bias, const KStage& ks,
+                                            float rst, v4i (&pv)[NKB], int g) {
+  float gs[NKB * 4];                   // partial row sums, added as a tree
 #pragma unroll
-  for (int kb = 0; kb < BN / 32; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     uint32_t pw[4];
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
       if constexpr (VPT) {
-        const float4 wv = *reinterpret_cast<const float4*>(sg.wr + kb * 32 + j4 * 8 + g * 4);
-        wr[0] = wv.x; wr[1] = wv.y; wr[2] = wv.z; wr[3] = wv.w;
+        const float4 sv = *reinterpret_cast<const float4*>(ks.sv + kb * 32 + j4 * 8 + g * 4);
+        wr[0] = sv.x * rst; wr[1] = sv.y * rst; wr[2] = sv.z * rst; wr[3] = sv.w * rst;
       }
       uint32_t word = 0;
+      float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float uu = u[kb][j4 * 4 + e];
-        float y = exp2_hw(__builtin_fmaf(uu, c2, -bias));
-        if constexpr (MASK) y = (uu == kNegInf) ? 0.0f : y;
-        if constexpr (CLAMP) y = fminf(y, 127.0f);
-        lsum += y;
-        word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y * wr[e] : y, e, word);
+        y[e] = exp2_hw(__builtin_fmaf(uu, c2, -bias));
+        if constexpr (MASK) y[e] = (uu == kNegInf) ? 0.0f : y[e];
+        if constexpr (CLAMP) y[e] = fminf(y[e], 127.0f);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
       }
+      gs[kb * 4 + j4] = (y[0] + y[1]) + (y[2] + y[3]);
       pw[j4] = word;
     }
     pv[kb] = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]), static_cast<int>(pw[3])};
   }
-  return lsum;
+#pragma unroll
+  for (int w = NKB * 4; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) gs[i] += gs[i + w / 2];
+  return gs[0];
 }
 
-constexpr float kLog2_127 = 6.988684686772166f;
-// the INT32 run of P_hat . V_hat is converted to fp32 at least every this many
-// tiles, keeping |sum| <= 127 * 127 * keys below 2^31
-constexpr int kMaxIntTiles = 32768 / BN;
-// re-base the fp32 accumulator when the running max has grown by this much
-// (base 2) since its frame was set
-constexpr float kRebase = 60.0f;
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool DUMP>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int D, bool scales, bool vpt) {
+  Bufs bf;
+  bf.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.k + kv_base * D), 0, a.Lkv * D, kBufWord3);
+  bf.v = bf.k;
+  bf.sk = bf.k;
+  bf.sv = bf.k;
+  if (scales) {
+    bf.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.v + kv_base * D), 0, a.Lkv * D, kBufWord3);
+    bf.sk = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.s_k + kv_base), 0, a.Lkv * 4, kBufWord3);
+    if (vpt) bf.sv = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.s_v + kv_base), 0, a.Lkv * 4, kBufWord3);
+  }
+  return bf;
+}
+
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<D>;
-  __shared__ Smem sm;
+  constexpr bool kLdsAcc = !VPT;
+  __shared__ Smem<D, kLdsAcc> sm;
 
   const int bh = blockIdx.x;
   const int rb = gridDim.y - 1 - blockIdx.y;          // longest (causal) row blocks first
@@ -299,15 +391,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int64_t kv_base = (static_cast<int64_t>(b) * a.Hkv + hk) * a.Lkv;
   const int64_t q_base = static_cast<int64_t>(bh) * a.Lq;
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets tile decisions be scalar
+  const int lane = tid & 63;
   const int g = lane >> 5;          // which 16 keys / channels of a 32-block this lane holds
   const int lr = lane & 31;         // query row within the wavefront
   const int qw0 = rb * BM + wave * 32;
   const int qi = qw0 + lr;
   const bool qvalid = qi < a.Lq;
-  const bool wave_live = qw0 < a.Lq;
   const int shift = a.Lkv - a.Lq;   // bottom-right causal alignment
+
+  const Bufs bf = make_bufs(a, kv_base, D, true, VPT);
+  Map<D> mp;
+  mp.init(tid);
 
   // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk.
   v4i qf[G::NC];
@@ -316,148 +412,196 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
     qf[c] = v4i{0, 0, 0, 0};
     if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
   }
-  const float sq = (qvalid && !DUMP) ? a.s_q[q_base + qi] : 0.0f;
+  const float sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
   const float c2 = sq * inv_sqrt_d * kLog2e;          // base-2 logit per unit of S_int * s_K
   const int lim = CAUSAL ? qi + shift : a.Lkv - 1;    // last visible key of this row
-  const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;                        // smallest in the wave
-  const int lim_last = CAUSAL ? min(qw0 + 31, a.Lq - 1) + shift : a.Lkv - 1;     // largest in the wave
+  const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;   // smallest in the wavefront
 
   const int last_q = min(rb * BM + BM - 1, a.Lq - 1);
   const int kv_end = CAUSAL ? min(a.Lkv, last_q + shift + 1) : a.Lkv;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  // running max (base 2), partial row sum of 127 * P_tilde over this lane's keys
+  // softmax state: running max (base 2), partial sum of 127 P_tilde over this lane's keys
   float m = kNegInf, l = 0.0f;
-  float acc[G::NC][16];                // fp32 output accumulator (O^T, query in the lane)
-  v16i acc_i[G::NC];                   // INT32 run of P_hat . V_hat since the last conversion
+  float acc[G::NC][16];                // fp32 O^T accumulator (registers: per-token V)
+  v16i acc_i[G::NC];                   // INT32 accumulation of P_hat . V_hat
+  float4* const acc_lds = reinterpret_cast<float4*>(sm.acc) + wave * (G::NC * 4 * 64) + lane;
 #pragma unroll
   for (int c = 0; c < G::NC; ++c) {
-    acc_i[c] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    acc_i[c] = zero16();
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+    if constexpr (kLdsAcc) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc_lds[(c * 4 + q) * 64] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
   }
-  int int_tiles = 0;
   float m_f = kNegInf;                 // frame of acc (per-tensor V)
+  int int_tiles = 0;
+  float alpha_prev = 1.0f, st_prev = 0.0f;   // per-token V: rescale and V scale of the previous tile
 
-  TileRegs<D> nx;
-  load_tile<D, VPT, DUMP>(nx, a, kv_base, 0);
-  store_tile<D, VPT, DUMP>(sm.stage[0], nx);
+  // ---- prologue: K(0), K(1) staged; S(0) computed ----
+  KRegs<D> kx;
+  VRegs<D> vx;
+  load_k<D, true, VPT>(kx, bf, mp, 0);
+  store_k<D, true, VPT>(sm.ks[0], kx, mp);
+  if (n_tiles > 1) {
+    load_k<D, true, VPT>(kx, bf, mp, BN);
+    store_k<D, true, VPT>(sm.ks[1], kx, mp);
+  }
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  v16i s_a[NKB], s_b[NKB];             // S of the current / next tile (roles swap every tile)
+  v4i p_a[NKB], p_b[NKB];              // P_hat of the previous / current tile
+  qk_tile<D>(s_a, sm.ks[0], qf, lr, g);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) p_a[kb] = v4i{0, 0, 0, 0};
+
+  // One tile of the pipeline: PV(t-1) [MFMA] | dequant(t) [VALU] |
+  // QK(t+1) [MFMA] | softmax(t) [VALU] | fold | stage K(t+2), V(t) | barrier.
+  auto step = [&](int t, v16i (&s_cur)[NKB], v16i (&s_nxt)[NKB], const v4i (&p_prev)[NKB], v4i (&p_cur)[NKB])
+      __attribute__((always_inline)) {
     const int k0 = t * BN;
-    const Stage& sg = sm.stage[t & 1];
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile<D, VPT, DUMP>(nx, a, kv_base, k0 + BN);   // in flight during compute
+    const KStage& ks_cur = sm.ks[t % 3];
+    // global loads for later tiles, in flight during this tile's math
+    if (t + 2 < n_tiles) load_k<D, true, VPT>(kx, bf, mp, k0 + 2 * BN);
+    load_v<D>(vx, bf, mp, k0);
 
-    if (wave_live && k0 <= lim_last) {
-      // ---- S^T = K_hat . Q_hat^T, exact INT32, 32 keys per block ----
-      v16i s[BN / 32];
+    // PV(t-1) runs unconditionally (P of "tile -1" is zero) and QK(t+1) reads
+    // a stale stage past the last tile (its result is unused), so the common
+    // case below is two straight-line blocks: [PV(t-1) MFMAs | dequant(t)]
+    // and [QK(t+1) MFMAs | softmax(t)], each interleaved by the scheduler.
+    if constexpr (VPT) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        s[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < G::NC; ++c) {
-          const v4i ka = *reinterpret_cast<const v4i*>(sg.k + (kb * 32 + lr) * G::KSTR + c * 32 + g * 16);
-          s[kb] = mfma_i8(ka, qf[c], s[kb]);
-        }
-      }
-
-      if constexpr (DUMP) {
-        if (qvalid) {
-#pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-              if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
-            }
-        }
-      } else {
-        // ---- dequantize (u = S_int * s_K[j]; the row factor is c2), mask ----
-        const bool need_mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
-        float u[BN / 32][16];
-        float mx = need_mask ? dequant_tile<D, true>(s, sg, u, k0, lim, a.Lkv, g)
-                             : dequant_tile<D, false>(s, sg, u, k0, lim, a.Lkv, g);
-        mx = pair_max(mx);
-        // c2 >= 0, so max(u) * c2 == max(u * c2) under monotone rounding
-        const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;
-        const float m_new = fmaxf(m, mx2);
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = exp2_hw(m - m_use);        // 1 if unchanged, 0 on the first tile
-        const float bias = m_use - kLog2_127;          // exp2(u c2 - bias) = 127 P_tilde
-
-        // ---- 127 P_tilde, row sum, P_hat = rne(127 P_tilde) packed as MFMA operands ----
-        v4i pv[BN / 32];
-        const bool clamp = __any(fabsf(m_use) >= 32768.0f);
-        float lsum;
-        if (clamp)
-          lsum = need_mask ? probs_tile<VPT, true, true>(u, c2, bias, sg, pv, g)
-                           : probs_tile<VPT, false, true>(u, c2, bias, sg, pv, g);
-        else
-          lsum = need_mask ? probs_tile<VPT, true, false>(u, c2, bias, sg, pv, g)
-                           : probs_tile<VPT, false, false>(u, c2, bias, sg, pv, g);
-        l = alpha * l + lsum;
-
-        if constexpr (VPT) {
-          // per-token V: the tile scale s_t changes per tile, so convert every tile
-          v16i tv[G::NC];
-          pv_tile<D, true>(tv, sg, pv, lr, g);
-          const float st = sg.st;
-#pragma unroll
-          for (int c = 0; c < G::NC; ++c)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[c][v] = alpha * acc[c][v] + st * static_cast<float>(tv[c][v]);
-        } else {
-          // per-tensor V: keep summing P_hat . V_hat in INT32 while no row of
-          // the wavefront moves its max (alpha == 1 for all); convert to fp32
-          // when one does (same sums, fp32 rounding only)
-          // acc is kept in its own frame m_f (it holds 2^(m_f - m) times the
-          // fp32 part of the total); the INT32 run is in the frame of m, the
-          // max before this tile, and is folded in with one factor per lane.
-          const bool flush = __any(m_new > m) || int_tiles >= kMaxIntTiles;
-          if (flush) {
-            if (m_f == kNegInf) m_f = m_use;
-            float fold = exp2_hw(m - m_f);               // 0 before the first tile
-            if (__any(m_use - m_f > kRebase)) {          // keep acc far from overflow
-              const float r = exp2_hw(m_f - m_use);
-#pragma unroll
-              for (int c = 0; c < G::NC; ++c)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[c][v] *= r;
-              fold *= r;
-              m_f = m_use;
-            }
-#pragma unroll
-            for (int c = 0; c < G::NC; ++c) {
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(fold, static_cast<float>(acc_i[c][v]), acc[c][v]);
-              acc_i[c] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-            }
-            int_tiles = 0;
-          }
-          pv_tile<D, false>(acc_i, sg, pv, lr, g);
-          ++int_tiles;
-        }
-        m = m_new;
-      }
+      for (int c = 0; c < G::NC; ++c) acc_i[c] = zero16();
     }
+    const KStage& ks_nxt = sm.ks[(t + 1) % 3];
+    const bool mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
+    float u[NKB][16];
+    float mx;
+    if (!mask) {
+      pv_tile<D>(acc_i, sm.vs[(t + 1) & 1], p_prev, lr, g);     // V stage of tile t-1
+      mx = dequant_tile<false>(s_cur, ks_cur, u, k0, lim, a.Lkv, g);
+      interleave<8, 11>();
+    } else {
+      pv_tile<D>(acc_i, sm.vs[(t + 1) & 1], p_prev, lr, g);
+      mx = dequant_tile<true>(s_cur, ks_cur, u, k0, lim, a.Lkv, g);
+    }
+    ++int_tiles;
 
-    if (more) store_tile<D, VPT, DUMP>(sm.stage[(t + 1) & 1], nx);
+    // ---- softmax(t): running max, 127 P_tilde, row sum, P_hat; QK(t+1) alongside ----
+    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;   // c2 >= 0: max(u) c2 == max(u c2)
+    const float m_new = fmaxf(m, mx2);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = exp2_hw(m - m_use);            // 1 if unchanged, 0 on the first tile
+    const float bias = m_use - kLog2_127;              // exp2(u c2 - bias) = 127 P_tilde
+    float rst = 0.0f, st_cur = 0.0f;
+    if constexpr (VPT) {
+      st_cur = ks_cur.stp[0];
+#pragma unroll
+      for (int i = 1; i < BN / 64; ++i) st_cur = fmaxf(st_cur, ks_cur.stp[i]);
+      rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
+    }
+    const bool clamp = __any(fabsf(m_use) >= kClampAbove);
+    float lsum;
+    if (!mask && !clamp) {
+      qk_tile<D>(s_nxt, ks_nxt, qf, lr, g);
+      lsum = probs_tile<VPT, false, false>(u, c2, bias, ks_cur, rst, p_cur, g);
+      interleave<8, 16>();
+    } else {
+      qk_tile<D>(s_nxt, ks_nxt, qf, lr, g);
+      if (!clamp)
+        lsum = probs_tile<VPT, true, false>(u, c2, bias, ks_cur, rst, p_cur, g);
+      else
+        lsum = mask ? probs_tile<VPT, true, true>(u, c2, bias, ks_cur, rst, p_cur, g)
+                    : probs_tile<VPT, false, true>(u, c2, bias, ks_cur, rst, p_cur, g);
+    }
+    l = alpha * l + lsum;
+
+    if constexpr (VPT) {
+      // per-token V: tile scales differ, so each tile's INT32 product is
+      // converted on its own: acc = alpha(t-1) acc + s_t(t-1) PV(t-1)
+#pragma unroll
+      for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          acc[c][v] = __builtin_fmaf(alpha_prev, acc[c][v], st_prev * static_cast<float>(acc_i[c][v]));
+      alpha_prev = alpha;
+      st_prev = st_cur;
+    } else if (__any(m_new > m) || int_tiles >= kMaxIntTiles) {
+      // tile t raised some row's max: the INT32 run (tiles before t, frame m)
+      // goes into acc (frame m_f) before PV(t) starts a new run
+      if (m_f == kNegInf) m_f = m_use;
+      float f = exp2_hw(m - m_f);                     // 0 before the first tile
+      float r = 1.0f;
+      if (__any(m_use - m_f > kRebase)) {             // keep acc far from overflow
+        r = exp2_hw(m_f - m_use);
+        f *= r;
+        m_f = m_use;
+      }
+#pragma unroll
+      for (int c = 0; c < G::NC; ++c) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float4 x = acc_lds[(c * 4 + q) * 64];
+          x.x = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 0]), x.x * r);
+          x.y = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 1]), x.y * r);
+          x.z = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 2]), x.z * r);
+          x.w = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 3]), x.w * r);
+          acc_lds[(c * 4 + q) * 64] = x;
+        }
+        acc_i[c] = zero16();
+      }
+      int_tiles = 0;
+    }
+    m = m_new;
+
+    // ---- stage K(t+2) and V(t) for the next iterations ----
+    if (t + 2 < n_tiles) store_k<D, true, VPT>(sm.ks[(t + 2) % 3], kx, mp);
+    store_v<D>(sm.vs[t & 1], vx, mp);
     __syncthreads();
-  }
+  };
 
-  if constexpr (DUMP) return;
-  if (!wave_live) return;
-  if constexpr (!VPT) {
+  // unrolled by two so the current / next buffers swap roles without copies
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, s_a, s_b, p_a, p_b);
+    step(t + 1, s_b, s_a, p_b, p_a);
+  }
+  if (t < n_tiles) {
+    step(t, s_a, s_b, p_a, p_b);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) p_a[kb] = p_b[kb];
+  }
+  // p_a now holds P_hat of the last tile
+
+  // ---- PV of the last tile ----
+  if constexpr (VPT) {
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) acc_i[c] = zero16();
+    pv_tile<D>(acc_i, sm.vs[(n_tiles - 1) & 1], p_a, lr, g);
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        acc[c][v] = __builtin_fmaf(alpha_prev, acc[c][v], st_prev * static_cast<float>(acc_i[c][v]));
+  } else {
+    pv_tile<D>(acc_i, sm.vs[(n_tiles - 1) & 1], p_a, lr, g);
     // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run
     const float back = exp2_hw(m_f - m);
 #pragma unroll
     for (int c = 0; c < G::NC; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(back, acc[c][v], static_cast<float>(acc_i[c][v]));
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = acc_lds[(c * 4 + q) * 64];
+        acc[c][4 * q + 0] = __builtin_fmaf(back, x.x, static_cast<float>(acc_i[c][4 * q + 0]));
+        acc[c][4 * q + 1] = __builtin_fmaf(back, x.y, static_cast<float>(acc_i[c][4 * q + 1]));
+        acc[c][4 * q + 2] = __builtin_fmaf(back, x.z, static_cast<float>(acc_i[c][4 * q + 2]));
+        acc[c][4 * q + 3] = __builtin_fmaf(back, x.w, static_cast<float>(acc_i[c][4 * q + 3]));
+      }
   }
+
   const float ltot = pair_sum(l);                      // 127 * l
   if (!qvalid) return;
   const float scale = (VPT ? 1.0f : a.s_v[0]) / ltot;
@@ -483,32 +627,87 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   if (a.lse && g == 0) a.lse[q_base + qi] = (m + __builtin_log2f(ltot) - kLog2_127) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool DUMP>
+// Logits dump: the same K staging and Q.K^T tile code as the forward, writing
+// the exact INT32 logit of every visible pair.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_logits_kernel(FwdArgs a) {
+  __shared__ KStage ks;
+  const int bh = blockIdx.x;
+  const int rb = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int hk = h / (a.H / a.Hkv);
+  const int64_t kv_base = (static_cast<int64_t>(b) * a.Hkv + hk) * a.Lkv;
+  const int64_t q_base = static_cast<int64_t>(bh) * a.Lq;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 5, lr = lane & 31;
+  const int qi = rb * BM + (tid >> 6) * 32 + lr;
+  const bool qvalid = qi < a.Lq;
+  const int lim = CAUSAL ? qi + (a.Lkv - a.Lq) : a.Lkv - 1;
+  const Bufs bf = make_bufs(a, kv_base, D, false, false);
+  Map<D> mp;
+  mp.init(tid);
+  v4i qf[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    qf[c] = v4i{0, 0, 0, 0};
+    if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
+  }
+  const int last_q = min(rb * BM + BM - 1, a.Lq - 1);
+  const int kv_end = CAUSAL ? min(a.Lkv, last_q + (a.Lkv - a.Lq) + 1) : a.Lkv;
+  for (int k0 = 0; k0 < kv_end; k0 += BN) {
+    KRegs<D> kx;
+    load_k<D, false, false>(kx, bf, mp, k0);
+    __syncthreads();
+    store_k<D, false, false>(ks, kx, mp);
+    __syncthreads();
+    v16i s[NKB];
+    qk_tile<D>(s, ks, qf, lr, g);
+    if (qvalid) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
+        }
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
 hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(n_rb));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, DUMP>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool DUMP>
+template <int D, bool CAUSAL>
 hipError_t launch_vo(const FwdArgs& a, hipStream_t st) {
-  if (DUMP) return launch_t<D, CAUSAL, false, false, DUMP>(a, st);
   if (a.v_per_token)
-    return a.o_f16 ? launch_t<D, CAUSAL, true, true, DUMP>(a, st) : launch_t<D, CAUSAL, true, false, DUMP>(a, st);
-  return a.o_f16 ? launch_t<D, CAUSAL, false, true, DUMP>(a, st) : launch_t<D, CAUSAL, false, false, DUMP>(a, st);
+    return a.o_f16 ? launch_t<D, CAUSAL, true, true>(a, st) : launch_t<D, CAUSAL, true, false>(a, st);
+  return a.o_f16 ? launch_t<D, CAUSAL, false, true>(a, st) : launch_t<D, CAUSAL, false, false>(a, st);
 }
 
-template <bool DUMP>
-hipError_t launch_any(const FwdArgs& a, hipStream_t st) {
-  if (a.d == 64)
-    return a.causal ? launch_vo<64, true, DUMP>(a, st) : launch_vo<64, false, DUMP>(a, st);
-  return a.causal ? launch_vo<128, true, DUMP>(a, st) : launch_vo<128, false, DUMP>(a, st);
+template <int D, bool CAUSAL>
+hipError_t launch_logits_t(const FwdArgs& a, hipStream_t st) {
+  const int n_rb = (a.Lq + BM - 1) / BM;
+  const dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(n_rb));
+  hipLaunchKernelGGL((attn_logits_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const FwdArgs& a, hipStream_t st) { return launch_any<false>(a, st); }
-hipError_t launch_debug_logits(const FwdArgs& a, hipStream_t st) { return launch_any<true>(a, st); }
+hipError_t launch_prefill(const FwdArgs& a, hipStream_t st) {
+  if (a.d == 64) return a.causal ? launch_vo<64, true>(a, st) : launch_vo<64, false>(a, st);
+  return a.causal ? launch_vo<128, true>(a, st) : launch_vo<128, false>(a, st);
+}
+
+hipError_t launch_debug_logits(const FwdArgs& a, hipStream_t st) {
+  if (a.d == 64) return a.causal ? launch_logits_t<64, true>(a, st) : launch_logits_t<64, false>(a, st);
+  return a.causal ? launch_logits_t<128, true>(a, st) : launch_logits_t<128, false>(a, st);
+}
 
 }  // namespace attn

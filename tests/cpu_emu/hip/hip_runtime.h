@@ -219,6 +219,33 @@ inline uint32_t cvt_pk_u8_f32(float f, int byte, uint32_t old) {
   return (old & ~(0xffu << (8 * byte))) | (v << (8 * byte));
 }
 
+// raw buffer resource: base address and size in bytes; loads at or past the
+// end return 0 per dword, as the hardware's range check does for raw buffers
+struct BufRsrc {
+  const unsigned char* base;
+  uint32_t n;
+};
+inline BufRsrc make_buffer_rsrc(const void* base, int n) { return {static_cast<const unsigned char*>(base), static_cast<uint32_t>(n)}; }
+template <int NDW>
+inline void buffer_load(const BufRsrc& r, uint32_t voff, uint32_t soff, uint32_t* out) {
+  for (int i = 0; i < NDW; ++i) {
+    const uint64_t off = static_cast<uint64_t>(voff) + soff + 4u * i;
+    if (off + 4 <= r.n) std::memcpy(&out[i], r.base + off, 4);
+    else out[i] = 0u;
+  }
+}
+typedef int emu_v4i __attribute__((ext_vector_type(4)));
+typedef int emu_v2i __attribute__((ext_vector_type(2)));
+inline uint32_t raw_buffer_load_b32(const BufRsrc& r, uint32_t voff, uint32_t soff) {
+  uint32_t v; buffer_load<1>(r, voff, soff, &v); return v;
+}
+inline emu_v2i raw_buffer_load_b64(const BufRsrc& r, uint32_t voff, uint32_t soff) {
+  uint32_t v[2]; buffer_load<2>(r, voff, soff, v); emu_v2i o; std::memcpy(&o, v, 8); return o;
+}
+inline emu_v4i raw_buffer_load_b128(const BufRsrc& r, uint32_t voff, uint32_t soff) {
+  uint32_t v[4]; buffer_load<4>(r, voff, soff, v); emu_v4i o; std::memcpy(&o, v, 16); return o;
+}
+
 inline float bits_to_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
 
@@ -237,6 +264,15 @@ inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); ret
 #define __builtin_amdgcn_permlane32_swap(x, y, fi, bc) emu::permlane32_swap(x, y)
 #define __builtin_amdgcn_cvt_pk_u8_f32(f, b, old) emu::cvt_pk_u8_f32(f, b, old)
 #define __any(p) emu::wave_any(p)
+#define __builtin_amdgcn_readfirstlane(x) (x)
+typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;
+#define __builtin_amdgcn_make_buffer_rsrc(base, stride, n, flags) emu::make_buffer_rsrc(base, n)
+#define __builtin_amdgcn_raw_buffer_load_b32(r, v, s, aux) emu::raw_buffer_load_b32(r, v, s)
+#define __builtin_amdgcn_raw_buffer_load_b64(r, v, s, aux) emu::raw_buffer_load_b64(r, v, s)
+#define __builtin_amdgcn_raw_buffer_load_b128(r, v, s, aux) emu::raw_buffer_load_b128(r, v, s)
+#define __builtin_amdgcn_sched_group_barrier(m, n, id) ((void)0)
+#define __builtin_amdgcn_sched_barrier(m) ((void)0)
+#define __builtin_amdgcn_s_setprio(p) ((void)0)
 #define hipLaunchKernelGGL(K, G, B, S, ST, ...) emu::launch(G, B, [&]() { K(__VA_ARGS__); })
 
 using std::max;
