@@ -71,9 +71,8 @@ constexpr int kMaxIntTiles = 32768 / BN;
 // re-base the fp32 accumulator when the running max has grown by this much
 // (base 2) since its frame was set
 constexpr float kRebase = 60.0f;
-// beyond this |running max| (base 2) the fp32 rounding of the exponent
-// argument could push the max key's 127 P_tilde past 127.5
-constexpr float kClampAbove = 32768.0f;
+// relative guard on the softmax bias (see the tile loop)
+constexpr float kBiasGuard = 4.76837158203125e-07f;   // 2^-21
 
 template <int D>
 struct Geo {
@@ -116,16 +115,11 @@ struct KStage {
 struct VStage {
   alignas(16) int8_t vt[128 * (BN + 16)];
 };
-// For per-tensor V the fp32 accumulator is touched only when a fold happens,
-// so it lives in LDS (16 KB per wavefront at d = 128), lane-contiguous in
-// float4 units: the accumulator values (c, 4q..4q+3) of lane l sit at float
-// offset ((wave * NC + c) * 4 + q) * 256 + 4 l, so every access is a
-// conflict-free 1 KB wavefront transfer.
-template <int D, bool LDS_ACC>
+// K and V stages are double-buffered: a stage is rewritten one barrier after
+// its last read.
 struct Smem {
-  KStage ks[3];
+  KStage ks[2];
   VStage vs[2];
-  alignas(16) float acc[LDS_ACC ? 4 * (D / 32) * 16 * 64 : 4];
 };
 
 struct Bufs {
@@ -284,10 +278,13 @@ __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const VStage& vs, c
 }
 
 // u = S_int * s_K[j] for this lane's keys (the query's factor c2 comes
-// later); masked keys get -inf. Returns the max over the lane pair.
+// later); masked keys get -inf. rel = (last visible key of the row) - k0 -
+// 4 g, so key index j of the tile is visible iff (j - 4 g) <= rel, a compare
+// of a compile-time constant with one per-lane value. Returns the max over
+// the lane pair.
 template <bool MASK>
-__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage& ks, float (&u)[NKB][16], int k0,
-                                              int lim, int Lkv, int g) {
+__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage& ks, float (&u)[NKB][16], int rel,
+                                              int g) {
   // the maximum is taken as a tree (independent partial maxima), so a single
   // wavefront per SIMD is not held up by a long dependency chain
   float gm[NKB * 4];
@@ -301,10 +298,7 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = static_cast<float>(s[kb][j4 * 4 + e]) * skk[e];
-        if constexpr (MASK) {
-          const int key = k0 + jl + e;
-          x = (key < Lkv && key <= lim) ? x : kNegInf;
-        }
+        if constexpr (MASK) x = (kb * 32 + j4 * 8 + e <= rel) ? x : kNegInf;
         u[kb][j4 * 4 + e] = x;
       }
       const float* x = &u[kb][j4 * 4];
@@ -321,9 +315,7 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage
 
 // y = exp2(u c2 - bias) = 127 P_tilde; returns this lane's sum of y and packs
 // P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV operands.
-// CLAMP: when |running max| >= kClampAbove, y is clamped to 127 (the value the
-// max key has exactly), since exponent rounding could otherwise give 128.
-template <bool VPT, bool MASK, bool CLAMP>
+template <bool VPT, bool MASK>
 __device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2, float bias, const KStage& ks,
                                             float rst, v4i (&pv)[NKB], int g) {
   float gs[NKB * 4];                   // partial row sums, added as a tree
@@ -344,7 +336,6 @@ __device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2,
         const float uu = u[kb][j4 * 4 + e];
         y[e] = exp2_hw(__builtin_fmaf(uu, c2, -bias));
         if constexpr (MASK) y[e] = (uu == kNegInf) ? 0.0f : y[e];
-        if constexpr (CLAMP) y[e] = fminf(y[e], 127.0f);
         word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
       }
       gs[kb * 4 + j4] = (y[0] + y[1]) + (y[2] + y[3]);
@@ -378,14 +369,27 @@ __device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int
   return bf;
 }
 
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a) {
-  using G = Geo<D>;
-  constexpr bool kLdsAcc = !VPT;
-  __shared__ Smem<D, kLdsAcc> sm;
+// Workgroup -> (b*h, row block). Workgroups are dealt to the 8 XCDs round
+// robin, so consecutive ids land on different XCDs (each with its own L2);
+// the id is re-numbered so that each XCD walks whole heads, row blocks of a
+// head back to back (longest causal block first). The workgroups resident on
+// one XCD then share the K/V of two or three heads.
+__device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
+  const int n = gridDim.x, id = blockIdx.x;
+  const int xcd = id & 7, slot = id >> 3;
+  const int w = xcd * (n >> 3) + min(xcd, n & 7) + slot;
+  bh = w / n_rb;
+  rb = n_rb - 1 - (w - bh * n_rb);
+}
 
-  const int bh = blockIdx.x;
-  const int rb = gridDim.y - 1 - blockIdx.y;          // longest (causal) row blocks first
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
+  using G = Geo<D>;
+  __shared__ Smem sm;
+
+  const int n_rb = (a.Lq + BM - 1) / BM;
+  int bh, rb;
+  tile_of_block(n_rb, bh, rb);
   const int b = bh / a.H, h = bh % a.H;
   const int hk = h / (a.H / a.Hkv);
   const int64_t kv_base = (static_cast<int64_t>(b) * a.Hkv + hk) * a.Lkv;
@@ -424,78 +428,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a) {
 
   // softmax state: running max (base 2), partial sum of 127 P_tilde over this lane's keys
   float m = kNegInf, l = 0.0f;
-  float acc[G::NC][16];                // fp32 O^T accumulator (registers: per-token V)
+  float acc[G::NC][16];                // fp32 O^T accumulator
   v16i acc_i[G::NC];                   // INT32 accumulation of P_hat . V_hat
-  float4* const acc_lds = reinterpret_cast<float4*>(sm.acc) + wave * (G::NC * 4 * 64) + lane;
 #pragma unroll
   for (int c = 0; c < G::NC; ++c) {
     acc_i[c] = zero16();
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
-    if constexpr (kLdsAcc) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc_lds[(c * 4 + q) * 64] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
   }
   float m_f = kNegInf;                 // frame of acc (per-tensor V)
-  int int_tiles = 0;
-  float alpha_prev = 1.0f, st_prev = 0.0f;   // per-token V: rescale and V scale of the previous tile
+  int int_tiles = 0;                   // tiles in the current INT32 run
 
-  // ---- prologue: K(0), K(1) staged; S(0) computed ----
+  // ---- prologue: K(0), V(0) staged ----
   KRegs<D> kx;
   VRegs<D> vx;
   load_k<D, true, VPT>(kx, bf, mp, 0);
+  load_v<D>(vx, bf, mp, 0);
   store_k<D, true, VPT>(sm.ks[0], kx, mp);
-  if (n_tiles > 1) {
-    load_k<D, true, VPT>(kx, bf, mp, BN);
-    store_k<D, true, VPT>(sm.ks[1], kx, mp);
-  }
+  store_v<D>(sm.vs[0], vx, mp);
   __syncthreads();
 
-  v16i s_a[NKB], s_b[NKB];             // S of the current / next tile (roles swap every tile)
-  v4i p_a[NKB], p_b[NKB];              // P_hat of the previous / current tile
-  qk_tile<D>(s_a, sm.ks[0], qf, lr, g);
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) p_a[kb] = v4i{0, 0, 0, 0};
-
-  // One tile of the pipeline: PV(t-1) [MFMA] | dequant(t) [VALU] |
-  // QK(t+1) [MFMA] | softmax(t) [VALU] | fold | stage K(t+2), V(t) | barrier.
-  auto step = [&](int t, v16i (&s_cur)[NKB], v16i (&s_nxt)[NKB], const v4i (&p_prev)[NKB], v4i (&p_cur)[NKB])
-      __attribute__((always_inline)) {
+  // One tile: QK(t) [MFMA] | dequant, softmax(t) [VALU] | fold | PV(t)
+  // [MFMA] | stage K(t+1), V(t+1) | barrier. The wavefront of the other
+  // workgroup on the same SIMD issues its VALU work while this one waits on
+  // the matrix core, and the other way round.
+  for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * BN;
-    const KStage& ks_cur = sm.ks[t % 3];
-    // global loads for later tiles, in flight during this tile's math
-    if (t + 2 < n_tiles) load_k<D, true, VPT>(kx, bf, mp, k0 + 2 * BN);
-    load_v<D>(vx, bf, mp, k0);
-
-    // PV(t-1) runs unconditionally (P of "tile -1" is zero) and QK(t+1) reads
-    // a stale stage past the last tile (its result is unused), so the common
-    // case below is two straight-line blocks: [PV(t-1) MFMAs | dequant(t)]
-    // and [QK(t+1) MFMAs | softmax(t)], each interleaved by the scheduler.
-    if constexpr (VPT) {
-#pragma unroll
-      for (int c = 0; c < G::NC; ++c) acc_i[c] = zero16();
+    const KStage& ks_cur = sm.ks[t & 1];
+    const bool more = t + 1 < n_tiles;
+    // global loads of the next tile, in flight during this tile's math
+    if (more) {
+      load_k<D, true, VPT>(kx, bf, mp, k0 + BN);
+      load_v<D>(vx, bf, mp, k0 + BN);
     }
-    const KStage& ks_nxt = sm.ks[(t + 1) % 3];
+    v16i s[NKB];
+    qk_tile<D>(s, ks_cur, qf, lr, g);
     const bool mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
+    // key index j of the tile is visible iff j - 4 g <= rel
+    const int rel = mask ? min(lim, a.Lkv - 1) - k0 - 4 * g : BN;
     float u[NKB][16];
-    float mx;
-    if (!mask) {
-      pv_tile<D>(acc_i, sm.vs[(t + 1) & 1], p_prev, lr, g);     // V stage of tile t-1
-      mx = dequant_tile<false>(s_cur, ks_cur, u, k0, lim, a.Lkv, g);
-      interleave<8, 11>();
-    } else {
-      pv_tile<D>(acc_i, sm.vs[(t + 1) & 1], p_prev, lr, g);
-      mx = dequant_tile<true>(s_cur, ks_cur, u, k0, lim, a.Lkv, g);
-    }
-    ++int_tiles;
+    const float mx = dequant_tile<true>(s, ks_cur, u, rel, g);
 
-    // ---- softmax(t): running max, 127 P_tilde, row sum, P_hat; QK(t+1) alongside ----
+    // ---- softmax(t): running max, 127 P_tilde, row sum, P_hat ----
     const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;   // c2 >= 0: max(u) c2 == max(u c2)
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = exp2_hw(m - m_use);            // 1 if unchanged, 0 on the first tile
-    const float bias = m_use - kLog2_127;              // exp2(u c2 - bias) = 127 P_tilde
+    // exp2(u c2 - bias) = 127 P_tilde. The guard term |m| 2^-21 keeps the
+    // max key's value below 127.5 however large |m| is (the fp32 rounding of
+    // u c2 and of the bias grows with |m|); P_hat and the row sum scale
+    // together, so it cancels in O.
+    const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
     float rst = 0.0f, st_cur = 0.0f;
     if constexpr (VPT) {
       st_cur = ks_cur.stp[0];
@@ -503,103 +486,62 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(FwdArgs a) {
       for (int i = 1; i < BN / 64; ++i) st_cur = fmaxf(st_cur, ks_cur.stp[i]);
       rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
     }
-    const bool clamp = __any(fabsf(m_use) >= kClampAbove);
-    float lsum;
-    if (!mask && !clamp) {
-      qk_tile<D>(s_nxt, ks_nxt, qf, lr, g);
-      lsum = probs_tile<VPT, false, false>(u, c2, bias, ks_cur, rst, p_cur, g);
-      interleave<8, 16>();
-    } else {
-      qk_tile<D>(s_nxt, ks_nxt, qf, lr, g);
-      if (!clamp)
-        lsum = probs_tile<VPT, true, false>(u, c2, bias, ks_cur, rst, p_cur, g);
-      else
-        lsum = mask ? probs_tile<VPT, true, true>(u, c2, bias, ks_cur, rst, p_cur, g)
-                    : probs_tile<VPT, false, true>(u, c2, bias, ks_cur, rst, p_cur, g);
-    }
+    v4i p[NKB];
+    const float lsum = probs_tile<VPT, true>(u, c2, bias, ks_cur, rst, p, g);
     l = alpha * l + lsum;
 
+    if constexpr (!VPT) {
+      if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
+        // tile t raised some row's max: the INT32 run (tiles before t, frame
+        // m) goes into acc (frame m_f) before PV(t) starts a new run
+        if (m_f == kNegInf) m_f = m_use;
+        float f = exp2_hw(m - m_f);                   // 0 before the first tile
+        float r = 1.0f;
+        if (__any(m_use - m_f > kRebase)) {           // keep acc far from overflow
+          r = exp2_hw(m_f - m_use);
+          f *= r;
+          m_f = m_use;
+        }
+#pragma unroll
+        for (int c = 0; c < G::NC; ++c) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(f, static_cast<float>(acc_i[c][v]), acc[c][v] * r);
+          acc_i[c] = zero16();
+        }
+        int_tiles = 1;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < G::NC; ++c) acc_i[c] = zero16();
+    }
+    m = m_new;
+
+    pv_tile<D>(acc_i, sm.vs[t & 1], p, lr, g);
     if constexpr (VPT) {
       // per-token V: tile scales differ, so each tile's INT32 product is
-      // converted on its own: acc = alpha(t-1) acc + s_t(t-1) PV(t-1)
+      // converted on its own: acc = alpha acc + s_t PV(t)
 #pragma unroll
       for (int c = 0; c < G::NC; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          acc[c][v] = __builtin_fmaf(alpha_prev, acc[c][v], st_prev * static_cast<float>(acc_i[c][v]));
-      alpha_prev = alpha;
-      st_prev = st_cur;
-    } else if (__any(m_new > m) || int_tiles >= kMaxIntTiles) {
-      // tile t raised some row's max: the INT32 run (tiles before t, frame m)
-      // goes into acc (frame m_f) before PV(t) starts a new run
-      if (m_f == kNegInf) m_f = m_use;
-      float f = exp2_hw(m - m_f);                     // 0 before the first tile
-      float r = 1.0f;
-      if (__any(m_use - m_f > kRebase)) {             // keep acc far from overflow
-        r = exp2_hw(m_f - m_use);
-        f *= r;
-        m_f = m_use;
-      }
-#pragma unroll
-      for (int c = 0; c < G::NC; ++c) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 x = acc_lds[(c * 4 + q) * 64];
-          x.x = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 0]), x.x * r);
-          x.y = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 1]), x.y * r);
-          x.z = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 2]), x.z * r);
-          x.w = __builtin_fmaf(f, static_cast<float>(acc_i[c][4 * q + 3]), x.w * r);
-          acc_lds[(c * 4 + q) * 64] = x;
-        }
-        acc_i[c] = zero16();
-      }
-      int_tiles = 0;
+          acc[c][v] = __builtin_fmaf(alpha, acc[c][v], st_cur * static_cast<float>(acc_i[c][v]));
     }
-    m = m_new;
 
-    // ---- stage K(t+2) and V(t) for the next iterations ----
-    if (t + 2 < n_tiles) store_k<D, true, VPT>(sm.ks[(t + 2) % 3], kx, mp);
-    store_v<D>(sm.vs[t & 1], vx, mp);
+    // ---- stage K(t+1), V(t+1) ----
+    if (more) {
+      store_k<D, true, VPT>(sm.ks[(t + 1) & 1], kx, mp);
+      store_v<D>(sm.vs[(t + 1) & 1], vx, mp);
+    }
     __syncthreads();
-  };
-
-  // unrolled by two so the current / next buffers swap roles without copies
-  int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(t, s_a, s_b, p_a, p_b);
-    step(t + 1, s_b, s_a, p_b, p_a);
   }
-  if (t < n_tiles) {
-    step(t, s_a, s_b, p_a, p_b);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) p_a[kb] = p_b[kb];
-  }
-  // p_a now holds P_hat of the last tile
 
-  // ---- PV of the last tile ----
-  if constexpr (VPT) {
-#pragma unroll
-    for (int c = 0; c < G::NC; ++c) acc_i[c] = zero16();
-    pv_tile<D>(acc_i, sm.vs[(n_tiles - 1) & 1], p_a, lr, g);
-#pragma unroll
-    for (int c = 0; c < G::NC; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        acc[c][v] = __builtin_fmaf(alpha_prev, acc[c][v], st_prev * static_cast<float>(acc_i[c][v]));
-  } else {
-    pv_tile<D>(acc_i, sm.vs[(n_tiles - 1) & 1], p_a, lr, g);
+  if constexpr (!VPT) {
     // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run
     const float back = exp2_hw(m_f - m);
 #pragma unroll
     for (int c = 0; c < G::NC; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 x = acc_lds[(c * 4 + q) * 64];
-        acc[c][4 * q + 0] = __builtin_fmaf(back, x.x, static_cast<float>(acc_i[c][4 * q + 0]));
-        acc[c][4 * q + 1] = __builtin_fmaf(back, x.y, static_cast<float>(acc_i[c][4 * q + 1]));
-        acc[c][4 * q + 2] = __builtin_fmaf(back, x.z, static_cast<float>(acc_i[c][4 * q + 2]));
-        acc[c][4 * q + 3] = __builtin_fmaf(back, x.w, static_cast<float>(acc_i[c][4 * q + 3]));
-      }
+      for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(back, acc[c][v], static_cast<float>(acc_i[c][v]));
   }
 
   const float ltot = pair_sum(l);                      // 127 * l
@@ -678,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void attn_logits_kernel(FwdArgs a) {
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
 hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
-  const dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(n_rb));
+  const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
   hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
