@@ -13,18 +13,26 @@
 // ------------------
 // One workgroup = 4 wavefronts = kPrefillBM (128) query rows of one (b, h);
 // each wavefront owns 32 rows. K/V stream through LDS in tiles of kPrefillBN
-// (64) keys shared by the 4 wavefronts.
+// (64) keys shared by the 4 wavefronts. Two workgroups share a CU (256 VGPRs
+// per lane at d = 128): while one wavefront of a SIMD waits on the matrix
+// core, the other issues its softmax arithmetic.
 //
 // Both products use v_mfma_i32_32x32x32_i8. The logits are computed
-// transposed, S^T = K_hat . Q_hat^T, so that in the 32x32 INT32 result every
-// lane holds 16 keys of ONE query (lane l: query l % 32, keys
-// (v/4)*8 + (l/32)*4 + v%4 for accumulator v): row max and row sum need one
-// cross-half step (v_permlane32_swap). The quantized probabilities of a lane
-// are exactly the 16 int8 B-operand values of O^T = V_hat^T . P_hat^T for the
-// same 32 keys, so P never leaves registers. V tiles are transposed while
-// staged (4x4 byte transposes with v_perm) and stored in the key order the P
-// operand implies, so each operand fetch is one 16-byte LDS read. O^T keeps
-// the query in the lane, so the per-row rescale is lane-local.
+// transposed, S^T = K_hat . Q_hat^T, so that every lane holds keys of ONE
+// query: row max and row sum need one cross-half step (v_permlane32_swap).
+// The K operand rows are read in a permuted order chosen so that lane l holds
+// the 16 CONSECUTIVE keys 16 (l / 32) .. +15 of each 32-key block; those 16
+// values, quantized, are exactly the lane's B operand of O^T = V_hat^T .
+// P_hat^T, so P never leaves registers. O^T keeps the query in the lane, so
+// the per-row rescale is lane-local.
+//
+// Staging. K and V tiles go from HBM straight into LDS (buffer loads with
+// the LDS destination: no registers, no LDS store instructions), in their
+// natural [key][channel] layout with the 16-byte chunks of each row XOR-
+// swizzled. The V^T operand is read with ds_read_b64_tr_b8, which hands each
+// lane 8 consecutive keys of one channel. Three stages form a ring: tile t+2
+// is requested while tile t is computed, and a stage is waited for one tile
+// after it was requested.
 //
 // Instruction budget. On gfx950 the issue time of the VALU work per
 // (query, key) pair is the first-order cost next to the pair's MFMA work, so
@@ -33,19 +41,11 @@
 // v_exp_f32, one add for the row sum and one v_cvt_pk_u8_f32 (round to
 // nearest even, saturating) that quantizes P and packs it into the MFMA
 // operand. Everything else is per tile or per workgroup:
-//  - loads use raw buffer resources built once per workgroup: the tile offset
-//    is the scalar offset, per-lane offsets never change, and out-of-range
-//    keys read as zero in hardware (no compares, no 64-bit address math);
 //  - for per-tensor V the P_hat . V_hat products keep accumulating in the
 //    INT32 MFMA accumulator while no row of the wavefront raises its max and
-//    are folded into the fp32 accumulator (which keeps its own frame, and
-//    lives in LDS since only folds touch it) only when one does; s_V is
-//    applied once in the epilogue;
+//    are folded into the fp32 accumulator (which keeps its own frame) only
+//    when one does; s_V is applied once in the epilogue;
 //  - masking code runs only on diagonal / ragged tiles.
-// Software pipeline: iteration t issues the MFMAs of QK(t+1) and PV(t-1)
-// next to the VALU work of softmax(t) and of dequantizing S(t+1), so the
-// matrix core works while the VALU computes probabilities. K stages are
-// triple-buffered and V stages double-buffered; each tile has one barrier.
 #include "attn_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -53,13 +53,18 @@
 namespace attn {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
 constexpr int NKB = BN / 32;                 // 32-key blocks per tile
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kStages = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_127 = 6.988684686772166f;
@@ -74,231 +79,178 @@ constexpr float kRebase = 60.0f;
 // relative guard on the softmax bias (see the tile loop)
 constexpr float kBiasGuard = 4.76837158203125e-07f;   // 2^-21
 
-template <int D>
-struct Geo {
-  static constexpr int KSTR = D + 16;             // LDS bytes per K row (padding spreads banks)
-  static constexpr int VSTR = BN + 16;            // LDS bytes per V^T row
-  static constexpr int NC = D / 32;               // 32-channel chunks of the head dim
-  static constexpr int KPT = BN * D / 16 / kThreads;            // 16-byte K chunks per thread
-  static constexpr int VITEMS = (D / 4) * (BN / 8);             // (channel quad, key octet) items
-  static constexpr int VPT_ITEMS = (VITEMS + kThreads - 1) / kThreads;
-};
-
 __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Transpose a 4x4 byte block: r[i] holds bytes (row i, cols 0..3); returns
-// c[j] holding bytes (rows 0..3, col j).
-__device__ __forceinline__ void transpose4x4(const uint32_t* r, uint32_t* c) {
-  const uint32_t lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
-  const uint32_t hi01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
-  const uint32_t lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
-  const uint32_t hi23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
-  c[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);  // r0b0 r1b0 r2b0 r3b0
-  c[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-  c[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-  c[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most N vector-memory loads are outstanding and
+// all LDS operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier without a memory fence: the waits above are the only
+// ones the stage protocol needs (a fenced barrier would also wait for the
+// stage requested two tiles ahead). The empty asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// K stage: K rows (padded), per-key s_K, per-token V scales and the partial
-// maxima of those scales (one per wavefront that loaded them).
-struct KStage {
-  alignas(16) int8_t k[BN * (128 + 16)];
+// LDS-destination buffer loads (16 or 4 bytes per lane, lane l's bytes at
+// dst + size l) and the transposing LDS read, as plain functions: the
+// gfx950-only forms are checked in the host compilation pass too, where a
+// template would turn the check into a substitution failure.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+}
+
+// One pipeline stage: a K tile and a V tile ([key][channel], 16-byte chunks
+// swizzled per row), s_K and s_V of the tile's keys.
+template <int D>
+struct Stage {
+  alignas(16) int8_t k[BN * D];
+  alignas(16) int8_t v[BN * D];
   alignas(16) float sk[BN];
   alignas(16) float sv[BN];
-  float stp[BN / 64];
 };
-// V stage: V^T rows (one per channel, padded), keys in P-operand order.
-struct VStage {
-  alignas(16) int8_t vt[128 * (BN + 16)];
-};
-// K and V stages are double-buffered: a stage is rewritten one barrier after
-// its last read.
-struct Smem {
-  KStage ks[2];
-  VStage vs[2];
-};
+
+// Position of 16-byte chunk j of tile row r is chunk j ^ swz(r) of that row.
+// The swizzle makes both operand reads conflict-free: the K reads (8 lanes
+// per LDS cycle read keys {0-3, 16-19} + 4i of a block) and the transposed V
+// reads (16 lanes read 8 consecutive keys).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return (r & 7) ^ ((r >> 2) & 4);
+  else return ((r >> 1) & 3) ^ (((r >> 4) & 1) << 1);
+}
+
+// Key held by MFMA row i of the S^T tile: row i = 8 (v / 4) + 4 g + v % 4 of
+// lane group g, register v, carries key 16 g + v.
+__device__ __forceinline__ int key_of_row(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
 
 struct Bufs {
   __amdgpu_buffer_rsrc_t k, v, sk, sv;
 };
 
-// Per-thread load/store offsets (fixed for the whole kernel).
+// Per-lane LDS / global offsets, fixed for the whole kernel.
 template <int D>
-struct Map {
-  using G = Geo<D>;
-  uint32_t k_src[G::KPT];        // byte offset of a 16-byte K chunk within a tile
-  int k_dst[G::KPT];             // its LDS offset within the K stage
-  uint32_t v_src[G::VPT_ITEMS];  // byte offset of key0's channel quad within a tile
-  int v_dst[G::VPT_ITEMS];       // LDS offset of row 4*dq, 8-byte slot of the key octet
-  bool v_live[G::VPT_ITEMS];
+struct Lanes {
+  static constexpr int NC = D / 32;                  // 32-channel chunks of the head dim
+  static constexpr int LPW = BN * D / 1024 / kWaves; // 1 KB stage loads per wavefront per operand
+  uint32_t ld[LPW];   // tile byte offset of the 16-byte chunk this lane moves in load i
+  int koff[NC];       // LDS offset (block 0) of this lane's K operand, channel chunk c
+  int voff[NC];       // LDS offset (block 0, first 8 keys) of this lane's transposed V read
 
-  __device__ __forceinline__ void init(int tid) {
+  __device__ __forceinline__ void init(int wave, int lane) {
+    // a 1 KB load writes lane l's 16 bytes to LDS slot 64 n + l; the lane
+    // fetches the global chunk that the swizzle places in that slot
 #pragma unroll
-    for (int i = 0; i < G::KPT; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / (D / 16), cc = id % (D / 16);
-      k_src[i] = static_cast<uint32_t>(row * D + cc * 16);
-      k_dst[i] = row * G::KSTR + cc * 16;
+    for (int i = 0; i < LPW; ++i) {
+      const int slot = (wave * LPW + i) * 64 + lane;
+      const int r = slot / (D / 16), pos = slot % (D / 16);
+      ld[i] = static_cast<uint32_t>(r * D + (pos ^ swz<D>(r)) * 16);
     }
-    // a wavefront takes 8 channel quads x 8 key octets, so its 8-byte LDS
-    // writes spread over all banks
+    const int lr = lane & 31, g = lane >> 5;
+    const int kr = key_of_row(lr);
 #pragma unroll
-    for (int i = 0; i < G::VPT_ITEMS; ++i) {
-      const int item = tid + i * kThreads;
-      v_live[i] = item < G::VITEMS;
-      const int wc = item / 64, l = item % 64;
-      const int dq = (wc % (D / 32)) * 8 + (l % 8);
-      const int ko = (wc / (D / 32)) * 8 + (l / 8);
-      const int kb = ko / 4, gq = (ko % 4) / 2, hh = ko % 2;
-      const int key0 = kb * 32 + 16 * hh + 4 * gq;     // keys key0..+3 and key0+8..+11
-      v_src[i] = static_cast<uint32_t>(key0 * D + dq * 4);
-      v_dst[i] = (dq * 4) * G::VSTR + kb * 32 + gq * 16 + 8 * hh;
-    }
+    for (int c = 0; c < NC; ++c) koff[c] = kr * D + (((2 * c + g) ^ swz<D>(kr)) * 16);
+    // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte
+    // i % 8 of the rows addressed by lanes 2 b + i / 8 (b = 0..7). Lane
+    // 16 q + i addresses key 16 (q / 2) + i / 2, channels 32 c + 16 (q % 2)
+    // + 8 (i % 2) .. +7, so lane l ends with channel 32 c + l % 32, keys
+    // 16 (l / 32) .. +7.
+    const int q = lane >> 4, i16 = lane & 15;
+    const int vr = 16 * (q >> 1) + (i16 >> 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) voff[c] = vr * D + (((2 * c + (q & 1)) ^ swz<D>(vr)) * 16) + 8 * (i16 & 1);
   }
 };
 
-// Next tiles' data between their global loads and their LDS stores.
-template <int D>
-struct KRegs {
-  v4i k[Geo<D>::KPT];
-  float sk, sv;
-};
-template <int D>
-struct VRegs {
-  uint32_t v[Geo<D>::VPT_ITEMS][8];
-};
-
-// SCALES: also load s_K (and, for per-token V, s_V); the logits-only kernel
-// has no scale pointers and must not touch them.
-template <int D, bool SCALES, bool VPT>
-__device__ __forceinline__ void load_k(KRegs<D>& r, const Bufs& bf, const Map<D>& mp, int k0) {
-  const int tid = threadIdx.x;
+// Request tile k0 into a stage: K (and V) rows plus the scales. Each
+// wavefront issues its scale load first, then LPW loads per operand, so
+// wait_vm_lds<N> with N = 2 LPW (K and V) leaves at most the newest tile's
+// K/V loads in flight.
+template <int D, bool KV, bool VPT>
+__device__ __forceinline__ void request_tile(Stage<D>& st, const Bufs& bf, const Lanes<D>& ln, int wave, int lane,
+                                             int k0) {
+  constexpr int LPW = Lanes<D>::LPW;
+  if (KV) {
+    if (wave == 0) lds_load4(bf.sk, st.sk, lane * 4, k0 * 4);
+    if (VPT && wave == 1) lds_load4(bf.sv, st.sv, lane * 4, k0 * 4);
+  }
   const uint32_t soff = static_cast<uint32_t>(k0) * D;
 #pragma unroll
-  for (int i = 0; i < Geo<D>::KPT; ++i) r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bf.k, mp.k_src[i], soff, 0);
-  r.sk = 0.0f;
-  r.sv = 0.0f;
-  if constexpr (SCALES) {
-    if (tid < BN) r.sk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bf.sk, tid * 4, k0 * 4, 0));
-    if (VPT && tid >= kThreads - BN)
-      r.sv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bf.sv, (tid - (kThreads - BN)) * 4, k0 * 4, 0));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_v(VRegs<D>& r, const Bufs& bf, const Map<D>& mp, int k0) {
-  const uint32_t soff = static_cast<uint32_t>(k0) * D;
-#pragma unroll
-  for (int it = 0; it < Geo<D>::VPT_ITEMS; ++it) {
-    if (!mp.v_live[it]) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r.v[it][i] = __builtin_amdgcn_raw_buffer_load_b32(bf.v, mp.v_src[it] + i * D, soff, 0);
-      r.v[it][4 + i] = __builtin_amdgcn_raw_buffer_load_b32(bf.v, mp.v_src[it] + (8 + i) * D, soff, 0);
-    }
-  }
-}
-
-template <int D, bool SCALES, bool VPT>
-__device__ __forceinline__ void store_k(KStage& s, const KRegs<D>& r, const Map<D>& mp) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < Geo<D>::KPT; ++i) *reinterpret_cast<v4i*>(s.k + mp.k_dst[i]) = r.k[i];
-  if constexpr (SCALES) {
-    if (tid < BN) s.sk[tid] = r.sk;
-    if (VPT && tid >= kThreads - BN) {
-      const int j = tid - (kThreads - BN);
-      s.sv[j] = r.sv;
-      float st = r.sv;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) st = fmaxf(st, __shfl_xor(st, off, 64));
-      if ((j & 63) == 0) s.stp[j >> 6] = st;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_v(VStage& s, const VRegs<D>& r, const Map<D>& mp) {
-  using G = Geo<D>;
-#pragma unroll
-  for (int it = 0; it < G::VPT_ITEMS; ++it) {
-    if (!mp.v_live[it]) continue;
-    uint32_t lo[4], hi[4];
-    transpose4x4(&r.v[it][0], lo);
-    transpose4x4(&r.v[it][4], hi);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint2*>(s.vt + mp.v_dst[it] + j * G::VSTR) = make_uint2(lo[j], hi[j]);
-  }
-}
-
-// Scheduling hint for the straight-line block just emitted: alternate one
-// MFMA with N_VALU VALU instructions, NM times, so the matrix core works
-// while the VALU does the softmax arithmetic.
-template <int NM, int N_VALU>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, N_VALU, 0);   // VALU
+  for (int i = 0; i < LPW; ++i) {
+    const int n = wave * LPW + i;
+    lds_load16(bf.k, st.k + n * 1024, ln.ld[i], soff);
+    if (KV) lds_load16(bf.v, st.v + n * 1024, ln.ld[i], soff);
   }
 }
 
 // S^T for one tile: exact INT32 logits, 32 keys per block (shared with the
 // logits-dump kernel).
 template <int D>
-__device__ __forceinline__ void qk_tile(v16i (&s)[NKB], const KStage& ks, const v4i (&qf)[D / 32], int lr, int g) {
-  using G = Geo<D>;
+__device__ __forceinline__ void qk_tile(v16i (&s)[NKB], const int8_t* kst, const Lanes<D>& ln, const v4i (&qf)[D / 32]) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c)
+  for (int c = 0; c < D / 32; ++c)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const v4i ka = *reinterpret_cast<const v4i*>(ks.k + (kb * 32 + lr) * G::KSTR + c * 32 + g * 16);
+      const v4i ka = *reinterpret_cast<const v4i*>(kst + kb * 32 * D + ln.koff[c]);
       s[kb] = mfma_i8(ka, qf[c], s[kb]);
     }
 }
 
 // O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T.
 template <int D>
-__device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const VStage& vs, const v4i (&pv)[NKB], int lr, int g) {
-  using G = Geo<D>;
+__device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, const Lanes<D>& ln,
+                                        const v4i (&pv)[NKB]) {
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c)
+  for (int c = 0; c < D / 32; ++c)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const v4i va = *reinterpret_cast<const v4i*>(vs.vt + (c * 32 + lr) * G::VSTR + kb * 32 + g * 16);
-      acc[c] = mfma_i8(va, pv[kb], acc[c]);
+      const int8_t* p = vst + kb * 32 * D + ln.voff[c];
+      const v2i lo = lds_read_tr8(p);
+      const v2i hi = lds_read_tr8(p + 8 * D);
+      acc[c] = mfma_i8(v4i{lo.x, lo.y, hi.x, hi.y}, pv[kb], acc[c]);
     }
 }
 
 // u = S_int * s_K[j] for this lane's keys (the query's factor c2 comes
 // later); masked keys get -inf. rel = (last visible key of the row) - k0 -
-// 4 g, so key index j of the tile is visible iff (j - 4 g) <= rel, a compare
-// of a compile-time constant with one per-lane value. Returns the max over
-// the lane pair.
+// 16 g, so entry v of block kb is visible iff 32 kb + v <= rel, a compare of
+// a compile-time constant with one per-lane value. Returns the max over the
+// lane pair.
 template <bool MASK>
-__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage& ks, float (&u)[NKB][16], int rel,
+__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float* sk, float (&u)[NKB][16], int rel,
                                               int g) {
-  // the maximum is taken as a tree (independent partial maxima), so a single
-  // wavefront per SIMD is not held up by a long dependency chain
+  // the maximum is taken as a tree (independent partial maxima), so one
+  // wavefront is not held up by a long dependency chain
   float gm[NKB * 4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-      const int jl = kb * 32 + j4 * 8 + g * 4;
-      const float4 skv = *reinterpret_cast<const float4*>(ks.sk + jl);
+      const float4 skv = *reinterpret_cast<const float4*>(sk + kb * 32 + g * 16 + j4 * 4);
       const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = static_cast<float>(s[kb][j4 * 4 + e]) * skk[e];
-        if constexpr (MASK) x = (kb * 32 + j4 * 8 + e <= rel) ? x : kNegInf;
+        if constexpr (MASK) x = (kb * 32 + j4 * 4 + e <= rel) ? x : kNegInf;
         u[kb][j4 * 4 + e] = x;
       }
       const float* x = &u[kb][j4 * 4];
@@ -315,8 +267,9 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const KStage
 
 // y = exp2(u c2 - bias) = 127 P_tilde; returns this lane's sum of y and packs
 // P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV operands.
-template <bool VPT, bool MASK>
-__device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2, float bias, const KStage& ks,
+// Masked keys have u = -inf and c2 >= FLT_MIN, so their y is exactly 0.
+template <bool VPT>
+__device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2, float bias, const float* sv,
                                             float rst, v4i (&pv)[NKB], int g) {
   float gs[NKB * 4];                   // partial row sums, added as a tree
 #pragma unroll
@@ -326,16 +279,14 @@ __device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2,
     for (int j4 = 0; j4 < 4; ++j4) {
       float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
       if constexpr (VPT) {
-        const float4 sv = *reinterpret_cast<const float4*>(ks.sv + kb * 32 + j4 * 8 + g * 4);
-        wr[0] = sv.x * rst; wr[1] = sv.y * rst; wr[2] = sv.z * rst; wr[3] = sv.w * rst;
+        const float4 s4 = *reinterpret_cast<const float4*>(sv + kb * 32 + g * 16 + j4 * 4);
+        wr[0] = s4.x * rst; wr[1] = s4.y * rst; wr[2] = s4.z * rst; wr[3] = s4.w * rst;
       }
       uint32_t word = 0;
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float uu = u[kb][j4 * 4 + e];
-        y[e] = exp2_hw(__builtin_fmaf(uu, c2, -bias));
-        if constexpr (MASK) y[e] = (uu == kNegInf) ? 0.0f : y[e];
+        y[e] = exp2_hw(__builtin_fmaf(u[kb][j4 * 4 + e], c2, -bias));
         word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
       }
       gs[kb * 4 + j4] = (y[0] + y[1]) + (y[2] + y[3]);
@@ -353,6 +304,15 @@ __device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2,
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// s_t of a tile for per-token V: the largest s_V[j] over the tile's keys
+// below Lkv (a stage may hold stale entries past the end).
+__device__ __forceinline__ float tile_vscale(const float* sv, int lane, int k0, int Lkv) {
+  float x = (k0 + lane < Lkv) ? sv[lane] : 0.0f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
 }
 
 __device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int D, bool scales, bool vpt) {
@@ -384,8 +344,9 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
 
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
-  using G = Geo<D>;
-  __shared__ Smem sm;
+  constexpr int NC = D / 32;
+  constexpr int LPW = Lanes<D>::LPW;
+  __shared__ Stage<D> sm[kStages];
 
   const int n_rb = (a.Lq + BM - 1) / BM;
   int bh, rb;
@@ -406,32 +367,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int shift = a.Lkv - a.Lq;   // bottom-right causal alignment
 
   const Bufs bf = make_bufs(a, kv_base, D, true, VPT);
-  Map<D> mp;
-  mp.init(tid);
-
-  // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk.
-  v4i qf[G::NC];
-#pragma unroll
-  for (int c = 0; c < G::NC; ++c) {
-    qf[c] = v4i{0, 0, 0, 0};
-    if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
-  }
-  const float sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
-  const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
-  const float c2 = sq * inv_sqrt_d * kLog2e;          // base-2 logit per unit of S_int * s_K
-  const int lim = CAUSAL ? qi + shift : a.Lkv - 1;    // last visible key of this row
-  const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;   // smallest in the wavefront
+  Lanes<D> ln;
+  ln.init(wave, lane);
 
   const int last_q = min(rb * BM + BM - 1, a.Lq - 1);
   const int kv_end = CAUSAL ? min(a.Lkv, last_q + shift + 1) : a.Lkv;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
+  // scale slots start at zero: a load past Lkv may leave a slot untouched
+  for (int i = tid; i < kStages * BN; i += kThreads) {
+    sm[i / BN].sk[i % BN] = 0.0f;
+    sm[i / BN].sv[i % BN] = 0.0f;
+  }
+
+  // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk. Loaded
+  // before the first stage requests, so that the prologue's wait covers it.
+  v4i qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = v4i{0, 0, 0, 0};
+    if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
+  }
+  const float sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
+  __syncthreads();
+  request_tile<D, true, VPT>(sm[0], bf, ln, wave, lane, 0);
+  if (n_tiles > 1) request_tile<D, true, VPT>(sm[1], bf, ln, wave, lane, BN);
+  const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
+  // base-2 logit per unit of S_int * s_K. Kept >= FLT_MIN so that -inf * c2
+  // stays -inf for masked keys; a zero query (s_Q = 0) has S_int = 0 and all
+  // its logits stay exactly 0.
+  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, 1.17549435e-38f);
+  const int lim = CAUSAL ? qi + shift : a.Lkv - 1;    // last visible key of this row
+  const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;   // smallest in the wavefront
+
   // softmax state: running max (base 2), partial sum of 127 P_tilde over this lane's keys
   float m = kNegInf, l = 0.0f;
-  float acc[G::NC][16];                // fp32 O^T accumulator
-  v16i acc_i[G::NC];                   // INT32 accumulation of P_hat . V_hat
+  float acc[NC][16];                   // fp32 O^T accumulator
+  v16i acc_i[NC];                      // INT32 accumulation of P_hat . V_hat
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c) {
+  for (int c = 0; c < NC; ++c) {
     acc_i[c] = zero16();
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
@@ -439,38 +413,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   float m_f = kNegInf;                 // frame of acc (per-tensor V)
   int int_tiles = 0;                   // tiles in the current INT32 run
 
-  // ---- prologue: K(0), V(0) staged ----
-  KRegs<D> kx;
-  VRegs<D> vx;
-  load_k<D, true, VPT>(kx, bf, mp, 0);
-  load_v<D>(vx, bf, mp, 0);
-  store_k<D, true, VPT>(sm.ks[0], kx, mp);
-  store_v<D>(sm.vs[0], vx, mp);
-  __syncthreads();
+  // tile 0 must have landed (tile 1 may still be in flight)
+  if (n_tiles > 1) wait_vm_lds<2 * LPW>();
+  else wait_vm_lds<0>();
+  bare_barrier();
+  // The wait above also covered the Q loads (issued before it). Passing the
+  // fragment through an empty asm statement tells the compiler so; otherwise
+  // it waits for them again inside the tile loop, which would also wait for
+  // the newest stage request.
+#pragma unroll
+  for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
 
-  // One tile: QK(t) [MFMA] | dequant, softmax(t) [VALU] | fold | PV(t)
-  // [MFMA] | stage K(t+1), V(t+1) | barrier. The wavefront of the other
-  // workgroup on the same SIMD issues its VALU work while this one waits on
-  // the matrix core, and the other way round.
-  for (int t = 0; t < n_tiles; ++t) {
+  // One tile: request t+2 | QK(t) [MFMA] | dequant, softmax(t) [VALU] | fold
+  // | PV(t) [MFMA] | wait for t+1 | barrier. The stage being read and the
+  // stage being filled are distinct objects, passed as restrict pointers: the
+  // compiler then knows that this tile's LDS reads do not depend on the loads
+  // just issued and adds no wait for them.
+  auto step = [&](int t, const Stage<D>* __restrict__ st, Stage<D>* __restrict__ nx) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    const KStage& ks_cur = sm.ks[t & 1];
-    const bool more = t + 1 < n_tiles;
-    // global loads of the next tile, in flight during this tile's math
-    if (more) {
-      load_k<D, true, VPT>(kx, bf, mp, k0 + BN);
-      load_v<D>(vx, bf, mp, k0 + BN);
-    }
+    const bool req = t + 2 < n_tiles;
+    if (req) request_tile<D, true, VPT>(*nx, bf, ln, wave, lane, k0 + 2 * BN);
+
     v16i s[NKB];
-    qk_tile<D>(s, ks_cur, qf, lr, g);
+    qk_tile<D>(s, st->k, ln, qf);
     const bool mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
-    // key index j of the tile is visible iff j - 4 g <= rel
-    const int rel = mask ? min(lim, a.Lkv - 1) - k0 - 4 * g : BN;
     float u[NKB][16];
-    const float mx = dequant_tile<true>(s, ks_cur, u, rel, g);
+    float mx;
+    if (!mask) {
+      mx = dequant_tile<false>(s, st->sk, u, 0, g);
+    } else {
+      mx = dequant_tile<true>(s, st->sk, u, min(lim, a.Lkv - 1) - k0 - 16 * g, g);
+    }
 
     // ---- softmax(t): running max, 127 P_tilde, row sum, P_hat ----
-    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;   // c2 >= 0: max(u) c2 == max(u c2)
+    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;   // c2 > 0: max(u) c2 == max(u c2)
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = exp2_hw(m - m_use);            // 1 if unchanged, 0 on the first tile
@@ -481,13 +457,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
     float rst = 0.0f, st_cur = 0.0f;
     if constexpr (VPT) {
-      st_cur = ks_cur.stp[0];
-#pragma unroll
-      for (int i = 1; i < BN / 64; ++i) st_cur = fmaxf(st_cur, ks_cur.stp[i]);
+      st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);
       rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
     }
     v4i p[NKB];
-    const float lsum = probs_tile<VPT, true>(u, c2, bias, ks_cur, rst, p, g);
+    const float lsum = probs_tile<VPT>(u, c2, bias, st->sv, rst, p, g);
     l = alpha * l + lsum;
 
     if constexpr (!VPT) {
@@ -503,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           m_f = m_use;
         }
 #pragma unroll
-        for (int c = 0; c < G::NC; ++c) {
+        for (int c = 0; c < NC; ++c) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(f, static_cast<float>(acc_i[c][v]), acc[c][v] * r);
           acc_i[c] = zero16();
@@ -512,34 +486,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < G::NC; ++c) acc_i[c] = zero16();
+      for (int c = 0; c < NC; ++c) acc_i[c] = zero16();
     }
     m = m_new;
 
-    pv_tile<D>(acc_i, sm.vs[t & 1], p, lr, g);
+    pv_tile<D>(acc_i, st->v, ln, p);
     if constexpr (VPT) {
       // per-token V: tile scales differ, so each tile's INT32 product is
       // converted on its own: acc = alpha acc + s_t PV(t)
 #pragma unroll
-      for (int c = 0; c < G::NC; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           acc[c][v] = __builtin_fmaf(alpha, acc[c][v], st_cur * static_cast<float>(acc_i[c][v]));
     }
 
-    // ---- stage K(t+1), V(t+1) ----
-    if (more) {
-      store_k<D, true, VPT>(sm.ks[(t + 1) & 1], kx, mp);
-      store_v<D>(sm.vs[(t + 1) & 1], vx, mp);
-    }
-    __syncthreads();
+    // tile t+1 must have landed before anyone reads it; after the barrier
+    // every wavefront is done with stage t, which tile t+3 reuses
+    if (req) wait_vm_lds<2 * LPW>();
+    else wait_vm_lds<0>();
+    bare_barrier();
+  };
+
+  int s_cur = 0;                       // stage of tile t; tile t+2 goes to the one before it
+  for (int t = 0; t < n_tiles; ++t) {
+    const int s_req = s_cur == 0 ? kStages - 1 : s_cur - 1;
+    step(t, &sm[s_cur], &sm[s_req]);
+    s_cur = s_cur == kStages - 1 ? 0 : s_cur + 1;
   }
 
   if constexpr (!VPT) {
     // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run
     const float back = exp2_hw(m_f - m);
 #pragma unroll
-    for (int c = 0; c < G::NC; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(back, acc[c][v], static_cast<float>(acc_i[c][v]));
   }
@@ -549,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const float scale = (VPT ? 1.0f : a.s_v[0]) / ltot;
   const int64_t orow = (q_base + qi) * D;
 #pragma unroll
-  for (int c = 0; c < G::NC; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = c * 32 + j4 * 8 + g * 4;
@@ -573,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 // the exact INT32 logit of every visible pair.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_logits_kernel(FwdArgs a) {
-  __shared__ KStage ks;
+  __shared__ Stage<D> st;
   const int bh = blockIdx.x;
   const int rb = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
@@ -581,14 +561,15 @@ __global__ __launch_bounds__(kThreads) void attn_logits_kernel(FwdArgs a) {
   const int64_t kv_base = (static_cast<int64_t>(b) * a.Hkv + hk) * a.Lkv;
   const int64_t q_base = static_cast<int64_t>(bh) * a.Lq;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5, lr = lane & 31;
-  const int qi = rb * BM + (tid >> 6) * 32 + lr;
+  const int qi = rb * BM + wave * 32 + lr;
   const bool qvalid = qi < a.Lq;
   const int lim = CAUSAL ? qi + (a.Lkv - a.Lq) : a.Lkv - 1;
   const Bufs bf = make_bufs(a, kv_base, D, false, false);
-  Map<D> mp;
-  mp.init(tid);
+  Lanes<D> ln;
+  ln.init(wave, lane);
   v4i qf[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
@@ -598,22 +579,22 @@ __global__ __launch_bounds__(kThreads) void attn_logits_kernel(FwdArgs a) {
   const int last_q = min(rb * BM + BM - 1, a.Lq - 1);
   const int kv_end = CAUSAL ? min(a.Lkv, last_q + (a.Lkv - a.Lq) + 1) : a.Lkv;
   for (int k0 = 0; k0 < kv_end; k0 += BN) {
-    KRegs<D> kx;
-    load_k<D, false, false>(kx, bf, mp, k0);
-    __syncthreads();
-    store_k<D, false, false>(ks, kx, mp);
-    __syncthreads();
+    request_tile<D, false, false>(st, bf, ln, wave, lane, k0);
+    wait_vm_lds<0>();
+    bare_barrier();
     v16i s[NKB];
-    qk_tile<D>(s, ks, qf, lr, g);
+    qk_tile<D>(s, st.k, ln, qf);
     if (qvalid) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = k0 + kb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          const int key = k0 + kb * 32 + g * 16 + v;
           if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
         }
     }
+    wait_vm_lds<0>();
+    bare_barrier();              // every wavefront has read the stage before it is refilled
   }
 }
 
