@@ -470,16 +470,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         // m) goes into acc (frame m_f) before PV(t) starts a new run
         if (m_f == kNegInf) m_f = m_use;
         float f = exp2_hw(m - m_f);                   // 0 before the first tile
-        float r = 1.0f;
         if (__any(m_use - m_f > kRebase)) {           // keep acc far from overflow
-          r = exp2_hw(m_f - m_use);
+          const float r = exp2_hw(m_f - m_use);
           f *= r;
           m_f = m_use;
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[c][v] *= r;
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(f, static_cast<float>(acc_i[c][v]), acc[c][v] * r);
+          for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(f, static_cast<float>(acc_i[c][v]), acc[c][v]);
           acc_i[c] = zero16();
         }
         int_tiles = 1;

@@ -196,6 +196,22 @@ inline u32x2 permlane32_swap(uint32_t x, uint32_t y) {
   return r;
 }
 
+// ds_swizzle_b32 in bit mode (offset bit 15 clear): within each group of 32
+// lanes, lane l reads lane ((l & and_mask) | or_mask) ^ xor_mask, with the
+// masks in offset bits 4:0, 9:5 and 14:10
+inline int ds_swizzle(int x, int offset) {
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  std::memcpy(w.slot[self], &x, 4);
+  w.bar.arrive_and_wait();
+  const int am = offset & 31, om = (offset >> 5) & 31, xm = (offset >> 10) & 31;
+  const int src = (self & ~31) | ((((self & 31) & am) | om) ^ xm);
+  int r;
+  std::memcpy(&r, w.slot[src], 4);
+  w.bar.arrive_and_wait();
+  return r;
+}
+
 inline int wave_any(int p) {
   Wave& w = *ctx.wave;
   const int self = ctx.lane;
@@ -305,6 +321,7 @@ typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;
   emu::buffer_load_lds(r, (void*)(dst), size, (v) + (off), s)
 #define __builtin_amdgcn_ds_read_tr8_b64_v2i32(p) emu::ds_read_tr8_b64((const void*)(p))
 #define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_ds_swizzle(x, off) emu::ds_swizzle(x, off)
 #define __builtin_amdgcn_s_barrier() emu::syncthreads()
 #define __builtin_amdgcn_sched_group_barrier(m, n, id) ((void)0)
 #define __builtin_amdgcn_sched_barrier(m) ((void)0)
@@ -317,6 +334,8 @@ using std::min;
 inline float __fmul_rn(float a, float b) { return a * b; }   // built with -ffp-contract=off
 inline float __fdiv_rn(float a, float b) { return a / b; }
 inline float __uint_as_float(uint32_t u) { return emu::bits_to_float(u); }
+inline float __int_as_float(int i) { return emu::bits_to_float(static_cast<uint32_t>(i)); }
+inline int __float_as_int(float f) { return static_cast<int>(emu::float_to_bits(f)); }
 inline uint32_t __float_as_uint(float f) { return emu::float_to_bits(f); }
 inline uint32_t atomicMax(uint32_t* p, uint32_t v) { return __atomic_fetch_max(p, v, __ATOMIC_RELAXED); }
 
