@@ -3,6 +3,8 @@
 // synchronizes; every check happens before the first launch.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "attn_internal.h"
 
 namespace {
@@ -29,14 +31,24 @@ attn_status check_shape(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t L
 
 namespace attn {
 
-// Decode-shaped problems (few query rows per KV head) take the split-KV
-// kernel; everything else the prefill kernel with one KV pass per row block.
+// Decode-shaped problems (at most kDecodeRows query rows per KV head: the
+// GQA group's heads times Lq) take the split-KV kernel, the KV length cut in
+// chunks so that about kDecodeTargetChunks chunks stream in parallel;
+// everything else takes the prefill kernel with one KV pass per row block.
 void fwd_schedule(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal, int* kv_tile,
                   int* kv_split_len, int* use_decode) {
-  (void)B; (void)H; (void)Hkv; (void)Lq; (void)Lkv; (void)d; (void)causal;
+  (void)d; (void)causal;
   *kv_tile = kPrefillBN;
   *kv_split_len = 0;
   *use_decode = 0;
+  if (int64_t{H / Hkv} * Lq > kDecodeRows) return;
+  const int64_t groups = int64_t{B} * Hkv;
+  const int64_t want = (kDecodeTargetChunks + groups - 1) / groups;
+  const int64_t most = std::max<int64_t>(1, (Lkv + kDecodeMinChunk - 1) / kDecodeMinChunk);
+  const int64_t n = std::min(std::max<int64_t>(1, want), most);
+  const int64_t len = (Lkv + n - 1) / n;
+  *kv_split_len = static_cast<int>((len + kDecodeBN - 1) / kDecodeBN * kDecodeBN);
+  *use_decode = 1;
 }
 
 size_t fwd_workspace_bytes(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal) {

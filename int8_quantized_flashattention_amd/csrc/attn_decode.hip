@@ -1,6 +1,432 @@
-// Split-KV decode kernel: not built yet; the schedule never selects it.
+// Split-KV INT8 attention for decode-shaped problems on gfx950: few query
+// rows per KV head (a GQA group of H / Hkv heads times Lq queries, at most
+// 16 rows), long KV. The work is bound by streaming K_hat and V_hat from HBM
+// once, so the KV length is split into chunks processed in parallel, each by
+// one wavefront, and a second kernel merges the chunks.
+//
+// Method as in the prefill kernel: "INT-FlashAttention: Enabling Flash
+// Attention for INT8 Quantization" (abstract); integer logits, the
+// s_Q s_K / sqrt(d) dequantization and the s_V P V_hat form from "IntAttention:
+// A Fully Integer Attention Pipeline for Efficient Edge Inference" §2.1, §3.1
+// (Eq. 4); P quantized with multiplier 127 (IntAttention §3.2); each chunk is
+// one online-softmax pass in tiles of kDecodeBN keys and the chunk results are
+// merged by their row maxima (the same identity as the per-tile rescale of
+// "FlashAttention-3", abstract).
+//
+// Per wavefront: the 16 rows of one v_mfma_i32_16x16x64_i8 tile hold the
+// group's query rows (row r = (head - Hkv-group start) * Lq + query); K/V tiles
+// go from HBM straight into a 3-stage LDS ring (buffer loads with LDS
+// destination, rows swizzled), V^T operands come from ds_read_b64_tr_b8.
+// Lane l holds query row l % 16 and, in each of the 4 key blocks of 16, keys
+// 4 b + 0..3 of its lane group, that is the 16 consecutive keys 16 (l / 16)
+// .. +15 of the tile, which are exactly its P operand for O^T = V^T P^T.
 #include "attn_internal.h"
+#include "cdna4_ops.h"
+
+#include <hip/hip_fp16.h>
 
 namespace attn {
-hipError_t launch_decode(const FwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int BN = kDecodeBN;
+static_assert(BN == kPrefillBN, "one KV tile size for every schedule");
+constexpr int NB = BN / 16;                  // 16-key blocks per tile
+constexpr int QR = 16;                       // query rows per wavefront (MFMA tile)
+constexpr int kStages = 3;
+// the INT32 run of P_hat . V_hat is folded into fp32 at least every this many
+// tiles, keeping |sum| <= 127 * 127 * keys below 2^31
+constexpr int kMaxIntTiles = 32768 / BN;
+
+template <int D>
+struct DStage {
+  alignas(16) int8_t k[BN * D];
+  alignas(16) int8_t v[BN * D];
+  alignas(16) float sk[BN];
+  alignas(16) float sv[BN];
+};
+
+// Key of the tile held by MFMA row r of key block b of S^T (16x16 C layout:
+// lane l holds rows 4 (l / 16) + 0..3), chosen so that lane l ends up with
+// keys 16 (l / 16) + 4 b + 0..3.
+__device__ __forceinline__ int key_of_row16(int b, int r) { return 16 * (r >> 2) + 4 * b + (r & 3); }
+
+template <int D>
+struct DLanes {
+  static constexpr int NC = D / 64;            // 64-channel chunks (K dim of QK)
+  static constexpr int NCB = D / 16;           // 16-channel blocks of O
+  static constexpr int NLD = BN * D / 1024;    // 1 KB loads per operand per tile
+  uint32_t ld[NLD];
+  int koff[2][NC];     // K operand LDS offset, key blocks 0 / 1 (blocks 2 / 3: + 8 D)
+  int voff[NCB];       // transposed V read offset, channel block cb, keys +0..7 (+8 D: 8..15)
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) ld[n] = tile_load_off<D>(n, lane);
+    const int r = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int kr = key_of_row16(b, r);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) koff[b][c] = kr * D + (((4 * c + grp) ^ swz<D>(kr)) * 16);
+    }
+    // lane 16 grp + i addresses key 16 grp + i / 2, channels 16 cb + 8 (i % 2)
+    // .. +7, so after the transposing read lane l holds channel 16 cb + l % 16,
+    // keys 16 (l / 16) .. +7
+    const int vr = 16 * grp + (r >> 1);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) voff[cb] = vr * D + ((cb ^ swz<D>(vr)) * 16) + 8 * (r & 1);
+  }
+};
+
+// Loads per tile issued by the (single) wavefront.
+template <int D, bool VPT>
+constexpr int loads_per_tile() { return 2 * DLanes<D>::NLD + 1 + (VPT ? 1 : 0); }
+
+template <int D, bool VPT>
+__device__ __forceinline__ void request_tile(DStage<D>& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                             __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
+                                             const DLanes<D>& ln, int lane, int k0) {
+  lds_load4(rsk, st.sk, lane * 4, k0 * 4);
+  if (VPT) lds_load4(rsv, st.sv, lane * 4, k0 * 4);
+  const uint32_t soff = static_cast<uint32_t>(k0) * D;
+#pragma unroll
+  for (int n = 0; n < DLanes<D>::NLD; ++n) {
+    lds_load16(rk, st.k + n * 1024, ln.ld[n], soff);
+    lds_load16(rv, st.v + n * 1024, ln.ld[n], soff);
+  }
+}
+
+// x of lane l ^ 16 (ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 within 32
+// lanes); max / sum over a row's lanes l, l ^ 16, l ^ 32, l ^ 48.
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, xor16(x));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  x = x + xor16(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Partial result of one (KV group, chunk): per row the running max m (base
+// 2, -inf if the chunk had no visible key), 127 l, and acc[D] (fp32, frame m;
+// per-tensor V without s_V).
+struct Partials {
+  float* acc;     // [groups][n_split][R][D]
+  float* ml;      // [groups][n_split][R][2]
+};
+
+__device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, int R, int D) {
+  Partials p;
+  p.acc = static_cast<float*>(ws);
+  p.ml = p.acc + static_cast<int64_t>(groups) * n_split * R * D;
+  return p;
+}
+
+template <int D, bool CAUSAL, bool VPT>
+__global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
+  constexpr int NC = D / 64;
+  constexpr int NCB = D / 16;
+  constexpr int NL = loads_per_tile<D, VPT>();
+  __shared__ DStage<D> sm[kStages];
+
+  const int G = a.H / a.Hkv;                 // query heads per KV head
+  const int R = G * a.Lq;                    // query rows of the group (<= 16)
+  const int groups = a.B * a.Hkv;
+  const int gi = blockIdx.x / n_split, split = blockIdx.x % n_split;
+  const int b = gi / a.Hkv, hk = gi % a.Hkv;
+  const int64_t kv_base = static_cast<int64_t>(gi) * a.Lkv;
+
+  const int lane = threadIdx.x;
+  const int grp = lane >> 4, r = lane & 15;
+  const bool rvalid = r < R;
+  const int head = hk * G + (rvalid ? r / a.Lq : 0);
+  const int qi = rvalid ? r % a.Lq : 0;
+  const int64_t qrow = (static_cast<int64_t>(b) * a.H + head) * a.Lq + qi;
+  const int shift = a.Lkv - a.Lq;            // bottom-right causal alignment
+  const int lim = CAUSAL ? qi + shift : a.Lkv - 1;   // last visible key of this row
+  const int lim_first = CAUSAL ? shift : a.Lkv - 1;  // smallest over the rows
+
+  // this chunk's keys [s0, s1), cut at the last key any row sees
+  const int s0 = split * split_len;
+  const int kv_end = CAUSAL ? min(a.Lkv, a.Lq - 1 + shift + 1) : a.Lkv;
+  const int s1 = min(kv_end, s0 + split_len);
+  const int n_tiles = s1 > s0 ? (s1 - s0 + BN - 1) / BN : 0;
+
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base * D, a.Lkv * D);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base * D, a.Lkv * D);
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(a.s_k + kv_base, a.Lkv * 4);
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(VPT ? a.s_v + kv_base : a.s_k + kv_base, a.Lkv * 4);
+  DLanes<D> ln;
+  ln.init(lane);
+
+  // Q fragment (B operand of S^T): 16 bytes per 64-channel chunk; s_Q.
+  v4i qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = zero4();
+    if (rvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + qrow * D + c * 64 + grp * 16);
+  }
+  float sq = rvalid ? a.s_q[qrow] : 0.0f;
+
+  // scale slots start at zero: a load past Lkv may leave a slot untouched
+  for (int i = lane; i < kStages * BN; i += 64) {
+    sm[i / BN].sk[i % BN] = 0.0f;
+    sm[i / BN].sv[i % BN] = 0.0f;
+  }
+  __syncthreads();
+  if (n_tiles > 0) request_tile<D, VPT>(sm[0], rk, rv, rsk, rsv, ln, lane, s0);
+  if (n_tiles > 1) request_tile<D, VPT>(sm[1], rk, rv, rsk, rsv, ln, lane, s0 + BN);
+  if (n_tiles > 1) wait_vm_lds<NL>();
+  else wait_vm_lds<0>();
+  // the wait covered the Q loads too (issued first); tell the compiler
+#pragma unroll
+  for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
+  asm volatile("" : "+v"(sq));
+
+  const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
+  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);   // base-2 logit per S_int s_K
+
+  float m = kNegInf, l = 0.0f;
+  float acc[NCB][4];
+  v4i acc_i[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    acc_i[cb] = zero4();
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[cb][v] = 0.0f;
+  }
+  float m_f = kNegInf;
+  int int_tiles = 0;
+
+  auto step = [&](int t, const DStage<D>* __restrict__ st, DStage<D>* __restrict__ nx) __attribute__((always_inline)) {
+    const int k0 = s0 + t * BN;
+    const bool req = t + 2 < n_tiles;
+    if (req) request_tile<D, VPT>(*nx, rk, rv, rsk, rsv, ln, lane, k0 + 2 * BN);
+
+    // S^T = K_hat . Q_hat^T, exact INT32
+    v4i s[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) s[kb] = zero4();
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        const v4i ka = *reinterpret_cast<const v4i*>(st->k + ln.koff[kb & 1][c] + (kb >> 1) * 8 * D);
+        s[kb] = mfma16(ka, qf[c], s[kb]);
+      }
+
+    // u = S_int s_K[j], -inf past the chunk end or the causal limit; key
+    // 16 grp + 4 kb + e of the tile is visible iff 4 kb + e <= rel
+    const bool mask = (k0 + BN > s1) || (CAUSAL && k0 + BN - 1 > lim_first);
+    const int rel = min(lim, s1 - 1) - k0 - 16 * grp;
+    float u[NB][4];
+    float gm[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      const float4 skv = *reinterpret_cast<const float4*>(st->sk + grp * 16 + kb * 4);
+      const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = static_cast<float>(s[kb][e]) * skk[e];
+        u[kb][e] = (!mask || kb * 4 + e <= rel) ? x : kNegInf;
+      }
+      gm[kb] = fmaxf(fmaxf(u[kb][0], u[kb][1]), fmaxf(u[kb][2], u[kb][3]));
+    }
+    const float mx = row_max4(fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3])));
+
+    // online softmax in base 2 with 127 folded into the bias
+    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;
+    const float m_new = fmaxf(m, mx2);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = exp2_hw(m - m_use);
+    const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
+    float st_cur = 0.0f, rst = 0.0f;
+    if constexpr (VPT) {
+      // s_t: largest s_V[j] over the tile's keys inside the chunk
+      float x = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+      st_cur = x;
+      rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
+    }
+    uint32_t pw[NB];
+    float gs[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (VPT) {
+        const float4 s4 = *reinterpret_cast<const float4*>(st->sv + grp * 16 + kb * 4);
+        wr[0] = s4.x * rst; wr[1] = s4.y * rst; wr[2] = s4.z * rst; wr[3] = s4.w * rst;
+      }
+      uint32_t word = 0;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = exp2_hw(__builtin_fmaf(u[kb][e], c2, -bias));     // 127 P_tilde
+        word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
+      }
+      gs[kb] = (y[0] + y[1]) + (y[2] + y[3]);
+      pw[kb] = word;
+    }
+    const v4i p = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]),
+                      static_cast<int>(pw[3])};
+    l = alpha * l + ((gs[0] + gs[1]) + (gs[2] + gs[3]));
+
+    if constexpr (!VPT) {
+      if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
+        // fold the INT32 run (frame m) into acc (frame m_f)
+        if (m_f == kNegInf) m_f = m_use;
+        float f = exp2_hw(m - m_f);
+        if (__any(m_use - m_f > kRebase)) {
+          const float rb = exp2_hw(m_f - m_use);
+          f *= rb;
+          m_f = m_use;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[cb][v] *= rb;
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[cb][v] = __builtin_fmaf(f, static_cast<float>(acc_i[cb][v]), acc[cb][v]);
+          acc_i[cb] = zero4();
+        }
+        int_tiles = 1;
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc_i[cb] = zero4();
+    }
+    m = m_new;
+
+    // O^T += V_hat^T . P_hat^T
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const v2i lo = lds_read_tr8(st->v + ln.voff[cb]);
+      const v2i hi = lds_read_tr8(st->v + ln.voff[cb] + 8 * D);
+      acc_i[cb] = mfma16(v4i{lo.x, lo.y, hi.x, hi.y}, p, acc_i[cb]);
+    }
+    if constexpr (VPT) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[cb][v] = __builtin_fmaf(alpha, acc[cb][v], st_cur * static_cast<float>(acc_i[cb][v]));
+    }
+
+    // tile t+1 must have landed; this wavefront is the stage ring's only user
+    if (req) wait_vm_lds<NL>();
+    else wait_vm_lds<0>();
+  };
+
+  int s_cur = 0;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int s_req = s_cur == 0 ? kStages - 1 : s_cur - 1;
+    step(t, &sm[s_cur], &sm[s_req]);
+    s_cur = s_cur == kStages - 1 ? 0 : s_cur + 1;
+  }
+
+  if constexpr (!VPT) {
+    const float back = (m == kNegInf) ? 0.0f : exp2_hw(m_f - m);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[cb][v] = __builtin_fmaf(back, acc[cb][v], static_cast<float>(acc_i[cb][v]));
+  }
+  const float ltot = row_sum4(l);
+  if (!rvalid) return;
+  const Partials pt = partials(a.workspace, groups, n_split, R, D);
+  const int64_t prow = (static_cast<int64_t>(gi) * n_split + split) * R + r;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+    *reinterpret_cast<float4*>(pt.acc + prow * D + cb * 16 + grp * 4) =
+        make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+  if (grp == 0) *reinterpret_cast<float2*>(pt.ml + prow * 2) = make_float2(m, ltot);
+}
+
+// Merge of the chunk partials of one query row per wavefront:
+// O = sum_s 2^(m_s - M) acc_s * scale / sum_s 2^(m_s - M) 127 l_s.
+template <int D, bool OUT_F16>
+__global__ __launch_bounds__(256) void attn_decode_combine(FwdArgs a, int n_split) {
+  constexpr int CPL = D / 64;                // channels per lane
+  const int G = a.H / a.Hkv;
+  const int R = G * a.Lq;
+  const int groups = a.B * a.Hkv;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= static_cast<int64_t>(a.B) * a.H * a.Lq) return;
+  const int lane = threadIdx.x & 63;
+  const int qi = static_cast<int>(row % a.Lq);
+  const int head = static_cast<int>((row / a.Lq) % a.H);
+  const int b = static_cast<int>(row / (static_cast<int64_t>(a.Lq) * a.H));
+  const int gi = b * a.Hkv + head / G;
+  const int r = (head % G) * a.Lq + qi;
+  const Partials pt = partials(a.workspace, groups, n_split, R, D);
+  const int64_t p0 = static_cast<int64_t>(gi) * n_split * R + r;   // split s: p0 + s R
+
+  float M = kNegInf;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pt.ml[(p0 + static_cast<int64_t>(s) * R) * 2]);
+  float L = 0.0f, o[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[c] = 0.0f;
+  for (int s = 0; s < n_split; ++s) {
+    const int64_t pr = p0 + static_cast<int64_t>(s) * R;
+    const float ms = pt.ml[pr * 2];
+    if (ms == kNegInf) continue;
+    const float f = exp2_hw(ms - M);
+    L = __builtin_fmaf(f, pt.ml[pr * 2 + 1], L);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[c] = __builtin_fmaf(f, pt.acc[pr * D + lane * CPL + c], o[c]);
+  }
+  const float scale = (a.v_per_token ? 1.0f : a.s_v[0]) / L;
+  if constexpr (OUT_F16) {
+    __half* out = static_cast<__half*>(a.o) + row * D + lane * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = __float2half_rn(o[c] * scale);
+  } else {
+    float* out = static_cast<float*>(a.o) + row * D + lane * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = o[c] * scale;
+  }
+  if (a.lse && lane == 0) a.lse[row] = (M + __builtin_log2f(L) - kLog2_127) * kLn2;
+}
+
+template <int D, bool CAUSAL, bool VPT>
+hipError_t launch_dec(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
+  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT>), grid, dim3(64), 0, st, a, split_len, n_split);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
+  if (a.causal) return a.v_per_token ? launch_dec<D, true, true>(a, split_len, n_split, st)
+                                     : launch_dec<D, true, false>(a, split_len, n_split, st);
+  return a.v_per_token ? launch_dec<D, false, true>(a, split_len, n_split, st)
+                       : launch_dec<D, false, false>(a, split_len, n_split, st);
+}
+
+template <int D>
+hipError_t launch_combine(const FwdArgs& a, int n_split, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.B) * a.H * a.Lq;
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (a.o_f16) hipLaunchKernelGGL((attn_decode_combine<D, true>), grid, dim3(256), 0, st, a, n_split);
+  else hipLaunchKernelGGL((attn_decode_combine<D, false>), grid, dim3(256), 0, st, a, n_split);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const FwdArgs& a, int split_len, hipStream_t st) {
+  const int n_split = (a.Lkv + split_len - 1) / split_len;
+  hipError_t e = a.d == 64 ? launch_d<64>(a, split_len, n_split, st) : launch_d<128>(a, split_len, n_split, st);
+  if (e != hipSuccess) return e;
+  return a.d == 64 ? launch_combine<64>(a, n_split, st) : launch_combine<128>(a, n_split, st);
+}
+
 }  // namespace attn

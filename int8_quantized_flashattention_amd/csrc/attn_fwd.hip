@@ -47,17 +47,12 @@
 //    when one does; s_V is applied once in the epilogue;
 //  - masking code runs only on diagonal / ragged tiles.
 #include "attn_internal.h"
+#include "cdna4_ops.h"
 
 #include <hip/hip_fp16.h>
 
 namespace attn {
 namespace {
-
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int BM = kPrefillBM;
 constexpr int BN = kPrefillBN;
@@ -65,57 +60,9 @@ constexpr int NKB = BN / 32;                 // 32-key blocks per tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStages = 3;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLog2_127 = 6.988684686772166f;
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kBufWord3 = 0x00020000;        // raw buffer, 32-bit data format
 // the INT32 run of P_hat . V_hat is folded into fp32 at least every this many
 // tiles, keeping |sum| <= 127 * 127 * keys below 2^31
 constexpr int kMaxIntTiles = 32768 / BN;
-// re-base the fp32 accumulator when the running max has grown by this much
-// (base 2) since its frame was set
-constexpr float kRebase = 60.0f;
-// relative guard on the softmax bias (see the tile loop)
-constexpr float kBiasGuard = 4.76837158203125e-07f;   // 2^-21
-
-__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): wait until at most N vector-memory loads are outstanding and
-// all LDS operations are done.
-template <int N>
-__device__ __forceinline__ void wait_vm_lds() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-// Workgroup barrier without a memory fence: the waits above are the only
-// ones the stage protocol needs (a fenced barrier would also wait for the
-// stage requested two tiles ahead). The empty asm statements keep the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// LDS-destination buffer loads (16 or 4 bytes per lane, lane l's bytes at
-// dst + size l) and the transposing LDS read, as plain functions: the
-// gfx950-only forms are checked in the host compilation pass too, where a
-// template would turn the check into a substitution failure.
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
-}
-__device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
-}
 
 // One pipeline stage: a K tile and a V tile ([key][channel], 16-byte chunks
 // swizzled per row), s_K and s_V of the tile's keys.
@@ -126,16 +73,6 @@ struct Stage {
   alignas(16) float sk[BN];
   alignas(16) float sv[BN];
 };
-
-// Position of 16-byte chunk j of tile row r is chunk j ^ swz(r) of that row.
-// The swizzle makes both operand reads conflict-free: the K reads (8 lanes
-// per LDS cycle read keys {0-3, 16-19} + 4i of a block) and the transposed V
-// reads (16 lanes read 8 consecutive keys).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return (r & 7) ^ ((r >> 2) & 4);
-  else return ((r >> 1) & 3) ^ (((r >> 4) & 1) << 1);
-}
 
 // Key held by MFMA row i of the S^T tile: row i = 8 (v / 4) + 4 g + v % 4 of
 // lane group g, register v, carries key 16 g + v.
@@ -155,14 +92,9 @@ struct Lanes {
   int voff[NC];       // LDS offset (block 0, first 8 keys) of this lane's transposed V read
 
   __device__ __forceinline__ void init(int wave, int lane) {
-    // a 1 KB load writes lane l's 16 bytes to LDS slot 64 n + l; the lane
-    // fetches the global chunk that the swizzle places in that slot
+    // load i of this wavefront fills LDS slots 64 (LPW wave + i) + lane
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int slot = (wave * LPW + i) * 64 + lane;
-      const int r = slot / (D / 16), pos = slot % (D / 16);
-      ld[i] = static_cast<uint32_t>(r * D + (pos ^ swz<D>(r)) * 16);
-    }
+    for (int i = 0; i < LPW; ++i) ld[i] = tile_load_off<D>(wave * LPW + i, lane);
     const int lr = lane & 31, g = lane >> 5;
     const int kr = key_of_row(lr);
 #pragma unroll
@@ -317,14 +249,14 @@ __device__ __forceinline__ float tile_vscale(const float* sv, int lane, int k0, 
 
 __device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int D, bool scales, bool vpt) {
   Bufs bf;
-  bf.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.k + kv_base * D), 0, a.Lkv * D, kBufWord3);
+  bf.k = make_rsrc(a.k + kv_base * D, a.Lkv * D);
   bf.v = bf.k;
   bf.sk = bf.k;
   bf.sv = bf.k;
   if (scales) {
-    bf.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.v + kv_base * D), 0, a.Lkv * D, kBufWord3);
-    bf.sk = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.s_k + kv_base), 0, a.Lkv * 4, kBufWord3);
-    if (vpt) bf.sv = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.s_v + kv_base), 0, a.Lkv * 4, kBufWord3);
+    bf.v = make_rsrc(a.v + kv_base * D, a.Lkv * D);
+    bf.sk = make_rsrc(a.s_k + kv_base, a.Lkv * 4);
+    if (vpt) bf.sv = make_rsrc(a.s_v + kv_base, a.Lkv * 4);
   }
   return bf;
 }
@@ -396,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // base-2 logit per unit of S_int * s_K. Kept >= FLT_MIN so that -inf * c2
   // stays -inf for masked keys; a zero query (s_Q = 0) has S_int = 0 and all
   // its logits stay exactly 0.
-  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, 1.17549435e-38f);
+  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
   const int lim = CAUSAL ? qi + shift : a.Lkv - 1;    // last visible key of this row
   const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;   // smallest in the wavefront
 
@@ -450,10 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = exp2_hw(m - m_use);            // 1 if unchanged, 0 on the first tile
-    // exp2(u c2 - bias) = 127 P_tilde. The guard term |m| 2^-21 keeps the
-    // max key's value below 127.5 however large |m| is (the fp32 rounding of
-    // u c2 and of the bias grows with |m|); P_hat and the row sum scale
-    // together, so it cancels in O.
+    // exp2(u c2 - bias) = 127 P_tilde, bias with the guard term |m| 2^-21
     const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
     float rst = 0.0f, st_cur = 0.0f;
     if constexpr (VPT) {

@@ -26,8 +26,10 @@ constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
 
 // Decode (split-KV) geometry.
-constexpr int kDecodeBN = 64;           // keys per tile
-constexpr int kDecodeMaxGroup = 8;      // query heads per KV head handled by one workgroup
+constexpr int kDecodeBN = 64;              // keys per tile (the same tile as prefill)
+constexpr int kDecodeRows = 16;            // query rows per KV head (GQA group x Lq) at most
+constexpr int kDecodeTargetChunks = 3072;  // KV chunks (one wavefront each) to aim for
+constexpr int kDecodeMinChunk = 256;       // keys per chunk at least
 
 // Schedule the fused forward uses for this problem (what changes the result).
 void fwd_schedule(int B, int H, int Hkv, int Lq, int Lkv, int d, int causal, int* kv_tile,

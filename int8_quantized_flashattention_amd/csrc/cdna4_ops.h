@@ -1,0 +1,105 @@
+// gfx950 building blocks shared by the attention kernels of libattn_int8:
+// the INT8 MFMA shapes, LDS-destination buffer loads, the transposing LDS
+// read, explicit memory waits and a fence-free barrier, and the LDS row
+// swizzle of K/V tiles. Internal header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+namespace {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2_127 = 6.988684686772166f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kFltMin = 1.17549435e-38f;
+constexpr int kBufWord3 = 0x00020000;        // raw buffer, 32-bit data format
+// re-base an fp32 accumulator when the running max has grown by this much
+// (base 2) since its frame was set
+constexpr float kRebase = 60.0f;
+// relative guard on the softmax bias: exp2(u c2 - bias) with bias =
+// m - log2(127) + |m| 2^-21 keeps the max key's 127 P_tilde below 127.5
+// however large |m| is (the fp32 rounding of u c2 and of the bias grows with
+// |m|); P_hat and the row sum scale together, so the guard cancels in O
+constexpr float kBiasGuard = 4.76837158203125e-07f;   // 2^-21
+
+__device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
+__device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 32x32x32 and 16x16x64 INT8 products with INT32 accumulation
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most N vector-memory loads are outstanding and
+// all LDS operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier without a memory fence: the explicit waits above are
+// the only ones a stage ring needs (a fenced barrier would also wait for the
+// stages requested ahead). The empty asm statements keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS-destination buffer loads (16 or 4 bytes per lane, lane l's bytes at
+// dst + size l) and the transposing LDS read, as plain functions: the
+// gfx950-only forms are checked in the host compilation pass too, where a
+// template would turn the check into a substitution failure.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
+}
+// ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
+// the 8-byte rows addressed by lanes 2 b + i / 8 (b = 0..7 gives byte b)
+__device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+}
+
+// Raw buffer resource over nbytes bytes (loads at or past the end read 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, nbytes, kBufWord3);
+}
+
+// K/V tile rows of D bytes are stored with their 16-byte chunks permuted:
+// chunk j of row r sits at chunk position j ^ swz(r). The permutation makes
+// the operand reads conflict-free: 8 lanes reading the same chunk of rows
+// {0-3, 16-19} + 4 i, and 16 lanes reading 8 consecutive rows.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return (r & 7) ^ ((r >> 2) & 4);
+  else return ((r >> 1) & 3) ^ (((r >> 4) & 1) << 1);
+}
+
+// Tile byte offset of the 16-byte chunk that a 1 KB LDS-destination load
+// writes into LDS slot 64 n + lane of a swizzled tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_load_off(int n, int lane) {
+  const int slot = n * 64 + lane;
+  const int r = slot / (D / 16), pos = slot % (D / 16);
+  return static_cast<uint32_t>(r * D + (pos ^ swz<D>(r)) * 16);
+}
+
+}  // namespace
+}  // namespace attn

@@ -53,6 +53,7 @@ struct alignas(16) float4 { float x, y, z, w; };
 struct alignas(8) uint2 { unsigned x, y; };
 struct alignas(16) uint4 { unsigned x, y, z, w; };
 inline float4 make_float4(float a, float b, float c, float d) { return {a, b, c, d}; }
+inline float2 make_float2(float a, float b) { return {a, b}; }
 inline uint2 make_uint2(unsigned a, unsigned b) { return {a, b}; }
 
 namespace emu {
@@ -212,6 +213,8 @@ inline int ds_swizzle(int x, int offset) {
   return r;
 }
 
+inline void wave_sync() { ctx.wave->bar.arrive_and_wait(); }
+
 inline int wave_any(int p) {
   Wave& w = *ctx.wave;
   const int self = ctx.lane;
@@ -320,7 +323,10 @@ typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;
 #define __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, size, v, s, off, aux) \
   emu::buffer_load_lds(r, (void*)(dst), size, (v) + (off), s)
 #define __builtin_amdgcn_ds_read_tr8_b64_v2i32(p) emu::ds_read_tr8_b64((const void*)(p))
-#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+// s_waitcnt: the wavefront's lanes run in lockstep on the hardware, so the
+// loads every lane issued before the wait (LDS-destination loads included)
+// are complete for all of them after it; the emulated lanes meet here
+#define __builtin_amdgcn_s_waitcnt(x) emu::wave_sync()
 #define __builtin_amdgcn_ds_swizzle(x, off) emu::ds_swizzle(x, off)
 #define __builtin_amdgcn_s_barrier() emu::syncthreads()
 #define __builtin_amdgcn_sched_group_barrier(m, n, id) ((void)0)
@@ -342,6 +348,7 @@ inline uint32_t atomicMax(uint32_t* p, uint32_t v) { return __atomic_fetch_max(p
 struct __half { _Float16 v; };
 struct alignas(4) __half2 { _Float16 x, y; };
 inline float2 __half22float2(__half2 h) { return {static_cast<float>(h.x), static_cast<float>(h.y)}; }
+inline __half __float2half_rn(float a) { return {static_cast<_Float16>(a)}; }
 inline __half2 __floats2half2_rn(float a, float b) {
   return {static_cast<_Float16>(a), static_cast<_Float16>(b)};
 }

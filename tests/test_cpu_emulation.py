@@ -86,6 +86,9 @@ def test_emulated_logits(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal):
     (1, 2, 2, 130, 257, 128, 1, 1, F32, 1), (1, 4, 1, 3, 333, 64, 0, 1, F32, 1),
     # large logits: the running max keeps growing by tens of units (re-basing path)
     (1, 2, 2, 256, 640, 128, 1, 0, F32, 12), (1, 1, 1, 64, 500, 64, 0, 0, F32, 30),
+    # split-KV decode shapes: several chunks, GQA groups of up to 16 rows
+    (2, 8, 2, 1, 1500, 128, 0, 0, F16, 1), (1, 4, 1, 4, 700, 128, 1, 1, F32, 1),
+    (1, 8, 1, 2, 520, 64, 1, 0, F32, 1), (1, 2, 1, 1, 3000, 64, 0, 0, F32, 12),
 ])
 def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt, gain):
     r = np.random.Generator(np.random.PCG64(B * 100 + Lq * 7 + Lkv))
