@@ -7,15 +7,23 @@ fused attention forward. `value` is algorithmic INT8 ops (4 d per visible
 query-key pair) per second of step time, in TOPS.
 
 Also reported on the same JSON line:
-  roofline      the fused attention kernel alone: its average duration from HIP
+  roofline      the fused attention launch alone (prefill kernel, or split-KV
+                decode kernel plus chunk merge): its average duration from HIP
                 events around each launch in the timed region, against the
-                dense INT8 MFMA peak (5.0 POP/s)
+                dense INT8 MFMA peak (5.0 POP/s) or, for decode shapes, HBM
+                (8 TB/s); `traffic` is the HBM bytes per launch measured with
+                rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy of known
+                size), read from profiles/ and given only while the kernel
+                sources still match the ones measured
   cpu_baseline  the oracle (plain C++, all host threads given to it) timed on
                 a bounded, seeded sample of the workload's query rows
   kernels       per-kernel averages (quantize passes, attention) in the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-calibration     (1 GiB device copies, for the
+                                               HBM counter scale)
 """
+import hashlib
 import argparse
 import json
 import os
@@ -44,7 +52,50 @@ def parse():
                     help="target wall time of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the fused attention launches (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run five 1 GiB device-to-device copies and exit")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "int8_quantized_flashattention_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_files):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, or None when there is none or the kernel changed since."""
+    path = os.path.join(PROFILES, "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_hash(kernel_files):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
 
 
 def host_threads():
@@ -101,6 +152,9 @@ def main():
     import int8_quantized_flashattention_amd as m
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = WORKLOADS[args.workload]
     q, k, v = w.inputs()
     dq, dk, dv = (torch.from_numpy(a).cuda() for a in (q, k, v))
@@ -168,7 +222,14 @@ def main():
         gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = "attn_fwd_kernel"
+    decode = m.attn_int8_fwd_workspace_size(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal) > 0
+    if decode:
+        roof["kernel"] = "attn_decode_kernel + attn_decode_combine"
+        kfiles = ["attn_decode.hip", "cdna4_ops.h", "attn_internal.h"]
+    else:
+        roof["kernel"] = "attn_fwd_kernel"
+        kfiles = ["attn_fwd.hip", "cdna4_ops.h", "attn_internal.h"]
+    roof["traffic"] = measured_traffic(w.name, kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
 
