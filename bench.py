@@ -1,9 +1,10 @@
 """Benchmark of the INT8 attention forward hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input that is
-already resident in HBM: per-token INT8 quantization of Q and K, INT8
-quantization of V (per tensor or per token, as the workload says), and the
-fused attention forward. `value` is algorithmic INT8 ops (4 d per visible
+already resident in HBM: per-token INT8 quantization of K, INT8 quantization
+of V (per tensor or per token, as the workload says), and the fused attention
+forward, which quantizes Q per token as it loads it (`--q-path separate`
+quantizes Q in its own pass and feeds the INT8 forward instead). `value` is algorithmic INT8 ops (4 d per visible
 query-key pair) per second of step time, in TOPS.
 
 Also reported on the same JSON line:
@@ -20,6 +21,7 @@ Also reported on the same JSON line:
   kernels       per-kernel averages (quantize passes, attention) in the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--q-path fused|separate]
        python bench.py --copy-calibration     (1 GiB device copies, for the
                                                HBM counter scale)
 """
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default="l4096_outlier", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--q-path", choices=["fused", "separate"], default="fused",
+                    help="quantize Q inside the attention kernels (fused) or in its own pass")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the fused attention launches (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -173,13 +177,19 @@ def main():
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda") if ws_n else None
     stream = torch.cuda.current_stream()
 
+    fused_q = args.q_path == "fused"
+
     def quantize():
-        m.attn_quantize_rows(dq, 1, qh, sq)
+        if not fused_q:
+            m.attn_quantize_rows(dq, 1, qh, sq)
         m.attn_quantize_rows(dk, 1, kh, sk)
         m.attn_quantize_rows(dv, rps_v, vh, sv)
 
     def attend():
-        m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+        if fused_q:
+            m.attn_int8_fwd_qfloat(dq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+        else:
+            m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
 
     for _ in range(args.warmup):
         if not args.attn_only:
@@ -208,11 +218,15 @@ def main():
     value = ops / (step_ms * 1e-3) / 1e12
     kernel_tops = ops / (attn_ms * 1e-3) / 1e12
     tile, split = m.attn_int8_fwd_schedule(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
-    kv_bytes = 2 * w.B * w.Hkv * w.Lkv * d + 4 * (2 * w.B * w.Hkv * w.Lkv + w.B * w.H * w.Lq)
+    kv_bytes = 2 * w.B * w.Hkv * w.Lkv * d + 4 * 2 * w.B * w.Hkv * w.Lkv
+    q_bytes = q.nbytes if fused_q else q.size + 4 * w.B * w.H * w.Lq
     o_bytes = w.B * w.H * w.Lq * d * (2 if w.o_dtype == "f16" else 4)
-    attn_bytes = w.B * w.H * w.Lq * d + kv_bytes + o_bytes      # compulsory HBM bytes
-    in_bytes = (q.nbytes + k.nbytes + v.nbytes)
-    quant_bytes = (in_bytes if w.v_per_token else in_bytes + v.nbytes) + q.size + k.size + v.size
+    attn_bytes = q_bytes + kv_bytes + o_bytes      # compulsory HBM bytes
+    # quantize passes: read x (V twice when one scale covers the tensor), write codes and scales
+    quantized = [k, v] if fused_q else [q, k, v]
+    quant_bytes = sum(x.nbytes + x.size + 4 * (x.size // d) for x in quantized)
+    if not w.v_per_token:
+        quant_bytes += v.nbytes - 4 * (v.size // d) + 4
 
     bound_mfma = ops / attn_bytes > PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if bound_mfma:
@@ -229,7 +243,7 @@ def main():
     else:
         roof["kernel"] = "attn_fwd_kernel"
         kfiles = ["attn_fwd.hip", "cdna4_ops.h", "attn_internal.h"]
-    roof["traffic"] = measured_traffic(w.name, kfiles)
+    roof["traffic"] = measured_traffic(w.name + ("" if fused_q else "_separate_q"), kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
 
@@ -244,8 +258,9 @@ def main():
                    "inputs": "%s N(0,1)%s" % (w.in_dtype, ", 1 percent of head-dim channels x20 in Q and K"
                                               if w.outlier_seed is not None else ""),
                    "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
-                   "step": "attention only" if args.attn_only else
-                           "quantize Q,K,V + fused attention"},
+                   "step": ("attention only" if args.attn_only else
+                            "quantize K,V + fused attention (Q quantized in the kernel)" if fused_q else
+                            "quantize Q,K,V + fused attention")},
         "roofline": roof,
         "kernels": {"attention_ms": round(attn_ms, 4), "quantize_ms": round(quant_ms, 4),
                     "attention_tops": round(kernel_tops, 2),

@@ -115,6 +115,29 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
                           size_t workspace_bytes, void* stream);
 
 /*
+ * attn_int8_fwd_qfloat — attn_int8_fwd with the per-token quantization of Q
+ * fused into the kernels' Q load (IntAttention §2.1 Eq. 3, token-level as in
+ * the INT-FlashAttention abstract): each query row is quantized in the kernel
+ * with exactly the arithmetic of attn_quantize_rows (rows_per_scale = 1), so
+ * the result is bit-identical to attn_quantize_rows followed by attn_int8_fwd,
+ * without the separate pass over Q.
+ *
+ *   q       [B, H, Lq, d] of q_dt (fp32 or fp16), device, 16-byte aligned.
+ *   q_hat   optional int8 output [B, H, Lq, d] (16-byte aligned) receiving the
+ *           codes the kernel used, or NULL.
+ *   s_q     optional fp32 output [B, H, Lq] (4-byte aligned) receiving the
+ *           per-token scales, or NULL.
+ *   Every other argument, the schedule and the workspace are as for
+ *   attn_int8_fwd.
+ */
+attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
+                                 const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                 attn_dtype o_dt, float* lse, int8_t* q_hat, float* s_q, int32_t B,
+                                 int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                 int32_t causal, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * attn_int8_fwd_workspace_size — bytes of device workspace attn_int8_fwd needs
  * for this problem (0 when it needs none; split-KV decode shapes need room for
  * the per-split partial results). Returns 0 for invalid problems as well;

@@ -26,6 +26,9 @@ SIGNATURES = {
     "attn_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "attn_int8_fwd_qfloat": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P,
+                                            ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                            _I32, _I32, _P, _SZ, _P]),
     "attn_int8_fwd_workspace_size": (_SZ, [_I32] * 7),
     "attn_int8_fwd_schedule": (ctypes.c_int, [_I32] * 7 + [_P, _P]),
     "attn_int8_debug_logits": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -116,21 +119,18 @@ def attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal):
     return t.value, s.value
 
 
-def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
-                  return_lse=False, out=None, lse=None, workspace=None, stream=None):
-    """Fused INT8 attention forward. q [B,H,Lq,d] int8, k/v [B,Hkv,Lkv,d] int8,
-    s_q [B*H*Lq], s_k [B*Hkv*Lkv], s_v [1] or [B*Hkv*Lkv] (fp32).
-    Returns O (and lse when return_lse)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+def _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out, lse, workspace):
+    """Shape checks and output / workspace allocation shared by both forwards."""
+    for t, n in ((k, "k"), (v, "v")):
         _dev(t, n, torch.int8)
-    for t, n in ((s_q, "s_q"), (s_k, "s_k"), (s_v, "s_v")):
+    for t, n in ((s_k, "s_k"), (s_v, "s_v")):
         _dev(t, n, torch.float32)
     B, H, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Hkv, Lkv, d) or tuple(v.shape) != (B, Hkv, Lkv, d):
         raise ValueError("k and v must be [B, Hkv, Lkv, d] matching q")
-    if s_q.numel() != B * H * Lq or s_k.numel() != B * Hkv * Lkv:
-        raise ValueError("s_q / s_k sizes do not match q / k")
+    if s_k.numel() != B * Hkv * Lkv:
+        raise ValueError("s_k size does not match k")
     if s_v.numel() != (B * Hkv * Lkv if v_per_token else 1):
         raise ValueError("s_v size does not match v_per_token")
     if o_dtype not in (torch.float16, torch.float32):
@@ -146,12 +146,55 @@ def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.flo
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (B, H, Hkv, Lq, Lkv, d), out, lse, workspace, ws_bytes
+
+
+def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
+                  return_lse=False, out=None, lse=None, workspace=None, stream=None):
+    """Fused INT8 attention forward. q [B,H,Lq,d] int8, k/v [B,Hkv,Lkv,d] int8,
+    s_q [B*H*Lq], s_k [B*Hkv*Lkv], s_v [1] or [B*Hkv*Lkv] (fp32).
+    Returns O (and lse when return_lse)."""
+    _dev(q, "q", torch.int8)
+    _dev(s_q, "s_q", torch.float32)
+    shape, out, lse, workspace, ws_bytes = _fwd_common(q, k, s_k, v, s_v, v_per_token, causal,
+                                                       o_dtype, return_lse, out, lse, workspace)
+    if s_q.numel() != shape[0] * shape[1] * shape[3]:
+        raise ValueError("s_q size does not match q")
     st = _lib.attn_int8_fwd(_ptr(q), _ptr(s_q), _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
                             ATTN_VSCALE_PER_TOKEN if v_per_token else ATTN_VSCALE_PER_TENSOR,
                             _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32, _ptr(lse),
-                            B, H, Hkv, Lq, Lkv, d, int(causal), _ptr(workspace), ws_bytes,
-                            _stream(stream))
+                            *shape, int(causal), _ptr(workspace), ws_bytes, _stream(stream))
     _check("attn_int8_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_int8_fwd_qfloat(q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
+                         return_lse=False, q_hat=None, s_q=None, out=None, lse=None, workspace=None,
+                         stream=None):
+    """The forward with Q given in fp16/fp32 [B,H,Lq,d]: the kernels quantize
+    each Q row per token themselves (the same codes and scales as
+    attn_quantize_rows). q_hat (int8 like q) and s_q ([B*H*Lq] fp32), when
+    given, receive them. Returns O (and lse when return_lse)."""
+    _dev(q, "q")
+    if q.dtype not in (torch.float16, torch.float32):
+        raise TypeError("q must be float16 or float32")
+    shape, out, lse, workspace, ws_bytes = _fwd_common(q, k, s_k, v, s_v, v_per_token, causal,
+                                                       o_dtype, return_lse, out, lse, workspace)
+    if q_hat is not None:
+        _dev(q_hat, "q_hat", torch.int8)
+        if tuple(q_hat.shape) != tuple(q.shape):
+            raise ValueError("q_hat must have q's shape")
+    if s_q is not None:
+        _dev(s_q, "s_q", torch.float32)
+        if s_q.numel() != shape[0] * shape[1] * shape[3]:
+            raise ValueError("s_q size does not match q")
+    st = _lib.attn_int8_fwd_qfloat(_ptr(q), ATTN_F16 if q.dtype == torch.float16 else ATTN_F32,
+                                   _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
+                                   ATTN_VSCALE_PER_TOKEN if v_per_token else ATTN_VSCALE_PER_TENSOR,
+                                   _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32,
+                                   _ptr(lse), _ptr(q_hat), _ptr(s_q), *shape, int(causal),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    _check("attn_int8_fwd_qfloat", st)
     return (out, lse) if return_lse else out
 
 
@@ -172,15 +215,15 @@ def attn_int8_debug_logits(q, k, causal, out=None, stream=None):
 
 
 def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, return_lse=False):
-    """The whole path from fp16/fp32 Q, K, V: per-token quantization of Q and K,
-    per-tensor or per-token quantization of V, then the fused forward."""
-    B, H, Lq, d = q.shape
-    qh, sq = attn_quantize_rows(q, 1)
+    """The whole path from fp16/fp32 Q, K, V: per-token quantization of K,
+    per-tensor or per-token quantization of V, then the forward, which
+    quantizes Q per token as it loads it."""
+    d = q.shape[-1]
     kh, sk = attn_quantize_rows(k, 1)
     vh, sv = attn_quantize_rows(v, 1 if v_per_token else v.numel() // d)
-    return attn_int8_fwd(qh, sq, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
+    return attn_int8_fwd_qfloat(q, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
 
 
-__all__ = ["attn_quantize_rows", "attn_int8_fwd", "attn_int8_fwd_workspace_size",
+__all__ = ["attn_quantize_rows", "attn_int8_fwd", "attn_int8_fwd_qfloat", "attn_int8_fwd_workspace_size",
            "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
            "AttnError", "LIB_PATH", "SIGNATURES"]

@@ -110,26 +110,38 @@ attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq
   return ATTN_OK;
 }
 
-attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
-                          const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
-                          attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv,
-                          int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (!q || !s_q || !k || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
+namespace {
+
+// Shared body of attn_int8_fwd and attn_int8_fwd_qfloat (q_float != NULL:
+// float Q, quantized in the kernels).
+attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, attn_dtype q_dt,
+                       int8_t* q_hat, float* s_q_out, const int8_t* k, const float* s_k,
+                       const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                       attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq,
+                       int32_t Lkv, int32_t d, int32_t causal, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!k || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
+  if (q_float) {
+    if (q_dt != ATTN_F32 && q_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q_float, 16) || (q_hat && !aligned(q_hat, 16)) || (s_q_out && !aligned(s_q_out, 4)))
+      return ATTN_ERR_INVALID_ARG;
+  } else {
+    if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(s_q, 4)) return ATTN_ERR_INVALID_ARG;
+  }
   if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN) return ATTN_ERR_INVALID_ARG;
   if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
   if (s != ATTN_OK) return s;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
-    return ATTN_ERR_INVALID_ARG;
-  if (!aligned(s_q, 4) || !aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4)))
-    return ATTN_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4))) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return ATTN_ERR_INVALID_ARG;
 
   attn::FwdArgs a{};
   a.q = q; a.s_q = s_q; a.k = k; a.s_k = s_k; a.v = v; a.s_v = s_v;
+  a.q_float = q_float; a.q_float_f16 = (q_dt == ATTN_F16); a.q_hat_out = q_hat; a.s_q_out = s_q_out;
   a.o = o; a.lse = lse; a.s_dump = nullptr;
   a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
   a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN); a.o_f16 = (o_dt == ATTN_F16);
@@ -139,6 +151,29 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = dec ? attn::launch_decode(a, split, st) : attn::launch_prefill(a, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                          const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                          attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv,
+                          int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
+  return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
+                    B, H, Hkv, Lq, Lkv, d, causal, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
+                                 const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                 attn_dtype o_dt, float* lse, int8_t* q_hat, float* s_q, int32_t B,
+                                 int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                 int32_t causal, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!q) return ATTN_ERR_INVALID_ARG;
+  return fwd_common(nullptr, nullptr, q, q_dt, q_hat, s_q, k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H,
+                    Hkv, Lq, Lkv, d, causal, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_int8_debug_logits(const int8_t* q, const int8_t* k, int32_t B, int32_t H,

@@ -127,7 +127,7 @@ __device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, 
   return p;
 }
 
-template <int D, bool CAUSAL, bool VPT>
+template <int D, bool CAUSAL, bool VPT, bool QF>
 __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
   constexpr int NC = D / 64;
   constexpr int NCB = D / 16;
@@ -164,14 +164,30 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
   DLanes<D> ln;
   ln.init(lane);
 
-  // Q fragment (B operand of S^T): 16 bytes per 64-channel chunk; s_Q.
+  // Q fragment (B operand of S^T): 16 bytes per 64-channel chunk; s_Q. QF:
+  // the row arrives in fp16/fp32 and is quantized here (the quantizer's
+  // arithmetic; the row's 4 lanes share its absmax).
   v4i qf[NC];
+  float sq = 0.0f;
+  float xq[QF ? NC : 1][16];
+  if constexpr (QF) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    qf[c] = zero4();
-    if (rvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + qrow * D + c * 64 + grp * 16);
+    for (int c = 0; c < NC; ++c) {
+      if (rvalid) {
+        load16_as_f32(a.q_float, qrow * D + c * 64 + grp * 16, a.q_float_f16, xq[c]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xq[c][e] = 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = zero4();
+      if (rvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + qrow * D + c * 64 + grp * 16);
+    }
+    sq = rvalid ? a.s_q[qrow] : 0.0f;
   }
-  float sq = rvalid ? a.s_q[qrow] : 0.0f;
 
   // scale slots start at zero: a load past Lkv may leave a slot untouched
   for (int i = lane; i < kStages * BN; i += 64) {
@@ -181,6 +197,28 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
   __syncthreads();
   if (n_tiles > 0) request_tile<D, VPT>(sm[0], rk, rv, rsk, rsv, ln, lane, s0);
   if (n_tiles > 1) request_tile<D, VPT>(sm[1], rk, rv, rsk, rsv, ln, lane, s0 + BN);
+  if constexpr (QF) {
+    float am = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(xq[c][e]));
+    am = row_max4(am);
+    const float r = quant_recip(am);
+    sq = quant_scale(am);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qf[c] = v4i{static_cast<int>(quant_word(&xq[c][0], r)), static_cast<int>(quant_word(&xq[c][4], r)),
+                  static_cast<int>(quant_word(&xq[c][8], r)), static_cast<int>(quant_word(&xq[c][12], r))};
+    // each row of the group is written by exactly one chunk's wavefront
+    if (rvalid && split == 0) {
+      if (a.q_hat_out) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) *reinterpret_cast<v4i*>(a.q_hat_out + qrow * D + c * 64 + grp * 16) = qf[c];
+      }
+      if (a.s_q_out && grp == 0) a.s_q_out[qrow] = sq;
+    }
+  }
   if (n_tiles > 1) wait_vm_lds<NL>();
   else wait_vm_lds<0>();
   // the wait covered the Q loads too (issued first); tell the compiler
@@ -399,7 +437,10 @@ __global__ __launch_bounds__(256) void attn_decode_combine(FwdArgs a, int n_spli
 template <int D, bool CAUSAL, bool VPT>
 hipError_t launch_dec(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
-  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT>), grid, dim3(64), 0, st, a, split_len, n_split);
+  if (a.q_float)
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, true>), grid, dim3(64), 0, st, a, split_len, n_split);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   return hipGetLastError();
 }
 

@@ -274,7 +274,7 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
   rb = n_rb - 1 - (w - bh * n_rb);
 }
 
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
@@ -314,21 +314,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk. Loaded
   // before the first stage requests, so that the prologue's wait covers it.
+  // QF: the row arrives in fp16/fp32 and is quantized here, per token with
+  // the quantizer's arithmetic; the lane pair (l, l ^ 32) holds the row.
   v4i qf[NC];
+  float sq = 0.0f;
+  float xq[QF ? NC : 1][16];
+  if constexpr (QF) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    qf[c] = v4i{0, 0, 0, 0};
-    if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
+    for (int c = 0; c < NC; ++c) {
+      if (qvalid) {
+        load16_as_f32(a.q_float, (q_base + qi) * D + c * 32 + g * 16, a.q_float_f16, xq[c]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xq[c][e] = 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = v4i{0, 0, 0, 0};
+      if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
+    }
+    sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
   }
-  const float sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
   __syncthreads();
   request_tile<D, true, VPT>(sm[0], bf, ln, wave, lane, 0);
   if (n_tiles > 1) request_tile<D, true, VPT>(sm[1], bf, ln, wave, lane, BN);
-  const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
-  // base-2 logit per unit of S_int * s_K. Kept >= FLT_MIN so that -inf * c2
-  // stays -inf for masked keys; a zero query (s_Q = 0) has S_int = 0 and all
-  // its logits stay exactly 0.
-  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
+  if constexpr (QF) {
+    float am = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(xq[c][e]));
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+    am = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+    const float r = quant_recip(am);
+    sq = quant_scale(am);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qf[c] = v4i{static_cast<int>(quant_word(&xq[c][0], r)), static_cast<int>(quant_word(&xq[c][4], r)),
+                  static_cast<int>(quant_word(&xq[c][8], r)), static_cast<int>(quant_word(&xq[c][12], r))};
+    if (qvalid) {
+      if (a.q_hat_out) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          *reinterpret_cast<v4i*>(a.q_hat_out + (q_base + qi) * D + c * 32 + g * 16) = qf[c];
+      }
+      if (a.s_q_out && g == 0) a.s_q_out[q_base + qi] = sq;
+    }
+  }
   const int lim = CAUSAL ? qi + shift : a.Lkv - 1;    // last visible key of this row
   const int lim_first = CAUSAL ? qw0 + shift : a.Lkv - 1;   // smallest in the wavefront
 
@@ -350,11 +384,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   else wait_vm_lds<0>();
   bare_barrier();
   // The wait above also covered the Q loads (issued before it). Passing the
-  // fragment through an empty asm statement tells the compiler so; otherwise
+  // fragment and s_Q through empty asm statements tells the compiler so; otherwise
   // it waits for them again inside the tile loop, which would also wait for
   // the newest stage request.
 #pragma unroll
   for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
+  asm volatile("" : "+v"(sq));
+  const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
+  // base-2 logit per unit of S_int * s_K. Kept >= FLT_MIN so that -inf * c2
+  // stays -inf for masked keys; a zero query (s_Q = 0) has S_int = 0 and all
+  // its logits stay exactly 0.
+  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
 
   // One tile: request t+2 | QK(t) [MFMA] | dequant, softmax(t) [VALU] | fold
   // | PV(t) [MFMA] | wait for t+1 | barrier. The stage being read and the
@@ -534,7 +574,10 @@ template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
 hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16>), grid, dim3(kThreads), 0, st, a);
+  if (a.q_float)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, false>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

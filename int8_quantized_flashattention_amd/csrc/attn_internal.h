@@ -12,6 +12,8 @@ namespace attn {
 // Problem description after host-side validation.
 struct FwdArgs {
   const int8_t* q; const float* s_q;
+  // fused Q quantization: float Q in, optional code / scale outputs
+  const void* q_float; int q_float_f16; int8_t* q_hat_out; float* s_q_out;
   const int8_t* k; const float* s_k;
   const int8_t* v; const float* s_v;
   void* o; float* lse;

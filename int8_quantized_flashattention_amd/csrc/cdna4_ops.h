@@ -4,6 +4,7 @@
 // swizzle of K/V tiles. Internal header.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -75,6 +76,48 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, u
 // the 8-byte rows addressed by lanes 2 b + i / 8 (b = 0..7 gives byte b)
 __device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+}
+
+// The per-group quantizer's arithmetic, shared by the quantization pass and
+// the fused Q quantization (so both give identical codes): for absmax a,
+// r = 127 / a and s = a / 127 (correctly rounded; 0 when a == 0), and
+// q = clamp(rne(x * r), -127, 127) with x * r one rounded fp32 product.
+__device__ __forceinline__ float quant_recip(float a) { return a == 0.0f ? 0.0f : __fdiv_rn(127.0f, a); }
+__device__ __forceinline__ float quant_scale(float a) { return a == 0.0f ? 0.0f : __fdiv_rn(a, 127.0f); }
+__device__ __forceinline__ uint32_t quant_code(float x, float r) {
+  float t = __builtin_rintf(__fmul_rn(x, r));
+  t = fminf(127.0f, fmaxf(-127.0f, t));
+  return static_cast<uint32_t>(static_cast<int>(t)) & 0xffu;
+}
+// codes of 4 values, byte i from x[i]
+__device__ __forceinline__ uint32_t quant_word(const float* x, float r) {
+  return quant_code(x[0], r) | (quant_code(x[1], r) << 8) | (quant_code(x[2], r) << 16) | (quant_code(x[3], r) << 24);
+}
+
+// 16 consecutive Q values of one row as fp32 (fp16 or fp32 storage)
+__device__ __forceinline__ void load16_as_f32(const void* base, int64_t elem, bool f16, float (&x)[16]) {
+  if (f16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 raw = p[h];
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __half2 hv = *reinterpret_cast<const __half2*>(&w[i]);
+        const float2 f = __half22float2(hv);
+        x[h * 8 + 2 * i] = f.x;
+        x[h * 8 + 2 * i + 1] = f.y;
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = p[i];
+      x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+    }
+  }
 }
 
 // Raw buffer resource over nbytes bytes (loads at or past the end read 0)

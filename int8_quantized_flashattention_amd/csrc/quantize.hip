@@ -16,6 +16,7 @@
 // the bit pattern of |x| (non-negative floats order like their bits), then the
 // quantizing pass, whose re-read mostly hits the 256 MB last-level cache.
 #include "attn_internal.h"
+#include "cdna4_ops.h"
 
 #include <hip/hip_fp16.h>
 
@@ -24,6 +25,11 @@ namespace {
 
 constexpr int kChunk = 8;          // elements per lane per load
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;         // loads in flight per lane in the large-group quantize pass
+constexpr int kUnrollMax = 8;      // loads in flight per lane in the large-group absmax pass
+// blocks per group of the absmax pass at most: each ends with one atomicMax
+// on the group's slot, and same-address atomics serialize in L2
+constexpr int kMaxAbsmaxBlocks = 512;
 
 struct Chunk8 { float x[kChunk]; };
 
@@ -55,63 +61,66 @@ __device__ __forceinline__ float chunk_absmax(const Chunk8& c) {
   return m;
 }
 
-// q = clamp(rne(x * r)); the multiply is kept separate from the rounding (no
-// contraction) so the code is the RNE of the rounded product.
-__device__ __forceinline__ int quant1(float x, float r) {
-  float t = __builtin_rintf(__fmul_rn(x, r));
-  t = fminf(127.0f, fmaxf(-127.0f, t));
-  return static_cast<int>(t);
-}
-
 __device__ __forceinline__ void store_codes(int8_t* q, int64_t elem, const Chunk8& c, float r, bool zero) {
   uint32_t w0 = 0, w1 = 0;
   if (!zero) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w0 |= (static_cast<uint32_t>(quant1(c.x[i], r)) & 0xffu) << (8 * i);
-      w1 |= (static_cast<uint32_t>(quant1(c.x[4 + i], r)) & 0xffu) << (8 * i);
-    }
+    w0 = quant_word(&c.x[0], r);
+    w1 = quant_word(&c.x[4], r);
   }
   *reinterpret_cast<uint2*>(q + elem) = make_uint2(w0, w1);
 }
 
 // ---------------------------------------------------------------------------
-// Small groups: a team of T lanes (a power of two <= 64) owns one group and
-// each lane holds up to CH chunks in registers.
+// Small groups: a team of T lanes (a power of two <= 64) owns G consecutive
+// groups; each lane holds up to CH chunks of each in registers. All loads of
+// the G groups are issued before the first reduction, so a lane keeps
+// G * CH chunks in flight.
 // ---------------------------------------------------------------------------
-template <bool F16, int T, int CH>
+template <bool F16, int T, int CH, int G>
 __global__ __launch_bounds__(kThreads) void quantize_small_groups(
     const void* __restrict__ x, int64_t n_groups, int64_t group_elems, int8_t* __restrict__ q,
     float* __restrict__ scales) {
   constexpr int kTeams = kThreads / T;
   const int team = threadIdx.x / T;
   const int tl = threadIdx.x % T;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kTeams + team;
-  const bool live = g < n_groups;
-  const int64_t base = g * group_elems;
+  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kTeams + team) * G;
   const int n_chunks = static_cast<int>(group_elems / kChunk);
 
-  Chunk8 c[CH];
-  float a = 0.0f;
+  Chunk8 c[G][CH];
+  float a[G];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int ci = tl + i * T;
-    if (live && ci < n_chunks) {
-      c[i] = load_chunk<F16>(x, base + static_cast<int64_t>(ci) * kChunk);
-      a = fmaxf(a, chunk_absmax(c[i]));
+  for (int j = 0; j < G; ++j) {
+    a[j] = 0.0f;
+    const int64_t base = (g0 + j) * group_elems;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int ci = tl + i * T;
+      if (g0 + j < n_groups && ci < n_chunks) c[j][i] = load_chunk<F16>(x, base + static_cast<int64_t>(ci) * kChunk);
     }
   }
-  // team-wide maximum (exact: max is order-free)
 #pragma unroll
-  for (int off = T / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, T));
-  if (!live) return;
-  const bool zero = (a == 0.0f);
-  const float r = zero ? 0.0f : __fdiv_rn(127.0f, a);
-  if (tl == 0) scales[g] = zero ? 0.0f : __fdiv_rn(a, 127.0f);
+  for (int j = 0; j < G; ++j) {
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int ci = tl + i * T;
-    if (ci < n_chunks) store_codes(q, base + static_cast<int64_t>(ci) * kChunk, c[i], r, zero);
+    for (int i = 0; i < CH; ++i) {
+      const int ci = tl + i * T;
+      if (g0 + j < n_groups && ci < n_chunks) a[j] = fmaxf(a[j], chunk_absmax(c[j][i]));
+    }
+    // team-wide maximum (exact: max is order-free)
+#pragma unroll
+    for (int off = T / 2; off > 0; off >>= 1) a[j] = fmaxf(a[j], __shfl_xor(a[j], off, T));
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int64_t g = g0 + j;
+    if (g >= n_groups) break;
+    const bool zero = (a[j] == 0.0f);
+    const float r = quant_recip(a[j]);
+    if (tl == 0) scales[g] = quant_scale(a[j]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int ci = tl + i * T;
+      if (ci < n_chunks) store_codes(q, g * group_elems + static_cast<int64_t>(ci) * kChunk, c[j][i], r, zero);
+    }
   }
 }
 
@@ -131,10 +140,23 @@ __global__ __launch_bounds__(kThreads) void absmax_large_groups(const void* __re
   const int64_t g = blockIdx.x;
   const int64_t base = g * group_elems;
   const int64_t n_chunks = group_elems / kChunk;
-  float a = 0.0f;
-  for (int64_t ci = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x; ci < n_chunks;
-       ci += static_cast<int64_t>(gridDim.y) * kThreads)
-    a = fmaxf(a, chunk_absmax(load_chunk<F16>(x, base + ci * kChunk)));
+  // kUnrollMax independent loads per lane in flight per round
+  const int64_t stride = static_cast<int64_t>(gridDim.y) * kThreads;
+  float am[kUnrollMax];
+#pragma unroll
+  for (int u = 0; u < kUnrollMax; ++u) am[u] = 0.0f;
+  int64_t ci = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x;
+  for (; ci + (kUnrollMax - 1) * stride < n_chunks; ci += kUnrollMax * stride) {
+    Chunk8 c[kUnrollMax];
+#pragma unroll
+    for (int u = 0; u < kUnrollMax; ++u) c[u] = load_chunk<F16>(x, base + (ci + u * stride) * kChunk);
+#pragma unroll
+    for (int u = 0; u < kUnrollMax; ++u) am[u] = fmaxf(am[u], chunk_absmax(c[u]));
+  }
+  for (; ci < n_chunks; ci += stride) am[0] = fmaxf(am[0], chunk_absmax(load_chunk<F16>(x, base + ci * kChunk)));
+  float a = am[0];
+#pragma unroll
+  for (int u = 1; u < kUnrollMax; ++u) a = fmaxf(a, am[u]);
   for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
   __shared__ float wmax[kThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
@@ -156,25 +178,32 @@ __global__ __launch_bounds__(kThreads) void quantize_large_groups(const void* __
   const int64_t n_chunks = group_elems / kChunk;
   const float a = __uint_as_float(bits[g]);
   const bool zero = (a == 0.0f);
-  const float r = zero ? 0.0f : __fdiv_rn(127.0f, a);
-  for (int64_t ci = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x; ci < n_chunks;
-       ci += static_cast<int64_t>(gridDim.y) * kThreads)
-    store_codes(q, base + ci * kChunk, load_chunk<F16>(x, base + ci * kChunk), r, zero);
+  const float r = quant_recip(a);
+  const int64_t stride = static_cast<int64_t>(gridDim.y) * kThreads;
+  int64_t ci = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x;
+  for (; ci + (kUnroll - 1) * stride < n_chunks; ci += kUnroll * stride) {
+    Chunk8 c[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) c[u] = load_chunk<F16>(x, base + (ci + u * stride) * kChunk);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) store_codes(q, base + (ci + u * stride) * kChunk, c[u], r, zero);
+  }
+  for (; ci < n_chunks; ci += stride) store_codes(q, base + ci * kChunk, load_chunk<F16>(x, base + ci * kChunk), r, zero);
 }
 
 __global__ void finalize_scales(float* scales, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) {
-    const float a = __uint_as_float(reinterpret_cast<const uint32_t*>(scales)[i]);
-    scales[i] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, 127.0f);
+    scales[i] = quant_scale(__uint_as_float(reinterpret_cast<const uint32_t*>(scales)[i]));
   }
 }
 
-template <bool F16, int T, int CH>
+template <bool F16, int T, int CH, int G>
 hipError_t run_small(const void* x, int64_t n_groups, int64_t ge, int8_t* q, float* s, hipStream_t st) {
   constexpr int kTeams = kThreads / T;
-  const int64_t blocks = (n_groups + kTeams - 1) / kTeams;
-  hipLaunchKernelGGL((quantize_small_groups<F16, T, CH>), dim3(static_cast<unsigned>(blocks)),
+  const int64_t per_block = int64_t{kTeams} * G;
+  const int64_t blocks = (n_groups + per_block - 1) / per_block;
+  hipLaunchKernelGGL((quantize_small_groups<F16, T, CH, G>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, st, x, n_groups, ge, q, s);
   return hipGetLastError();
 }
@@ -185,20 +214,21 @@ hipError_t run(const void* x, int64_t n_rows, int n_cols, int64_t rps, int8_t* q
   const int64_t ge = rps * static_cast<int64_t>(n_cols);
   const int64_t n_groups = n_rows / rps;
   const int64_t n_chunks = ge / kChunk;
-  if (n_chunks <= 8) return run_small<F16, 8, 1>(x, n_groups, ge, q, s, st);
-  if (n_chunks <= 16) return run_small<F16, 16, 1>(x, n_groups, ge, q, s, st);
-  if (n_chunks <= 32) return run_small<F16, 32, 1>(x, n_groups, ge, q, s, st);
-  if (n_chunks <= 64) return run_small<F16, 64, 1>(x, n_groups, ge, q, s, st);
-  if (n_chunks <= 256) return run_small<F16, 64, 4>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 8) return run_small<F16, 8, 1, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 16) return run_small<F16, 16, 1, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 32) return run_small<F16, 32, 1, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 64) return run_small<F16, 64, 1, 1>(x, n_groups, ge, q, s, st);
+  if (n_chunks <= 256) return run_small<F16, 64, 4, 1>(x, n_groups, ge, q, s, st);
   // large groups: zero the maxima, atomic max, quantize, turn maxima into scales
   uint32_t* bits = reinterpret_cast<uint32_t*>(s);
   const unsigned zb = static_cast<unsigned>((n_groups + 255) / 256);
   hipLaunchKernelGGL(zero_bits, dim3(zb), dim3(256), 0, st, bits, n_groups);
-  const int64_t per_block = static_cast<int64_t>(kThreads) * 4;   // chunks per block per pass
+  const int64_t per_block = static_cast<int64_t>(kThreads) * 4 * kUnroll;   // chunks per block
   int64_t bpg = (n_chunks + per_block - 1) / per_block;
   if (bpg > 2048) bpg = 2048;
   const dim3 grid(static_cast<unsigned>(n_groups), static_cast<unsigned>(bpg));
-  hipLaunchKernelGGL(absmax_large_groups<F16>, grid, dim3(kThreads), 0, st, x, ge, bits);
+  const dim3 grid_max(static_cast<unsigned>(n_groups), static_cast<unsigned>(bpg < kMaxAbsmaxBlocks ? bpg : kMaxAbsmaxBlocks));
+  hipLaunchKernelGGL(absmax_large_groups<F16>, grid_max, dim3(kThreads), 0, st, x, ge, bits);
   hipLaunchKernelGGL(quantize_large_groups<F16>, grid, dim3(kThreads), 0, st, x, ge,
                      static_cast<const uint32_t*>(bits), q);
   hipLaunchKernelGGL(finalize_scales, dim3(zb), dim3(256), 0, st, s, n_groups);

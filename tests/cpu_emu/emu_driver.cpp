@@ -5,6 +5,8 @@
 //   emu_driver quant  x.bin dt n_rows n_cols rps  q.out s.out
 //   emu_driver fwd    q.bin sq.bin k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out
+//   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt
+//                     B H Hkv Lq Lkv d causal  o.out lse.out qhat.out sq.out
 //   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
 #include <cstdio>
 #include <cstdlib>
@@ -75,6 +77,32 @@ int main(int argc, char** argv) {
                        nullptr);
     write_file(argv[17], o, osz);
     write_file(argv[18], lse, nq * 4);
+  } else if (mode == "fwdq" && argc == 21) {
+    const int qdt = std::atoi(argv[3]);
+    const int vmode = std::atoi(argv[8]), odt = std::atoi(argv[9]);
+    const int B = std::atoi(argv[10]), H = std::atoi(argv[11]), Hkv = std::atoi(argv[12]);
+    const int Lq = std::atoi(argv[13]), Lkv = std::atoi(argv[14]), d = std::atoi(argv[15]);
+    const int causal = std::atoi(argv[16]);
+    const size_t nq = size_t(B) * H * Lq, nk = size_t(B) * Hkv * Lkv;
+    void* qf = read_file(argv[2], nq * d * (qdt == ATTN_F16 ? 2 : 4));
+    auto* k = static_cast<int8_t*>(read_file(argv[4], nk * d));
+    auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
+    auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode ? nk : 1) * 4));
+    const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
+    void* o = alloc(osz);
+    float* lse = static_cast<float*>(alloc(nq * 4));
+    auto* qh = static_cast<int8_t*>(alloc(nq * d));
+    float* sq = static_cast<float*>(alloc(nq * 4));
+    const size_t ws_n = attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
+    void* ws = ws_n ? std::aligned_alloc(256, (ws_n + 255) / 256 * 256) : nullptr;
+    st = attn_int8_fwd_qfloat(qf, static_cast<attn_dtype>(qdt), k, sk, v, sv,
+                              static_cast<attn_vscale>(vmode), o, static_cast<attn_dtype>(odt), lse,
+                              qh, sq, B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n, nullptr);
+    write_file(argv[17], o, osz);
+    write_file(argv[18], lse, nq * 4);
+    write_file(argv[19], qh, nq * d);
+    write_file(argv[20], sq, nq * 4);
   } else if (mode == "logits" && argc == 12) {
     const int B = std::atoi(argv[4]), H = std::atoi(argv[5]), Hkv = std::atoi(argv[6]);
     const int Lq = std::atoi(argv[7]), Lkv = std::atoi(argv[8]), d = std::atoi(argv[9]);

@@ -4,6 +4,9 @@ through the oracle on the same bytes, and compare.
 Tolerance for O (fp32 or fp16 output): max-abs error <= 2e-2 and relative
 Frobenius error <= 1e-2 against the oracle run with the GPU's KV schedule.
 The quantized tensors, their scales and the INT32 logits must be bit-exact.
+The forward that quantizes fp16/fp32 Q itself must return the quantizer's
+codes and scales and the same O and lse, bit for bit, as the forward fed with
+them.
 """
 import sys
 
@@ -91,6 +94,17 @@ def run_problem(lib, q, k, v, causal, v_per_token, o_dtype, rows=None, check_lse
         vh, sv, vd, svd = quantize_subset(lib, v, batches)
     tdt = torch.float16 if o_dtype == "f16" else torch.float32
     o, lse = lib.attn_int8_fwd(qd, sqd, kd, skd, vd, svd, v_per_token, causal, tdt, return_lse=True)
+    # the same problem with Q given in floating point (quantized in the kernel)
+    qh2 = torch.empty_like(qd)
+    sq2 = torch.empty_like(sqd)
+    o2, lse2 = lib.attn_int8_fwd_qfloat(dev(q), kd, skd, vd, svd, v_per_token, causal, tdt,
+                                        return_lse=True, q_hat=qh2, s_q=sq2)
+    assert torch.equal(qh2, qd), "fused Q codes differ from the quantizer's"
+    assert torch.equal(sq2.view(torch.int32), sqd.view(torch.int32)), "fused s_Q differs"
+    assert torch.equal(o2.view(torch.int16 if tdt == torch.float16 else torch.int32),
+                       o.view(torch.int16 if tdt == torch.float16 else torch.int32)), "fused-Q O differs"
+    assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32)), "fused-Q lse differs"
+    del o2, lse2, qh2, sq2
     og = host(o).astype(np.float32)
     lg = host(lse)
     tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)

@@ -67,6 +67,29 @@ def test_fwd_rejects_before_launch(kw, expect):
     assert fwd(**kw) == expect
 
 
+def fwdq(**kw):
+    args = dict(q=A, q_dt=1, k=A, s_k=A, v=A, s_v=A, v_mode=0, o=A, o_dt=1, lse=None, q_hat=None,
+                s_q=None, B=1, H=2, Hkv=1, Lq=8, Lkv=8, d=64, causal=0, ws=None, ws_bytes=0)
+    args.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return L.attn_int8_fwd_qfloat(p(args["q"]), args["q_dt"], p(args["k"]), p(args["s_k"]),
+                                  p(args["v"]), p(args["s_v"]), args["v_mode"], p(args["o"]),
+                                  args["o_dt"], p(args["lse"]), p(args["q_hat"]), p(args["s_q"]),
+                                  args["B"], args["H"], args["Hkv"], args["Lq"], args["Lkv"],
+                                  args["d"], args["causal"], p(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(q_dt=4), INVALID), (dict(k=None), INVALID),
+    (dict(s_v=None), INVALID), (dict(o=None), INVALID), (dict(v_mode=3), INVALID),
+    (dict(q=A + 8), INVALID), (dict(q_hat=A + 4), INVALID), (dict(s_q=A + 2), INVALID),
+    (dict(H=3, Hkv=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(B=1, H=2, Hkv=1, Lq=1, Lkv=4096), INVALID),   # decode schedule needs a workspace
+])
+def test_fwd_qfloat_rejects_before_launch(kw, expect):
+    assert fwdq(**kw) == expect
+
+
 def test_quantize_rejects_before_launch():
     p = ctypes.c_void_p
     q = lambda **kw: L.attn_quantize_rows(

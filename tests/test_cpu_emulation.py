@@ -114,6 +114,34 @@ def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, o
     assert np.abs(lse - lo).max() <= 1e-4 * max(1.0, np.abs(lo).max())
 
 
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,qdt", [
+    (1, 2, 1, 130, 200, 128, 1, 0, np.float16), (2, 3, 3, 65, 65, 64, 0, 1, np.float32),
+    (1, 8, 2, 1, 700, 128, 0, 0, np.float16), (1, 4, 1, 3, 300, 64, 1, 1, np.float32),
+])
+def test_emulated_attention_float_q(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, qdt):
+    # the forward that quantizes fp16/fp32 Q itself gives the quantizer's
+    # codes and scales, and the same O and lse as the forward fed with them
+    r = np.random.Generator(np.random.PCG64(B * 1000 + Lq + Lkv))
+    q = (r.standard_normal((B, H, Lq, d)) * 3).astype(qdt)
+    q[0, 0, min(1, Lq - 1)] = 0                      # an all-zero row: s_Q = 0
+    k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    qh, sq = oracle.quantize_rows(q, 1)
+    kh, sk = oracle.quantize_rows(k, 1)
+    vh, sv = oracle.quantize_rows(v, 1 if vpt else v.size // d)
+    out = {n: os.path.join(str(tmp_path), n) for n in ("o1", "l1", "o2", "l2", "qh", "sq")}
+    kv = [put(tmp_path, n + ".bin", a) for n, a in (("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
+    shape = [B, H, Hkv, Lq, Lkv, d, causal]
+    run(exe, tmp_path, ["fwdq", put(tmp_path, "qf.bin", q), F16 if qdt == np.float16 else F32, *kv,
+                        vpt, F32, *shape, out["o1"], out["l1"], out["qh"], out["sq"]])
+    run(exe, tmp_path, ["fwd", put(tmp_path, "q.bin", qh), put(tmp_path, "sq.bin", sq), *kv,
+                        vpt, F32, *shape, out["o2"], out["l2"]])
+    assert np.array_equal(np.fromfile(out["qh"], np.int8).reshape(qh.shape), qh)
+    assert np.array_equal(np.fromfile(out["sq"], np.uint32), sq.view(np.uint32))
+    for a, b in (("o1", "o2"), ("l1", "l2")):
+        assert np.array_equal(np.fromfile(out[a], np.uint32), np.fromfile(out[b], np.uint32))
+
+
 def test_emulated_attention_huge_logits(exe, tmp_path):
     # Q = K = 60 N(0,1): logits ~5e4, where fp32 rounding of the exponent
     # argument could otherwise push the max key's probability code past 127
