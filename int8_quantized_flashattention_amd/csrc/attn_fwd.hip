@@ -147,8 +147,10 @@ __device__ __forceinline__ void qk_tile(v16i (&s)[NKB], const int8_t* kst, const
     }
 }
 
-// O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T.
-template <int D>
+// O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T (FRESH: acc[c] =
+// V_hat^T . P_hat^T, the first product taking the inline constant 0 as its
+// accumulator, so a new INT32 run needs no zeroing instructions).
+template <int D, bool FRESH>
 __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, const Lanes<D>& ln,
                                         const v4i (&pv)[NKB]) {
 #pragma unroll
@@ -158,7 +160,7 @@ __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, 
       const int8_t* p = vst + kb * 32 * D + ln.voff[c];
       const v2i lo = lds_read_tr8(p);
       const v2i hi = lds_read_tr8(p + 8 * D);
-      acc[c] = mfma_i8(v4i{lo.x, lo.y, hi.x, hi.y}, pv[kb], acc[c]);
+      acc[c] = mfma_i8(v4i{lo.x, lo.y, hi.x, hi.y}, pv[kb], (FRESH && kb == 0) ? zero16() : acc[c]);
     }
 }
 
@@ -378,6 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   }
   float m_f = kNegInf;                 // frame of acc (per-tensor V)
   int int_tiles = 0;                   // tiles in the current INT32 run
+  bool fresh = true;                   // the next PV starts a new INT32 run
 
   // tile 0 must have landed (tile 1 may still be in flight)
   if (n_tiles > 1) wait_vm_lds<2 * LPW>();
@@ -452,17 +455,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[c][v] = __builtin_fmaf(f, static_cast<float>(acc_i[c][v]), acc[c][v]);
-          acc_i[c] = zero16();
         }
+        fresh = true;
         int_tiles = 1;
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc_i[c] = zero16();
     }
     m = m_new;
 
-    pv_tile<D>(acc_i, st->v, ln, p);
+    // per-token V converts every tile's product on its own: always a new run
+    if (VPT || fresh) pv_tile<D, true>(acc_i, st->v, ln, p);
+    else pv_tile<D, false>(acc_i, st->v, ln, p);
+    fresh = false;
     if constexpr (VPT) {
       // per-token V: tile scales differ, so each tile's INT32 product is
       // converted on its own: acc = alpha acc + s_t PV(t)
