@@ -48,7 +48,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the clocks settle over the first tens of ms)")
     ap.add_argument("--workload", default="l4096_outlier", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample (0 disables the CPU baseline)")

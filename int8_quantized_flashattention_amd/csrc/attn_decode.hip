@@ -14,9 +14,13 @@
 // "FlashAttention-3", abstract).
 //
 // Per wavefront: the 16 rows of one v_mfma_i32_16x16x64_i8 tile hold the
-// group's query rows (row r = (head - Hkv-group start) * Lq + query); K/V tiles
-// go from HBM straight into a 3-stage LDS ring (buffer loads with LDS
-// destination, rows swizzled), V^T operands come from ds_read_b64_tr_b8.
+// group's query rows (row r = (head - Hkv-group start) * Lq + query). K tiles
+// go from HBM straight into registers, already in the MFMA operand layout
+// (two register slots: tile t+2 is loaded into tile t's slot as soon as the
+// QK of tile t has read it); V tiles and the scales go into a 3-stage LDS ring
+// (buffer loads with LDS destination, rows swizzled), since the V^T operands
+// need the transposing ds_read_b64_tr_b8. Keeping K out of LDS halves the ring,
+// so twice as many wavefronts (and loads in flight) fit on a CU.
 // Lane l holds query row l % 16 and, in each of the 4 key blocks of 16, keys
 // 4 b + 0..3 of its lane group, that is the 16 consecutive keys 16 (l / 16)
 // .. +15 of the tile, which are exactly its P operand for O^T = V^T P^T.
@@ -24,6 +28,8 @@
 #include "cdna4_ops.h"
 
 #include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -39,7 +45,6 @@ constexpr int kMaxIntTiles = 32768 / BN;
 
 template <int D>
 struct DStage {
-  alignas(16) int8_t k[BN * D];
   alignas(16) int8_t v[BN * D];
   alignas(16) float sk[BN];
   alignas(16) float sv[BN];
@@ -54,9 +59,12 @@ template <int D>
 struct DLanes {
   static constexpr int NC = D / 64;            // 64-channel chunks (K dim of QK)
   static constexpr int NCB = D / 16;           // 16-channel blocks of O
-  static constexpr int NLD = BN * D / 1024;    // 1 KB loads per operand per tile
+  static constexpr int NLD = BN * D / 1024;    // 1 KB LDS loads of V per tile
   uint32_t ld[NLD];
-  int koff[2][NC];     // K operand LDS offset, key blocks 0 / 1 (blocks 2 / 3: + 8 D)
+  // K operand of key block kb, channel chunk c: 16 bytes of key row
+  // key_of_row16(kb & 1, r) + 8 (kb >> 1), channels 64 c + 16 grp; the byte
+  // offset within the tile is kg[kb & 1] + (8 D (kb >> 1) + 64 c)
+  uint32_t kg[2];
   int voff[NCB];       // transposed V read offset, channel block cb, keys +0..7 (+8 D: 8..15)
 
   __device__ __forceinline__ void init(int lane) {
@@ -64,11 +72,7 @@ struct DLanes {
     for (int n = 0; n < NLD; ++n) ld[n] = tile_load_off<D>(n, lane);
     const int r = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int kr = key_of_row16(b, r);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) koff[b][c] = kr * D + (((4 * c + grp) ^ swz<D>(kr)) * 16);
-    }
+    for (int b = 0; b < 2; ++b) kg[b] = static_cast<uint32_t>(key_of_row16(b, r) * D + 16 * grp);
     // lane 16 grp + i addresses key 16 grp + i / 2, channels 16 cb + 8 (i % 2)
     // .. +7, so after the transposing read lane l holds channel 16 cb + l % 16,
     // keys 16 (l / 16) .. +7
@@ -78,22 +82,43 @@ struct DLanes {
   }
 };
 
-// Loads per tile issued by the (single) wavefront.
-template <int D, bool VPT>
-constexpr int loads_per_tile() { return 2 * DLanes<D>::NLD + 1 + (VPT ? 1 : 0); }
+// K operand registers of one tile: key block kb, channel chunk c at kb NC + c
+template <int D>
+using KRegs = v4i[NB * (D / 64)];
 
+// After a wait that covered a slot's loads: passing the slot through an empty
+// asm statement makes that point its definition for the compiler, which then
+// adds no wait of its own before the MFMAs that read it.
+template <int D>
+__device__ __forceinline__ void landed(KRegs<D>& kr) {
+#pragma unroll
+  for (int i = 0; i < NB * (D / 64); ++i) asm volatile("" : "+v"(kr[i]));
+}
+
+// Loads per tile issued by the (single) wavefront (all count in vmcnt).
 template <int D, bool VPT>
-__device__ __forceinline__ void request_tile(DStage<D>& st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                             __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
-                                             const DLanes<D>& ln, int lane, int k0) {
+constexpr int loads_per_tile() { return DLanes<D>::NLD + 1 + (VPT ? 1 : 0) + NB * (D / 64); }
+
+// V tile and scales of the tile at key k0 into an LDS stage
+template <int D, bool VPT>
+__device__ __forceinline__ void request_vs(DStage<D>& st, __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rsk,
+                                           __amdgpu_buffer_rsrc_t rsv, const DLanes<D>& ln, int lane, int k0) {
   lds_load4(rsk, st.sk, lane * 4, k0 * 4);
   if (VPT) lds_load4(rsv, st.sv, lane * 4, k0 * 4);
   const uint32_t soff = static_cast<uint32_t>(k0) * D;
 #pragma unroll
-  for (int n = 0; n < DLanes<D>::NLD; ++n) {
-    lds_load16(rk, st.k + n * 1024, ln.ld[n], soff);
-    lds_load16(rv, st.v + n * 1024, ln.ld[n], soff);
-  }
+  for (int n = 0; n < DLanes<D>::NLD; ++n) lds_load16(rv, st.v + n * 1024, ln.ld[n], soff);
+}
+
+// K operands of the tile at key k0 into a register slot
+template <int D>
+__device__ __forceinline__ void request_k(KRegs<D>& kr, __amdgpu_buffer_rsrc_t rk, const DLanes<D>& ln, int k0) {
+  constexpr int NC = D / 64;
+  const uint32_t soff = static_cast<uint32_t>(k0) * D;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[kb * NC + c] = buf_load16(rk, ln.kg[kb & 1] + 8 * D * (kb >> 1) + 64 * c, soff);
 }
 
 // x of lane l ^ 16 (ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 within 32
@@ -128,7 +153,8 @@ __device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, 
 }
 
 template <int D, bool CAUSAL, bool VPT, bool QF>
-__global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
+// two wavefronts per SIMD (registers <= 256): the LDS ring allows six per CU
+__global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
   constexpr int NC = D / 64;
   constexpr int NCB = D / 16;
   constexpr int NL = loads_per_tile<D, VPT>();
@@ -195,8 +221,16 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
     sm[i / BN].sv[i % BN] = 0.0f;
   }
   __syncthreads();
-  if (n_tiles > 0) request_tile<D, VPT>(sm[0], rk, rv, rsk, rsv, ln, lane, s0);
-  if (n_tiles > 1) request_tile<D, VPT>(sm[1], rk, rv, rsk, rsv, ln, lane, s0 + BN);
+  // Every request is issued, also past the last tile: such a request starts at
+  // key Lkv, where every lane's offset lies outside the buffers, so it fetches
+  // nothing (the loads return 0). Unconditional loads keep the compiler's own
+  // register waits exact.
+  KRegs<D> kr[2];                          // K operands, slot t % 2 holds tile t
+  const int k_first = n_tiles > 0 ? s0 : a.Lkv, k_second = n_tiles > 1 ? s0 + BN : a.Lkv;
+  request_vs<D, VPT>(sm[0], rv, rsk, rsv, ln, lane, k_first);
+  request_k<D>(kr[0], rk, ln, k_first);
+  request_vs<D, VPT>(sm[1], rv, rsk, rsv, ln, lane, k_second);
+  request_k<D>(kr[1], rk, ln, k_second);
   if constexpr (QF) {
     float am = 0.0f;
 #pragma unroll
@@ -219,9 +253,9 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
       if (a.s_q_out && grp == 0) a.s_q_out[qrow] = sq;
     }
   }
-  if (n_tiles > 1) wait_vm_lds<NL>();
-  else wait_vm_lds<0>();
-  // the wait covered the Q loads too (issued first); tell the compiler
+  wait_vm_lds<NL>();                   // tile 0 (and the Q loads, issued first) landed
+  landed<D>(kr[0]);
+  // the wait covered the Q loads too; tell the compiler
 #pragma unroll
   for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
   asm volatile("" : "+v"(sq));
@@ -241,10 +275,17 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
   float m_f = kNegInf;
   int int_tiles = 0;
 
-  auto step = [&](int t, const DStage<D>* __restrict__ st, DStage<D>* __restrict__ nx) __attribute__((always_inline)) {
+  // One tile t with K in register slot S = t % 2 (a compile-time index, so the
+  // slots stay in registers): request V and scales of t+2 | QK | request K of
+  // t+2 into slot S | softmax | PV | wait for t+1. The LDS stage read and the
+  // stage filled are passed as restrict pointers so the compiler adds no waits
+  // for the loads just issued.
+  auto step = [&](auto slot, int t, const DStage<D>* __restrict__ st, DStage<D>* __restrict__ nx)
+                  __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
     const int k0 = s0 + t * BN;
-    const bool req = t + 2 < n_tiles;
-    if (req) request_tile<D, VPT>(*nx, rk, rv, rsk, rsv, ln, lane, k0 + 2 * BN);
+    const int kq = t + 2 < n_tiles ? k0 + 2 * BN : a.Lkv;
+    request_vs<D, VPT>(*nx, rv, rsk, rsv, ln, lane, kq);
 
     // S^T = K_hat . Q_hat^T, exact INT32
     v4i s[NB];
@@ -253,10 +294,8 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        const v4i ka = *reinterpret_cast<const v4i*>(st->k + ln.koff[kb & 1][c] + (kb >> 1) * 8 * D);
-        s[kb] = mfma16(ka, qf[c], s[kb]);
-      }
+      for (int kb = 0; kb < NB; ++kb) s[kb] = mfma16(kr[S][kb * NC + c], qf[c], s[kb]);
+    request_k<D>(kr[S], rk, ln, kq);
 
     // u = S_int s_K[j], -inf past the chunk end or the causal limit; key
     // 16 grp + 4 kb + e of the tile is visible iff 4 kb + e <= rel
@@ -359,16 +398,24 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(FwdArgs a, int split_le
     }
 
     // tile t+1 must have landed; this wavefront is the stage ring's only user
-    if (req) wait_vm_lds<NL>();
-    else wait_vm_lds<0>();
+    wait_vm_lds<NL>();
+    landed<D>(kr[1 - S]);
   };
 
-  int s_cur = 0;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int s_req = s_cur == 0 ? kStages - 1 : s_cur - 1;
-    step(t, &sm[s_cur], &sm[s_req]);
-    s_cur = s_cur == kStages - 1 ? 0 : s_cur + 1;
+  int s_cur = 0;                       // LDS stage of tile t; tile t+2 goes to the one before it
+  auto next = [](int i) { return i == kStages - 1 ? 0 : i + 1; };
+  auto prev = [](int i) { return i == 0 ? kStages - 1 : i - 1; };
+  // pairs of tiles (slots 0, 1) with no branch between them, then an odd last
+  // tile: the K slots then stay in fixed registers across the loop
+  int t = 0;
+  for (; t + 2 <= n_tiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t, &sm[s_cur], &sm[prev(s_cur)]);
+    s_cur = next(s_cur);
+    step(std::integral_constant<int, 1>{}, t + 1, &sm[s_cur], &sm[prev(s_cur)]);
+    s_cur = next(s_cur);
   }
+  if (t < n_tiles) step(std::integral_constant<int, 0>{}, t, &sm[s_cur], &sm[prev(s_cur)]);
+  wait_vm_lds<0>();                    // the last (empty) requests, before the LDS is released
 
   if constexpr (!VPT) {
     const float back = (m == kNegInf) ? 0.0f : exp2_hw(m_f - m);

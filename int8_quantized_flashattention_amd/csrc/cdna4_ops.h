@@ -8,6 +8,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Lower bound on wavefronts per SIMD for a kernel (caps its registers); a
+// host-side stand-in of the HIP headers may define it away.
+#ifndef ATTN_WAVES_PER_EU
+#define ATTN_WAVES_PER_EU(n) __attribute__((amdgpu_waves_per_eu(n)))
+#endif
+
 namespace attn {
 namespace {
 
@@ -71,6 +77,11 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* dst, 
 }
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
+}
+// 16 bytes per lane from a raw buffer into registers (zero where the offset
+// lies outside the buffer)
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
 // the 8-byte rows addressed by lanes 2 b + i / 8 (b = 0..7 gives byte b)

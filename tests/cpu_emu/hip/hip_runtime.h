@@ -316,6 +316,8 @@ inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); ret
 #define __any(p) emu::wave_any(p)
 #define __builtin_amdgcn_readfirstlane(x) (x)
 typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;
+// no register-allocation hints on the host
+#define ATTN_WAVES_PER_EU(n)
 #define __builtin_amdgcn_make_buffer_rsrc(base, stride, n, flags) emu::make_buffer_rsrc(base, n)
 #define __builtin_amdgcn_raw_buffer_load_b32(r, v, s, aux) emu::raw_buffer_load_b32(r, v, s)
 #define __builtin_amdgcn_raw_buffer_load_b64(r, v, s, aux) emu::raw_buffer_load_b64(r, v, s)
