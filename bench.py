@@ -4,7 +4,10 @@ A step is one pass of the whole path over one batch of synthetic input that is
 already resident in HBM: per-token INT8 quantization of K, INT8 quantization
 of V (per tensor or per token, as the workload says), and the fused attention
 forward, which quantizes Q per token as it loads it (`--q-path separate`
-quantizes Q in its own pass and feeds the INT8 forward instead). `value` is algorithmic INT8 ops (4 d per visible
+quantizes Q in its own pass and feeds the INT8 forward instead). For the
+decode workload K and V sit in an INT8 cache quantized once, before timing; a
+step appends the newest token's K and V to the cache (quantize-on-append) and
+runs the forward over the whole cache. `value` is algorithmic INT8 ops (4 d per visible
 query-key pair) per second of step time, in TOPS.
 
 Also reported on the same JSON line:
@@ -179,10 +182,21 @@ def main():
     stream = torch.cuda.current_stream()
 
     fused_q = args.q_path == "fused"
+    if w.kv_cache:
+        assert w.v_per_token, "an appendable cache has per-token V scales"
+        # the cache holds every token; each step re-appends the newest one
+        # (position Lkv - 1) with the same values
+        m.attn_quantize_rows(dk, 1, kh, sk)
+        m.attn_quantize_rows(dv, 1, vh, sv)
+        k_new, v_new = dk[:, :, -1:].contiguous(), dv[:, :, -1:].contiguous()
 
     def quantize():
         if not fused_q:
             m.attn_quantize_rows(dq, 1, qh, sq)
+        if w.kv_cache:
+            m.attn_kv_append(k_new, kh, sk, w.Lkv - 1)
+            m.attn_kv_append(v_new, vh, sv, w.Lkv - 1)
+            return
         m.attn_quantize_rows(dk, 1, kh, sk)
         m.attn_quantize_rows(dv, rps_v, vh, sv)
 
@@ -224,7 +238,9 @@ def main():
     o_bytes = w.B * w.H * w.Lq * d * (2 if w.o_dtype == "f16" else 4)
     attn_bytes = q_bytes + kv_bytes + o_bytes      # compulsory HBM bytes
     # quantize passes: read x (V twice when one scale covers the tensor), write codes and scales
-    quantized = [k, v] if fused_q else [q, k, v]
+    quantized = [k, v] if not w.kv_cache else [k[:, :, -1:], v[:, :, -1:]]
+    if not fused_q:
+        quantized.append(q)
     quant_bytes = sum(x.nbytes + x.size + 4 * (x.size // d) for x in quantized)
     if not w.v_per_token:
         quant_bytes += v.nbytes - 4 * (v.size // d) + 4
@@ -259,9 +275,11 @@ def main():
                    "inputs": "%s N(0,1)%s" % (w.in_dtype, ", 1 percent of head-dim channels x20 in Q and K"
                                               if w.outlier_seed is not None else ""),
                    "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
+                   "kv_cache": bool(w.kv_cache),
                    "step": ("attention only" if args.attn_only else
-                            "quantize K,V + fused attention (Q quantized in the kernel)" if fused_q else
-                            "quantize Q,K,V + fused attention")},
+                            ("append the new token's K,V to the INT8 cache" if w.kv_cache else "quantize K,V")
+                            + (" + fused attention (Q quantized in the kernel)" if fused_q else
+                               " + quantize Q + fused attention"))},
         "roofline": roof,
         "kernels": {"attention_ms": round(attn_ms, 4), "quantize_ms": round(quant_ms, 4),
                     "attention_tops": round(kernel_tops, 2),

@@ -79,6 +79,31 @@ attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, i
                                int64_t rows_per_scale, int8_t* q, float* scales, void* stream);
 
 /*
+ * attn_kv_append — per-token INT8 quantization of new K or V tokens straight
+ * into their rows of an INT8 cache (quantize-on-append; the per-token
+ * quantizer of IntAttention §2.1 Eq. 3 with the token-level granularity of the
+ * INT-FlashAttention abstract, so the cache holds exactly what
+ * attn_quantize_rows would produce for the whole tensor).
+ *
+ *   x       [B, Hkv, T, d] new tokens of x_dt (fp32 or fp16), device,
+ *           16-byte aligned.
+ *   cache   [B, Hkv, L_max, d] int8, device, 8-byte aligned: rows pos ..
+ *           pos + T - 1 of every (b, kv head) receive the codes of the new
+ *           tokens; no other row is touched.
+ *   scales  [B, Hkv, L_max] fp32, device, 4-byte aligned: the matching
+ *           per-token scales.
+ *   d       a multiple of 8, at most 2048 (else ATTN_ERR_UNSUPPORTED).
+ *   B, Hkv, T, L_max >= 1; 0 <= pos and pos + T <= L_max (else
+ *           ATTN_ERR_INVALID_ARG). The cache must have fewer than 2^31 elements.
+ *
+ * Codes and scales follow attn_quantize_rows with rows_per_scale = 1 exactly.
+ * Only per-token scales can be appended (a per-tensor scale would change the
+ * rows already in the cache).
+ */
+attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
+                           int8_t* cache, float* scales, int32_t L_max, int32_t pos, void* stream);
+
+/*
  * attn_int8_fwd — fused INT8 attention forward (INT-FlashAttention abstract:
  * FlashAttention forward with fully INT8 inputs; formulas as listed at the top
  * of this header).

@@ -24,6 +24,7 @@ ATTN_VSCALE_PER_TENSOR, ATTN_VSCALE_PER_TOKEN = 0, 1
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
     "attn_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
+    "attn_kv_append": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
     "attn_int8_fwd_qfloat": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P,
@@ -104,6 +105,27 @@ def attn_quantize_rows(x, rows_per_scale=1, q=None, scales=None, stream=None):
                                  n_rows, n_cols, rows_per_scale, _ptr(q), _ptr(scales), _stream(stream))
     _check("attn_quantize_rows", st)
     return q, scales
+
+
+def attn_kv_append(x, cache, scales, pos, stream=None):
+    """Per-token quantization of new tokens x [B,Hkv,T,d] (fp16/fp32) into rows
+    pos .. pos+T-1 of the INT8 cache [B,Hkv,L_max,d] and its scales
+    [B,Hkv,L_max]; the codes equal attn_quantize_rows(.., 1) of the same rows."""
+    _dev(x, "x")
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    _dev(cache, "cache", torch.int8)
+    _dev(scales, "scales", torch.float32)
+    B, Hkv, T, d = x.shape
+    if cache.dim() != 4 or tuple(cache.shape[:2]) != (B, Hkv) or cache.shape[3] != d:
+        raise ValueError("cache must be [B, Hkv, L_max, d] matching x")
+    L_max = cache.shape[2]
+    if scales.numel() != B * Hkv * L_max:
+        raise ValueError("scales must hold B * Hkv * L_max values")
+    st = _lib.attn_kv_append(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32, B, Hkv, T, d,
+                             _ptr(cache), _ptr(scales), L_max, int(pos), _stream(stream))
+    _check("attn_kv_append", st)
+    return cache, scales
 
 
 def attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal):
@@ -224,6 +246,6 @@ def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, re
     return attn_int8_fwd_qfloat(q, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
 
 
-__all__ = ["attn_quantize_rows", "attn_int8_fwd", "attn_int8_fwd_qfloat", "attn_int8_fwd_workspace_size",
+__all__ = ["attn_quantize_rows", "attn_kv_append", "attn_int8_fwd", "attn_int8_fwd_qfloat", "attn_int8_fwd_workspace_size",
            "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
            "AttnError", "LIB_PATH", "SIGNATURES"]

@@ -91,6 +91,20 @@ attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, i
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
+                           int8_t* cache, float* scales, int32_t L_max, int32_t pos, void* stream) {
+  if (!x || !cache || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || L_max < 1 || pos < 0 || T > L_max - pos)
+    return ATTN_ERR_INVALID_ARG;
+  if (d % 8 != 0 || d > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t{B} * Hkv * L_max * d > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(cache, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_append(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache,
+                                           scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t attn_int8_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
                                     int32_t d, int32_t causal) {
   if (check_shape(B, H, Hkv, Lq, Lkv, d, causal) != ATTN_OK) return 0;

@@ -42,6 +42,11 @@ size_t fwd_workspace_bytes(int B, int H, int Hkv, int Lq, int Lkv, int d, int ca
 
 hipError_t launch_quantize(const void* x, int x_f16, int64_t n_rows, int n_cols,
                            int64_t rows_per_scale, int8_t* q, float* scales, hipStream_t st);
+// per-token quantization of segments x t_new new rows into rows pos .. pos +
+// t_new - 1 of each segment's l_max-row block of (cache, scales)
+constexpr int kMaxAppendCols = 2048;
+hipError_t launch_append(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max,
+                         int pos, int8_t* cache, float* scales, hipStream_t st);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t st);
 hipError_t launch_debug_logits(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const FwdArgs& a, int split_len, hipStream_t st);

@@ -76,10 +76,16 @@ __device__ __forceinline__ void store_codes(int8_t* q, int64_t elem, const Chunk
 // the G groups are issued before the first reduction, so a lane keeps
 // G * CH chunks in flight.
 // ---------------------------------------------------------------------------
-template <bool F16, int T, int CH, int G>
+// Where group g of the input goes (MAP): output group (g / seg_in) * seg_out +
+// off + g % seg_in, e.g. new tokens into their rows of a cache.
+struct RowMap {
+  int64_t seg_in, seg_out, off;
+};
+
+template <bool F16, int T, int CH, int G, bool MAP>
 __global__ __launch_bounds__(kThreads) void quantize_small_groups(
     const void* __restrict__ x, int64_t n_groups, int64_t group_elems, int8_t* __restrict__ q,
-    float* __restrict__ scales) {
+    float* __restrict__ scales, RowMap map) {
   constexpr int kTeams = kThreads / T;
   const int team = threadIdx.x / T;
   const int tl = threadIdx.x % T;
@@ -113,13 +119,14 @@ __global__ __launch_bounds__(kThreads) void quantize_small_groups(
   for (int j = 0; j < G; ++j) {
     const int64_t g = g0 + j;
     if (g >= n_groups) break;
+    const int64_t go = MAP ? (g / map.seg_in) * map.seg_out + map.off + g % map.seg_in : g;
     const bool zero = (a[j] == 0.0f);
     const float r = quant_recip(a[j]);
-    if (tl == 0) scales[g] = quant_scale(a[j]);
+    if (tl == 0) scales[go] = quant_scale(a[j]);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int ci = tl + i * T;
-      if (ci < n_chunks) store_codes(q, g * group_elems + static_cast<int64_t>(ci) * kChunk, c[j][i], r, zero);
+      if (ci < n_chunks) store_codes(q, go * group_elems + static_cast<int64_t>(ci) * kChunk, c[j][i], r, zero);
     }
   }
 }
@@ -199,13 +206,30 @@ __global__ void finalize_scales(float* scales, int64_t n) {
 }
 
 template <bool F16, int T, int CH, int G>
-hipError_t run_small(const void* x, int64_t n_groups, int64_t ge, int8_t* q, float* s, hipStream_t st) {
+hipError_t run_small(const void* x, int64_t n_groups, int64_t ge, int8_t* q, float* s, hipStream_t st,
+                     const RowMap* map = nullptr) {
   constexpr int kTeams = kThreads / T;
   const int64_t per_block = int64_t{kTeams} * G;
   const int64_t blocks = (n_groups + per_block - 1) / per_block;
-  hipLaunchKernelGGL((quantize_small_groups<F16, T, CH, G>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kThreads), 0, st, x, n_groups, ge, q, s);
+  if (map)
+    hipLaunchKernelGGL((quantize_small_groups<F16, T, CH, G, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, st, x, n_groups, ge, q, s, *map);
+  else
+    hipLaunchKernelGGL((quantize_small_groups<F16, T, CH, G, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, st, x, n_groups, ge, q, s, RowMap{1, 1, 0});
   return hipGetLastError();
+}
+
+// Per-token groups of at most kMaxAppendCols columns, written through a row map.
+template <bool F16>
+hipError_t run_mapped(const void* x, int64_t n_rows, int n_cols, int8_t* q, float* s, const RowMap& map,
+                      hipStream_t st) {
+  const int64_t n_chunks = n_cols / kChunk;
+  if (n_chunks <= 8) return run_small<F16, 8, 1, 1>(x, n_rows, n_cols, q, s, st, &map);
+  if (n_chunks <= 16) return run_small<F16, 16, 1, 1>(x, n_rows, n_cols, q, s, st, &map);
+  if (n_chunks <= 32) return run_small<F16, 32, 1, 1>(x, n_rows, n_cols, q, s, st, &map);
+  if (n_chunks <= 64) return run_small<F16, 64, 1, 1>(x, n_rows, n_cols, q, s, st, &map);
+  return run_small<F16, 64, 4, 1>(x, n_rows, n_cols, q, s, st, &map);
 }
 
 template <bool F16>
@@ -241,6 +265,14 @@ hipError_t launch_quantize(const void* x, int x_f16, int64_t n_rows, int n_cols,
                            int8_t* q, float* scales, hipStream_t st) {
   return x_f16 ? run<true>(x, n_rows, n_cols, rps, q, scales, st)
                : run<false>(x, n_rows, n_cols, rps, q, scales, st);
+}
+
+hipError_t launch_append(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max,
+                         int pos, int8_t* cache, float* scales, hipStream_t st) {
+  const RowMap map{t_new, l_max, pos};
+  const int64_t n_rows = segments * t_new;
+  return x_f16 ? run_mapped<true>(x, n_rows, n_cols, cache, scales, map, st)
+               : run_mapped<false>(x, n_rows, n_cols, cache, scales, map, st);
 }
 
 }  // namespace attn

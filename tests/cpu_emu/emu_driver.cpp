@@ -8,6 +8,8 @@
 //   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out qhat.out sq.out
 //   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
+//   emu_driver append x.bin dt B Hkv T d L_max pos  cache.out scales.out
+//                     (cache and scales start filled with 0x63 bytes)
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -103,6 +105,20 @@ int main(int argc, char** argv) {
     write_file(argv[18], lse, nq * 4);
     write_file(argv[19], qh, nq * d);
     write_file(argv[20], sq, nq * 4);
+  } else if (mode == "append" && argc == 12) {
+    const int dt = std::atoi(argv[3]);
+    const int B = std::atoi(argv[4]), Hkv = std::atoi(argv[5]), T = std::atoi(argv[6]);
+    const int d = std::atoi(argv[7]), L = std::atoi(argv[8]), pos = std::atoi(argv[9]);
+    const size_t esz = dt == ATTN_F16 ? 2 : 4;
+    void* x = read_file(argv[2], size_t(B) * Hkv * T * d * esz);
+    const size_t nc = size_t(B) * Hkv * L * d, ns = size_t(B) * Hkv * L;
+    auto* c = static_cast<int8_t*>(alloc(nc));
+    auto* sc = static_cast<float*>(alloc(ns * 4));
+    std::memset(c, 0x63, nc);
+    std::memset(sc, 0x63, ns * 4);
+    st = attn_kv_append(x, static_cast<attn_dtype>(dt), B, Hkv, T, d, c, sc, L, pos, nullptr);
+    write_file(argv[10], c, nc);
+    write_file(argv[11], sc, ns * 4);
   } else if (mode == "logits" && argc == 12) {
     const int B = std::atoi(argv[4]), H = std::atoi(argv[5]), Hkv = std::atoi(argv[6]);
     const int Lq = std::atoi(argv[7]), Lkv = std::atoi(argv[8]), d = std::atoi(argv[9]);

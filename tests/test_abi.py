@@ -90,6 +90,27 @@ def test_fwd_qfloat_rejects_before_launch(kw, expect):
     assert fwdq(**kw) == expect
 
 
+def test_kv_append_rejects_before_launch():
+    p = ctypes.c_void_p
+    f = lambda **kw: L.attn_kv_append(
+        p(kw.get("x", A)), kw.get("dt", 1), kw.get("B", 2), kw.get("Hkv", 2), kw.get("T", 1),
+        kw.get("d", 128), p(kw.get("c", A)), p(kw.get("s", A)), kw.get("L", 16), kw.get("pos", 15), None)
+    assert f(x=None) == INVALID
+    assert f(c=None) == INVALID
+    assert f(s=None) == INVALID
+    assert f(dt=3) == INVALID
+    assert f(T=0) == INVALID
+    assert f(pos=-1) == INVALID
+    assert f(pos=16) == INVALID            # pos + T > L_max
+    assert f(T=2, pos=15) == INVALID
+    assert f(d=60) == UNSUPPORTED          # not a multiple of 8
+    assert f(d=4096) == UNSUPPORTED        # wider than one team handles
+    assert f(B=4096, Hkv=64, L=8192) == UNSUPPORTED
+    assert f(x=A + 8) == INVALID
+    assert f(c=A + 4) == INVALID
+    assert f(s=A + 2) == INVALID
+
+
 def test_quantize_rejects_before_launch():
     p = ctypes.c_void_p
     q = lambda **kw: L.attn_quantize_rows(

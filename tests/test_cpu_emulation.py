@@ -58,6 +58,27 @@ def test_emulated_quantize(exe, tmp_path, rows, cols, rps, dt):
     assert np.array_equal(q, qo) and np.array_equal(s.view(np.uint32), so.view(np.uint32))
 
 
+@pytest.mark.parametrize("B,Hkv,T,d,L,pos,dt", [
+    (2, 3, 1, 128, 40, 39, np.float16), (1, 2, 5, 64, 16, 0, np.float32), (2, 2, 7, 128, 30, 11, np.float16),
+    (1, 1, 3, 2048, 5, 2, np.float32), (1, 2, 4, 24, 4, 0, np.float16),
+])
+def test_emulated_kv_append(exe, tmp_path, B, Hkv, T, d, L, pos, dt):
+    r = np.random.Generator(np.random.PCG64(T * 100 + d))
+    x = (r.standard_normal((B, Hkv, T, d)) * 4).astype(dt)
+    x[-1, -1, -1] = 0
+    co, so = os.path.join(str(tmp_path), "c.out"), os.path.join(str(tmp_path), "s.out")
+    run(exe, tmp_path, ["append", put(tmp_path, "x.bin", x), F16 if dt == np.float16 else F32, B, Hkv, T, d, L,
+                        pos, co, so])
+    c = np.fromfile(co, np.int8).reshape(B, Hkv, L, d)
+    s = np.fromfile(so, np.uint32).reshape(B, Hkv, L)
+    qo, sc = oracle.quantize_rows(x, 1)
+    assert np.array_equal(c[:, :, pos:pos + T], qo)
+    assert np.array_equal(s[:, :, pos:pos + T].reshape(-1), sc.view(np.uint32))
+    keep = np.ones(L, bool)
+    keep[pos:pos + T] = False
+    assert np.all(c[:, :, keep] == 0x63) and np.all(s[:, :, keep] == 0x63636363)
+
+
 @pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal", [
     (1, 1, 1, 128, 128, 64, 0), (2, 4, 2, 77, 130, 128, 1), (1, 2, 1, 1, 200, 128, 0),
     (1, 2, 2, 50, 190, 64, 1), (1, 1, 1, 1, 1, 64, 1), (1, 1, 1, 300, 300, 128, 1),

@@ -55,3 +55,31 @@ def test_quantize_all_zero_tensor(lib):
     x = np.zeros((16, 128), np.float16)
     q, s, _, _ = quantize_both(lib, x, 16)
     assert np.all(q == 0) and np.all(s == 0)
+
+
+# quantize-on-append into an INT8 cache: (B, Hkv, T, d, L_max, pos, dtype)
+APPEND = [
+    (2, 3, 1, 128, 40, 39, np.float16), (1, 8, 5, 64, 16, 0, np.float32),
+    (3, 2, 7, 128, 100, 50, np.float16), (1, 1, 33, 2048, 33, 0, np.float32),
+    (64, 8, 1, 128, 8192, 8191, np.float16),
+]
+
+
+@pytest.mark.parametrize("B,Hkv,T,d,L,pos,dt", APPEND)
+def test_kv_append_matches_oracle(lib, B, Hkv, T, d, L, pos, dt):
+    import torch
+    import oracle
+    log("kv append B=%d Hkv=%d T=%d d=%d L_max=%d pos=%d %s" % (B, Hkv, T, d, L, pos, np.dtype(dt).name))
+    r = _rng(B * 7 + T * 13 + d)
+    x = (r.standard_normal((B, Hkv, T, d)) * r.uniform(0.1, 10)).astype(dt)
+    x[0, 0, 0] = 0                                          # an all-zero token
+    cache = torch.full((B, Hkv, L, d), 99, dtype=torch.int8, device="cuda")   # sentinel
+    scales = torch.full((B, Hkv, L), -1.0, dtype=torch.float32, device="cuda")
+    lib.attn_kv_append(torch.from_numpy(x).cuda(), cache, scales, pos)
+    c, s = cache.cpu().numpy(), scales.cpu().numpy()
+    qo, so = oracle.quantize_rows(x, 1)
+    assert np.array_equal(c[:, :, pos:pos + T], qo)
+    assert np.array_equal(s[:, :, pos:pos + T].reshape(-1).view(np.uint32), so.view(np.uint32))
+    keep = np.ones(L, bool)
+    keep[pos:pos + T] = False
+    assert np.all(c[:, :, keep] == 99) and np.all(s[:, :, keep] == -1.0)

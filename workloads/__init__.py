@@ -50,6 +50,8 @@ class Workload:
     o_dtype: str             # "f16" or "f32"
     seeds: Tuple[int, int, int]
     outlier_seed: Optional[int] = None
+    # K/V live in an INT8 cache quantized once; a step appends one new token
+    kv_cache: bool = False
     note: str = field(default="", compare=False)
 
     @property
@@ -104,7 +106,7 @@ WORKLOADS = {
     # long context, per-token V
     "l16384": W("l16384", 1, 32, 32, 16384, 16384, 128, True, True, "f16", "f16", (401, 402, 403)),
     # decode-shaped GQA over an int8 KV cache with per-token scales
-    "decode": W("decode", 64, 32, 8, 1, 8192, 128, False, True, "f16", "f16", (501, 502, 503)),
+    "decode": W("decode", 64, 32, 8, 1, 8192, 128, False, True, "f16", "f16", (501, 502, 503), kv_cache=True),
 }
 
 __all__ = ["gaussian", "outlier_channels", "Workload", "WORKLOADS"]
