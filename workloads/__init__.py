@@ -27,6 +27,26 @@ def gaussian(shape, seed, dtype=np.float16, outlier_channels=None, outlier_gain=
     return x.astype(dtype)
 
 
+def gaussian_chunked(shape, seed, chunk_rows=1 << 20, threads=16):
+    """A seeded N(0,1) fp32 tensor drawn in parallel: the rows (last axis) are
+    cut into chunks of `chunk_rows`, chunk i drawn from its own PCG64 stream
+    spawned from SeedSequence(seed) (the same values for any thread count).
+    For tensors of ~2^31 elements, where one stream takes about a minute."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = int(np.prod(shape))
+    per = chunk_rows * shape[-1]
+    out = np.empty(n, np.float32)
+    seqs = np.random.SeedSequence(seed).spawn((n + per - 1) // per)
+
+    def fill(i):
+        np.random.Generator(np.random.PCG64(seqs[i])).standard_normal(
+            out=out[i * per:(i + 1) * per], dtype=np.float32)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(len(seqs))))
+    return out.reshape(shape)
+
+
 def outlier_channels(d, seed, fraction=0.01):
     """The seeded head-dim channels scaled for the outlier workload:
     max(1, round(fraction * d)) distinct channels."""
@@ -109,4 +129,4 @@ WORKLOADS = {
     "decode": W("decode", 64, 32, 8, 1, 8192, 128, False, True, "f16", "f16", (501, 502, 503), kv_cache=True),
 }
 
-__all__ = ["gaussian", "outlier_channels", "Workload", "WORKLOADS"]
+__all__ = ["gaussian", "gaussian_chunked", "outlier_channels", "Workload", "WORKLOADS"]
