@@ -54,7 +54,9 @@ typedef enum {
 
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1 } attn_dtype;
 
-typedef enum { ATTN_VSCALE_PER_TENSOR = 0, ATTN_VSCALE_PER_TOKEN = 1 } attn_vscale;
+/* V scale granularity: one scale for the tensor, one per token, or one per
+ * (batch, kv head) (a block granularity, IntAttention §3.3). */
+typedef enum { ATTN_VSCALE_PER_TENSOR = 0, ATTN_VSCALE_PER_TOKEN = 1, ATTN_VSCALE_PER_HEAD = 2 } attn_vscale;
 
 /*
  * attn_quantize_rows — symmetric INT8 quantization of groups of rows
@@ -110,8 +112,9 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
  *
  *   q    int8 [B, H, Lq, d]      s_q fp32 [B, H, Lq]       (per-token scales)
  *   k    int8 [B, Hkv, Lkv, d]   s_k fp32 [B, Hkv, Lkv]    (per-token scales)
- *   v    int8 [B, Hkv, Lkv, d]   s_v fp32 [1] (ATTN_VSCALE_PER_TENSOR) or
- *                                    [B, Hkv, Lkv] (ATTN_VSCALE_PER_TOKEN)
+ *   v    int8 [B, Hkv, Lkv, d]   s_v fp32 [1] (ATTN_VSCALE_PER_TENSOR),
+ *                                    [B, Hkv, Lkv] (ATTN_VSCALE_PER_TOKEN) or
+ *                                    [B, Hkv] (ATTN_VSCALE_PER_HEAD)
  *   o    [B, H, Lq, d] of o_dt (fp32 or fp16, rounded to nearest even)
  *   lse  fp32 [B, H, Lq] natural-log log-sum-exp of the scaled logits, or NULL
  *   d    64 or 128 (else ATTN_ERR_UNSUPPORTED)
@@ -127,9 +130,10 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
  * Per row the kernel visits the KV tiles reported by attn_int8_fwd_schedule
  * in ascending order. For tile t with running max m' (after the tile):
  * P_tilde = exp(S - m'), l = alpha l + sum P_tilde, P_hat = rne(P_tilde w_j)
- * with w_j = 127 (per-tensor V) or 127 s_V[j] / s_t (per-token V, s_t = the
- * largest s_V of the tile's keys), acc = alpha acc + s_t * (P_hat . V_hat)
- * (s_t = s_V for per-tensor V), and finally O = acc / (127 l). Because P_hat
+ * with w_j = 127 (per-tensor and per-head V) or 127 s_V[j] / s_t (per-token V,
+ * s_t = the largest s_V of the tile's keys), acc = alpha acc + s_t *
+ * (P_hat . V_hat) (s_t = s_V for per-tensor V, the (batch, kv head)'s s_V for
+ * per-head V), and finally O = acc / (127 l). Because P_hat
  * follows the running max, O depends on the tile size and split points; they
  * are part of the result's definition and are reported by the schedule query.
  */

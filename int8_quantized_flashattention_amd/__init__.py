@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libattn_int8.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_F32, ATTN_F16 = 0, 1
-ATTN_VSCALE_PER_TENSOR, ATTN_VSCALE_PER_TOKEN = 0, 1
+ATTN_VSCALE_PER_TENSOR, ATTN_VSCALE_PER_TOKEN, ATTN_VSCALE_PER_HEAD = 0, 1, 2
 
 # every function the C header declares, with its ctypes signature
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -141,6 +141,14 @@ def attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal):
     return t.value, s.value
 
 
+def _vmode(v_per_token):
+    """V scale mode from False / True / "head" (or 0 / 1 / 2)."""
+    if isinstance(v_per_token, str):
+        return {"tensor": ATTN_VSCALE_PER_TENSOR, "token": ATTN_VSCALE_PER_TOKEN,
+                "head": ATTN_VSCALE_PER_HEAD}[v_per_token]
+    return int(v_per_token)
+
+
 def _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out, lse, workspace):
     """Shape checks and output / workspace allocation shared by both forwards."""
     for t, n in ((k, "k"), (v, "v")):
@@ -153,8 +161,10 @@ def _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out
         raise ValueError("k and v must be [B, Hkv, Lkv, d] matching q")
     if s_k.numel() != B * Hkv * Lkv:
         raise ValueError("s_k size does not match k")
-    if s_v.numel() != (B * Hkv * Lkv if v_per_token else 1):
-        raise ValueError("s_v size does not match v_per_token")
+    mode = _vmode(v_per_token)
+    if s_v.numel() != {ATTN_VSCALE_PER_TENSOR: 1, ATTN_VSCALE_PER_TOKEN: B * Hkv * Lkv,
+                       ATTN_VSCALE_PER_HEAD: B * Hkv}.get(mode, -1):
+        raise ValueError("s_v size does not match the V scale mode")
     if o_dtype not in (torch.float16, torch.float32):
         raise TypeError("o_dtype must be float16 or float32")
     if out is None:
@@ -174,8 +184,9 @@ def _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out
 def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
                   return_lse=False, out=None, lse=None, workspace=None, stream=None):
     """Fused INT8 attention forward. q [B,H,Lq,d] int8, k/v [B,Hkv,Lkv,d] int8,
-    s_q [B*H*Lq], s_k [B*Hkv*Lkv], s_v [1] or [B*Hkv*Lkv] (fp32).
-    Returns O (and lse when return_lse)."""
+    s_q [B*H*Lq], s_k [B*Hkv*Lkv], s_v (fp32) [1] (v_per_token False),
+    [B*Hkv*Lkv] (True) or [B*Hkv] (v_per_token "head": one scale per (batch,
+    kv head)). Returns O (and lse when return_lse)."""
     _dev(q, "q", torch.int8)
     _dev(s_q, "s_q", torch.float32)
     shape, out, lse, workspace, ws_bytes = _fwd_common(q, k, s_k, v, s_v, v_per_token, causal,
@@ -183,7 +194,7 @@ def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.flo
     if s_q.numel() != shape[0] * shape[1] * shape[3]:
         raise ValueError("s_q size does not match q")
     st = _lib.attn_int8_fwd(_ptr(q), _ptr(s_q), _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
-                            ATTN_VSCALE_PER_TOKEN if v_per_token else ATTN_VSCALE_PER_TENSOR,
+                            _vmode(v_per_token),
                             _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32, _ptr(lse),
                             *shape, int(causal), _ptr(workspace), ws_bytes, _stream(stream))
     _check("attn_int8_fwd", st)
@@ -212,7 +223,7 @@ def attn_int8_fwd_qfloat(q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.f
             raise ValueError("s_q size does not match q")
     st = _lib.attn_int8_fwd_qfloat(_ptr(q), ATTN_F16 if q.dtype == torch.float16 else ATTN_F32,
                                    _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
-                                   ATTN_VSCALE_PER_TOKEN if v_per_token else ATTN_VSCALE_PER_TENSOR,
+                                   _vmode(v_per_token),
                                    _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32,
                                    _ptr(lse), _ptr(q_hat), _ptr(s_q), *shape, int(causal),
                                    _ptr(workspace), ws_bytes, _stream(stream))

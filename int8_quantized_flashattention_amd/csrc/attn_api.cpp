@@ -143,7 +143,8 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
     if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(s_q, 4)) return ATTN_ERR_INVALID_ARG;
   }
-  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN) return ATTN_ERR_INVALID_ARG;
+  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN && v_mode != ATTN_VSCALE_PER_HEAD)
+    return ATTN_ERR_INVALID_ARG;
   if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
   if (s != ATTN_OK) return s;
@@ -158,7 +159,8 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
   a.q_float = q_float; a.q_float_f16 = (q_dt == ATTN_F16); a.q_hat_out = q_hat; a.s_q_out = s_q_out;
   a.o = o; a.lse = lse; a.s_dump = nullptr;
   a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
-  a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN); a.o_f16 = (o_dt == ATTN_F16);
+  a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN);
+  a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.o_f16 = (o_dt == ATTN_F16);
   a.workspace = workspace;
   int tile, split, dec;
   attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);

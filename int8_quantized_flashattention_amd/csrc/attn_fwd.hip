@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const float ltot = pair_sum(l);                      // 127 * l
   if (!qvalid) return;
-  const float scale = (VPT ? 1.0f : a.s_v[0]) / ltot;
+  const float scale = (VPT ? 1.0f : a.s_v[a.v_per_head ? b * a.Hkv + hk : 0]) / ltot;
   const int64_t orow = (q_base + qi) * D;
 #pragma unroll
   for (int c = 0; c < NC; ++c)

@@ -20,6 +20,7 @@ struct FwdArgs {
   int32_t* s_dump;          // debug logits output (dump variant only)
   int B, H, Hkv, Lq, Lkv, d;
   int causal, v_per_token, o_f16;
+  int v_per_head;      // s_v holds one scale per (batch, kv head)
   void* workspace;
 };
 

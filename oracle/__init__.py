@@ -108,6 +108,8 @@ def attn_int8(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal
               kv_tile, kv_split_len=0, rows=None, nthreads=0, L=None):
     """Step-by-step INT8 attention forward. Returns (O fp32, lse fp32).
 
+    v_per_token: the V scale mode, 0 (or False) one scale for the tensor, 1 (or
+    True) one per token [B*Hkv*Lkv], 2 one per (batch, kv head) [B*Hkv].
     O is [B,H,Lq,d] (rows None) or [len(rows), d]."""
     args = [np.ascontiguousarray(a) for a in (q, s_q, k, s_k, v, s_v)]
     for a, dt in zip(args, (np.int8, np.float32, np.int8, np.float32, np.int8, np.float32)):

@@ -34,6 +34,9 @@
 //    quantized with multiplier w_j = (127 * s_V[j]) / s_t.
 //  * P_hat = rne(P_tilde * w) of the exact product (at most 48 significant
 //    bits, so exact in double); w = 127 for per-tensor V.
+//  * per-head V (one scale per (batch, kv head), a block granularity that
+//    IA §3.3 lists as compatible): the tile scale is that head's s_V and
+//    w = 127, i.e. the per-tensor arithmetic with the head's own scale.
 //  * the running max used to quantize a tile is the max after that tile (m').
 //  * rowsum l accumulates the fp32 P_tilde before quantization.
 //  * INT32 accumulation inside a tile, fp32 across tiles.
@@ -147,7 +150,7 @@ struct Problem {
   const int8_t* q; const float* s_q;
   const int8_t* k; const float* s_k;
   const int8_t* v; const float* s_v;
-  int v_per_token;
+  int v_mode;    // V scales: 0 one per tensor, 1 per token, 2 per (batch, kv head)
   int B, H, Hkv, Lq, Lkv, d, causal;
   int kv_tile, kv_split_len;
 };
@@ -174,7 +177,9 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
   const int8_t* kmat = P.k + kv_base * d;
   const int8_t* vmat = P.v + kv_base * d;
   const float* sk = P.s_k + kv_base;
-  const float* sv = P.v_per_token ? (P.s_v + kv_base) : P.s_v;
+  const float* sv = P.v_mode == 1 ? (P.s_v + kv_base)
+                  : P.v_mode == 2 ? (P.s_v + (PLANT("v_head_no_batch") ? hk : static_cast<int64_t>(b) * P.Hkv + hk))
+                  : P.s_v;
 
   // Bottom-right aligned causal mask: last visible key of this row.
   int64_t last = P.Lkv - 1;
@@ -224,7 +229,7 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
       if (PLANT("no_alpha")) alpha = (m == NEG_INF) ? 0.0f : 1.0f;
       // Scale of this tile's V contribution and per-key P multipliers.
       float st;
-      if (P.v_per_token) {
+      if (P.v_mode == 1) {
         st = 0.0f;
         for (int jj = 0; jj < n; ++jj) st = std::max(st, sv[t0 + jj]);
       } else {
@@ -236,7 +241,7 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
         pt[jj] = p;
         lsum += p;
         float wj;
-        if (P.v_per_token) wj = (st > 0.0f) ? (127.0f * sv[t0 + jj]) / st : 0.0f;
+        if (P.v_mode == 1) wj = (st > 0.0f) ? (127.0f * sv[t0 + jj]) / st : 0.0f;
         else wj = 127.0f;
         w[jj] = wj;
         // P_hat = rne(P_tilde * w): signed INT8 probabilities with multiplier
@@ -312,6 +317,7 @@ bool problem_ok(const Problem& P) {
   if (P.kv_tile < 1) return false;
   if (P.kv_split_len < 0 || (P.kv_split_len > 0 && P.kv_split_len % P.kv_tile)) return false;
   if (P.causal && P.Lq > P.Lkv) return false;
+  if (P.v_mode < 0 || P.v_mode > 2) return false;
   return true;
 }
 
@@ -371,11 +377,11 @@ int oracle_logits_i32(const int8_t* q, const int8_t* k, int32_t B, int32_t H, in
 // rows == NULL: every (b,h,i) row; o is [B,H,Lq,d], lse is [B,H,Lq].
 // rows != NULL: n_rows flat row ids (b*H + h)*Lq + i; o is [n_rows,d], lse [n_rows].
 int oracle_attn_int8(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
-                     const int8_t* v, const float* s_v, int32_t v_per_token,
+                     const int8_t* v, const float* s_v, int32_t v_mode,
                      int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                      int32_t causal, int32_t kv_tile, int32_t kv_split_len,
                      const int64_t* rows, int64_t n_rows, float* o, float* lse, int nthreads) {
-  Problem P{q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
+  Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
   if (!problem_ok(P)) return 1;
   const int64_t total = static_cast<int64_t>(B) * H * Lq;
   const int64_t n = rows ? n_rows : total;
@@ -394,13 +400,13 @@ int oracle_attn_int8(const int8_t* q, const float* s_q, const int8_t* k, const f
 // Same as oracle_attn_int8 for one row, also returning the per-key trace
 // (each array has Lkv entries; masked keys keep S = -inf and P = 0).
 int oracle_attn_int8_trace(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
-                           const int8_t* v, const float* s_v, int32_t v_per_token,
+                           const int8_t* v, const float* s_v, int32_t v_mode,
                            int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                            int32_t causal, int32_t kv_tile, int32_t kv_split_len,
                            int32_t b, int32_t h, int32_t i, float* o, float* lse,
                            float* S, float* m_tile, float* p_tilde, int32_t* p_hat, float* w,
                            float* split_m) {
-  Problem P{q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
+  Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
   if (!problem_ok(P) || b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Lq) return 1;
   const float NEG_INF = -std::numeric_limits<float>::infinity();
   for (int j = 0; j < Lkv; ++j) {

@@ -68,7 +68,7 @@ int main(int argc, char** argv) {
     auto* k = static_cast<int8_t*>(read_file(argv[4], nk * d));
     auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
     auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
-    auto* sv = static_cast<float*>(read_file(argv[7], (vmode ? nk : 1) * 4));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : 1) * 4));
     const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
     void* o = alloc(osz);
     float* lse = static_cast<float*>(alloc(nq * 4));
@@ -90,7 +90,7 @@ int main(int argc, char** argv) {
     auto* k = static_cast<int8_t*>(read_file(argv[4], nk * d));
     auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
     auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
-    auto* sv = static_cast<float*>(read_file(argv[7], (vmode ? nk : 1) * 4));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : 1) * 4));
     const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
     void* o = alloc(osz);
     float* lse = static_cast<float*>(alloc(nq * 4));

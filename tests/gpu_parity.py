@@ -80,14 +80,17 @@ def run_problem(lib, q, k, v, causal, v_per_token, o_dtype, rows=None, check_lse
     those entries (per-token V only, where batch entries are independent)."""
     B, H, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
-    log("[%s] B=%d H=%d Hkv=%d Lq=%d Lkv=%d d=%d causal=%d vpt=%d o=%s" %
+    # V scales: "head" one per (batch, kv head), else a truth value: per token / per tensor
+    v_per_token = "head" if isinstance(v_per_token, str) and v_per_token == "head" else bool(v_per_token)
+    log("[%s] B=%d H=%d Hkv=%d Lq=%d Lkv=%d d=%d causal=%d vpt=%s o=%s" %
         (tag, B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o_dtype))
     if batches is None:
         qh, sq, qd, sqd = quantize_both(lib, q, 1)
         kh, sk, kd, skd = quantize_both(lib, k, 1)
-        vh, sv, vd, svd = quantize_both(lib, v, 1 if v_per_token else v.size // d)
+        vh, sv, vd, svd = quantize_both(lib, v, 1 if v_per_token is True else
+                                        Lkv if v_per_token == "head" else v.size // d)
     else:
-        assert v_per_token and rows is None
+        assert v_per_token is True and rows is None
         batches = np.asarray(batches)
         qh, sq, qd, sqd = quantize_subset(lib, q, batches)
         kh, sk, kd, skd = quantize_subset(lib, k, batches)
@@ -110,7 +113,8 @@ def run_problem(lib, q, k, v, causal, v_per_token, o_dtype, rows=None, check_lse
     tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
     if batches is not None:
         og, lg, B = og[batches], lg[batches], len(batches)
-    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, v_per_token, B, H, Hkv, Lq, Lkv, d, causal,
+    mode = 2 if v_per_token == "head" else int(bool(v_per_token))
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, mode, B, H, Hkv, Lq, Lkv, d, causal,
                               tile, split, rows=rows)
     if rows is None:
         compare_o(og, oo, tag)

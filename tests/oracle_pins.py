@@ -480,6 +480,48 @@ def pin_attn_per_token_equal_scales(L):
     assert np.array_equal(o1, o2)
 
 
+def pin_attn_per_head_equal_scales(L):
+    # per-head V (mode 2) whose head scales all equal the tensor scale gives the
+    # per-tensor result bit for bit
+    r = _rng(53)
+    B, H, Hkv, Lq, Lkv, d = 2, 4, 2, 9, 70, 64
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
+    k, v = (r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32) for _ in range(2))
+    qh, sq, kh, sk, vh, sv = _quantize_all(q, k, v, False, L)
+    o1, l1 = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 0, B, H, Hkv, Lq, Lkv, d, True, 32, L=L)
+    s_head = np.full(B * Hkv, sv[0], np.float32)
+    o2, l2 = oracle.attn_int8(qh, sq, kh, sk, vh, s_head, 2, B, H, Hkv, Lq, Lkv, d, True, 32, L=L)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_attn_per_head_is_per_tensor_per_slice(L):
+    # per-head V: the output of every (batch, query head) equals a per-tensor run
+    # on that batch entry's KV head alone with its own scale (a wrong scale
+    # index picks another head's scale and fails)
+    r = _rng(54)
+    B, H, Hkv, Lq, Lkv, d = 2, 6, 3, 11, 90, 64
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
+    k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    v *= r.uniform(0.2, 5.0, size=(B, Hkv, 1, 1)).astype(np.float32)     # distinct head scales
+    qh, sq = oracle.quantize_rows(q, 1, L=L)
+    kh, sk = oracle.quantize_rows(k, 1, L=L)
+    vh, sv = oracle.quantize_rows(v, Lkv, L=L)                            # one scale per (b, kv head)
+    assert sv.shape == (B * Hkv,) and len(set(sv.tolist())) == B * Hkv
+    o, l = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 2, B, H, Hkv, Lq, Lkv, d, True, 32, L=L)
+    g = H // Hkv
+    sqr = sq.reshape(B, H, Lq)
+    skr = sk.reshape(B, Hkv, Lkv)
+    for b in range(B):
+        for h in range(H):
+            hk = h // g
+            c = np.ascontiguousarray
+            o1, l1 = oracle.attn_int8(c(qh[b:b + 1, h:h + 1]), c(sqr[b, h]), c(kh[b:b + 1, hk:hk + 1]),
+                                      c(skr[b, hk]), c(vh[b:b + 1, hk:hk + 1]), sv[b * Hkv + hk:b * Hkv + hk + 1],
+                                      0, 1, 1, 1, Lq, Lkv, d, True, 32, L=L)
+            assert np.array_equal(o[b, h], o1[0, 0]) and np.array_equal(l[b, h], l1[0, 0])
+
+
 def pin_attn_single_tile_two_pass(L):
     # Bc >= Lkv: one tile, so the max is the true row max and the method reduces
     # to the two-pass form O = s_V sum_j rne(127 e^{S_j - m}) V_hat_j / (127 sum_j e^{S_j - m}).

@@ -54,7 +54,7 @@ def fwd(**kw):
     (dict(q=None), INVALID), (dict(s_q=None), INVALID), (dict(k=None), INVALID),
     (dict(s_k=None), INVALID), (dict(v=None), INVALID), (dict(s_v=None), INVALID),
     (dict(o=None), INVALID),
-    (dict(v_mode=2), INVALID), (dict(o_dt=5), INVALID),
+    (dict(v_mode=3), INVALID), (dict(o_dt=5), INVALID),
     (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Hkv=0), INVALID), (dict(Lq=0), INVALID),
     (dict(Lkv=-3), INVALID), (dict(d=0), INVALID),
     (dict(H=3, Hkv=2), INVALID), (dict(causal=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID),

@@ -110,6 +110,8 @@ def test_emulated_logits(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal):
     # split-KV decode shapes: several chunks, GQA groups of up to 16 rows
     (2, 8, 2, 1, 1500, 128, 0, 0, F16, 1), (1, 4, 1, 4, 700, 128, 1, 1, F32, 1),
     (1, 8, 1, 2, 520, 64, 1, 0, F32, 1), (1, 2, 1, 1, 3000, 64, 0, 0, F32, 12),
+    # V scales per (batch, kv head): prefill and split-KV decode shapes
+    (2, 4, 2, 77, 130, 128, 1, 2, F16, 1), (2, 8, 2, 1, 700, 128, 0, 2, F32, 1),
 ])
 def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt, gain):
     r = np.random.Generator(np.random.PCG64(B * 100 + Lq * 7 + Lkv))
@@ -120,7 +122,7 @@ def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, o
     v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
     qh, sq = oracle.quantize_rows(q, 1)
     kh, sk = oracle.quantize_rows(k, 1)
-    vh, sv = oracle.quantize_rows(v, 1 if vpt else v.size // d)
+    vh, sv = oracle.quantize_rows(v, {0: v.size // d, 1: 1, 2: Lkv}[vpt])
     oo_p, lo_p = os.path.join(str(tmp_path), "o.out"), os.path.join(str(tmp_path), "l.out")
     files = [put(tmp_path, n + ".bin", a) for n, a in
              (("q", qh), ("sq", sq), ("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
@@ -149,7 +151,7 @@ def test_emulated_attention_float_q(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal
     v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
     qh, sq = oracle.quantize_rows(q, 1)
     kh, sk = oracle.quantize_rows(k, 1)
-    vh, sv = oracle.quantize_rows(v, 1 if vpt else v.size // d)
+    vh, sv = oracle.quantize_rows(v, {0: v.size // d, 1: 1, 2: Lkv}[vpt])
     out = {n: os.path.join(str(tmp_path), n) for n in ("o1", "l1", "o2", "l2", "qh", "sq")}
     kv = [put(tmp_path, n + ".bin", a) for n, a in (("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
     shape = [B, H, Hkv, Lq, Lkv, d, causal]
