@@ -128,5 +128,10 @@ WORKLOADS = {
     # decode-shaped GQA over an int8 KV cache with per-token scales
     "decode": W("decode", 64, 32, 8, 1, 8192, 128, False, True, "f16", "f16", (501, 502, 503), kv_cache=True),
 }
+# causal prefill over context lengths 1K .. 16K (B1 H32 d128, per-tensor V)
+for _i, _L in enumerate((1024, 2048, 4096, 8192, 16384)):
+    _s = 600 + _i
+    WORKLOADS["sweep_%dk" % (_L // 1024)] = W("sweep_%dk" % (_L // 1024), 1, 32, 32, _L, _L, 128, True, False,
+                                               "f16", "f16", (_s, _s + 10, _s + 20))
 
 __all__ = ["gaussian", "gaussian_chunked", "outlier_channels", "Workload", "WORKLOADS"]
