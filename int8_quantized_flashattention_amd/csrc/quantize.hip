@@ -29,7 +29,7 @@ constexpr int kUnroll = 4;         // loads in flight per lane in the large-grou
 constexpr int kUnrollMax = 8;      // loads in flight per lane in the large-group absmax pass
 // blocks per group of the absmax pass at most: each ends with one atomicMax
 // on the group's slot, and same-address atomics serialize in L2
-constexpr int kMaxAbsmaxBlocks = 512;
+constexpr int kMaxAbsmaxBlocks = 256;    // measured: 128 and 512+ are slower
 
 struct Chunk8 { float x[kChunk]; };
 
