@@ -110,6 +110,8 @@ def test_emulated_logits(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal):
     # split-KV decode shapes: several chunks, GQA groups of up to 16 rows
     (2, 8, 2, 1, 1500, 128, 0, 0, F16, 1), (1, 4, 1, 4, 700, 128, 1, 1, F32, 1),
     (1, 8, 1, 2, 520, 64, 1, 0, F32, 1), (1, 2, 1, 1, 3000, 64, 0, 0, F32, 12),
+    # schedule boundaries: 16 and 17 rows per KV head, more queries than keys
+    (1, 16, 1, 1, 333, 128, 0, 1, F32, 1), (1, 34, 2, 1, 300, 128, 0, 0, F32, 1), (1, 2, 2, 300, 50, 64, 0, 1, F16, 1),
     # V scales per (batch, kv head): prefill and split-KV decode shapes
     (2, 4, 2, 77, 130, 128, 1, 2, F16, 1), (2, 8, 2, 1, 700, 128, 0, 2, F32, 1),
 ])

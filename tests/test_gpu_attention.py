@@ -70,6 +70,10 @@ SWEEP = [  # B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o
     (3, 8, 1, 129, 65, 128, 0, 0, "f16"), (1, 8, 2, 257, 1000, 128, 1, 1, "f16"),
     (2, 16, 4, 16, 700, 128, 0, 1, "f16"), (1, 4, 4, 640, 640, 128, 1, 0, "f32"),
     (1, 32, 8, 3, 333, 64, 0, 1, "f32"), (2, 2, 2, 1000, 1001, 64, 1, 0, "f16"),
+    # schedule boundaries: 16 rows per KV head (the largest decode-path group),
+    # 17 (the smallest prefill-path one), more queries than keys (non-causal)
+    (1, 16, 1, 1, 333, 128, 0, 1, "f32"), (1, 8, 1, 2, 333, 64, 1, 0, "f16"),
+    (1, 34, 2, 1, 300, 128, 0, 0, "f32"), (1, 2, 2, 300, 50, 64, 0, 1, "f16"),
     # V scales per (batch, kv head)
     (2, 8, 2, 77, 130, 128, 1, "head", "f16"), (2, 16, 4, 1, 700, 128, 0, "head", "f32"),
     (3, 4, 4, 300, 300, 64, 1, "head", "f32"),
