@@ -37,14 +37,17 @@ def _bind(L):
     L.oracle_float_to_half.argtypes = [P, P, I64]
     L.oracle_quantize_rows.argtypes = [P, F, I64, I32, I64, P, P]
     L.oracle_logits_i32.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, F]
+    FL = ctypes.c_float
     L.oracle_attn_int8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
-                                   I32, I32, I32, P, I64, P, P, F]
+                                   I32, I32, I32, I32, FL, P, I64, P, P, F]
     L.oracle_attn_int8_trace.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
-                                         I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
+                                         I32, I32, I32, I32, FL, I32, I32, I32, P, P, P, P, P, P,
+                                         P, P]
+    L.oracle_index_softmax_lut.argtypes = [I32, FL, P]
     L.oracle_attn_ref_f64.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P, F]
     for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows",
                "oracle_logits_i32", "oracle_attn_int8", "oracle_attn_int8_trace",
-               "oracle_attn_ref_f64"):
+               "oracle_attn_ref_f64", "oracle_index_softmax_lut"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -104,12 +107,25 @@ def logits_i32(q, k, B, H, Hkv, Lq, Lkv, d, nthreads=0, L=None):
     return out
 
 
+def index_softmax_lut(bits, clip, L=None):
+    """The IndexSoftmax table: 2^bits int32 entries for clipping threshold clip."""
+    out = np.empty(1 << bits, np.int32) if 1 <= bits <= 8 else None
+    _check((L or lib()).oracle_index_softmax_lut(int(bits), float(clip), _p(out)), "index_softmax_lut")
+    return out
+
+
+def _lut_args(index_softmax):
+    return (0, 0.0) if index_softmax is None else (int(index_softmax[0]), float(index_softmax[1]))
+
+
 def attn_int8(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal,
-              kv_tile, kv_split_len=0, rows=None, nthreads=0, L=None):
+              kv_tile, kv_split_len=0, rows=None, nthreads=0, L=None, index_softmax=None):
     """Step-by-step INT8 attention forward. Returns (O fp32, lse fp32).
 
     v_per_token: the V scale mode, 0 (or False) one scale for the tensor, 1 (or
     True) one per token [B*Hkv*Lkv], 2 one per (batch, kv head) [B*Hkv].
+    index_softmax: None (exp softmax) or (b, c): IndexSoftmax with a 2^b-entry
+    table and clipping threshold c.
     O is [B,H,Lq,d] (rows None) or [len(rows), d]."""
     args = [np.ascontiguousarray(a) for a in (q, s_q, k, s_k, v, s_v)]
     for a, dt in zip(args, (np.int8, np.float32, np.int8, np.float32, np.int8, np.float32)):
@@ -124,14 +140,14 @@ def attn_int8(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal
         o = np.empty((nr, d), np.float32)
         lse = np.empty((nr,), np.float32)
     rc = (L or lib()).oracle_attn_int8(*(_p(a) for a in args), int(v_per_token), B, H, Hkv, Lq, Lkv,
-                                       d, int(causal), kv_tile, kv_split_len, _p(r), nr, _p(o),
-                                       _p(lse), nthreads)
+                                       d, int(causal), kv_tile, kv_split_len,
+                                       *_lut_args(index_softmax), _p(r), nr, _p(o), _p(lse), nthreads)
     _check(rc, "attn_int8")
     return o, lse
 
 
 def attn_int8_trace(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal,
-                    kv_tile, kv_split_len, b, h, i, L=None):
+                    kv_tile, kv_split_len, b, h, i, L=None, index_softmax=None):
     """One row with its per-key trace: dict of O, lse, S, m_tile, p_tilde, p_hat, w, split_m."""
     args = [np.ascontiguousarray(a) for a in (q, s_q, k, s_k, v, s_v)]
     o = np.empty(d, np.float32)
@@ -139,7 +155,8 @@ def attn_int8_trace(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, 
     S, mt, pt, w, sm = (np.empty(Lkv, np.float32) for _ in range(5))
     ph = np.empty(Lkv, np.int32)
     rc = (L or lib()).oracle_attn_int8_trace(*(_p(a) for a in args), int(v_per_token), B, H, Hkv,
-                                             Lq, Lkv, d, int(causal), kv_tile, kv_split_len, b, h, i,
+                                             Lq, Lkv, d, int(causal), kv_tile, kv_split_len,
+                                             *_lut_args(index_softmax), b, h, i,
                                              _p(o), _p(lse), _p(S), _p(mt), _p(pt), _p(ph), _p(w),
                                              _p(sm))
     _check(rc, "attn_int8_trace")
@@ -162,5 +179,5 @@ def attn_ref_f64(q, k, v, B, H, Hkv, Lq, Lkv, d, causal, rows=None, nthreads=0, 
     return o
 
 
-__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "logits_i32", "attn_int8",
+__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "logits_i32", "index_softmax_lut", "attn_int8",
            "attn_int8_trace", "attn_ref_f64"]

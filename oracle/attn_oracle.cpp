@@ -15,8 +15,12 @@
 //         INT8 quantization with zero point 0 and scale absmax/127, Eq. 3;
 //         integer logits with INT32 accumulation; output O ~ s_V * P * V_hat),
 //         §2.2 (max-subtracted stable softmax), §3.1 (logit rescale factor
-//         alpha = s_Q s_K / sqrt(d), Eq. 4), §3.2 (prior methods quantize the
-//         probabilities as signed INT8 with a multiplier of 127).
+//         alpha = s_Q s_K / sqrt(d), Eq. 4; IndexSoftmax: clipping of the
+//         distance to the row max at c, a 2^b-entry exponential table indexed
+//         by floor(distance / c * (2^b - 1))), §3.2 (prior methods quantize
+//         the probabilities as signed INT8 with a multiplier of 127; integer
+//         row sum and normalisation of the table's values), §4 ablation
+//         (recommended (b, c) = (5, 6.6)).
 //  [FA3]  "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
 //         Low-precision", abstract: tiled attention with the softmax fused
 //         block by block (online softmax).
@@ -44,6 +48,10 @@
 //    j <= i + (Lkv - Lq).
 //  * GQA: query head h reads kv head h / (H / Hkv).
 //  * 1/sqrt(d) is the fp32 rounding of the double value.
+//  * IndexSoftmax: see index_softmax_lut and attend_row_lut below (table
+//    sampled at the left end of each index bucket with multiplier 127; the
+//    distance taken on the dequantized logit; online rescale by exp; the
+//    normalisation by the integer row sum at the output).
 //
 // Build: g++ -std=c++17 -O2 -fno-fast-math -ffp-contract=off -fPIC -shared
 //        -pthread (see oracle/build.py). -ffp-contract=off keeps every fp32
@@ -153,6 +161,8 @@ struct Problem {
   int v_mode;    // V scales: 0 one per tensor, 1 per token, 2 per (batch, kv head)
   int B, H, Hkv, Lq, Lkv, d, causal;
   int kv_tile, kv_split_len;
+  int lut_bits;  // 0: exp softmax; b >= 1: IndexSoftmax with a 2^b-entry table
+  float clip;    // IndexSoftmax clipping threshold c (natural-log units)
 };
 
 // Per-key trace of one row, for the invariant tests.
@@ -292,6 +302,149 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
   if (lse) *lse = M + std::log(L);
 }
 
+// ---------------------------------------------------------------------------
+// IndexSoftmax (IA §3.1 "IndexSoftmax": integer-domain clipping and the
+// table-driven exponential; IA §3.2: integer row sum and normalisation),
+// read for this path's per-token scales and online tiles.
+//
+// Table: 2^b entries over the clipped distance range [0, c]; entry i stands
+// for the exponential at the left end of its index bucket, i.e. distance
+// c * i / (2^b - 1), as a signed 7-bit probability (the INT8 products are
+// signed, so the multiplier is 127 as for the exp path, not 255):
+//   LUT[i] = rne(127 * exp(-x_i)),  x_i = (double)c * i / (2^b - 1)
+// evaluated in double, left to right.
+void index_softmax_lut(int bits, float c, int32_t* lut) {
+  const int n = (1 << bits) - 1;
+  for (int i = 0; i <= n; ++i) {
+    double x = static_cast<double>(c) * static_cast<double>(i) / static_cast<double>(n);
+    if (PLANT("lut_half_step")) x = x * 0.5;
+    lut[i] = static_cast<int32_t>(std::nearbyint(127.0 * std::exp(-x)));
+  }
+}
+
+// One query row with IndexSoftmax in place of exp.
+//
+// The pages define the distance on the integer logits of per-tensor scales
+// (Delta = rowmax(A_hat) - A_hat, c_int = round(c sqrt(d) / (s_Q s_K)),
+// idx = floor(min(Delta, c_int) / c_int * (2^b - 1))). With one scale per
+// key, integer distances no longer measure logit differences, so the
+// distance is taken on the dequantized logit instead, which is the pages'
+// formula with c_int replaced by its exact value c / alpha:
+//   u_j   = S_int[j] * s_K[j]                        (fp32)
+//   m_u   = running max of u over the visible keys so far (this tile included)
+//   kappa = (s_Q * (1/sqrt(d))) * ((2^b - 1) / c)     (fp32, in that order)
+//   x_j   = fma(u_j, -kappa, m_u * kappa)             (fp32, one rounding)
+//   idx_j = min(floor(max(x_j, 0)), 2^b - 1)
+//   E_j   = LUT[idx_j] for visible keys, 0 for masked ones
+// Online over tiles as in the exp path: when the max rises, acc and the row
+// sum are rescaled by alpha = exp((m_u_old - m_u_new) * s_Q / sqrt(d)) (fp32);
+// the row sum adds the integer sum of the tile's E (IA §3.2's wide integer
+// accumulation), T = E . V_hat is exact INT32, and the normalisation by the
+// row sum moves to the output, O = acc / l (the FlashAttention order: the
+// pages normalise P before P.V, which needs the whole row first).
+void attend_row_lut(const Problem& P, int b, int h, int i, float* o, float* lse, RowTrace* tr) {
+  const int d = P.d;
+  const int group = P.H / P.Hkv;
+  const int hk = h / group;
+  const int64_t qrow = (static_cast<int64_t>(b) * P.H + h) * P.Lq + i;
+  const int8_t* qv = P.q + qrow * d;
+  const float sq = P.s_q[qrow];
+  const int64_t kv_base = (static_cast<int64_t>(b) * P.Hkv + hk) * P.Lkv;
+  const int8_t* kmat = P.k + kv_base * d;
+  const int8_t* vmat = P.v + kv_base * d;
+  const float* sk = P.s_k + kv_base;
+  const float sv = P.v_mode == 2 ? P.s_v[static_cast<int64_t>(b) * P.Hkv + hk] : P.s_v[0];
+
+  int64_t last = P.Lkv - 1;                      // bottom-right aligned causal mask
+  if (P.causal) last = static_cast<int64_t>(i) + (P.Lkv - P.Lq);
+  const float inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+  const float NEG_INF = -std::numeric_limits<float>::infinity();
+
+  const int n_idx = (1 << P.lut_bits) - 1;
+  std::vector<int32_t> lut(static_cast<size_t>(n_idx) + 1);
+  index_softmax_lut(P.lut_bits, P.clip, lut.data());
+  const float g = sq * inv_sqrt_d;               // natural-log logit per unit of u
+  const float k_b = static_cast<float>(static_cast<double>(n_idx) / static_cast<double>(P.clip));
+  const float kappa = PLANT("lut_no_query_scale") ? inv_sqrt_d * k_b : g * k_b;
+
+  const int Bc = P.kv_tile;
+  const int split_len = P.kv_split_len > 0 ? P.kv_split_len : P.Lkv;
+  const int n_splits = (P.Lkv + split_len - 1) / split_len;
+
+  std::vector<float> acc(d), u(Bc);
+  std::vector<int32_t> e(Bc), T(d);
+  std::vector<float> sm(n_splits), sl(n_splits), sacc(static_cast<size_t>(n_splits) * d);
+
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const int s0 = sp * split_len;
+    const int s1 = std::min(P.Lkv, s0 + split_len);
+    float m = NEG_INF, l = 0.0f;                 // running max (u units), row sum (table units)
+    std::fill(acc.begin(), acc.end(), 0.0f);
+    for (int t0 = s0; t0 < s1; t0 += Bc) {
+      const int n = std::min(s1, t0 + Bc) - t0;
+      float mt = NEG_INF;
+      for (int jj = 0; jj < n; ++jj) {
+        const int j = t0 + jj;
+        if (j > last) { u[jj] = NEG_INF; continue; }
+        u[jj] = static_cast<float>(dot_i8(qv, kmat + static_cast<int64_t>(j) * d, d)) * sk[j];
+        mt = std::max(mt, u[jj]);
+      }
+      const float m_new = std::max(m, mt);
+      if (m_new == NEG_INF) continue;            // nothing visible yet
+      const float alpha = (m == NEG_INF) ? 0.0f : std::exp((m - m_new) * g);
+      const float mu = m_new * kappa;
+      int64_t esum = 0;                          // integer row sum of the tile
+      for (int jj = 0; jj < n; ++jj) {
+        if (u[jj] == NEG_INF) { e[jj] = 0; continue; }
+        const float x = std::fma(u[jj], -kappa, mu);
+        int idx;
+        if (PLANT("lut_round_index")) idx = x <= 0.0f ? 0 : (x >= n_idx ? n_idx : static_cast<int>(std::nearbyint(x)));
+        else idx = x <= 0.0f ? 0 : (x >= n_idx ? n_idx : static_cast<int>(std::floor(x)));
+        if (PLANT("lut_no_clip")) idx = x <= 0.0f ? 0 : static_cast<int>(std::floor(x)) % (n_idx + 1);
+        e[jj] = lut[idx];
+        esum += e[jj];
+      }
+      l = alpha * l + static_cast<float>(esum);
+      for (int c = 0; c < d; ++c) T[c] = 0;      // T = E . V_hat, exact
+      for (int jj = 0; jj < n; ++jj) {
+        if (e[jj] == 0) continue;
+        const int8_t* vr = vmat + static_cast<int64_t>(t0 + jj) * d;
+        for (int c = 0; c < d; ++c) T[c] += e[jj] * static_cast<int32_t>(vr[c]);
+      }
+      for (int c = 0; c < d; ++c) acc[c] = alpha * acc[c] + sv * static_cast<float>(T[c]);
+      m = m_new;
+      if (tr) {
+        for (int jj = 0; jj < n; ++jj) {
+          const int j = t0 + jj;
+          tr->S[j] = u[jj] == NEG_INF ? NEG_INF : u[jj] * g;
+          tr->m_tile[j] = m_new * g;
+          tr->p_tilde[j] = static_cast<float>(e[jj]) / 127.0f;
+          tr->p_hat[j] = e[jj];
+          tr->w[j] = 127.0f;
+        }
+      }
+    }
+    sm[sp] = m; sl[sp] = l;
+    std::copy(acc.begin(), acc.end(), sacc.begin() + static_cast<size_t>(sp) * d);
+    if (tr) for (int j = s0; j < s1; ++j) tr->split_m[j] = m == NEG_INF ? NEG_INF : m * g;
+  }
+
+  // merge the splits by their maxima
+  float M = NEG_INF;
+  for (int sp = 0; sp < n_splits; ++sp) M = std::max(M, sm[sp]);
+  float L = 0.0f;
+  std::fill(acc.begin(), acc.end(), 0.0f);
+  for (int sp = 0; sp < n_splits; ++sp) {
+    if (sm[sp] == NEG_INF) continue;
+    const float f = std::exp((sm[sp] - M) * g);
+    L += f * sl[sp];
+    for (int c = 0; c < d; ++c) acc[c] += f * sacc[static_cast<size_t>(sp) * d + c];
+  }
+  // O = acc / l: the table's factor 127 is in both, so it cancels
+  for (int c = 0; c < d; ++c) o[c] = acc[c] / L;
+  if (lse) *lse = M * g + std::log(L / 127.0f);
+}
+
 template <class F>
 void parallel_for(int64_t n, int nthreads, F f) {
   if (nthreads <= 0) nthreads = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
@@ -318,6 +471,10 @@ bool problem_ok(const Problem& P) {
   if (P.kv_split_len < 0 || (P.kv_split_len > 0 && P.kv_split_len % P.kv_tile)) return false;
   if (P.causal && P.Lq > P.Lkv) return false;
   if (P.v_mode < 0 || P.v_mode > 2) return false;
+  if (P.lut_bits < 0 || P.lut_bits > 8) return false;
+  // IndexSoftmax: a finite positive clip, and no per-token V (whose per-key
+  // weights would re-round the table's codes)
+  if (P.lut_bits > 0 && (!(P.clip > 0.0f) || !std::isfinite(P.clip) || P.v_mode == 1)) return false;
   return true;
 }
 
@@ -357,6 +514,13 @@ int oracle_quantize_rows(const void* x, int x_is_half, int64_t n_rows, int32_t n
   return 0;
 }
 
+// The IndexSoftmax table for b = bits (1..8) and clip c: 2^b entries.
+int oracle_index_softmax_lut(int32_t bits, float c, int32_t* lut) {
+  if (bits < 1 || bits > 8 || !(c > 0.0f) || !std::isfinite(c)) return 1;
+  index_softmax_lut(bits, c, lut);
+  return 0;
+}
+
 // S_int[b,h,i,j] = sum_c Q_hat[b,h,i,c] * K_hat[b,h/(H/Hkv),j,c] for every pair
 // (mask not applied; the caller compares the visible pairs).
 int oracle_logits_i32(const int8_t* q, const int8_t* k, int32_t B, int32_t H, int32_t Hkv,
@@ -379,9 +543,11 @@ int oracle_logits_i32(const int8_t* q, const int8_t* k, int32_t B, int32_t H, in
 int oracle_attn_int8(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
                      const int8_t* v, const float* s_v, int32_t v_mode,
                      int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
-                     int32_t causal, int32_t kv_tile, int32_t kv_split_len,
-                     const int64_t* rows, int64_t n_rows, float* o, float* lse, int nthreads) {
-  Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
+                     int32_t causal, int32_t kv_tile, int32_t kv_split_len, int32_t lut_bits,
+                     float clip, const int64_t* rows, int64_t n_rows, float* o, float* lse,
+                     int nthreads) {
+  Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len,
+            lut_bits, clip};
   if (!problem_ok(P)) return 1;
   const int64_t total = static_cast<int64_t>(B) * H * Lq;
   const int64_t n = rows ? n_rows : total;
@@ -391,8 +557,8 @@ int oracle_attn_int8(const int8_t* q, const float* s_q, const int8_t* k, const f
     const int64_t id = rows ? rows[r] : r;
     const int i = static_cast<int>(id % Lq);
     const int64_t bh = id / Lq;
-    attend_row(P, static_cast<int>(bh / H), static_cast<int>(bh % H), i, o + r * d,
-               lse ? lse + r : nullptr, nullptr);
+    (P.lut_bits ? attend_row_lut : attend_row)(P, static_cast<int>(bh / H), static_cast<int>(bh % H), i,
+                                               o + r * d, lse ? lse + r : nullptr, nullptr);
   });
   return 0;
 }
@@ -403,17 +569,19 @@ int oracle_attn_int8_trace(const int8_t* q, const float* s_q, const int8_t* k, c
                            const int8_t* v, const float* s_v, int32_t v_mode,
                            int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                            int32_t causal, int32_t kv_tile, int32_t kv_split_len,
+                           int32_t lut_bits, float clip,
                            int32_t b, int32_t h, int32_t i, float* o, float* lse,
                            float* S, float* m_tile, float* p_tilde, int32_t* p_hat, float* w,
                            float* split_m) {
-  Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len};
+  Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len,
+            lut_bits, clip};
   if (!problem_ok(P) || b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Lq) return 1;
   const float NEG_INF = -std::numeric_limits<float>::infinity();
   for (int j = 0; j < Lkv; ++j) {
     S[j] = NEG_INF; m_tile[j] = NEG_INF; p_tilde[j] = 0.0f; p_hat[j] = 0; w[j] = 0.0f; split_m[j] = NEG_INF;
   }
   RowTrace tr{S, m_tile, p_tilde, p_hat, w, split_m};
-  attend_row(P, b, h, i, o, lse, &tr);
+  (P.lut_bits ? attend_row_lut : attend_row)(P, b, h, i, o, lse, &tr);
   return 0;
 }
 

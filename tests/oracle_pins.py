@@ -557,4 +557,112 @@ def pin_attn_vs_exact_gaussian(L):
         assert diff <= 0.10 and cos >= 0.99, (diff, cos)
 
 
+# ----------------------------------------------------------------------------
+# IndexSoftmax (IntAttention §3.1-3.2)
+# ----------------------------------------------------------------------------
+def pin_lut_closed_form(L):
+    # clip c = 31 ln 2 with b = 5 puts the table's grid at multiples of ln 2,
+    # so entry i is 127 / 2^i rounded; i = 1 sits at the tie 63.5, where the
+    # fp32 rounding of c decides
+    lut = oracle.index_softmax_lut(5, np.float32(31 * math.log(2)), L=L)
+    assert lut.shape == (32,)
+    assert lut[1] in (63, 64)
+    assert list(lut[[0] + list(range(2, 32))]) == [127, 32, 16, 8, 4, 2, 1] + [0] * 24
+    # every (b, c): exp(0) at entry 0, a non-increasing table, exp(-c) at the end
+    for b in (1, 3, 5, 8):
+        for c in (0.5, 5.5, 6.6, 7.7, 20.0):
+            t = oracle.index_softmax_lut(b, c, L=L)
+            assert t.shape == (1 << b,) and t[0] == 127 and np.all(np.diff(t) <= 0)
+            assert abs(t[-1] - 127 * math.exp(-c)) <= 0.5 + 1e-9
+
+
+def _lut_pages_integer(qh, kh, vh, sv, e_tab, c_int, nb, causal, tile, split, g):
+    """IndexSoftmax written with the pages' integer quantities, for per-tensor
+    scales: Delta = (running) rowmax(A_hat) - A_hat, Delta' = min(Delta, c_int),
+    idx = floor(Delta' (2^b - 1) / c_int) in exact integers, E = LUT[idx]; tiles
+    rescaled by exp(g (m_old - m_new)) (g = s_Q s_K / sqrt(d)); splits merged by
+    their maxima; O = s_V sum E V_hat / sum E. fp64."""
+    Lq, Lkv = qh.shape[0], kh.shape[0]
+    A = qh.astype(np.int64) @ kh.astype(np.int64).T
+    o = np.zeros((Lq, vh.shape[1]))
+    lse = np.zeros(Lq)
+    split = split or Lkv
+    for i in range(Lq):
+        last = i + Lkv - Lq if causal else Lkv - 1
+        parts = []
+        for s0 in range(0, Lkv, split):
+            m, l, acc = None, 0.0, np.zeros(vh.shape[1])
+            for t0 in range(s0, min(Lkv, s0 + split), tile):
+                keys = [j for j in range(t0, min(Lkv, s0 + split, t0 + tile)) if j <= last]
+                if not keys:
+                    continue
+                m_new = max(int(A[i, keys].max()), m if m is not None else -(1 << 62))
+                alpha = 0.0 if m is None else math.exp(g * (m - m_new))
+                E = np.zeros(len(keys), np.int64)
+                for n, j in enumerate(keys):
+                    delta = m_new - int(A[i, j])
+                    E[n] = e_tab[(min(delta, c_int) * nb) // c_int]
+                l = alpha * l + float(E.sum())
+                acc = alpha * acc + sv * (E @ vh[keys].astype(np.int64)).astype(np.float64)
+                m = m_new
+            if m is not None:
+                parts.append((m, l, acc))
+        M = max(p[0] for p in parts)
+        Lt = sum(math.exp(g * (p[0] - M)) * p[1] for p in parts)
+        o[i] = sum(math.exp(g * (p[0] - M)) * p[2] for p in parts) / Lt
+        lse[i] = g * M + math.log(Lt / 127.0)
+    return o, lse
+
+
+def pin_lut_pages_integer_formula(L):
+    # s_Q = s_K = 1/8, d = 64, c = 7.75: alpha = s_Q s_K / sqrt(d) = 2^-9, so
+    # c_int = c / alpha = 3968 is an exact integer, and (2^b - 1) / c = 4 makes
+    # the oracle's fp32 distance exact; the per-token reading must then give
+    # the pages' integer-domain indices key for key
+    r = _rng(611)
+    d, c, b = 64, 7.75, 5
+    g = 2.0 ** -9
+    c_int = 3968
+    e_tab = oracle.index_softmax_lut(b, c, L=L)
+    for causal, Lq, Lkv, tile, split, vmode in ((False, 5, 40, 40, 0, 0), (True, 6, 40, 40, 0, 2),
+                                                (False, 4, 70, 16, 0, 0), (True, 5, 70, 16, 32, 2),
+                                                (False, 3, 50, 8, 24, 0)):
+        qh = r.integers(-127, 128, (Lq, d)).astype(np.int8)
+        # small K codes spread the distances over the table (c_int = 3968) and
+        # past the clip
+        kh = r.integers(-5, 6, (Lkv, d)).astype(np.int8)
+        vh = r.integers(-127, 128, (Lkv, d)).astype(np.int8)
+        sv = np.float32(0.03125) if vmode == 0 else np.array([0.0625], np.float32)
+        sq = np.full(Lq, 0.125, np.float32)
+        sk = np.full(Lkv, 0.125, np.float32)
+        o, lse = oracle.attn_int8(qh, sq, kh, sk, vh, np.atleast_1d(sv), vmode, 1, 1, 1, Lq, Lkv, d,
+                                  causal, tile, split, L=L, index_softmax=(b, c))
+        ref, lref = _lut_pages_integer(qh, kh, vh, float(np.atleast_1d(sv)[0]), e_tab, c_int, 31, causal,
+                                       tile, split, g)
+        assert np.allclose(o.reshape(Lq, d), ref, rtol=2e-5, atol=2e-5 * np.abs(ref).max()), (causal, tile, split)
+        assert np.allclose(lse.reshape(Lq), lref, rtol=1e-5, atol=1e-5)
+
+
+def pin_lut_table_values_reach_output(L):
+    # one query, keys whose logit distances to the max are exactly the table's
+    # grid points: with V = one-hot rows, O recovers each key's table value
+    # divided by their sum (the integer row sum of IA §3.2)
+    d, b, c = 64, 3, 7.0                 # grid step c / 7 = 1 in logit units
+    Lkv = 8
+    # s_Q = s_K = 1, sqrt(d) = 8: A_hat = 8 (100 - j) puts key j at distance j
+    qh = np.zeros((1, d), np.int8)
+    qh[0, 0] = 8
+    kh = np.zeros((Lkv, d), np.int8)
+    kh[:, 0] = 100 - np.arange(Lkv)
+    vh = np.zeros((Lkv, d), np.int8)
+    vh[np.arange(Lkv), np.arange(Lkv) + 1] = 1
+    sq = np.array([1.0], np.float32)
+    sk = np.full(Lkv, 1.0, np.float32)
+    o, _ = oracle.attn_int8(qh, sq, kh, sk, vh, np.array([1.0], np.float32), 0, 1, 1, 1, 1, Lkv, d,
+                            False, 8, 0, L=L, index_softmax=(b, c))
+    e = np.array([round(127 * math.exp(-j)) for j in range(Lkv)], np.float64)
+    assert list(oracle.index_softmax_lut(b, c, L=L)) == list(e.astype(int))
+    assert np.allclose(o.reshape(d)[1:Lkv + 1], e / e.sum(), rtol=1e-6, atol=1e-7)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
