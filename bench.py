@@ -23,8 +23,12 @@ Also reported on the same JSON line:
                 a bounded, seeded sample of the workload's query rows
   kernels       per-kernel averages (quantize passes, attention) in the timed region
 
+`--softmax index` times the same step with IndexSoftmax (a 2^b-entry
+exponential table, `--lut-bits`, `--lut-clip`) in place of the exp softmax; that
+forward takes INT8 Q, so Q is then quantized in its own pass.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--q-path fused|separate]
+                       [--q-path fused|separate] [--softmax exp|index]
        python bench.py --copy-calibration     (1 GiB device copies, for the
                                                HBM counter scale)
 """
@@ -58,6 +62,10 @@ def parse():
                     help="target wall time of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--q-path", choices=["fused", "separate"], default="fused",
                     help="quantize Q inside the attention kernels (fused) or in its own pass")
+    ap.add_argument("--softmax", choices=["exp", "index"], default="exp",
+                    help="exp softmax, or IndexSoftmax (table lookup; INT8 Q from its own pass)")
+    ap.add_argument("--lut-bits", type=int, default=5, help="IndexSoftmax table bits b")
+    ap.add_argument("--lut-clip", type=float, default=6.6, help="IndexSoftmax clipping threshold c")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the fused attention launches (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -114,7 +122,7 @@ def host_threads():
     return max(1, min(16, n))
 
 
-def cpu_baseline(w, q, k, v, target_s):
+def cpu_baseline(w, q, k, v, target_s, index_softmax=None):
     """Time the oracle's INT8 attention on a seeded sample of rows, scaled so
     the timed call lasts about target_s seconds."""
     import oracle
@@ -138,7 +146,7 @@ def cpu_baseline(w, q, k, v, target_s):
         rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
         oracle.attn_int8(qh, sq, kh, sk, vh, sv, w.v_per_token, w.B, w.H, w.Hkv, w.Lq, w.Lkv, w.d,
-                         w.causal, tile, split, rows=rows, nthreads=nth)
+                         w.causal, tile, split, rows=rows, nthreads=nth, index_softmax=index_softmax)
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or n >= total_rows:
             break
@@ -146,7 +154,8 @@ def cpu_baseline(w, q, k, v, target_s):
     return {"value": ops_of(rows) / dt / 1e12, "unit": "TOPS", "cores": nth, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": "%d of %d query rows (seeded uniform sample), INT8 attention step only "
-                      "(quantization excluded), %d host threads" % (rows.size, total_rows, nth)}
+                      "(quantization excluded)%s, %d host threads"
+                      % (rows.size, total_rows, ", IndexSoftmax" if index_softmax else "", nth)}
 
 
 def main():
@@ -181,7 +190,13 @@ def main():
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda") if ws_n else None
     stream = torch.cuda.current_stream()
 
-    fused_q = args.q_path == "fused"
+    lut = args.softmax == "index"
+    lut_args = (args.lut_bits, float(np.float32(args.lut_clip))) if lut else None
+    if lut and w.v_per_token:
+        print("IndexSoftmax takes one V scale per tensor or per head; workload %s has per-token V"
+              % w.name, file=sys.stderr)
+        sys.exit(2)
+    fused_q = args.q_path == "fused" and not lut     # the IndexSoftmax forward takes INT8 Q
     if w.kv_cache:
         assert w.v_per_token, "an appendable cache has per-token V scales"
         # the cache holds every token; each step re-appends the newest one
@@ -201,7 +216,10 @@ def main():
         m.attn_quantize_rows(dv, rps_v, vh, sv)
 
     def attend():
-        if fused_q:
+        if lut:
+            m.attn_int8_fwd_index_softmax(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, lut_args[0],
+                                          lut_args[1], out=o, workspace=ws)
+        elif fused_q:
             m.attn_int8_fwd_qfloat(dq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
         else:
             m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
@@ -260,7 +278,10 @@ def main():
     else:
         roof["kernel"] = "attn_fwd_kernel"
         kfiles = ["attn_fwd.hip", "cdna4_ops.h", "attn_internal.h"]
-    roof["traffic"] = measured_traffic(w.name + ("" if fused_q else "_separate_q"), kfiles)
+    if lut:
+        roof["kernel"] += " (IndexSoftmax)"
+    roof["traffic"] = measured_traffic(w.name + ("_index_softmax" if lut else "" if fused_q else "_separate_q"),
+                                       kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
 
@@ -276,6 +297,7 @@ def main():
                                               if w.outlier_seed is not None else ""),
                    "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
                    "kv_cache": bool(w.kv_cache),
+                   "softmax": "index_softmax(b=%d, c=%g)" % lut_args if lut else "exp",
                    "step": ("attention only" if args.attn_only else
                             ("append the new token's K,V to the INT8 cache" if w.kv_cache else "quantize K,V")
                             + (" + fused attention (Q quantized in the kernel)" if fused_q else
@@ -287,7 +309,7 @@ def main():
                     if quant_ms > 0 and not args.attn_only else None},
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, lut_args)
     print(json.dumps(out), flush=True)
 
 

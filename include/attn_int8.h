@@ -22,8 +22,9 @@
  *
  * Conventions shared by every entry point:
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except the
- *    two output pointers of attn_int8_fwd_schedule (host). The library never
- *    allocates, frees, copies between host and device, or synchronizes.
+ *    output pointers of attn_int8_fwd_schedule and attn_index_softmax_table
+ *    (host). The library never allocates, frees, copies between host and
+ *    device, or synchronizes.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns at once.
  *  - All arguments are checked on the host before anything is launched. On any
@@ -165,6 +166,50 @@ attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k
                                  int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                                  int32_t causal, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * attn_int8_fwd_index_softmax — attn_int8_fwd with IndexSoftmax in place of
+ * the exp softmax ("IntAttention: A Fully Integer Attention Pipeline for
+ * Efficient Edge Inference", §3.1: the distance to the row max clipped at c
+ * and mapped to a 2^b-entry exponential table by
+ * idx = floor(distance / c * (2^b - 1)); §3.2: integer row sum and
+ * normalisation; §4 ablation: (b, c) = (5, 6.6) recommended), read for
+ * per-token Q/K scales and online KV tiles:
+ *
+ *   table   E_tab[i] = rne(127 exp(-(double)c * i / (2^b - 1)))  (signed
+ *           7-bit, as the INT8 products are signed; attn_index_softmax_table)
+ *   u_j     = S_int[j] * s_K[j]                                   (fp32)
+ *   m_u     = running max of u over the visible keys up to this tile's end
+ *   kappa   = (s_Q * (1/sqrt(d))) * ((2^b - 1) / c)               (fp32)
+ *   idx_j   = min(floor(max(fma(u_j, -kappa, m_u * kappa), 0)), 2^b - 1)
+ *   E_j     = E_tab[idx_j] (0 for masked keys); l = alpha l + sum_j E_j
+ *           (the integer tile sum), acc = alpha acc + s_V (E . V_hat)
+ *           (INT32 per tile), alpha = exp((m_u,old - m_u,new) s_Q / sqrt(d))
+ *   O       = acc / l; lse = m_u s_Q / sqrt(d) + ln(l / 127).
+ *
+ * The distance is the dequantized logit's (the pages' integer distance with
+ * c_int at its exact value c / alpha; with one scale per key an integer
+ * distance does not measure logits). Arguments, layouts, schedule, workspace
+ * and errors are those of attn_int8_fwd, plus:
+ *   lut_bits  b, 1..8 (else ATTN_ERR_INVALID_ARG)
+ *   clip      c, finite, in [1e-3, 1e3] (else ATTN_ERR_INVALID_ARG)
+ * v_mode ATTN_VSCALE_PER_TOKEN returns ATTN_ERR_UNSUPPORTED (per-key V
+ * weights would re-round the table's codes). Inputs whose scaled distances
+ * overflow fp32 are outside the contract.
+ */
+attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const int8_t* k,
+                                        const float* s_k, const int8_t* v, const float* s_v,
+                                        attn_vscale v_mode, void* o, attn_dtype o_dt, float* lse,
+                                        int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                                        int32_t d, int32_t causal, int32_t lut_bits, float clip,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_index_softmax_table — the table attn_int8_fwd_index_softmax uses for
+ * (lut_bits, clip) (IntAttention §3.1-3.2; formula above), written to the
+ * HOST buffer table[2^lut_bits]. Same parameter checks; no GPU work.
+ */
+attn_status attn_index_softmax_table(int32_t lut_bits, float clip, uint8_t* table);
 
 /*
  * attn_int8_fwd_workspace_size — bytes of device workspace attn_int8_fwd needs

@@ -30,6 +30,10 @@ SIGNATURES = {
     "attn_int8_fwd_qfloat": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P,
                                             ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _P, _SZ, _P]),
+    "attn_int8_fwd_index_softmax": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
+                                                   _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   ctypes.c_float, _P, _SZ, _P]),
+    "attn_index_softmax_table": (ctypes.c_int, [_I32, ctypes.c_float, _P]),
     "attn_int8_fwd_workspace_size": (_SZ, [_I32] * 7),
     "attn_int8_fwd_schedule": (ctypes.c_int, [_I32] * 7 + [_P, _P]),
     "attn_int8_debug_logits": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -231,6 +235,35 @@ def attn_int8_fwd_qfloat(q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.f
     return (out, lse) if return_lse else out
 
 
+def attn_int8_fwd_index_softmax(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
+                                lut_bits=5, clip=6.6, return_lse=False, out=None, lse=None, workspace=None,
+                                stream=None):
+    """The INT8 forward with IndexSoftmax (a 2^lut_bits-entry exponential
+    table over distances clipped at `clip`) in place of the exp softmax.
+    Arguments as attn_int8_fwd; V scales per tensor or per (batch, kv head)
+    (v_per_token False or "head")."""
+    _dev(q, "q", torch.int8)
+    _dev(s_q, "s_q", torch.float32)
+    shape, out, lse, workspace, ws_bytes = _fwd_common(q, k, s_k, v, s_v, v_per_token, causal,
+                                                       o_dtype, return_lse, out, lse, workspace)
+    if s_q.numel() != shape[0] * shape[1] * shape[3]:
+        raise ValueError("s_q size does not match q")
+    st = _lib.attn_int8_fwd_index_softmax(_ptr(q), _ptr(s_q), _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
+                                          _vmode(v_per_token),
+                                          _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32,
+                                          _ptr(lse), *shape, int(causal), int(lut_bits), float(clip),
+                                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check("attn_int8_fwd_index_softmax", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_index_softmax_table(lut_bits=5, clip=6.6):
+    """The library's IndexSoftmax table (host bytes, 2^lut_bits entries)."""
+    buf = (ctypes.c_uint8 * 256)()
+    _check("attn_index_softmax_table", _lib.attn_index_softmax_table(int(lut_bits), float(clip), buf))
+    return bytes(buf)[:1 << int(lut_bits)]
+
+
 def attn_int8_debug_logits(q, k, causal, out=None, stream=None):
     """INT32 logits of every visible pair from the prefill kernel's tile code;
     masked pairs keep out's previous contents (out defaults to zeros)."""
@@ -257,6 +290,7 @@ def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, re
     return attn_int8_fwd_qfloat(q, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
 
 
-__all__ = ["attn_quantize_rows", "attn_kv_append", "attn_int8_fwd", "attn_int8_fwd_qfloat", "attn_int8_fwd_workspace_size",
+__all__ = ["attn_quantize_rows", "attn_kv_append", "attn_int8_fwd", "attn_int8_fwd_qfloat",
+           "attn_int8_fwd_index_softmax", "attn_index_softmax_table", "attn_int8_fwd_workspace_size",
            "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
            "AttnError", "LIB_PATH", "SIGNATURES"]

@@ -4,6 +4,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
+#include <cstring>
 
 #include "attn_internal.h"
 
@@ -27,9 +29,25 @@ attn_status check_shape(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t L
   return ATTN_OK;
 }
 
+// IndexSoftmax parameters: 1 <= b <= 8, clip c finite in [1e-3, 1e3]
+bool lut_params_ok(int32_t bits, float clip) {
+  return bits >= 1 && bits <= 8 && std::isfinite(clip) && clip >= 1e-3f && clip <= 1e3f;
+}
+
 }  // namespace
 
 namespace attn {
+
+// Entry i samples the exponential at the left end of index bucket i, the
+// distance c i / (2^b - 1), as a signed 7-bit probability:
+// rne(127 exp(-(double)c * i / (2^b - 1))), in double, left to right.
+void index_softmax_table(int bits, float clip, uint8_t* out) {
+  const int n = (1 << bits) - 1;
+  for (int i = 0; i <= n; ++i) {
+    const double x = static_cast<double>(clip) * static_cast<double>(i) / static_cast<double>(n);
+    out[i] = static_cast<uint8_t>(std::nearbyint(127.0 * std::exp(-x)));
+  }
+}
 
 // Decode-shaped problems (at most kDecodeRows query rows per KV head: the
 // GQA group's heads times Lq) take the split-KV kernel, the KV length cut in
@@ -132,9 +150,10 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
                        int8_t* q_hat, float* s_q_out, const int8_t* k, const float* s_k,
                        const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
                        attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq,
-                       int32_t Lkv, int32_t d, int32_t causal, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int32_t Lkv, int32_t d, int32_t causal, int32_t lut_bits, float clip,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!k || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
+  if (lut_bits != 0 && !lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
   if (q_float) {
     if (q_dt != ATTN_F32 && q_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q_float, 16) || (q_hat && !aligned(q_hat, 16)) || (s_q_out && !aligned(s_q_out, 4)))
@@ -148,6 +167,8 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
   if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
   if (s != ATTN_OK) return s;
+  // IndexSoftmax kernels take INT8 Q and one V scale per tensor or per head
+  if (lut_bits != 0 && (q_float || v_mode == ATTN_VSCALE_PER_TOKEN)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_INVALID_ARG;
   if (!aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4))) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
@@ -162,6 +183,13 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
   a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN);
   a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.o_f16 = (o_dt == ATTN_F16);
   a.workspace = workspace;
+  if (lut_bits != 0) {
+    uint8_t tab[sizeof(a.lut_w)] = {};
+    attn::index_softmax_table(lut_bits, clip, tab);
+    std::memcpy(a.lut_w, tab, sizeof(tab));
+    a.lut_n = (1 << lut_bits) - 1;
+    a.lut_k = static_cast<float>(static_cast<double>(a.lut_n) / static_cast<double>(clip));
+  }
   int tile, split, dec;
   attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -178,7 +206,25 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
                           size_t workspace_bytes, void* stream) {
   if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
   return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
-                    B, H, Hkv, Lq, Lkv, d, causal, workspace, workspace_bytes, stream);
+                    B, H, Hkv, Lq, Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const int8_t* k,
+                                        const float* s_k, const int8_t* v, const float* s_v,
+                                        attn_vscale v_mode, void* o, attn_dtype o_dt, float* lse,
+                                        int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                                        int32_t d, int32_t causal, int32_t lut_bits, float clip,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
+  if (!lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
+  return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
+                    B, H, Hkv, Lq, Lkv, d, causal, lut_bits, clip, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_index_softmax_table(int32_t lut_bits, float clip, uint8_t* table) {
+  if (!table || !lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
+  attn::index_softmax_table(lut_bits, clip, table);
+  return ATTN_OK;
 }
 
 attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
@@ -189,7 +235,7 @@ attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k
                                  void* stream) {
   if (!q) return ATTN_ERR_INVALID_ARG;
   return fwd_common(nullptr, nullptr, q, q_dt, q_hat, s_q, k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H,
-                    Hkv, Lq, Lkv, d, causal, workspace, workspace_bytes, stream);
+                    Hkv, Lq, Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_int8_debug_logits(const int8_t* q, const int8_t* k, int32_t B, int32_t H,

@@ -152,13 +152,17 @@ __device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, 
   return p;
 }
 
-template <int D, bool CAUSAL, bool VPT, bool QF>
+// LUT: IndexSoftmax (table lookup) in place of the exp2 softmax; only with
+// per-tensor or per-head V and INT8 Q.
+template <int D, bool CAUSAL, bool VPT, bool QF, bool LUT>
 // two wavefronts per SIMD (registers <= 256): the LDS ring allows six per CU
 __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
+  static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and per-tensor or per-head V");
   constexpr int NC = D / 64;
   constexpr int NCB = D / 16;
   constexpr int NL = loads_per_tile<D, VPT>();
   __shared__ DStage<D> sm[kStages];
+  __shared__ uint32_t lut_s[LUT ? 65 : 1];
 
   const int G = a.H / a.Hkv;                 // query heads per KV head
   const int R = G * a.Lq;                    // query rows of the group (<= 16)
@@ -220,6 +224,9 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
     sm[i / BN].sk[i % BN] = 0.0f;
     sm[i / BN].sv[i % BN] = 0.0f;
   }
+  if constexpr (LUT) {
+    for (int i = lane; i < 65; i += 64) lut_s[i] = a.lut_w[i];
+  }
   __syncthreads();
   // Every request is issued, also past the last tile: such a request starts at
   // key Lkv, where every lane's offset lies outside the buffers, so it fetches
@@ -262,6 +269,10 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
 
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
   const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);   // base-2 logit per S_int s_K
+  // IndexSoftmax: table index per unit of u below the running max of u
+  const float kap = (sq * inv_sqrt_d) * a.lut_k;
+  const float nf = static_cast<float>(a.lut_n);
+  float m_u = kNegInf;
 
   float m = kNegInf, l = 0.0f;
   float acc[NCB][4];
@@ -321,38 +332,63 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = exp2_hw(m - m_use);
-    const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
     float st_cur = 0.0f, rst = 0.0f;
-    if constexpr (VPT) {
-      // s_t: largest s_V[j] over the tile's keys inside the chunk
-      float x = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-      st_cur = x;
-      rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
-    }
     uint32_t pw[NB];
-    float gs[NB];
+    float lsum;
+    if constexpr (LUT) {
+      // IndexSoftmax: E = table[min(floor(max(m_u kappa - u kappa, 0)), n)],
+      // masked keys read the zero slot; integer row sum by dot4
+      m_u = fmaxf(m_u, mx);
+      const float mu = m_u * kap;
+      const uint8_t* tab = reinterpret_cast<const uint8_t*>(lut_s);
+      uint32_t isum = 0;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      for (int kb = 0; kb < NB; ++kb) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(u[kb][e], -kap, mu), 0.0f, nf);
+          uint32_t idx = static_cast<uint32_t>(x);
+          idx = (!mask || kb * 4 + e <= rel) ? idx : static_cast<uint32_t>(kLutZero);
+          word |= static_cast<uint32_t>(tab[idx]) << (8 * e);
+        }
+        isum = __builtin_amdgcn_udot4(word, 0x01010101u, isum, false);
+        pw[kb] = word;
+      }
+      lsum = static_cast<float>(isum);
+    } else {
+      const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
       if constexpr (VPT) {
-        const float4 s4 = *reinterpret_cast<const float4*>(st->sv + grp * 16 + kb * 4);
-        wr[0] = s4.x * rst; wr[1] = s4.y * rst; wr[2] = s4.z * rst; wr[3] = s4.w * rst;
-      }
-      uint32_t word = 0;
-      float y[4];
+        // s_t: largest s_V[j] over the tile's keys inside the chunk
+        float x = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[e] = exp2_hw(__builtin_fmaf(u[kb][e], c2, -bias));     // 127 P_tilde
-        word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
+        for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+        st_cur = x;
+        rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
       }
-      gs[kb] = (y[0] + y[1]) + (y[2] + y[3]);
-      pw[kb] = word;
+      float gs[NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (VPT) {
+          const float4 s4 = *reinterpret_cast<const float4*>(st->sv + grp * 16 + kb * 4);
+          wr[0] = s4.x * rst; wr[1] = s4.y * rst; wr[2] = s4.z * rst; wr[3] = s4.w * rst;
+        }
+        uint32_t word = 0;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = exp2_hw(__builtin_fmaf(u[kb][e], c2, -bias));     // 127 P_tilde
+          word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
+        }
+        gs[kb] = (y[0] + y[1]) + (y[2] + y[3]);
+        pw[kb] = word;
+      }
+      lsum = (gs[0] + gs[1]) + (gs[2] + gs[3]);
     }
     const v4i p = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]),
                       static_cast<int>(pw[3])};
-    l = alpha * l + ((gs[0] + gs[1]) + (gs[2] + gs[3]));
+    l = alpha * l + lsum;
 
     if constexpr (!VPT) {
       if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
@@ -485,14 +521,23 @@ template <int D, bool CAUSAL, bool VPT>
 hipError_t launch_dec(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
   if (a.q_float)
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, true>), grid, dim3(64), 0, st, a, split_len, n_split);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, true, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   else
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dec_lut(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
+  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, false, false, true>), grid, dim3(64), 0, st, a, split_len, n_split);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
+  if (a.lut_n) return a.causal ? launch_dec_lut<D, true>(a, split_len, n_split, st)
+                               : launch_dec_lut<D, false>(a, split_len, n_split, st);
   if (a.causal) return a.v_per_token ? launch_dec<D, true, true>(a, split_len, n_split, st)
                                      : launch_dec<D, true, false>(a, split_len, n_split, st);
   return a.v_per_token ? launch_dec<D, false, true>(a, split_len, n_split, st)

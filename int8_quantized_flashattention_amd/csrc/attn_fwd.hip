@@ -235,6 +235,36 @@ __device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2,
   return gs[0];
 }
 
+// IndexSoftmax in place of exp2: x = m_u kappa - u kappa (one fma), the
+// table index is floor(x) clamped to [0, n] (med3, then a truncating convert
+// of a non-negative value), E = table[index] read from LDS; masked keys read
+// the zero slot. Packs E into the PV operands and returns this lane's integer
+// sum of E (four bytes per dot4 against ones).
+template <bool MASK>
+__device__ __forceinline__ float lut_tile(const float (&u)[NKB][16], float kap, float mu, float nf,
+                                          const uint8_t* tab, int rel, v4i (&pv)[NKB]) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(u[kb][j4 * 4 + e], -kap, mu), 0.0f, nf);
+        uint32_t idx = static_cast<uint32_t>(x);
+        if constexpr (MASK) idx = (kb * 32 + j4 * 4 + e <= rel) ? idx : static_cast<uint32_t>(kLutZero);
+        word |= static_cast<uint32_t>(tab[idx]) << (8 * e);
+      }
+      sum = __builtin_amdgcn_udot4(word, 0x01010101u, sum, false);
+      pw[j4] = word;
+    }
+    pv[kb] = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]), static_cast<int>(pw[3])};
+  }
+  return static_cast<float>(sum);
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -276,11 +306,15 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
   rb = n_rb - 1 - (w - bh * n_rb);
 }
 
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF>
+// LUT: IndexSoftmax (table lookup) in place of the exp2 softmax; only with
+// per-tensor or per-head V and INT8 Q.
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF, bool LUT>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
+  static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and per-tensor or per-head V");
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
   __shared__ Stage<D> sm[kStages];
+  __shared__ uint32_t lut_s[LUT ? 65 : 1];
 
   const int n_rb = (a.Lq + BM - 1) / BM;
   int bh, rb;
@@ -312,6 +346,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   for (int i = tid; i < kStages * BN; i += kThreads) {
     sm[i / BN].sk[i % BN] = 0.0f;
     sm[i / BN].sv[i % BN] = 0.0f;
+  }
+  if constexpr (LUT) {
+    if (tid < 65) lut_s[tid] = a.lut_w[tid];
   }
 
   // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk. Loaded
@@ -398,6 +435,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // stays -inf for masked keys; a zero query (s_Q = 0) has S_int = 0 and all
   // its logits stay exactly 0.
   const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
+  // IndexSoftmax: table index per unit of u below the running max, and the
+  // running max of u itself (kept beside m, which is in base-2 logits)
+  const float kap = (sq * inv_sqrt_d) * a.lut_k;
+  const float nf = static_cast<float>(a.lut_n);
+  float m_u = kNegInf;
 
   // One tile: request t+2 | QK(t) [MFMA] | dequant, softmax(t) [VALU] | fold
   // | PV(t) [MFMA] | wait for t+1 | barrier. The stage being read and the
@@ -425,15 +467,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = exp2_hw(m - m_use);            // 1 if unchanged, 0 on the first tile
-    // exp2(u c2 - bias) = 127 P_tilde, bias with the guard term |m| 2^-21
-    const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
-    float rst = 0.0f, st_cur = 0.0f;
-    if constexpr (VPT) {
-      st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);
-      rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
-    }
     v4i p[NKB];
-    const float lsum = probs_tile<VPT>(u, c2, bias, st->sv, rst, p, g);
+    float lsum;
+    float st_cur = 0.0f;
+    if constexpr (LUT) {
+      m_u = fmaxf(m_u, mx);
+      const float mu = m_u * kap;
+      const uint8_t* tab = reinterpret_cast<const uint8_t*>(lut_s);
+      if (!mask) lsum = lut_tile<false>(u, kap, mu, nf, tab, 0, p);
+      else lsum = lut_tile<true>(u, kap, mu, nf, tab, min(lim, a.Lkv - 1) - k0 - 16 * g, p);
+    } else {
+      // exp2(u c2 - bias) = 127 P_tilde, bias with the guard term |m| 2^-21
+      const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
+      float rst = 0.0f;
+      if constexpr (VPT) {
+        st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);
+        rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
+      }
+      lsum = probs_tile<VPT>(u, c2, bias, st->sv, rst, p, g);
+    }
     l = alpha * l + lsum;
 
     if constexpr (!VPT) {
@@ -578,14 +630,23 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
   if (a.q_float)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, true>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, true, false>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, false, false>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool OUT_F16>
+hipError_t launch_lut(const FwdArgs& a, hipStream_t st) {
+  const int n_rb = (a.Lq + BM - 1) / BM;
+  const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, false, true>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_vo(const FwdArgs& a, hipStream_t st) {
+  if (a.lut_n) return a.o_f16 ? launch_lut<D, CAUSAL, true>(a, st) : launch_lut<D, CAUSAL, false>(a, st);
   if (a.v_per_token)
     return a.o_f16 ? launch_t<D, CAUSAL, true, true>(a, st) : launch_t<D, CAUSAL, true, false>(a, st);
   return a.o_f16 ? launch_t<D, CAUSAL, false, true>(a, st) : launch_t<D, CAUSAL, false, false>(a, st);

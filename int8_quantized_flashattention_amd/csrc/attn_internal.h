@@ -22,7 +22,17 @@ struct FwdArgs {
   int causal, v_per_token, o_f16;
   int v_per_head;      // s_v holds one scale per (batch, kv head)
   void* workspace;
+  // IndexSoftmax: lut_n = 2^b - 1 (0: exp softmax), lut_k = (2^b - 1) / c in
+  // fp32, lut_w = the table's bytes (entry i at byte i), zero from byte
+  // lut_n + 1 on; byte kLutZero is the slot masked keys read
+  int lut_n;
+  float lut_k;
+  uint32_t lut_w[65];
 };
+constexpr int kLutZero = 256;
+
+// The IndexSoftmax table for b = bits and clip c (entries 0 .. 2^b - 1).
+void index_softmax_table(int bits, float clip, uint8_t* out);
 
 // Prefill kernel geometry: BM query rows per workgroup, BN keys per KV tile.
 constexpr int kPrefillBM = 128;

@@ -5,6 +5,9 @@
 //   emu_driver quant  x.bin dt n_rows n_cols rps  q.out s.out
 //   emu_driver fwd    q.bin sq.bin k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out
+//   emu_driver fwdlut q.bin sq.bin k.bin sk.bin v.bin sv.bin vmode odt
+//                     B H Hkv Lq Lkv d causal bits clip  o.out lse.out
+//   emu_driver lut    bits clip  table.out
 //   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out qhat.out sq.out
 //   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
@@ -57,7 +60,8 @@ int main(int argc, char** argv) {
     st = attn_quantize_rows(x, static_cast<attn_dtype>(dt), n_rows, n_cols, rps, q, s, nullptr);
     write_file(argv[7], q, n_rows * n_cols);
     write_file(argv[8], s, sizeof(float) * (n_rows / rps));
-  } else if (mode == "fwd" && argc == 19) {
+  } else if ((mode == "fwd" && argc == 19) || (mode == "fwdlut" && argc == 21)) {
+    const bool lut = mode == "fwdlut";
     const int vmode = std::atoi(argv[8]), odt = std::atoi(argv[9]);
     const int B = std::atoi(argv[10]), H = std::atoi(argv[11]), Hkv = std::atoi(argv[12]);
     const int Lq = std::atoi(argv[13]), Lkv = std::atoi(argv[14]), d = std::atoi(argv[15]);
@@ -74,11 +78,22 @@ int main(int argc, char** argv) {
     float* lse = static_cast<float*>(alloc(nq * 4));
     const size_t ws_n = attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
     void* ws = ws_n ? std::aligned_alloc(256, (ws_n + 255) / 256 * 256) : nullptr;
-    st = attn_int8_fwd(q, sq, k, sk, v, sv, static_cast<attn_vscale>(vmode), o,
-                       static_cast<attn_dtype>(odt), lse, B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n,
-                       nullptr);
-    write_file(argv[17], o, osz);
-    write_file(argv[18], lse, nq * 4);
+    if (lut)
+      st = attn_int8_fwd_index_softmax(q, sq, k, sk, v, sv, static_cast<attn_vscale>(vmode), o,
+                                       static_cast<attn_dtype>(odt), lse, B, H, Hkv, Lq, Lkv, d, causal,
+                                       std::atoi(argv[17]), std::strtof(argv[18], nullptr), ws, ws_n,
+                                       nullptr);
+    else
+      st = attn_int8_fwd(q, sq, k, sk, v, sv, static_cast<attn_vscale>(vmode), o,
+                         static_cast<attn_dtype>(odt), lse, B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n,
+                         nullptr);
+    write_file(argv[lut ? 19 : 17], o, osz);
+    write_file(argv[lut ? 20 : 18], lse, nq * 4);
+  } else if (mode == "lut" && argc == 5) {
+    const int bits = std::atoi(argv[2]);
+    uint8_t tab[256];
+    st = attn_index_softmax_table(bits, std::strtof(argv[3], nullptr), tab);
+    write_file(argv[4], tab, bits >= 1 && bits <= 8 ? size_t(1) << bits : 0);
   } else if (mode == "fwdq" && argc == 21) {
     const int qdt = std::atoi(argv[3]);
     const int vmode = std::atoi(argv[8]), odt = std::atoi(argv[9]);

@@ -296,6 +296,15 @@ inline emu_v2i ds_read_tr8_b64(const void* p) {
   return r;
 }
 
+// v_med3_f32 for b <= c: the middle value; a NaN first operand gives b
+inline float fmed3(float a, float b, float c) { return std::fmin(std::fmax(a, b), c); }
+
+// v_dot4_u32_u8: sum of the four byte products of a and b, plus c
+inline uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) {
+  for (int i = 0; i < 4; ++i) c += ((a >> (8 * i)) & 0xffu) * ((b >> (8 * i)) & 0xffu);
+  return c;
+}
+
 inline float bits_to_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
 
@@ -313,6 +322,8 @@ inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); ret
 #define __builtin_amdgcn_exp2f(x) std::exp2(static_cast<float>(x))
 #define __builtin_amdgcn_permlane32_swap(x, y, fi, bc) emu::permlane32_swap(x, y)
 #define __builtin_amdgcn_cvt_pk_u8_f32(f, b, old) emu::cvt_pk_u8_f32(f, b, old)
+#define __builtin_amdgcn_fmed3f(a, b, c) emu::fmed3(a, b, c)
+#define __builtin_amdgcn_udot4(a, b, c, clamp) emu::udot4(a, b, c)
 #define __any(p) emu::wave_any(p)
 #define __builtin_amdgcn_readfirstlane(x) (x)
 typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -88,6 +89,43 @@ def fwdq(**kw):
 ])
 def test_fwd_qfloat_rejects_before_launch(kw, expect):
     assert fwdq(**kw) == expect
+
+
+def fwdlut(**kw):
+    args = dict(q=A, s_q=A, k=A, s_k=A, v=A, s_v=A, v_mode=0, o=A, o_dt=1, lse=None, B=1, H=2, Hkv=1,
+                Lq=8, Lkv=8, d=64, causal=0, bits=5, clip=6.6, ws=None, ws_bytes=0)
+    args.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return L.attn_int8_fwd_index_softmax(p(args["q"]), p(args["s_q"]), p(args["k"]), p(args["s_k"]),
+                                         p(args["v"]), p(args["s_v"]), args["v_mode"], p(args["o"]),
+                                         args["o_dt"], p(args["lse"]), args["B"], args["H"], args["Hkv"],
+                                         args["Lq"], args["Lkv"], args["d"], args["causal"], args["bits"],
+                                         args["clip"], p(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(s_q=None), INVALID), (dict(s_v=None), INVALID), (dict(o=None), INVALID),
+    (dict(bits=0), INVALID), (dict(bits=9), INVALID), (dict(bits=-1), INVALID),
+    (dict(clip=0.0), INVALID), (dict(clip=-1.0), INVALID), (dict(clip=float("inf")), INVALID),
+    (dict(clip=float("nan")), INVALID), (dict(clip=5e-4), INVALID), (dict(clip=2e3), INVALID),
+    (dict(v_mode=1), UNSUPPORTED), (dict(v_mode=3), INVALID), (dict(o_dt=5), INVALID),
+    (dict(H=3, Hkv=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(q=A + 8), INVALID), (dict(o=A + 2), INVALID),
+    (dict(B=1, H=2, Hkv=1, Lq=1, Lkv=4096), INVALID),   # decode schedule needs a workspace
+])
+def test_fwd_index_softmax_rejects_before_launch(kw, expect):
+    assert fwdlut(**kw) == expect
+
+
+def test_index_softmax_table_query():
+    import oracle
+    for bits, clip in ((5, 6.6), (1, 1e-3), (8, 1e3), (3, 2.0)):
+        got = m.attn_index_softmax_table(bits, clip)
+        assert list(got) == list(oracle.index_softmax_lut(bits, float(np.float32(clip))))
+    buf = (ctypes.c_uint8 * 256)()
+    assert L.attn_index_softmax_table(0, 6.6, buf) == INVALID
+    assert L.attn_index_softmax_table(5, 0.0, buf) == INVALID
+    assert L.attn_index_softmax_table(5, 6.6, None) == INVALID
 
 
 def test_kv_append_rejects_before_launch():

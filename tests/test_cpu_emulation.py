@@ -183,3 +183,56 @@ def test_emulated_attention_huge_logits(exe, tmp_path):
     o = np.fromfile(oo_p, np.float32).reshape(B, H, L, d)
     oo, _ = oracle.attn_int8(qh, sq, qh, sq, vh, sv, False, B, H, H, L, L, d, True, 64, 0)
     assert np.abs(o - oo).max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
+
+
+@pytest.mark.parametrize("bits,clip", [(5, 6.6), (1, 0.001), (3, 2.0), (8, 7.7), (4, 1000.0), (5, 21.487562)])
+def test_emulated_index_softmax_table(exe, tmp_path, bits, clip):
+    # the library's table is the oracle's, byte for byte
+    out = os.path.join(str(tmp_path), "t.out")
+    run(exe, tmp_path, ["lut", bits, repr(float(np.float32(clip))), out])
+    got = np.fromfile(out, np.uint8)
+    assert np.array_equal(got.astype(np.int32), oracle.index_softmax_lut(bits, np.float32(clip)))
+
+
+LUT_CASES = [
+    # prefill: plain, causal with a ragged tail, GQA, fp16 out, per-head V
+    (1, 1, 1, 128, 128, 64, 0, 0, F32, 5, 6.6, 1), (2, 4, 2, 77, 130, 128, 1, 0, F16, 5, 6.6, 1),
+    (1, 3, 3, 300, 300, 64, 1, 2, F32, 3, 2.0, 1), (2, 4, 2, 130, 257, 128, 1, 2, F32, 8, 7.7, 1),
+    # a clip small enough that clipped keys keep a non-zero table value, and
+    # growing logits (the running max rises tile after tile)
+    (1, 2, 2, 256, 640, 128, 1, 0, F32, 4, 1.5, 12), (1, 1, 1, 64, 500, 64, 0, 0, F32, 5, 6.6, 30),
+    # split-KV decode shapes
+    (2, 8, 2, 1, 1500, 128, 0, 0, F16, 5, 6.6, 1), (1, 8, 1, 2, 520, 64, 1, 2, F32, 3, 2.0, 1),
+    (1, 16, 1, 1, 333, 128, 0, 0, F32, 5, 6.6, 12), (1, 4, 1, 4, 700, 128, 1, 0, F32, 2, 0.5, 1),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vmode,odt,bits,clip,gain", LUT_CASES)
+def test_emulated_attention_index_softmax(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vmode, odt, bits, clip,
+                                          gain):
+    r = np.random.Generator(np.random.PCG64(B * 300 + Lq * 11 + Lkv + bits))
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32) * np.float32(gain)
+    q[0, 0, 0] = 0                                   # an all-zero row: s_Q = 0, every logit 0
+    k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    k *= np.linspace(1.0, float(gain), Lkv, dtype=np.float32)[None, None, :, None]
+    v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    qh, sq = oracle.quantize_rows(q, 1)
+    kh, sk = oracle.quantize_rows(k, 1)
+    vh, sv = oracle.quantize_rows(v, {0: v.size // d, 2: Lkv}[vmode])
+    c32 = float(np.float32(clip))
+    oo_p, lo_p = os.path.join(str(tmp_path), "o.out"), os.path.join(str(tmp_path), "l.out")
+    files = [put(tmp_path, n + ".bin", a) for n, a in
+             (("q", qh), ("sq", sq), ("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
+    run(exe, tmp_path, ["fwdlut", *files, vmode, odt, B, H, Hkv, Lq, Lkv, d, causal, bits, repr(c32), oo_p, lo_p])
+    o = np.fromfile(oo_p, np.float16 if odt == F16 else np.float32).astype(np.float32).reshape(B, H, Lq, d)
+    lse = np.fromfile(lo_p, np.float32).reshape(B, H, Lq)
+    import int8_quantized_flashattention_amd as m
+    tile, split = m.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, vmode, B, H, Hkv, Lq, Lkv, d, causal, tile, split,
+                              index_softmax=(bits, c32))
+    # the table indices are the same fp32 operations on both sides, so only
+    # the rescale factors' and the sums' rounding differ
+    tol = 2e-3 if odt == F16 else 1e-4
+    assert np.abs(o - oo).max() <= tol * max(1.0, np.abs(oo).max())
+    assert np.linalg.norm(o - oo) / np.linalg.norm(oo) <= (1e-3 if odt == F16 else 1e-5)
+    assert np.abs(lse - lo).max() <= 1e-5 * max(1.0, np.abs(lo).max())
