@@ -265,6 +265,37 @@ __device__ __forceinline__ float lut_tile(const float (&u)[NKB][16], float kap, 
   return static_cast<float>(sum);
 }
 
+// The same with a table of key pairs (tables of at most 32 entries): entry
+// ia + 256 ib of the pair table holds E[ia] | E[ib] << 8, index 32 being the
+// zero slot, so one 16-bit LDS read serves two keys and two reads fill a
+// packed word of the PV operand.
+template <bool MASK>
+__device__ __forceinline__ float lut2_tile(const float (&u)[NKB][16], float kap, float mu, float nf,
+                                           const uint16_t* tab2, int rel, v4i (&pv)[NKB]) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      uint32_t idx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(u[kb][j4 * 4 + e], -kap, mu), 0.0f, nf);
+        idx[e] = static_cast<uint32_t>(x);
+        if constexpr (MASK) idx[e] = (kb * 32 + j4 * 4 + e <= rel) ? idx[e] : 32u;
+      }
+      const uint32_t lo = tab2[idx[0] + (idx[1] << 8)];
+      const uint32_t hi = tab2[idx[2] + (idx[3] << 8)];
+      const uint32_t word = lo | (hi << 16);
+      sum = __builtin_amdgcn_udot4(word, 0x01010101u, sum, false);
+      pw[j4] = word;
+    }
+    pv[kb] = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]), static_cast<int>(pw[3])};
+  }
+  return static_cast<float>(sum);
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -306,15 +337,17 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
   rb = n_rb - 1 - (w - bh * n_rb);
 }
 
-// LUT: IndexSoftmax (table lookup) in place of the exp2 softmax; only with
+// LUT: 0 exp2 softmax; 1 IndexSoftmax with the byte table; 2 IndexSoftmax
+// with the pair table (tables of at most 32 entries). IndexSoftmax only with
 // per-tensor or per-head V and INT8 Q.
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF, bool LUT>
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF, int LUT>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and per-tensor or per-head V");
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
   __shared__ Stage<D> sm[kStages];
   __shared__ uint32_t lut_s[LUT ? 65 : 1];
+  __shared__ uint16_t lut2_s[LUT == 2 ? kLutPairRows * 256 : 1];
 
   const int n_rb = (a.Lq + BM - 1) / BM;
   int bh, rb;
@@ -349,6 +382,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   }
   if constexpr (LUT) {
     if (tid < 65) lut_s[tid] = a.lut_w[tid];
+  }
+  if constexpr (LUT == 2) {
+    __syncthreads();
+    const uint8_t* tab = reinterpret_cast<const uint8_t*>(lut_s);   // zero from entry 32 on
+    for (int e = tid; e < kLutPairRows * kLutPairRows; e += kThreads) {
+      const int ia = e % kLutPairRows, ib = e / kLutPairRows;
+      lut2_s[ib * 256 + ia] = static_cast<uint16_t>(tab[ia] | (tab[ib] << 8));
+    }
   }
 
   // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk. Loaded
@@ -473,9 +514,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     if constexpr (LUT) {
       m_u = fmaxf(m_u, mx);
       const float mu = m_u * kap;
-      const uint8_t* tab = reinterpret_cast<const uint8_t*>(lut_s);
-      if (!mask) lsum = lut_tile<false>(u, kap, mu, nf, tab, 0, p);
-      else lsum = lut_tile<true>(u, kap, mu, nf, tab, min(lim, a.Lkv - 1) - k0 - 16 * g, p);
+      const int rel = min(lim, a.Lkv - 1) - k0 - 16 * g;
+      if constexpr (LUT == 2) {
+        if (!mask) lsum = lut2_tile<false>(u, kap, mu, nf, lut2_s, 0, p);
+        else lsum = lut2_tile<true>(u, kap, mu, nf, lut2_s, rel, p);
+      } else {
+        const uint8_t* tab = reinterpret_cast<const uint8_t*>(lut_s);
+        if (!mask) lsum = lut_tile<false>(u, kap, mu, nf, tab, 0, p);
+        else lsum = lut_tile<true>(u, kap, mu, nf, tab, rel, p);
+      }
     } else {
       // exp2(u c2 - bias) = 127 P_tilde, bias with the guard term |m| 2^-21
       const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
@@ -630,9 +677,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
   if (a.q_float)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, true, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, true, 0>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, false, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, false, 0>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -640,7 +687,10 @@ template <int D, bool CAUSAL, bool OUT_F16>
 hipError_t launch_lut(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, false, true>), grid, dim3(kThreads), 0, st, a);
+  if (a.lut_n < kLutPairRows - 1)      // n <= 31: entries and the zero slot fit
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, false, 2>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, false, 1>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

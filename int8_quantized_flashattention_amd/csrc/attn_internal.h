@@ -30,6 +30,8 @@ struct FwdArgs {
   uint32_t lut_w[65];
 };
 constexpr int kLutZero = 256;
+// pair table: indices 0 .. 31 and the zero slot 32 for either key
+constexpr int kLutPairRows = 33;
 
 // The IndexSoftmax table for b = bits and clip c (entries 0 .. 2^b - 1).
 void index_softmax_table(int bits, float clip, uint8_t* out);
