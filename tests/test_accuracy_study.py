@@ -16,6 +16,8 @@ attention for
   int8-255 the same with an unsigned P = rne(255 P~)
   int8-had int8 after rotating Q and K by the normalized Hadamard matrix
           (Q H)(K H)^T = Q K^T, which spreads outlier channels over all of d
+  lut-b-c int8 with IndexSoftmax (IntAttention §3.1-3.2) in place of exp: a
+          2^b-entry table over distances clipped at c (oracle)
 
 The comparison formats are written here in numpy; each is pinned before use:
 the e4m3 rounding against brute force over all codes, and the numpy INT8 loop
@@ -190,6 +192,13 @@ def errors(inputs):
             "int8-had": rel(int8_online(np.ascontiguousarray(q @ hd), np.ascontiguousarray(k @ hd), v, True, 127.0),
                             exact),
         }
+        qh, sq = oracle.quantize_rows(q, 1)
+        kh, sk = oracle.quantize_rows(k, 1)
+        vh, sv = oracle.quantize_rows(v, v.size // D)
+        for b, c in ((5, 6.6), (8, 6.6), (5, 5.5)):
+            o, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 0, B, H, H, L, L, D, True, TILE, 0,
+                                    index_softmax=(b, float(np.float32(c))))
+            e["lut-%d-%g" % (b, c)] = rel(o.reshape(exact.shape), exact)
         res[name] = e
     print("\nrelative Frobenius error of O vs exact fp64 attention (B1 H4 L1024 d128 causal)")
     for name, e in res.items():
@@ -216,3 +225,24 @@ def test_fp16_is_the_most_accurate(errors):
 
 def test_hadamard_helps_outlier_channels(errors):
     assert errors["outlier"]["int8-had"] < errors["outlier"]["int8"]
+
+
+def test_index_softmax_table_resolution(errors):
+    # b = 8 comes close to the exp path; the recommended b = 5 table is
+    # coarser (32 probability levels): within 4x of exp on Gaussian inputs,
+    # where the probability grid dominates, and close to it with outliers
+    for name in ("gauss", "outlier"):
+        assert errors[name]["lut-8-6.6"] <= 1.2 * errors[name]["int8"], name
+        assert errors[name]["lut-5-6.6"] > errors[name]["lut-8-6.6"], name
+    assert errors["gauss"]["lut-5-6.6"] <= 4.0 * errors["gauss"]["int8"]
+    assert errors["outlier"]["lut-5-6.6"] <= 1.5 * errors["outlier"]["int8"]
+
+
+def test_index_softmax_clip_must_zero_the_last_entry(errors):
+    # with the multiplier 127 and rounding to nearest, the table's last entry
+    # (the value every clipped key gets) is 127 e^-c rounded: 1 at c = 5.5,
+    # 0 from c = ln 254 = 5.54 on. Sharp rows (outlier channels) have
+    # hundreds of clipped keys, whose mass then swamps the row
+    assert oracle.index_softmax_lut(5, np.float32(5.5))[-1] == 1
+    assert oracle.index_softmax_lut(5, np.float32(6.6))[-1] == 0
+    assert errors["outlier"]["lut-5-5.5"] > 5 * errors["outlier"]["lut-5-6.6"]
