@@ -36,6 +36,7 @@ def _bind(L):
     L.oracle_half_to_float.argtypes = [P, P, I64]
     L.oracle_float_to_half.argtypes = [P, P, I64]
     L.oracle_quantize_rows.argtypes = [P, F, I64, I32, I64, P, P]
+    L.oracle_quantize_cols.argtypes = [P, F, I64, I64, I32, P, P]
     L.oracle_logits_i32.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, F]
     FL = ctypes.c_float
     L.oracle_attn_int8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
@@ -45,7 +46,7 @@ def _bind(L):
                                          P, P]
     L.oracle_index_softmax_lut.argtypes = [I32, FL, P]
     L.oracle_attn_ref_f64.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P, F]
-    for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows",
+    for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows", "oracle_quantize_cols",
                "oracle_logits_i32", "oracle_attn_int8", "oracle_attn_int8_trace",
                "oracle_attn_ref_f64", "oracle_index_softmax_lut"):
         getattr(L, fn).restype = ctypes.c_int
@@ -97,6 +98,26 @@ def quantize_rows(x, rows_per_scale=1, L=None):
     return q, s
 
 
+def quantize_cols(x, rows_per_group, L=None):
+    """Per-column symmetric INT8 quantization of groups of rows_per_group rows:
+    x [..., n_cols] (fp32 or fp16) read as [n_groups, rows_per_group, n_cols].
+    Returns (codes int8 like x, scales fp32 [n_groups * n_cols])."""
+    x = np.ascontiguousarray(x)
+    n_cols = x.shape[-1]
+    n_rows = x.size // n_cols
+    assert n_rows % rows_per_group == 0
+    n_groups = n_rows // rows_per_group
+    if x.dtype == np.float16:
+        src, is_half = x.view(np.uint16), 1
+    else:
+        src, is_half = np.ascontiguousarray(x, np.float32), 0
+    q = np.empty(x.shape, np.int8)
+    s = np.empty(n_groups * n_cols, np.float32)
+    _check((L or lib()).oracle_quantize_cols(_p(src), is_half, n_groups, rows_per_group, n_cols, _p(q), _p(s)),
+           "quantize_cols")
+    return q, s
+
+
 def logits_i32(q, k, B, H, Hkv, Lq, Lkv, d, nthreads=0, L=None):
     """All INT32 logits [B,H,Lq,Lkv] (mask not applied)."""
     q = np.ascontiguousarray(q, np.int8)
@@ -123,7 +144,8 @@ def attn_int8(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal
     """Step-by-step INT8 attention forward. Returns (O fp32, lse fp32).
 
     v_per_token: the V scale mode, 0 (or False) one scale for the tensor, 1 (or
-    True) one per token [B*Hkv*Lkv], 2 one per (batch, kv head) [B*Hkv].
+    True) one per token [B*Hkv*Lkv], 2 one per (batch, kv head) [B*Hkv], 3 one
+    per (batch, kv head, channel) [B*Hkv*d].
     index_softmax: None (exp softmax) or (b, c): IndexSoftmax with a 2^b-entry
     table and clipping threshold c.
     O is [B,H,Lq,d] (rows None) or [len(rows), d]."""
@@ -179,5 +201,5 @@ def attn_ref_f64(q, k, v, B, H, Hkv, Lq, Lkv, d, causal, rows=None, nthreads=0, 
     return o
 
 
-__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "logits_i32", "index_softmax_lut", "attn_int8",
+__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "quantize_cols", "logits_i32", "index_softmax_lut", "attn_int8",
            "attn_int8_trace", "attn_ref_f64"]

@@ -41,6 +41,10 @@
 //  * per-head V (one scale per (batch, kv head), a block granularity that
 //    IA §3.3 lists as compatible): the tile scale is that head's s_V and
 //    w = 127, i.e. the per-tensor arithmetic with the head's own scale.
+//  * per-channel V (one scale per (batch, kv head, channel), the per-channel
+//    granularity of IA §3.3): the scale is constant along the keys, so the
+//    tile sums carry no V scale (s_t = 1, w = 127) and channel c of the
+//    output is multiplied by its scale at the end.
 //  * the running max used to quantize a tile is the max after that tile (m').
 //  * rowsum l accumulates the fp32 P_tilde before quantization.
 //  * INT32 accumulation inside a tile, fp32 across tiles.
@@ -158,7 +162,8 @@ struct Problem {
   const int8_t* q; const float* s_q;
   const int8_t* k; const float* s_k;
   const int8_t* v; const float* s_v;
-  int v_mode;    // V scales: 0 one per tensor, 1 per token, 2 per (batch, kv head)
+  int v_mode;    // V scales: 0 one per tensor, 1 per token, 2 per (batch, kv head),
+                 // 3 per (batch, kv head, channel)
   int B, H, Hkv, Lq, Lkv, d, causal;
   int kv_tile, kv_split_len;
   int lut_bits;  // 0: exp softmax; b >= 1: IndexSoftmax with a 2^b-entry table
@@ -189,6 +194,7 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
   const float* sk = P.s_k + kv_base;
   const float* sv = P.v_mode == 1 ? (P.s_v + kv_base)
                   : P.v_mode == 2 ? (P.s_v + (PLANT("v_head_no_batch") ? hk : static_cast<int64_t>(b) * P.Hkv + hk))
+                  : P.v_mode == 3 ? (P.s_v + (PLANT("v_channel_no_head") ? 0 : (static_cast<int64_t>(b) * P.Hkv + hk) * d))
                   : P.s_v;
 
   // Bottom-right aligned causal mask: last visible key of this row.
@@ -242,6 +248,8 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
       if (P.v_mode == 1) {
         st = 0.0f;
         for (int jj = 0; jj < n; ++jj) st = std::max(st, sv[t0 + jj]);
+      } else if (P.v_mode == 3) {
+        st = 1.0f;       // per-channel scales multiply the output channels
       } else {
         st = sv[0];
       }
@@ -297,8 +305,12 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
     L += f * sl[sp];
     for (int c = 0; c < d; ++c) acc[c] += f * sacc[static_cast<size_t>(sp) * d + c];
   }
-  // Output: O = acc / (127 * l); s_V is already inside acc.
-  for (int c = 0; c < d; ++c) o[c] = acc[c] / (127.0f * L);
+  // Output: O = acc / (127 * l); s_V is already inside acc, except per-channel
+  // scales, which multiply their channel here.
+  for (int c = 0; c < d; ++c) {
+    const float sc = P.v_mode == 3 ? sv[PLANT("v_channel_transposed") ? (c * 7) % d : c] : 1.0f;
+    o[c] = (acc[c] * sc) / (127.0f * L);
+  }
   if (lse) *lse = M + std::log(L);
 }
 
@@ -353,7 +365,9 @@ void attend_row_lut(const Problem& P, int b, int h, int i, float* o, float* lse,
   const int8_t* kmat = P.k + kv_base * d;
   const int8_t* vmat = P.v + kv_base * d;
   const float* sk = P.s_k + kv_base;
-  const float sv = P.v_mode == 2 ? P.s_v[static_cast<int64_t>(b) * P.Hkv + hk] : P.s_v[0];
+  // V scale of the tile sums (1 for per-channel scales, applied at the output)
+  const float sv = P.v_mode == 2 ? P.s_v[static_cast<int64_t>(b) * P.Hkv + hk] : P.v_mode == 3 ? 1.0f : P.s_v[0];
+  const float* sv_ch = P.s_v + (static_cast<int64_t>(b) * P.Hkv + hk) * d;
 
   int64_t last = P.Lkv - 1;                      // bottom-right aligned causal mask
   if (P.causal) last = static_cast<int64_t>(i) + (P.Lkv - P.Lq);
@@ -441,7 +455,7 @@ void attend_row_lut(const Problem& P, int b, int h, int i, float* o, float* lse,
     for (int c = 0; c < d; ++c) acc[c] += f * sacc[static_cast<size_t>(sp) * d + c];
   }
   // O = acc / l: the table's factor 127 is in both, so it cancels
-  for (int c = 0; c < d; ++c) o[c] = acc[c] / L;
+  for (int c = 0; c < d; ++c) o[c] = (acc[c] * (P.v_mode == 3 ? sv_ch[c] : 1.0f)) / L;
   if (lse) *lse = M * g + std::log(L / 127.0f);
 }
 
@@ -470,7 +484,7 @@ bool problem_ok(const Problem& P) {
   if (P.kv_tile < 1) return false;
   if (P.kv_split_len < 0 || (P.kv_split_len > 0 && P.kv_split_len % P.kv_tile)) return false;
   if (P.causal && P.Lq > P.Lkv) return false;
-  if (P.v_mode < 0 || P.v_mode > 2) return false;
+  if (P.v_mode < 0 || P.v_mode > 3) return false;
   if (P.lut_bits < 0 || P.lut_bits > 8) return false;
   // IndexSoftmax: a finite positive clip, and no per-token V (whose per-key
   // weights would re-round the table's codes)
@@ -518,6 +532,26 @@ int oracle_quantize_rows(const void* x, int x_is_half, int64_t n_rows, int32_t n
 int oracle_index_softmax_lut(int32_t bits, float c, int32_t* lut) {
   if (bits < 1 || bits > 8 || !(c > 0.0f) || !std::isfinite(c)) return 1;
   index_softmax_lut(bits, c, lut);
+  return 0;
+}
+
+// Column groups: x is [n_groups, rows_per_group, n_cols]; each column of each
+// group is one quantization group (IA §3.3 lists per-channel scales as a
+// granularity the method is compatible with): scales [n_groups, n_cols].
+int oracle_quantize_cols(const void* x, int x_is_half, int64_t n_groups, int64_t rows_per_group,
+                         int32_t n_cols, int8_t* q, float* scales) {
+  if (n_groups < 1 || rows_per_group < 1 || n_cols < 1) return 1;
+  std::vector<float> col(static_cast<size_t>(rows_per_group));
+  std::vector<int8_t> qc(static_cast<size_t>(rows_per_group));
+  for (int64_t g = 0; g < n_groups; ++g)
+    for (int32_t c = 0; c < n_cols; ++c) {
+      for (int64_t r = 0; r < rows_per_group; ++r) {
+        const int64_t e = ((PLANT("cols_no_group") ? 0 : g * rows_per_group) + r) * n_cols + c;
+        col[r] = x_is_half ? half_bits_to_float(static_cast<const uint16_t*>(x)[e]) : static_cast<const float*>(x)[e];
+      }
+      quantize_group(col.data(), rows_per_group, qc.data(), scales + g * n_cols + c);
+      for (int64_t r = 0; r < rows_per_group; ++r) q[(g * rows_per_group + r) * n_cols + c] = qc[r];
+    }
   return 0;
 }
 

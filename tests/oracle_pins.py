@@ -522,6 +522,53 @@ def pin_attn_per_head_is_per_tensor_per_slice(L):
             assert np.array_equal(o[b, h], o1[0, 0]) and np.array_equal(l[b, h], l1[0, 0])
 
 
+def pin_quant_cols_are_rows_of_the_transpose(L):
+    # per-column quantization of a [rows, cols] group is per-row quantization
+    # of its transpose (the row quantizer is pinned above)
+    r = _rng(55)
+    for dt in (np.float32, np.float16):
+        x = (r.standard_normal((3, 37, 24)) * r.uniform(0.1, 9.0, size=(3, 1, 24))).astype(dt)
+        x[1, :, 5] = 0                                   # an all-zero column
+        qc, sc = oracle.quantize_cols(x, 37, L=L)
+        qt, st = oracle.quantize_rows(np.ascontiguousarray(np.swapaxes(x, 1, 2)), 1, L=L)
+        assert np.array_equal(qc, np.swapaxes(qt, 1, 2))
+        assert np.array_equal(sc.view(np.uint32), st.view(np.uint32))
+        assert sc[1 * 24 + 5] == 0 and not qc[1, :, 5].any()
+
+
+def pin_attn_per_channel_scales_channels(L):
+    # per-channel V (mode 3) is linear in each channel's scale: with scales
+    # s[b, hk, c], channel c of every output row of (b, hk) is the per-head
+    # result (scale 1) times s[b, hk, c]; equal channel scales give the
+    # per-head result with that scale. Distinct scales per head and channel
+    # catch a wrong head offset or channel index.
+    r = _rng(56)
+    B, H, Hkv, Lq, Lkv, d = 2, 4, 2, 7, 90, 64
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
+    k, v = (r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32) for _ in range(2))
+    qh, sq = oracle.quantize_rows(q, 1, L=L)
+    kh, sk = oracle.quantize_rows(k, 1, L=L)
+    vh, _ = oracle.quantize_rows(v, 1, L=L)
+    sch = r.uniform(0.01, 2.0, size=(B, Hkv, d)).astype(np.float32)
+    ones = np.ones(B * Hkv, np.float32)
+    for causal, tile, split, lut in ((True, 32, 0, None), (False, 16, 48, None), (True, 32, 0, (5, 6.6)),
+                                     (False, 16, 48, (3, 2.0))):
+        o3, l3 = oracle.attn_int8(qh, sq, kh, sk, vh, sch.reshape(-1), 3, B, H, Hkv, Lq, Lkv, d, causal, tile,
+                                  split, L=L, index_softmax=lut)
+        o2, l2 = oracle.attn_int8(qh, sq, kh, sk, vh, ones, 2, B, H, Hkv, Lq, Lkv, d, causal, tile, split, L=L,
+                                  index_softmax=lut)
+        want = o2 * np.repeat(sch, H // Hkv, axis=1)[:, :, None, :]
+        # fp32 rounding only: the scale multiplies the sums at a different step
+        assert np.allclose(o3, want, rtol=1e-6, atol=1e-6 * np.abs(want).max()), (causal, lut)
+        assert np.array_equal(l3, l2)
+        eq = np.repeat(sch[:, :, :1], d, axis=2)          # equal scales within each head
+        o3e, _ = oracle.attn_int8(qh, sq, kh, sk, vh, eq.reshape(-1), 3, B, H, Hkv, Lq, Lkv, d, causal, tile,
+                                  split, L=L, index_softmax=lut)
+        o2e, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sch[:, :, 0].reshape(-1).copy(), 2, B, H, Hkv, Lq, Lkv, d,
+                                  causal, tile, split, L=L, index_softmax=lut)
+        assert np.allclose(o3e, o2e, rtol=1e-6, atol=1e-6 * np.abs(o2e).max()), (causal, lut)
+
+
 def pin_attn_single_tile_two_pass(L):
     # Bc >= Lkv: one tile, so the max is the true row max and the method reduces
     # to the two-pass form O = s_V sum_j rne(127 e^{S_j - m}) V_hat_j / (127 sum_j e^{S_j - m}).
