@@ -55,9 +55,16 @@ typedef enum {
 
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1 } attn_dtype;
 
-/* V scale granularity: one scale for the tensor, one per token, or one per
- * (batch, kv head) (a block granularity, IntAttention §3.3). */
-typedef enum { ATTN_VSCALE_PER_TENSOR = 0, ATTN_VSCALE_PER_TOKEN = 1, ATTN_VSCALE_PER_HEAD = 2 } attn_vscale;
+/* V scale granularity: one scale for the tensor, one per token, one per
+ * (batch, kv head) (a block granularity), or one per (batch, kv head, channel)
+ * (the per-channel granularity); IntAttention §3.3 names both finer schemes as
+ * compatible with the method. */
+typedef enum {
+  ATTN_VSCALE_PER_TENSOR = 0,
+  ATTN_VSCALE_PER_TOKEN = 1,
+  ATTN_VSCALE_PER_HEAD = 2,
+  ATTN_VSCALE_PER_CHANNEL = 3
+} attn_vscale;
 
 /*
  * attn_quantize_rows — symmetric INT8 quantization of groups of rows
@@ -80,6 +87,28 @@ typedef enum { ATTN_VSCALE_PER_TENSOR = 0, ATTN_VSCALE_PER_TOKEN = 1, ATTN_VSCAL
  */
 attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols,
                                int64_t rows_per_scale, int8_t* q, float* scales, void* stream);
+
+/*
+ * attn_quantize_cols — symmetric INT8 quantization with one scale per column
+ * of each group of rows (the per-channel granularity IntAttention §3.3 names
+ * as compatible; the quantizer of §2.1 Eq. 3 applied to each column), e.g.
+ * V [B, Hkv, Lkv, d] as n_groups = B * Hkv groups of rows_per_group = Lkv rows
+ * gives the [B, Hkv, d] scales of ATTN_VSCALE_PER_CHANNEL.
+ *
+ *   x       [n_groups, rows_per_group, n_cols] of x_dt (fp32 or fp16), device,
+ *           16-byte aligned.
+ *   q       same shape, int8 output, device, 8-byte aligned.
+ *   scales  [n_groups, n_cols] fp32 output, device, 4-byte aligned.
+ *   n_cols  a multiple of 8, at most 2048 (else ATTN_ERR_UNSUPPORTED);
+ *           n_groups * n_cols < 2^31 (else ATTN_ERR_UNSUPPORTED).
+ *
+ * Per (group, column) with absmax a: the same arithmetic as
+ * attn_quantize_rows (s = a / 127, r = 127 / a, q = clamp(rne(x * r), +-127);
+ * a == 0 gives s = 0 and codes 0). While the call runs, `scales` is also used
+ * as scratch for the column maxima.
+ */
+attn_status attn_quantize_cols(const void* x, attn_dtype x_dt, int64_t n_groups, int64_t rows_per_group,
+                               int32_t n_cols, int8_t* q, float* scales, void* stream);
 
 /*
  * attn_kv_append — per-token INT8 quantization of new K or V tokens straight
@@ -114,8 +143,9 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
  *   q    int8 [B, H, Lq, d]      s_q fp32 [B, H, Lq]       (per-token scales)
  *   k    int8 [B, Hkv, Lkv, d]   s_k fp32 [B, Hkv, Lkv]    (per-token scales)
  *   v    int8 [B, Hkv, Lkv, d]   s_v fp32 [1] (ATTN_VSCALE_PER_TENSOR),
- *                                    [B, Hkv, Lkv] (ATTN_VSCALE_PER_TOKEN) or
- *                                    [B, Hkv] (ATTN_VSCALE_PER_HEAD)
+ *                                    [B, Hkv, Lkv] (ATTN_VSCALE_PER_TOKEN),
+ *                                    [B, Hkv] (ATTN_VSCALE_PER_HEAD) or
+ *                                    [B, Hkv, d] (ATTN_VSCALE_PER_CHANNEL)
  *   o    [B, H, Lq, d] of o_dt (fp32 or fp16, rounded to nearest even)
  *   lse  fp32 [B, H, Lq] natural-log log-sum-exp of the scaled logits, or NULL
  *   d    64 or 128 (else ATTN_ERR_UNSUPPORTED)
@@ -134,7 +164,8 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
  * with w_j = 127 (per-tensor and per-head V) or 127 s_V[j] / s_t (per-token V,
  * s_t = the largest s_V of the tile's keys), acc = alpha acc + s_t *
  * (P_hat . V_hat) (s_t = s_V for per-tensor V, the (batch, kv head)'s s_V for
- * per-head V), and finally O = acc / (127 l). Because P_hat
+ * per-head V, 1 for per-channel V), and finally O = acc / (127 l), channel c
+ * multiplied by its scale for per-channel V. Because P_hat
  * follows the running max, O depends on the tile size and split points; they
  * are part of the result's definition and are reported by the schedule query.
  */
@@ -184,8 +215,10 @@ attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k
  *   idx_j   = min(floor(max(fma(u_j, -kappa, m_u * kappa), 0)), 2^b - 1)
  *   E_j     = E_tab[idx_j] (0 for masked keys); l = alpha l + sum_j E_j
  *           (the integer tile sum), acc = alpha acc + s_V (E . V_hat)
- *           (INT32 per tile), alpha = exp((m_u,old - m_u,new) s_Q / sqrt(d))
- *   O       = acc / l; lse = m_u s_Q / sqrt(d) + ln(l / 127).
+ *           (INT32 per tile; s_V = 1 for per-channel V), alpha =
+ *           exp((m_u,old - m_u,new) s_Q / sqrt(d))
+ *   O       = acc / l (channel c times its scale for per-channel V);
+ *           lse = m_u s_Q / sqrt(d) + ln(l / 127).
  *
  * The distance is the dequantized logit's (the pages' integer distance with
  * c_int at its exact value c / alpha; with one scale per key an integer

@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libattn_int8.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_F32, ATTN_F16 = 0, 1
-ATTN_VSCALE_PER_TENSOR, ATTN_VSCALE_PER_TOKEN, ATTN_VSCALE_PER_HEAD = 0, 1, 2
+ATTN_VSCALE_PER_TENSOR, ATTN_VSCALE_PER_TOKEN, ATTN_VSCALE_PER_HEAD, ATTN_VSCALE_PER_CHANNEL = 0, 1, 2, 3
 
 # every function the C header declares, with its ctypes signature
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
     "attn_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
+    "attn_quantize_cols": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I32, _P, _P, _P]),
     "attn_kv_append": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
@@ -111,6 +112,31 @@ def attn_quantize_rows(x, rows_per_scale=1, q=None, scales=None, stream=None):
     return q, scales
 
 
+def attn_quantize_cols(x, rows_per_group, q=None, scales=None, stream=None):
+    """Symmetric INT8 quantization with one scale per column of each group of
+    `rows_per_group` rows of x (fp16 or fp32, last axis = columns), e.g. V
+    [B,Hkv,Lkv,d] with rows_per_group = Lkv gives per-channel scales
+    [B*Hkv*d]. Returns (q int8 like x, scales fp32)."""
+    _dev(x, "x")
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    n_cols = x.shape[-1]
+    n_rows = x.numel() // n_cols
+    if rows_per_group < 1 or n_rows % rows_per_group:
+        raise ValueError("rows_per_group must divide the number of rows")
+    n_groups = n_rows // rows_per_group
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(n_groups * n_cols, dtype=torch.float32, device=x.device)
+    _dev(q, "q", torch.int8)
+    _dev(scales, "scales", torch.float32)
+    st = _lib.attn_quantize_cols(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32, n_groups,
+                                 rows_per_group, n_cols, _ptr(q), _ptr(scales), _stream(stream))
+    _check("attn_quantize_cols", st)
+    return q, scales
+
+
 def attn_kv_append(x, cache, scales, pos, stream=None):
     """Per-token quantization of new tokens x [B,Hkv,T,d] (fp16/fp32) into rows
     pos .. pos+T-1 of the INT8 cache [B,Hkv,L_max,d] and its scales
@@ -146,10 +172,10 @@ def attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal):
 
 
 def _vmode(v_per_token):
-    """V scale mode from False / True / "head" (or 0 / 1 / 2)."""
+    """V scale mode from False / True / "head" / "channel" (or 0 / 1 / 2 / 3)."""
     if isinstance(v_per_token, str):
         return {"tensor": ATTN_VSCALE_PER_TENSOR, "token": ATTN_VSCALE_PER_TOKEN,
-                "head": ATTN_VSCALE_PER_HEAD}[v_per_token]
+                "head": ATTN_VSCALE_PER_HEAD, "channel": ATTN_VSCALE_PER_CHANNEL}[v_per_token]
     return int(v_per_token)
 
 
@@ -167,7 +193,7 @@ def _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out
         raise ValueError("s_k size does not match k")
     mode = _vmode(v_per_token)
     if s_v.numel() != {ATTN_VSCALE_PER_TENSOR: 1, ATTN_VSCALE_PER_TOKEN: B * Hkv * Lkv,
-                       ATTN_VSCALE_PER_HEAD: B * Hkv}.get(mode, -1):
+                       ATTN_VSCALE_PER_HEAD: B * Hkv, ATTN_VSCALE_PER_CHANNEL: B * Hkv * d}.get(mode, -1):
         raise ValueError("s_v size does not match the V scale mode")
     if o_dtype not in (torch.float16, torch.float32):
         raise TypeError("o_dtype must be float16 or float32")
@@ -189,8 +215,9 @@ def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.flo
                   return_lse=False, out=None, lse=None, workspace=None, stream=None):
     """Fused INT8 attention forward. q [B,H,Lq,d] int8, k/v [B,Hkv,Lkv,d] int8,
     s_q [B*H*Lq], s_k [B*Hkv*Lkv], s_v (fp32) [1] (v_per_token False),
-    [B*Hkv*Lkv] (True) or [B*Hkv] (v_per_token "head": one scale per (batch,
-    kv head)). Returns O (and lse when return_lse)."""
+    [B*Hkv*Lkv] (True), [B*Hkv] (v_per_token "head": one scale per (batch,
+    kv head)) or [B*Hkv*d] ("channel": one per (batch, kv head, channel)).
+    Returns O (and lse when return_lse)."""
     _dev(q, "q", torch.int8)
     _dev(s_q, "s_q", torch.float32)
     shape, out, lse, workspace, ws_bytes = _fwd_common(q, k, s_k, v, s_v, v_per_token, causal,
@@ -290,7 +317,7 @@ def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, re
     return attn_int8_fwd_qfloat(q, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
 
 
-__all__ = ["attn_quantize_rows", "attn_kv_append", "attn_int8_fwd", "attn_int8_fwd_qfloat",
+__all__ = ["attn_quantize_rows", "attn_quantize_cols", "attn_kv_append", "attn_int8_fwd", "attn_int8_fwd_qfloat",
            "attn_int8_fwd_index_softmax", "attn_index_softmax_table", "attn_int8_fwd_workspace_size",
            "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
            "AttnError", "LIB_PATH", "SIGNATURES"]

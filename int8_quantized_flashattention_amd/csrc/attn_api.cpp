@@ -109,6 +109,21 @@ attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, i
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_quantize_cols(const void* x, attn_dtype x_dt, int64_t n_groups, int64_t rows_per_group,
+                               int32_t n_cols, int8_t* q, float* scales, void* stream) {
+  if (!x || !q || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (n_groups < 1 || rows_per_group < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_cols % 8 != 0 || n_cols > attn::kMaxQuantCols) return ATTN_ERR_UNSUPPORTED;
+  if (n_groups > INT64_MAX / rows_per_group || n_groups * rows_per_group > INT64_MAX / n_cols)
+    return ATTN_ERR_INVALID_ARG;
+  if (n_groups * n_cols > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_quantize_cols(x, x_dt == ATTN_F16, n_groups, rows_per_group, n_cols, q,
+                                                  scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
                            int8_t* cache, float* scales, int32_t L_max, int32_t pos, void* stream) {
   if (!x || !cache || !scales) return ATTN_ERR_INVALID_ARG;
@@ -162,7 +177,8 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
     if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(s_q, 4)) return ATTN_ERR_INVALID_ARG;
   }
-  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN && v_mode != ATTN_VSCALE_PER_HEAD)
+  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN && v_mode != ATTN_VSCALE_PER_HEAD &&
+      v_mode != ATTN_VSCALE_PER_CHANNEL)
     return ATTN_ERR_INVALID_ARG;
   if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
@@ -181,7 +197,8 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
   a.o = o; a.lse = lse; a.s_dump = nullptr;
   a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
   a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN);
-  a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.o_f16 = (o_dt == ATTN_F16);
+  a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.v_per_channel = (v_mode == ATTN_VSCALE_PER_CHANNEL);
+  a.o_f16 = (o_dt == ATTN_F16);
   a.workspace = workspace;
   if (lut_bits != 0) {
     uint8_t tab[sizeof(a.lut_w)] = {};

@@ -601,14 +601,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const float ltot = pair_sum(l);                      // 127 * l
   if (!qvalid) return;
   const float scale = (VPT ? 1.0f : a.s_v[a.v_per_head ? b * a.Hkv + hk : 0]) / ltot;
+  // per-channel V: channel c of the output takes its own scale
+  const float* sch = a.s_v + (static_cast<int64_t>(b) * a.Hkv + hk) * D;
   const int64_t orow = (q_base + qi) * D;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = c * 32 + j4 * 8 + g * 4;
-      const float o0 = acc[c][j4 * 4 + 0] * scale, o1 = acc[c][j4 * 4 + 1] * scale;
-      const float o2 = acc[c][j4 * 4 + 2] * scale, o3 = acc[c][j4 * 4 + 3] * scale;
+      float cs[4] = {scale, scale, scale, scale};
+      if (!VPT && a.v_per_channel) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[e] = sch[d0 + e] / ltot;
+      }
+      const float o0 = acc[c][j4 * 4 + 0] * cs[0], o1 = acc[c][j4 * 4 + 1] * cs[1];
+      const float o2 = acc[c][j4 * 4 + 2] * cs[2], o3 = acc[c][j4 * 4 + 3] * cs[3];
       if constexpr (OUT_F16) {
         const __half2 h01 = __floats2half2_rn(o0, o1);
         const __half2 h23 = __floats2half2_rn(o2, o3);

@@ -21,6 +21,7 @@ struct FwdArgs {
   int B, H, Hkv, Lq, Lkv, d;
   int causal, v_per_token, o_f16;
   int v_per_head;      // s_v holds one scale per (batch, kv head)
+  int v_per_channel;   // s_v holds one scale per (batch, kv head, channel)
   void* workspace;
   // IndexSoftmax: lut_n = 2^b - 1 (0: exp softmax), lut_k = (2^b - 1) / c in
   // fp32, lut_w = the table's bytes (entry i at byte i), zero from byte
@@ -60,6 +61,10 @@ hipError_t launch_quantize(const void* x, int x_f16, int64_t n_rows, int n_cols,
 constexpr int kMaxAppendCols = 2048;
 hipError_t launch_append(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max,
                          int pos, int8_t* cache, float* scales, hipStream_t st);
+// per-column quantization of n_groups groups of rows_per_group rows
+constexpr int kMaxQuantCols = 2048;
+hipError_t launch_quantize_cols(const void* x, int x_f16, int64_t n_groups, int64_t rows_per_group, int n_cols,
+                                int8_t* q, float* scales, hipStream_t st);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t st);
 hipError_t launch_debug_logits(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const FwdArgs& a, int split_len, hipStream_t st);

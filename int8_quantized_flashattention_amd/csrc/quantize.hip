@@ -20,6 +20,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 namespace attn {
 namespace {
 
@@ -205,6 +207,97 @@ __global__ void finalize_scales(float* scales, int64_t n) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Column groups (one scale per column of each group of rows, e.g. per channel
+// of each (batch, kv head) of V): grid (n_groups, blocks_per_group). A lane
+// owns one 8-column chunk and strides over rows; the block's rows are cut in
+// rpi slots of ncc lanes each (ncc = n_cols / 8 <= 256).
+// ---------------------------------------------------------------------------
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void absmax_cols(const void* __restrict__ x, int64_t rows, int n_cols,
+                                                        uint32_t* __restrict__ bits) {
+  __shared__ float red[kThreads * kChunk];
+  const int ncc = n_cols / kChunk;
+  const int rpi = kThreads / ncc;
+  const int cc = threadIdx.x % ncc, rr = threadIdx.x / ncc;
+  const int64_t g = blockIdx.x;
+  float m[kChunk];
+#pragma unroll
+  for (int e = 0; e < kChunk; ++e) m[e] = 0.0f;
+  if (rr < rpi) {
+    const int64_t stride = static_cast<int64_t>(gridDim.y) * rpi;
+    int64_t r = static_cast<int64_t>(blockIdx.y) * rpi + rr;
+    for (; r + (kUnroll - 1) * stride < rows; r += kUnroll * stride) {
+      Chunk8 c[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) c[u] = load_chunk<F16>(x, ((g * rows) + r + u * stride) * n_cols + cc * kChunk);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) m[e] = fmaxf(m[e], fabsf(c[u].x[e]));
+    }
+    for (; r < rows; r += stride) {
+      const Chunk8 c = load_chunk<F16>(x, (g * rows + r) * n_cols + cc * kChunk);
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) m[e] = fmaxf(m[e], fabsf(c.x[e]));
+    }
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) red[rr * n_cols + cc * kChunk + e] = m[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < n_cols; c += kThreads) {
+    float a = red[c];
+    for (int i = 1; i < rpi; ++i) a = fmaxf(a, red[i * n_cols + c]);
+    atomicMax(bits + g * n_cols + c, __float_as_uint(a));   // |x| >= 0: float order == bit order
+  }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(kThreads) void quantize_cols(const void* __restrict__ x, int64_t rows, int n_cols,
+                                                          const uint32_t* __restrict__ bits, int8_t* __restrict__ q) {
+  __shared__ float rc[kMaxQuantCols];
+  const int64_t g = blockIdx.x;
+  for (int c = threadIdx.x; c < n_cols; c += kThreads) rc[c] = quant_recip(__uint_as_float(bits[g * n_cols + c]));
+  __syncthreads();
+  const int ncc = n_cols / kChunk;
+  const int rpi = kThreads / ncc;
+  const int cc = threadIdx.x % ncc, rr = threadIdx.x / ncc;
+  if (rr >= rpi) return;
+  float r[kChunk];
+#pragma unroll
+  for (int e = 0; e < kChunk; ++e) r[e] = rc[cc * kChunk + e];
+  const int64_t stride = static_cast<int64_t>(gridDim.y) * rpi;
+  for (int64_t row = static_cast<int64_t>(blockIdx.y) * rpi + rr; row < rows; row += stride) {
+    const int64_t elem = (g * rows + row) * n_cols + cc * kChunk;
+    const Chunk8 c = load_chunk<F16>(x, elem);
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      w[h] = quant_code(c.x[4 * h], r[4 * h]) | (quant_code(c.x[4 * h + 1], r[4 * h + 1]) << 8) |
+             (quant_code(c.x[4 * h + 2], r[4 * h + 2]) << 16) | (quant_code(c.x[4 * h + 3], r[4 * h + 3]) << 24);
+    *reinterpret_cast<uint2*>(q + elem) = make_uint2(w[0], w[1]);
+  }
+}
+
+template <bool F16>
+hipError_t run_cols(const void* x, int64_t n_groups, int64_t rows, int n_cols, int8_t* q, float* s, hipStream_t st) {
+  const int64_t n = n_groups * n_cols;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(s);
+  const unsigned zb = static_cast<unsigned>((n + 255) / 256);
+  hipLaunchKernelGGL(zero_bits, dim3(zb), dim3(256), 0, st, bits, n);
+  // about 2048 workgroups in all, each row slot covering at least 16 rows
+  const int rpi = kThreads / (n_cols / kChunk);
+  int64_t bpg = (rows + int64_t{rpi} * 16 - 1) / (int64_t{rpi} * 16);
+  const int64_t cap = std::max<int64_t>(1, 2048 / n_groups);
+  if (bpg > cap) bpg = cap;
+  const dim3 grid(static_cast<unsigned>(n_groups), static_cast<unsigned>(bpg));
+  hipLaunchKernelGGL(absmax_cols<F16>, grid, dim3(kThreads), 0, st, x, rows, n_cols, bits);
+  hipLaunchKernelGGL(quantize_cols<F16>, grid, dim3(kThreads), 0, st, x, rows, n_cols,
+                     static_cast<const uint32_t*>(bits), q);
+  hipLaunchKernelGGL(finalize_scales, dim3(zb), dim3(256), 0, st, s, n);
+  return hipGetLastError();
+}
+
 template <bool F16, int T, int CH, int G>
 hipError_t run_small(const void* x, int64_t n_groups, int64_t ge, int8_t* q, float* s, hipStream_t st,
                      const RowMap* map = nullptr) {
@@ -265,6 +358,12 @@ hipError_t launch_quantize(const void* x, int x_f16, int64_t n_rows, int n_cols,
                            int8_t* q, float* scales, hipStream_t st) {
   return x_f16 ? run<true>(x, n_rows, n_cols, rps, q, scales, st)
                : run<false>(x, n_rows, n_cols, rps, q, scales, st);
+}
+
+hipError_t launch_quantize_cols(const void* x, int x_f16, int64_t n_groups, int64_t rows_per_group, int n_cols,
+                                int8_t* q, float* scales, hipStream_t st) {
+  return x_f16 ? run_cols<true>(x, n_groups, rows_per_group, n_cols, q, scales, st)
+               : run_cols<false>(x, n_groups, rows_per_group, n_cols, q, scales, st);
 }
 
 hipError_t launch_append(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max,

@@ -8,6 +8,7 @@
 //   emu_driver fwdlut q.bin sq.bin k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal bits clip  o.out lse.out
 //   emu_driver lut    bits clip  table.out
+//   emu_driver qcols  x.bin dt n_groups rows n_cols  q.out s.out
 //   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out qhat.out sq.out
 //   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
@@ -72,7 +73,7 @@ int main(int argc, char** argv) {
     auto* k = static_cast<int8_t*>(read_file(argv[4], nk * d));
     auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
     auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
-    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : 1) * 4));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : vmode == 3 ? size_t(B) * Hkv * d : 1) * 4));
     const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
     void* o = alloc(osz);
     float* lse = static_cast<float*>(alloc(nq * 4));
@@ -89,6 +90,17 @@ int main(int argc, char** argv) {
                          nullptr);
     write_file(argv[lut ? 19 : 17], o, osz);
     write_file(argv[lut ? 20 : 18], lse, nq * 4);
+  } else if (mode == "qcols" && argc == 9) {
+    const int dt = std::atoi(argv[3]);
+    const int64_t n_groups = std::atoll(argv[4]), rows = std::atoll(argv[5]);
+    const int32_t n_cols = std::atoi(argv[6]);
+    const size_t n = size_t(n_groups) * rows * n_cols;
+    void* x = read_file(argv[2], n * (dt == ATTN_F16 ? 2 : 4));
+    auto* q = static_cast<int8_t*>(alloc(n));
+    auto* sc = static_cast<float*>(alloc(size_t(n_groups) * n_cols * 4));
+    st = attn_quantize_cols(x, static_cast<attn_dtype>(dt), n_groups, rows, n_cols, q, sc, nullptr);
+    write_file(argv[7], q, n);
+    write_file(argv[8], sc, size_t(n_groups) * n_cols * 4);
   } else if (mode == "lut" && argc == 5) {
     const int bits = std::atoi(argv[2]);
     uint8_t tab[256];
@@ -105,7 +117,7 @@ int main(int argc, char** argv) {
     auto* k = static_cast<int8_t*>(read_file(argv[4], nk * d));
     auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
     auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
-    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : 1) * 4));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : vmode == 3 ? size_t(B) * Hkv * d : 1) * 4));
     const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
     void* o = alloc(osz);
     float* lse = static_cast<float*>(alloc(nq * 4));

@@ -46,6 +46,18 @@ def quantize_both(lib, x, rows_per_scale):
     return qo, so, qd, sd
 
 
+def quantize_cols_both(lib, x, rows_per_group):
+    """Per-column quantization on the GPU and with the oracle; bit-exact."""
+    qd, sd = lib.attn_quantize_cols(dev(x), rows_per_group)
+    qg, sg = host(qd), host(sd)
+    qo, so = oracle.quantize_cols(x, rows_per_group)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32)), "column scales differ"
+    if not np.array_equal(qg, qo):
+        bad = np.argwhere(qg != qo)[:5]
+        raise AssertionError("column codes differ at %s" % bad.tolist())
+    return qo, so, qd, sd
+
+
 def compare_o(o_gpu, o_ref, what=""):
     o_gpu = np.asarray(o_gpu, np.float32)
     o_ref = np.asarray(o_ref, np.float32)
@@ -80,15 +92,20 @@ def run_problem(lib, q, k, v, causal, v_per_token, o_dtype, rows=None, check_lse
     those entries (per-token V only, where batch entries are independent)."""
     B, H, Lq, d = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
-    # V scales: "head" one per (batch, kv head), else a truth value: per token / per tensor
-    v_per_token = "head" if isinstance(v_per_token, str) and v_per_token == "head" else bool(v_per_token)
+    # V scales: "head" one per (batch, kv head), "channel" one per (batch, kv
+    # head, channel), else a truth value: per token / per tensor
+    v_per_token = v_per_token if isinstance(v_per_token, str) and v_per_token in ("head", "channel") \
+        else bool(v_per_token)
     log("[%s] B=%d H=%d Hkv=%d Lq=%d Lkv=%d d=%d causal=%d vpt=%s o=%s" %
         (tag, B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o_dtype))
     if batches is None:
         qh, sq, qd, sqd = quantize_both(lib, q, 1)
         kh, sk, kd, skd = quantize_both(lib, k, 1)
-        vh, sv, vd, svd = quantize_both(lib, v, 1 if v_per_token is True else
-                                        Lkv if v_per_token == "head" else v.size // d)
+        if v_per_token == "channel":
+            vh, sv, vd, svd = quantize_cols_both(lib, v, Lkv)
+        else:
+            vh, sv, vd, svd = quantize_both(lib, v, 1 if v_per_token is True else
+                                            Lkv if v_per_token == "head" else v.size // d)
     else:
         assert v_per_token is True and rows is None
         batches = np.asarray(batches)
@@ -113,7 +130,7 @@ def run_problem(lib, q, k, v, causal, v_per_token, o_dtype, rows=None, check_lse
     tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
     if batches is not None:
         og, lg, B = og[batches], lg[batches], len(batches)
-    mode = 2 if v_per_token == "head" else int(bool(v_per_token))
+    mode = {"head": 2, "channel": 3}.get(v_per_token, None) if isinstance(v_per_token, str) else int(v_per_token)
     oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, mode, B, H, Hkv, Lq, Lkv, d, causal,
                               tile, split, rows=rows)
     if rows is None:

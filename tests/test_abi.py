@@ -55,7 +55,7 @@ def fwd(**kw):
     (dict(q=None), INVALID), (dict(s_q=None), INVALID), (dict(k=None), INVALID),
     (dict(s_k=None), INVALID), (dict(v=None), INVALID), (dict(s_v=None), INVALID),
     (dict(o=None), INVALID),
-    (dict(v_mode=3), INVALID), (dict(o_dt=5), INVALID),
+    (dict(v_mode=4), INVALID), (dict(o_dt=5), INVALID),
     (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Hkv=0), INVALID), (dict(Lq=0), INVALID),
     (dict(Lkv=-3), INVALID), (dict(d=0), INVALID),
     (dict(H=3, Hkv=2), INVALID), (dict(causal=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID),
@@ -82,7 +82,7 @@ def fwdq(**kw):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(q_dt=4), INVALID), (dict(k=None), INVALID),
-    (dict(s_v=None), INVALID), (dict(o=None), INVALID), (dict(v_mode=3), INVALID),
+    (dict(s_v=None), INVALID), (dict(o=None), INVALID), (dict(v_mode=4), INVALID),
     (dict(q=A + 8), INVALID), (dict(q_hat=A + 4), INVALID), (dict(s_q=A + 2), INVALID),
     (dict(H=3, Hkv=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID), (dict(d=32), UNSUPPORTED),
     (dict(B=1, H=2, Hkv=1, Lq=1, Lkv=4096), INVALID),   # decode schedule needs a workspace
@@ -108,7 +108,7 @@ def fwdlut(**kw):
     (dict(bits=0), INVALID), (dict(bits=9), INVALID), (dict(bits=-1), INVALID),
     (dict(clip=0.0), INVALID), (dict(clip=-1.0), INVALID), (dict(clip=float("inf")), INVALID),
     (dict(clip=float("nan")), INVALID), (dict(clip=5e-4), INVALID), (dict(clip=2e3), INVALID),
-    (dict(v_mode=1), UNSUPPORTED), (dict(v_mode=3), INVALID), (dict(o_dt=5), INVALID),
+    (dict(v_mode=1), UNSUPPORTED), (dict(v_mode=4), INVALID), (dict(o_dt=5), INVALID),
     (dict(H=3, Hkv=2), INVALID), (dict(causal=1, Lq=9, Lkv=8), INVALID), (dict(d=96), UNSUPPORTED),
     (dict(q=A + 8), INVALID), (dict(o=A + 2), INVALID),
     (dict(B=1, H=2, Hkv=1, Lq=1, Lkv=4096), INVALID),   # decode schedule needs a workspace
@@ -163,6 +163,27 @@ def test_quantize_rejects_before_launch():
     assert q(rps=0) == INVALID
     assert q(rps=5) == INVALID          # 16 rows not divisible by 5
     assert q(n_cols=60) == UNSUPPORTED  # not a multiple of 8
+    assert q(x=A + 8) == INVALID
+    assert q(q=A + 4) == INVALID
+    assert q(s=A + 2) == INVALID
+
+
+def test_quantize_cols_rejects_before_launch():
+    p = ctypes.c_void_p
+    q = lambda **kw: L.attn_quantize_cols(
+        p(kw.get("x", A)), kw.get("dt", 1), kw.get("g", 4), kw.get("rows", 16), kw.get("n_cols", 64),
+        p(kw.get("q", A)), p(kw.get("s", A)), None)
+    assert q(x=None) == INVALID
+    assert q(q=None) == INVALID
+    assert q(s=None) == INVALID
+    assert q(dt=7) == INVALID
+    assert q(g=0) == INVALID
+    assert q(rows=0) == INVALID
+    assert q(n_cols=0) == INVALID
+    assert q(n_cols=60) == UNSUPPORTED            # not a multiple of 8
+    assert q(n_cols=4096) == UNSUPPORTED          # wider than one workgroup's columns
+    assert q(g=1 << 21, n_cols=2048) == UNSUPPORTED   # 2^32 scales
+    assert q(g=1 << 40, rows=1 << 30) == INVALID  # element count overflows
     assert q(x=A + 8) == INVALID
     assert q(q=A + 4) == INVALID
     assert q(s=A + 2) == INVALID

@@ -114,6 +114,9 @@ def test_emulated_logits(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal):
     (1, 16, 1, 1, 333, 128, 0, 1, F32, 1), (1, 34, 2, 1, 300, 128, 0, 0, F32, 1), (1, 2, 2, 300, 50, 64, 0, 1, F16, 1),
     # V scales per (batch, kv head): prefill and split-KV decode shapes
     (2, 4, 2, 77, 130, 128, 1, 2, F16, 1), (2, 8, 2, 1, 700, 128, 0, 2, F32, 1),
+    # V scales per (batch, kv head, channel)
+    (2, 4, 2, 77, 130, 128, 1, 3, F32, 1), (1, 3, 3, 300, 300, 64, 1, 3, F16, 1),
+    (2, 8, 2, 1, 700, 128, 0, 3, F32, 1), (1, 8, 1, 2, 520, 64, 1, 3, F16, 1),
 ])
 def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt, gain):
     r = np.random.Generator(np.random.PCG64(B * 100 + Lq * 7 + Lkv))
@@ -124,7 +127,11 @@ def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, o
     v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
     qh, sq = oracle.quantize_rows(q, 1)
     kh, sk = oracle.quantize_rows(k, 1)
-    vh, sv = oracle.quantize_rows(v, {0: v.size // d, 1: 1, 2: Lkv}[vpt])
+    if vpt == 3:
+        v *= r.uniform(0.1, 2.0, size=(B, Hkv, 1, d)).astype(np.float32)     # channels of different ranges
+        vh, sv = oracle.quantize_cols(v, Lkv)
+    else:
+        vh, sv = oracle.quantize_rows(v, {0: v.size // d, 1: 1, 2: Lkv}[vpt])
     oo_p, lo_p = os.path.join(str(tmp_path), "o.out"), os.path.join(str(tmp_path), "l.out")
     files = [put(tmp_path, n + ".bin", a) for n, a in
              (("q", qh), ("sq", sq), ("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
@@ -137,6 +144,22 @@ def test_emulated_attention(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vpt, o
     err = np.abs(o - oo)
     assert err.max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
     assert np.abs(lse - lo).max() <= 1e-4 * max(1.0, np.abs(lo).max())
+
+
+@pytest.mark.parametrize("rows,cols,groups,dt", [
+    (130, 128, 4, np.float16), (37, 24, 3, np.float32), (1, 8, 5, np.float16), (700, 64, 2, np.float32),
+    (3, 2048, 2, np.float16),
+])
+def test_emulated_quantize_cols(exe, tmp_path, rows, cols, groups, dt):
+    r = np.random.Generator(np.random.PCG64(rows * 7 + cols))
+    x = (r.standard_normal((groups, rows, cols)) * r.uniform(0.1, 9.0, size=(groups, 1, cols))).astype(dt)
+    x[0, :, 3] = 0                                   # an all-zero column
+    qo, so = os.path.join(str(tmp_path), "q.out"), os.path.join(str(tmp_path), "s.out")
+    run(exe, tmp_path, ["qcols", put(tmp_path, "x.bin", x), F16 if dt == np.float16 else F32, groups, rows, cols,
+                        qo, so])
+    qr, sr = oracle.quantize_cols(x, rows)
+    assert np.array_equal(np.fromfile(qo, np.int8).reshape(x.shape), qr)
+    assert np.array_equal(np.fromfile(so, np.uint32), sr.view(np.uint32))
 
 
 @pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,qdt", [

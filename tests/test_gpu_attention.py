@@ -77,6 +77,9 @@ SWEEP = [  # B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o
     # V scales per (batch, kv head)
     (2, 8, 2, 77, 130, 128, 1, "head", "f16"), (2, 16, 4, 1, 700, 128, 0, "head", "f32"),
     (3, 4, 4, 300, 300, 64, 1, "head", "f32"),
+    # V scales per (batch, kv head, channel)
+    (2, 8, 2, 77, 130, 128, 1, "channel", "f16"), (2, 16, 4, 1, 700, 128, 0, "channel", "f32"),
+    (1, 3, 3, 300, 300, 64, 1, "channel", "f32"), (1, 8, 1, 2, 520, 64, 1, "channel", "f16"),
 ]
 
 

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_parity import compare_o, host, log, quantize_both
+from gpu_parity import compare_o, host, log, quantize_both, quantize_cols_both
 from workloads import WORKLOADS, gaussian
 
 pytestmark = pytest.mark.gpu
@@ -33,14 +33,18 @@ def run_lut(lib, q, k, v, causal, vmode, odt, bits, clip, rows=None, tag=""):
         (tag, B, H, Hkv, Lq, Lkv, d, causal, vmode, odt, bits, c32))
     qh, sq, qd, sqd = quantize_both(lib, q, 1)
     kh, sk, kd, skd = quantize_both(lib, k, 1)
-    vh, sv, vd, svd = quantize_both(lib, v, Lkv if vmode == "head" else v.size // d)
+    if vmode == "channel":
+        vh, sv, vd, svd = quantize_cols_both(lib, v, Lkv)
+    else:
+        vh, sv, vd, svd = quantize_both(lib, v, Lkv if vmode == "head" else v.size // d)
     tdt = torch.float16 if odt == "f16" else torch.float32
     o, lse = lib.attn_int8_fwd_index_softmax(qd, sqd, kd, skd, vd, svd, vmode, causal, tdt, bits, c32,
                                              return_lse=True)
     og, lg = host(o).astype(np.float32), host(lse)
     tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
-    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 2 if vmode == "head" else 0, B, H, Hkv, Lq, Lkv, d,
-                              causal, tile, split, rows=rows, index_softmax=(bits, c32))
+    mode = {"tensor": 0, "head": 2, "channel": 3}[vmode]
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, mode, B, H, Hkv, Lq, Lkv, d, causal, tile, split, rows=rows,
+                              index_softmax=(bits, c32))
     og = og.reshape(-1, d) if rows is None else og.reshape(-1, d)[rows]
     lg = lg.reshape(-1) if rows is None else lg.reshape(-1)[rows]
     oo = oo.reshape(-1, d)
@@ -81,6 +85,8 @@ SWEEP = [  # B, H, Hkv, Lq, Lkv, d, causal, V scale, o, b, c
     (2, 8, 2, 1, 1500, 128, 0, "tensor", "f16", 5, 6.6), (1, 8, 1, 2, 520, 64, 1, "head", "f32", 3, 2.0),
     (1, 16, 1, 1, 333, 128, 0, "tensor", "f32", 5, 6.6), (1, 4, 1, 4, 700, 128, 1, "tensor", "f32", 2, 0.5),
     (4, 32, 8, 1, 4096, 128, 0, "head", "f32", 5, 6.6), (1, 34, 2, 1, 300, 128, 0, "tensor", "f32", 5, 6.6),
+    # V scales per (batch, kv head, channel)
+    (2, 4, 2, 130, 257, 128, 1, "channel", "f32", 5, 6.6), (2, 8, 2, 1, 1500, 128, 0, "channel", "f16", 8, 7.7),
 ]
 
 

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from gpu_parity import log, quantize_both
+from gpu_parity import quantize_cols_both, log, quantize_both
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +83,20 @@ def test_kv_append_matches_oracle(lib, B, Hkv, T, d, L, pos, dt):
     keep = np.ones(L, bool)
     keep[pos:pos + T] = False
     assert np.all(c[:, :, keep] == 99) and np.all(s[:, :, keep] == -1.0)
+
+
+# (groups, rows, cols, dtype): one scale per column of each group of rows,
+# from one row to the V tensor of the long-context shape, every column width
+COLS = [
+    (5, 1, 8, np.float16), (3, 37, 24, np.float32), (4, 130, 128, np.float16), (2, 700, 64, np.float32),
+    (2, 3, 2048, np.float16), (128, 4096, 128, np.float16), (1, 100000, 64, np.float32),
+]
+
+
+@pytest.mark.parametrize("groups,rows,cols,dt", COLS)
+def test_quantize_cols_matches_oracle(lib, groups, rows, cols, dt):
+    log("quantize cols groups=%d rows=%d cols=%d %s" % (groups, rows, cols, np.dtype(dt).name))
+    r = _rng(groups * 131 + rows + cols)
+    x = (r.standard_normal((groups, rows, cols)) * r.uniform(0.01, 30.0, size=(groups, 1, cols))).astype(dt)
+    x[0, :, cols // 2] = 0             # an all-zero column
+    quantize_cols_both(lib, x, rows)
