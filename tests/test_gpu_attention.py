@@ -105,3 +105,31 @@ def test_degenerate_inputs(lib):
     run_problem(lib, base[0], keq, base[2], False, True, "f32", tag="equal-k")
     big = (r.standard_normal((B, H, L, d)) * 60).astype(np.float16)  # peaked softmax
     run_problem(lib, big, big, base[2], True, False, "f16", tag="peaked")
+
+
+def test_per_block_v_via_per_token_scales(lib):
+    # per-block V scales (one per 64-key block, the KV tile): quantize V with
+    # rows_per_scale = 64 and repeat each block's scale over its keys; the
+    # per-token forward then uses that block's scale for the whole tile
+    # (w_j = 127 s / s), which the oracle's per-token mode states
+    import torch
+    from gpu_parity import compare_o, dev, host, quantize_both
+    import oracle
+    B, H, Hkv, L, d = 2, 8, 2, 640, 128
+    q = gaussian((B, H, L, d), 811, np.float16)
+    k = gaussian((B, Hkv, L, d), 812, np.float16)
+    v = gaussian((B, Hkv, L, d), 813, np.float16) * np.linspace(0.2, 3.0, L, dtype=np.float16)[:, None]
+    qh, sq, qd, sqd = quantize_both(lib, q, 1)
+    kh, sk, kd, skd = quantize_both(lib, k, 1)
+    vh, sb, vd, sbd = quantize_both(lib, v, 64)
+    assert sb.size == B * Hkv * L // 64
+    svd = torch.repeat_interleave(sbd, 64).contiguous()
+    sv = np.repeat(sb, 64)
+    q1h, sq1, q1d, sq1d = quantize_both(lib, np.ascontiguousarray(q[:, :, -1:]), 1)   # a decode shape
+    for Lq, causal in ((L, True), (L, False), (1, False)):
+        qa, sa, qb, sbq = (qh, sq, qd, sqd) if Lq == L else (q1h, sq1, q1d, sq1d)
+        o = lib.attn_int8_fwd(qb, sbq, kd, skd, vd, svd, True, causal, torch.float32)
+        tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, L, d, causal)
+        assert tile == 64 and split % 64 == 0
+        oo, _ = oracle.attn_int8(qa, sa, kh, sk, vh, sv, 1, B, H, Hkv, Lq, L, d, causal, tile, split)
+        compare_o(host(o), oo, "per-block V Lq=%d causal=%d" % (Lq, causal))
