@@ -193,7 +193,7 @@ def main():
     lut = args.softmax == "index"
     lut_args = (args.lut_bits, float(np.float32(args.lut_clip))) if lut else None
     if lut and w.v_per_token:
-        print("IndexSoftmax takes one V scale per tensor or per head; workload %s has per-token V"
+        print("IndexSoftmax takes V scales constant along the keys; workload %s has per-token V"
               % w.name, file=sys.stderr)
         sys.exit(2)
     fused_q = args.q_path == "fused" and not lut     # the IndexSoftmax forward takes INT8 Q

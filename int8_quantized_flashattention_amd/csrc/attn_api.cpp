@@ -183,7 +183,7 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
   if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
   if (s != ATTN_OK) return s;
-  // IndexSoftmax kernels take INT8 Q and one V scale per tensor or per head
+  // IndexSoftmax kernels take INT8 Q and V scales constant along the keys
   if (lut_bits != 0 && (q_float || v_mode == ATTN_VSCALE_PER_TOKEN)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_INVALID_ARG;
   if (!aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4))) return ATTN_ERR_INVALID_ARG;

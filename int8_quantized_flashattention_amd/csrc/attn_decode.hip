@@ -153,11 +153,11 @@ __device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, 
 }
 
 // LUT: IndexSoftmax (table lookup) in place of the exp2 softmax; only with
-// per-tensor or per-head V and INT8 Q.
+// V scales constant along the keys (per tensor, head or channel) and INT8 Q.
 template <int D, bool CAUSAL, bool VPT, bool QF, bool LUT>
 // two wavefronts per SIMD (registers <= 256): the LDS ring allows six per CU
 __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
-  static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and per-tensor or per-head V");
+  static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
   constexpr int NC = D / 64;
   constexpr int NCB = D / 16;
   constexpr int NL = loads_per_tile<D, VPT>();

@@ -339,10 +339,10 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
 
 // LUT: 0 exp2 softmax; 1 IndexSoftmax with the byte table; 2 IndexSoftmax
 // with the pair table (tables of at most 32 entries). IndexSoftmax only with
-// per-tensor or per-head V and INT8 Q.
+// V scales constant along the keys (per tensor, head or channel) and INT8 Q.
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF, int LUT>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
-  static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and per-tensor or per-head V");
+  static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
   __shared__ Stage<D> sm[kStages];
