@@ -23,7 +23,9 @@ Also reported on the same JSON line:
                 a bounded, seeded sample of the workload's query rows
   kernels       per-kernel averages (quantize passes, attention) in the timed region
 
-`--softmax index` times the same step with IndexSoftmax (a 2^b-entry
+`--qk int4` times the step with INT4 Q.K: Q and K in per-token 4-bit codes,
+K packed two codes per byte (the decode cache is then a packed K cache), Q
+quantized in its own pass. `--softmax index` times the same step with IndexSoftmax (a 2^b-entry
 exponential table, `--lut-bits`, `--lut-clip`) in place of the exp softmax; that
 forward takes INT8 Q, so Q is then quantized in its own pass.
 
@@ -64,6 +66,8 @@ def parse():
                     help="quantize Q inside the attention kernels (fused) or in its own pass")
     ap.add_argument("--softmax", choices=["exp", "index"], default="exp",
                     help="exp softmax, or IndexSoftmax (table lookup; INT8 Q from its own pass)")
+    ap.add_argument("--qk", choices=["int8", "int4"], default="int8",
+                    help="INT8 Q.K, or INT4 Q.K: 4-bit codes, K packed two per byte (Q from its own pass)")
     ap.add_argument("--lut-bits", type=int, default=5, help="IndexSoftmax table bits b")
     ap.add_argument("--lut-clip", type=float, default=6.6, help="IndexSoftmax clipping threshold c")
     ap.add_argument("--attn-only", action="store_true",
@@ -122,13 +126,14 @@ def host_threads():
     return max(1, min(16, n))
 
 
-def cpu_baseline(w, q, k, v, target_s, index_softmax=None):
+def cpu_baseline(w, q, k, v, target_s, index_softmax=None, q4=False):
     """Time the oracle's INT8 attention on a seeded sample of rows, scaled so
     the timed call lasts about target_s seconds."""
     import oracle
     rps_v = 1 if w.v_per_token else v.size // w.d
-    qh, sq = oracle.quantize_rows(q, 1)
-    kh, sk = oracle.quantize_rows(k, 1)
+    quant = oracle.quantize_rows_int4 if q4 else (lambda x: oracle.quantize_rows(x, 1))
+    qh, sq = quant(q)
+    kh, sk = quant(k)
     vh, sv = oracle.quantize_rows(v, rps_v)
     import int8_quantized_flashattention_amd as m
     tile, split = m.attn_int8_fwd_schedule(w.B, w.H, w.Hkv, w.Lq, w.Lkv, w.d, w.causal)
@@ -155,7 +160,8 @@ def cpu_baseline(w, q, k, v, target_s, index_softmax=None):
             "seconds": round(dt, 3),
             "sample": "%d of %d query rows (seeded uniform sample), INT8 attention step only "
                       "(quantization excluded)%s, %d host threads"
-                      % (rows.size, total_rows, ", IndexSoftmax" if index_softmax else "", nth)}
+                      % (rows.size, total_rows, ", IndexSoftmax" if index_softmax else ", INT4 Q.K codes" if q4 else "",
+                         nth)}
 
 
 def main():
@@ -196,27 +202,48 @@ def main():
         print("IndexSoftmax takes V scales constant along the keys; workload %s has per-token V"
               % w.name, file=sys.stderr)
         sys.exit(2)
-    fused_q = args.q_path == "fused" and not lut     # the IndexSoftmax forward takes INT8 Q
+    q4 = args.qk == "int4"
+    if lut and q4:
+        print("IndexSoftmax and INT4 Q.K are separate forwards", file=sys.stderr)
+        sys.exit(2)
+    fused_q = args.q_path == "fused" and not lut and not q4   # these forwards take INT8 codes of Q
+    if q4:
+        kh = torch.empty(dk.shape[:-1] + (d // 2,), dtype=torch.uint8, device="cuda")   # packed 4-bit K
+        ws_n = m.attn_int4qk_fwd_workspace_size(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
+        ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda") if ws_n else None
     if w.kv_cache:
         assert w.v_per_token, "an appendable cache has per-token V scales"
         # the cache holds every token; each step re-appends the newest one
         # (position Lkv - 1) with the same values
-        m.attn_quantize_rows(dk, 1, kh, sk)
+        if q4:
+            m.attn_quantize_rows_int4(dk, codes=False, packed=kh, scales=sk)
+        else:
+            m.attn_quantize_rows(dk, 1, kh, sk)
         m.attn_quantize_rows(dv, 1, vh, sv)
         k_new, v_new = dk[:, :, -1:].contiguous(), dv[:, :, -1:].contiguous()
 
     def quantize():
-        if not fused_q:
+        if q4:
+            m.attn_quantize_rows_int4(dq, codes=qh, packed=False, scales=sq)
+        elif not fused_q:
             m.attn_quantize_rows(dq, 1, qh, sq)
         if w.kv_cache:
-            m.attn_kv_append(k_new, kh, sk, w.Lkv - 1)
+            if q4:
+                m.attn_kv_append_int4(k_new, kh, sk, w.Lkv - 1)
+            else:
+                m.attn_kv_append(k_new, kh, sk, w.Lkv - 1)
             m.attn_kv_append(v_new, vh, sv, w.Lkv - 1)
             return
-        m.attn_quantize_rows(dk, 1, kh, sk)
+        if q4:
+            m.attn_quantize_rows_int4(dk, codes=False, packed=kh, scales=sk)
+        else:
+            m.attn_quantize_rows(dk, 1, kh, sk)
         m.attn_quantize_rows(dv, rps_v, vh, sv)
 
     def attend():
-        if lut:
+        if q4:
+            m.attn_int4qk_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+        elif lut:
             m.attn_int8_fwd_index_softmax(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, lut_args[0],
                                           lut_args[1], out=o, workspace=ws)
         elif fused_q:
@@ -251,7 +278,7 @@ def main():
     value = ops / (step_ms * 1e-3) / 1e12
     kernel_tops = ops / (attn_ms * 1e-3) / 1e12
     tile, split = m.attn_int8_fwd_schedule(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
-    kv_bytes = 2 * w.B * w.Hkv * w.Lkv * d + 4 * 2 * w.B * w.Hkv * w.Lkv
+    kv_bytes = (1.5 if q4 else 2) * w.B * w.Hkv * w.Lkv * d + 4 * 2 * w.B * w.Hkv * w.Lkv
     q_bytes = q.nbytes if fused_q else q.size + 4 * w.B * w.H * w.Lq
     o_bytes = w.B * w.H * w.Lq * d * (2 if w.o_dtype == "f16" else 4)
     attn_bytes = q_bytes + kv_bytes + o_bytes      # compulsory HBM bytes
@@ -260,6 +287,8 @@ def main():
     if not fused_q:
         quantized.append(q)
     quant_bytes = sum(x.nbytes + x.size + 4 * (x.size // d) for x in quantized)
+    if q4:      # K's codes are half a byte each
+        quant_bytes -= quantized[0].size // 2
     if not w.v_per_token:
         quant_bytes += v.nbytes - 4 * (v.size // d) + 4
 
@@ -280,8 +309,10 @@ def main():
         kfiles = ["attn_fwd.hip", "cdna4_ops.h", "attn_internal.h"]
     if lut:
         roof["kernel"] += " (IndexSoftmax)"
-    roof["traffic"] = measured_traffic(w.name + ("_index_softmax" if lut else "" if fused_q else "_separate_q"),
-                                       kfiles)
+    if q4:
+        roof["kernel"] += " (INT4 Q.K, packed K)" if decode else " (INT4 Q.K: K widened, then the INT8 kernel)"
+    roof["traffic"] = measured_traffic(w.name + ("_index_softmax" if lut else "_int4qk" if q4 else ""
+                                                 if fused_q else "_separate_q"), kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
 
@@ -298,8 +329,10 @@ def main():
                    "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
                    "kv_cache": bool(w.kv_cache),
                    "softmax": "index_softmax(b=%d, c=%g)" % lut_args if lut else "exp",
+                   "qk": args.qk,
                    "step": ("attention only" if args.attn_only else
-                            ("append the new token's K,V to the INT8 cache" if w.kv_cache else "quantize K,V")
+                            ("append the new token's K,V to the %s cache" % ("INT4-K/INT8-V" if q4 else "INT8")
+             if w.kv_cache else "quantize K,V")
                             + (" + fused attention (Q quantized in the kernel)" if fused_q else
                                " + quantize Q + fused attention"))},
         "roofline": roof,
@@ -309,7 +342,7 @@ def main():
                     if quant_ms > 0 and not args.attn_only else None},
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, lut_args)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, lut_args, q4)
     print(json.dumps(out), flush=True)
 
 

@@ -111,6 +111,39 @@ attn_status attn_quantize_cols(const void* x, attn_dtype x_dt, int64_t n_groups,
                                int32_t n_cols, int8_t* q, float* scales, void* stream);
 
 /*
+ * attn_quantize_rows_int4 — per-token symmetric 4-bit quantization for INT4
+ * Q.K ("INT-FlashAttention: Enabling Flash Attention for INT8 Quantization",
+ * abstract: the token-level scheme carries over to INT4; "IntAttention", §2.1
+ * related work: Q.K in INT4 with the value path kept at higher precision is
+ * nearly lossless). The quantizer of IntAttention §2.1 Eq. 3 with 7 levels
+ * per side instead of 127: per row with absmax a, s = a / 7, r = 7 / a
+ * (correctly rounded fp32 divisions), code = clamp(rne(x * r), -7, 7); a == 0
+ * gives s = 0 and codes 0.
+ *
+ *   x       [n_rows, n_cols] of x_dt (fp32 or fp16), device, 16-byte aligned.
+ *   codes   [n_rows, n_cols] int8 output (values -7..7), 8-byte aligned, or NULL.
+ *   packed  [n_rows, n_cols / 2] bytes output, 4-byte aligned, or NULL: per
+ *           group of 8 columns, byte j holds code[j] + 8 in its low nibble and
+ *           code[j + 4] + 8 in its high nibble (nibble n stands for n - 8).
+ *   scales  [n_rows] fp32 output, 4-byte aligned.
+ *   At least one of codes and packed. n_cols a multiple of 8, at most 2048
+ *   (else ATTN_ERR_UNSUPPORTED).
+ */
+attn_status attn_quantize_rows_int4(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int8_t* codes,
+                                    uint8_t* packed, float* scales, void* stream);
+
+/*
+ * attn_kv_append_int4 — attn_kv_append for a packed 4-bit K cache (INT4
+ * Q.K): the codes and scales of attn_quantize_rows_int4 for the T new tokens
+ * x [B, Hkv, T, d] written into rows pos .. pos + T - 1 of every (b, kv head)
+ * of cache4 [B, Hkv, L_max, d / 2] (4-byte aligned) and scales
+ * [B, Hkv, L_max]; no other row is touched. Argument rules as
+ * attn_kv_append.
+ */
+attn_status attn_kv_append_int4(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
+                                uint8_t* cache4, float* scales, int32_t L_max, int32_t pos, void* stream);
+
+/*
  * attn_kv_append — per-token INT8 quantization of new K or V tokens straight
  * into their rows of an INT8 cache (quantize-on-append; the per-token
  * quantizer of IntAttention §2.1 Eq. 3 with the token-level granularity of the
@@ -243,6 +276,32 @@ attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const
  * HOST buffer table[2^lut_bits]. Same parameter checks; no GPU work.
  */
 attn_status attn_index_softmax_table(int32_t lut_bits, float clip, uint8_t* table);
+
+/*
+ * attn_int4qk_fwd — the forward with K in packed 4-bit codes (INT4 Q.K; see
+ * attn_quantize_rows_int4 for the passages, the codes and the packed layout).
+ * gfx950 has no INT4 matrix instruction, so the codes are widened to INT8 for
+ * the same INT8 products: S_int = sum_c q_c k_c exactly, everything after it
+ * as attn_int8_fwd (the same schedule).
+ *
+ *   q    int8 [B, H, Lq, d] (codes of attn_quantize_rows_int4, -7..7 for INT4
+ *        Q.K; any int8 codes give the exact product)   s_q fp32 [B, H, Lq]
+ *   k4   packed [B, Hkv, Lkv, d / 2] bytes, 16-byte aligned   s_k fp32 [B, Hkv, Lkv]
+ *   v, s_v, v_mode, o, o_dt, lse, shapes, causal: as attn_int8_fwd.
+ *   workspace: at least attn_int4qk_fwd_workspace_size(...) bytes, 256-byte
+ *        aligned. Decode-shaped problems read the packed codes directly (the
+ *        split-KV partials as for attn_int8_fwd); other shapes first widen K
+ *        into the workspace (B Hkv Lkv d bytes) and run the INT8 kernel.
+ */
+attn_status attn_int4qk_fwd(const int8_t* q, const float* s_q, const uint8_t* k4, const float* s_k, const int8_t* v,
+                            const float* s_v, attn_vscale v_mode, void* o, attn_dtype o_dt, float* lse, int32_t B,
+                            int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_int4qk_fwd_workspace_size — bytes of workspace attn_int4qk_fwd needs
+ * (0 for invalid problems, which attn_int4qk_fwd then reports). */
+size_t attn_int4qk_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                      int32_t causal);
 
 /*
  * attn_int8_fwd_workspace_size — bytes of device workspace attn_int8_fwd needs

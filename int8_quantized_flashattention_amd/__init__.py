@@ -25,6 +25,11 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 SIGNATURES = {
     "attn_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _P]),
     "attn_quantize_cols": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I32, _P, _P, _P]),
+    "attn_quantize_rows_int4": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _P, _P, _P, _P]),
+    "attn_int4qk_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
+                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "attn_int4qk_fwd_workspace_size": (_SZ, [_I32] * 7),
+    "attn_kv_append_int4": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_kv_append": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
@@ -135,6 +140,56 @@ def attn_quantize_cols(x, rows_per_group, q=None, scales=None, stream=None):
                                  rows_per_group, n_cols, _ptr(q), _ptr(scales), _stream(stream))
     _check("attn_quantize_cols", st)
     return q, scales
+
+
+def attn_quantize_rows_int4(x, codes=True, packed=True, scales=None, stream=None):
+    """Per-token 4-bit quantization of x (fp16/fp32, last axis = row). codes
+    and packed: True (allocate), False (skip) or an output tensor. Returns
+    (codes int8 like x or None, packed uint8 [..., d/2] or None, scales fp32
+    [n_rows])."""
+    _dev(x, "x")
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    n_cols = x.shape[-1]
+    n_rows = x.numel() // n_cols
+    c = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is True else codes
+    p = torch.empty(tuple(x.shape[:-1]) + (n_cols // 2,), dtype=torch.uint8, device=x.device) \
+        if packed is True else packed
+    for t, n, dt in ((c, "codes", torch.int8), (p, "packed", torch.uint8)):
+        if t is not None and t is not False:
+            _dev(t, n, dt)
+    c = c if c is not False else None
+    p = p if p is not False else None
+    if scales is None:
+        scales = torch.empty(n_rows, dtype=torch.float32, device=x.device)
+    _dev(scales, "scales", torch.float32)
+    if scales.numel() != n_rows:
+        raise ValueError("scales must hold one value per row")
+    st = _lib.attn_quantize_rows_int4(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32, n_rows, n_cols,
+                                      _ptr(c), _ptr(p), _ptr(scales), _stream(stream))
+    _check("attn_quantize_rows_int4", st)
+    return c, p, scales
+
+
+def attn_kv_append_int4(x, cache4, scales, pos, stream=None):
+    """Per-token 4-bit codes of new tokens x [B,Hkv,T,d] (fp16/fp32) packed
+    into rows pos .. pos+T-1 of cache4 [B,Hkv,L_max,d/2] (uint8) and scales
+    [B,Hkv,L_max]."""
+    _dev(x, "x")
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    _dev(cache4, "cache4", torch.uint8)
+    _dev(scales, "scales", torch.float32)
+    B, Hkv, T, d = x.shape
+    if cache4.dim() != 4 or tuple(cache4.shape[:2]) != (B, Hkv) or cache4.shape[3] != d // 2:
+        raise ValueError("cache4 must be [B, Hkv, L_max, d/2] matching x")
+    L_max = cache4.shape[2]
+    if scales.numel() != B * Hkv * L_max:
+        raise ValueError("scales must hold B * Hkv * L_max values")
+    st = _lib.attn_kv_append_int4(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32, B, Hkv, T, d,
+                                  _ptr(cache4), _ptr(scales), L_max, int(pos), _stream(stream))
+    _check("attn_kv_append_int4", st)
+    return cache4, scales
 
 
 def attn_kv_append(x, cache, scales, pos, stream=None):
@@ -291,6 +346,51 @@ def attn_index_softmax_table(lut_bits=5, clip=6.6):
     return bytes(buf)[:1 << int(lut_bits)]
 
 
+def attn_int4qk_fwd(q, s_q, k4, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16, return_lse=False,
+                    out=None, lse=None, workspace=None, stream=None):
+    """The forward with K in packed 4-bit codes k4 [B,Hkv,Lkv,d/2] (uint8;
+    attn_quantize_rows_int4) and INT8 codes q. Other arguments as
+    attn_int8_fwd."""
+    _dev(q, "q", torch.int8)
+    _dev(s_q, "s_q", torch.float32)
+    _dev(k4, "k4", torch.uint8)
+    _dev(v, "v", torch.int8)
+    for t, n in ((s_k, "s_k"), (s_v, "s_v")):
+        _dev(t, n, torch.float32)
+    B, H, Lq, d = q.shape
+    Hkv, Lkv = v.shape[1], v.shape[2]
+    if tuple(k4.shape) != (B, Hkv, Lkv, d // 2) or tuple(v.shape) != (B, Hkv, Lkv, d):
+        raise ValueError("k4 must be [B, Hkv, Lkv, d/2] and v [B, Hkv, Lkv, d], matching q")
+    if s_q.numel() != B * H * Lq or s_k.numel() != B * Hkv * Lkv:
+        raise ValueError("s_q / s_k sizes do not match q / k4")
+    mode = _vmode(v_per_token)
+    if s_v.numel() != {ATTN_VSCALE_PER_TENSOR: 1, ATTN_VSCALE_PER_TOKEN: B * Hkv * Lkv,
+                       ATTN_VSCALE_PER_HEAD: B * Hkv, ATTN_VSCALE_PER_CHANNEL: B * Hkv * d}.get(mode, -1):
+        raise ValueError("s_v size does not match the V scale mode")
+    if o_dtype not in (torch.float16, torch.float32):
+        raise TypeError("o_dtype must be float16 or float32")
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=o_dtype, device=q.device)
+    _dev(out, "out", o_dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    need = int(_lib.attn_int4qk_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, int(causal)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.attn_int4qk_fwd(_ptr(q), _ptr(s_q), _ptr(k4), _ptr(s_k), _ptr(v), _ptr(s_v), mode, _ptr(out),
+                              ATTN_F16 if o_dtype == torch.float16 else ATTN_F32, _ptr(lse), B, H, Hkv, Lq, Lkv, d,
+                              int(causal), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("attn_int4qk_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_int4qk_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal):
+    return int(_lib.attn_int4qk_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, int(causal)))
+
+
 def attn_int8_debug_logits(q, k, causal, out=None, stream=None):
     """INT32 logits of every visible pair from the prefill kernel's tile code;
     masked pairs keep out's previous contents (out defaults to zeros)."""
@@ -317,7 +417,8 @@ def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, re
     return attn_int8_fwd_qfloat(q, kh, sk, vh, sv, v_per_token, causal, o_dtype, return_lse)
 
 
-__all__ = ["attn_quantize_rows", "attn_quantize_cols", "attn_kv_append", "attn_int8_fwd", "attn_int8_fwd_qfloat",
+__all__ = ["attn_quantize_rows", "attn_quantize_cols", "attn_quantize_rows_int4", "attn_kv_append",
+           "attn_int4qk_fwd", "attn_int4qk_fwd_workspace_size", "attn_kv_append_int4", "attn_int8_fwd", "attn_int8_fwd_qfloat",
            "attn_int8_fwd_index_softmax", "attn_index_softmax_table", "attn_int8_fwd_workspace_size",
            "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
            "AttnError", "LIB_PATH", "SIGNATURES"]

@@ -124,6 +124,35 @@ attn_status attn_quantize_cols(const void* x, attn_dtype x_dt, int64_t n_groups,
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_quantize_rows_int4(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int8_t* codes,
+                                    uint8_t* packed, float* scales, void* stream) {
+  if (!x || !scales || (!codes && !packed)) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (n_rows < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
+  if (n_cols % 8 != 0 || n_cols > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if ((n_rows + 3) / 4 > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || (codes && !aligned(codes, 8)) || (packed && !aligned(packed, 4)) || !aligned(scales, 4))
+    return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_quantize_int4(x, x_dt == ATTN_F16, n_rows, n_cols, codes, packed, scales,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_kv_append_int4(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
+                                uint8_t* cache4, float* scales, int32_t L_max, int32_t pos, void* stream) {
+  if (!x || !cache4 || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || L_max < 1 || pos < 0 || T > L_max - pos)
+    return ATTN_ERR_INVALID_ARG;
+  if (d % 8 != 0 || d > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t{B} * Hkv * L_max * d > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(cache4, 4) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_append_int4(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache4,
+                                                scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
                            int8_t* cache, float* scales, int32_t L_max, int32_t pos, void* stream) {
   if (!x || !cache || !scales) return ATTN_ERR_INVALID_ARG;
@@ -136,6 +165,17 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
   const hipError_t e = attn::launch_append(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache,
                                            scales, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_int4qk_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                      int32_t causal) {
+  if (check_shape(B, H, Hkv, Lq, Lkv, d, causal) != ATTN_OK) return 0;
+  int tile, split, dec;
+  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
+  if (dec) return attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
+  // prefill shapes: K unpacked to INT8 codes
+  const int64_t bytes = int64_t{B} * Hkv * Lkv * d;
+  return static_cast<size_t>((bytes + 255) / 256 * 256);
 }
 
 size_t attn_int8_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
@@ -236,6 +276,50 @@ attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const
   if (!lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
   return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
                     B, H, Hkv, Lq, Lkv, d, causal, lut_bits, clip, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_int4qk_fwd(const int8_t* q, const float* s_q, const uint8_t* k4, const float* s_k, const int8_t* v,
+                            const float* s_v, attn_vscale v_mode, void* o, attn_dtype o_dt, float* lse, int32_t B,
+                            int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !s_q || !k4 || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
+  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN && v_mode != ATTN_VSCALE_PER_HEAD &&
+      v_mode != ATTN_VSCALE_PER_CHANNEL)
+    return ATTN_ERR_INVALID_ARG;
+  if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
+  if (s != ATTN_OK) return s;
+  if (!aligned(q, 16) || !aligned(k4, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(s_q, 4) || !aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4)))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_int4qk_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ATTN_ERR_INVALID_ARG;
+
+  attn::FwdArgs a{};
+  a.q = q; a.s_q = s_q; a.k = reinterpret_cast<const int8_t*>(k4); a.s_k = s_k; a.v = v; a.s_v = s_v;
+  a.o = o; a.lse = lse; a.s_dump = nullptr;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
+  a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN);
+  a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.v_per_channel = (v_mode == ATTN_VSCALE_PER_CHANNEL);
+  a.o_f16 = (o_dt == ATTN_F16);
+  a.workspace = workspace;
+  int tile, split, dec;
+  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dec) {
+    a.k_int4 = 1;                      // the decode kernel reads the packed codes itself
+    e = attn::launch_decode(a, split, st);
+  } else {
+    // prefill shapes: unpack K into the workspace, then the INT8 kernel
+    e = attn::launch_unpack_int4(k4, int64_t{B} * Hkv * Lkv * d / 2, static_cast<int8_t*>(workspace), st);
+    if (e == hipSuccess) {
+      a.k = static_cast<const int8_t*>(workspace);
+      a.workspace = nullptr;
+      e = attn::launch_prefill(a, st);
+    }
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_index_softmax_table(int32_t lut_bits, float clip, uint8_t* table) {

@@ -86,6 +86,12 @@ struct DLanes {
 template <int D>
 using KRegs = v4i[NB * (D / 64)];
 
+// Packed 4-bit K (INT4 Q.K): the same operands at 8 bytes each. A key row is
+// d / 2 bytes; in each group of 8 channels, byte j holds channel j in its low
+// nibble and channel j + 4 in its high nibble, both stored as code + 8 (1..15).
+template <int D>
+using KRegs4 = v2i[NB * (D / 64)];
+
 // After a wait that covered a slot's loads: passing the slot through an empty
 // asm statement makes that point its definition for the compiler, which then
 // adds no wait of its own before the MFMAs that read it.
@@ -93,6 +99,22 @@ template <int D>
 __device__ __forceinline__ void landed(KRegs<D>& kr) {
 #pragma unroll
   for (int i = 0; i < NB * (D / 64); ++i) asm volatile("" : "+v"(kr[i]));
+}
+template <int D>
+__device__ __forceinline__ void landed(KRegs4<D>& kr) {
+#pragma unroll
+  for (int i = 0; i < NB * (D / 64); ++i) {
+    double t = __builtin_bit_cast(double, kr[i]);    // a 64-bit register pair
+    asm volatile("" : "+v"(t));
+    kr[i] = __builtin_bit_cast(v2i, t);
+  }
+}
+
+// 16 packed channels -> the 16 biased codes (1..15) of an INT8 operand: low
+// nibbles are channels 0..3 of each 8-channel group, high nibbles 4..7.
+__device__ __forceinline__ v4i unpack4(v2i p) {
+  const int m = 0x0F0F0F0F;
+  return v4i{p.x & m, (p.x >> 4) & m, p.y & m, (p.y >> 4) & m};
 }
 
 // Loads per tile issued by the (single) wavefront (all count in vmcnt).
@@ -119,6 +141,18 @@ __device__ __forceinline__ void request_k(KRegs<D>& kr, __amdgpu_buffer_rsrc_t r
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int c = 0; c < NC; ++c) kr[kb * NC + c] = buf_load16(rk, ln.kg[kb & 1] + 8 * D * (kb >> 1) + 64 * c, soff);
+}
+
+// packed K operands of the tile at key k0 into a register slot (d / 2 bytes per key)
+template <int D>
+__device__ __forceinline__ void request_k(KRegs4<D>& kr, __amdgpu_buffer_rsrc_t rk, const DLanes<D>& ln, int k0) {
+  constexpr int NC = D / 64;
+  const uint32_t soff = static_cast<uint32_t>(k0) * (D / 2);
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kr[kb * NC + c] = buf_load8(rk, ln.kg[kb & 1] / 2 + 4 * D * (kb >> 1) + 32 * c, soff);
 }
 
 // x of lane l ^ 16 (ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 within 32
@@ -154,10 +188,13 @@ __device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, 
 
 // LUT: IndexSoftmax (table lookup) in place of the exp2 softmax; only with
 // V scales constant along the keys (per tensor, head or channel) and INT8 Q.
-template <int D, bool CAUSAL, bool VPT, bool QF, bool LUT>
+// K4: K packed at 4 bits (INT4 Q.K); the biased codes k + 8 enter the MFMA
+// and its accumulator starts at -8 sum_c q_c, so S_int is exact.
+template <int D, bool CAUSAL, bool VPT, bool QF, bool LUT, bool K4>
 // two wavefronts per SIMD (registers <= 256): the LDS ring allows six per CU
 __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
+  static_assert(!K4 || (!LUT && !QF), "packed K with the exp softmax and INT8 Q");
   constexpr int NC = D / 64;
   constexpr int NCB = D / 16;
   constexpr int NL = loads_per_tile<D, VPT>();
@@ -187,7 +224,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   const int s1 = min(kv_end, s0 + split_len);
   const int n_tiles = s1 > s0 ? (s1 - s0 + BN - 1) / BN : 0;
 
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_base * D, a.Lkv * D);
+  const __amdgpu_buffer_rsrc_t rk = K4 ? make_rsrc(a.k + kv_base * (D / 2), a.Lkv * (D / 2))
+                                      : make_rsrc(a.k + kv_base * D, a.Lkv * D);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_base * D, a.Lkv * D);
   const __amdgpu_buffer_rsrc_t rsk = make_rsrc(a.s_k + kv_base, a.Lkv * 4);
   const __amdgpu_buffer_rsrc_t rsv = make_rsrc(VPT ? a.s_v + kv_base : a.s_k + kv_base, a.Lkv * 4);
@@ -232,7 +270,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   // key Lkv, where every lane's offset lies outside the buffers, so it fetches
   // nothing (the loads return 0). Unconditional loads keep the compiler's own
   // register waits exact.
-  KRegs<D> kr[2];                          // K operands, slot t % 2 holds tile t
+  std::conditional_t<K4, KRegs4<D>, KRegs<D>> kr[2];   // K operands, slot t % 2 holds tile t
   const int k_first = n_tiles > 0 ? s0 : a.Lkv, k_second = n_tiles > 1 ? s0 + BN : a.Lkv;
   request_vs<D, VPT>(sm[0], rv, rsk, rsv, ln, lane, k_first);
   request_k<D>(kr[0], rk, ln, k_first);
@@ -269,6 +307,16 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
 
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
   const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);   // base-2 logit per S_int s_K
+  // packed K: the QK accumulator starts at -8 sum_c q_c (the codes' bias)
+  int s_init = 0;
+  if constexpr (K4) {
+    int qs = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs = __builtin_amdgcn_sdot4(qf[c][i], 0x01010101, qs, false);
+    s_init = -8 * static_cast<int>(row_sum4(static_cast<float>(qs)));
+  }
   // IndexSoftmax: table index per unit of u below the running max of u
   const float kap = (sq * inv_sqrt_d) * a.lut_k;
   const float nf = static_cast<float>(a.lut_n);
@@ -301,11 +349,14 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
     // S^T = K_hat . Q_hat^T, exact INT32
     v4i s[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) s[kb] = zero4();
+    for (int kb = 0; kb < NB; ++kb) s[kb] = K4 ? v4i{s_init, s_init, s_init, s_init} : zero4();
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) s[kb] = mfma16(kr[S][kb * NC + c], qf[c], s[kb]);
+      for (int kb = 0; kb < NB; ++kb) {
+        if constexpr (K4) s[kb] = mfma16(unpack4(kr[S][kb * NC + c]), qf[c], s[kb]);
+        else s[kb] = mfma16(kr[S][kb * NC + c], qf[c], s[kb]);
+      }
     request_k<D>(kr[S], rk, ln, kq);
 
     // u = S_int s_K[j], -inf past the chunk end or the causal limit; key
@@ -525,16 +576,18 @@ template <int D, bool CAUSAL, bool VPT>
 hipError_t launch_dec(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
   if (a.q_float)
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, true, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, true, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+  else if (a.k_int4)
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false, false, true>), grid, dim3(64), 0, st, a, split_len, n_split);
   else
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dec_lut(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
-  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, false, false, true>), grid, dim3(64), 0, st, a, split_len, n_split);
+  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, false, false, true, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   return hipGetLastError();
 }
 

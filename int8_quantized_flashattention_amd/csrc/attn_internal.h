@@ -22,6 +22,7 @@ struct FwdArgs {
   int causal, v_per_token, o_f16;
   int v_per_head;      // s_v holds one scale per (batch, kv head)
   int v_per_channel;   // s_v holds one scale per (batch, kv head, channel)
+  int k_int4;          // k holds packed 4-bit codes (d / 2 bytes per key)
   void* workspace;
   // IndexSoftmax: lut_n = 2^b - 1 (0: exp softmax), lut_k = (2^b - 1) / c in
   // fp32, lut_w = the table's bytes (entry i at byte i), zero from byte
@@ -65,6 +66,14 @@ hipError_t launch_append(const void* x, int x_f16, int64_t segments, int t_new, 
 constexpr int kMaxQuantCols = 2048;
 hipError_t launch_quantize_cols(const void* x, int x_f16, int64_t n_groups, int64_t rows_per_group, int n_cols,
                                 int8_t* q, float* scales, hipStream_t st);
+// per-token 4-bit codes (int8 codes and / or packed nibbles) and scales
+hipError_t launch_quantize_int4(const void* x, int x_f16, int64_t n_rows, int n_cols, int8_t* codes,
+                                uint8_t* packed, float* scales, hipStream_t st);
+// per-token packed 4-bit codes of new rows into their rows of a packed cache
+hipError_t launch_append_int4(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max, int pos,
+                              uint8_t* cache4, float* scales, hipStream_t st);
+// packed 4-bit codes (n_bytes, a multiple of 4) -> int8 codes (2 n_bytes)
+hipError_t launch_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t st);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t st);
 hipError_t launch_debug_logits(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const FwdArgs& a, int split_len, hipStream_t st);

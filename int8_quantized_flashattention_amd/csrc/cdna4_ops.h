@@ -80,6 +80,9 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, u
 }
 // 16 bytes per lane from a raw buffer into registers (zero where the offset
 // lies outside the buffer)
+__device__ __forceinline__ v2i buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }

@@ -298,6 +298,102 @@ hipError_t run_cols(const void* x, int64_t n_groups, int64_t rows, int n_cols, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Per-token 4-bit codes (INT4 Q.K): s = a / 7, r = 7 / a, code = clamp(rne(x
+// r), -7, 7); int8 codes and / or the packed form (per 8-channel group, byte
+// j = (code[j] + 8) | (code[j + 4] + 8) << 4). A team of T lanes per row, CH
+// chunks of 8 values per lane.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int code4(float x, float r) {
+  const float t = fminf(7.0f, fmaxf(-7.0f, __builtin_rintf(__fmul_rn(x, r))));
+  return static_cast<int>(t);
+}
+
+template <bool F16, int T, int CH, bool MAP>
+__global__ __launch_bounds__(kThreads) void quantize_rows4(const void* __restrict__ x, int64_t n_rows, int n_cols,
+                                                           int8_t* __restrict__ codes, uint8_t* __restrict__ packed,
+                                                           float* __restrict__ scales, RowMap map) {
+  constexpr int kTeams = kThreads / T;
+  const int tl = threadIdx.x % T;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kTeams + threadIdx.x / T;
+  const int n_chunks = n_cols / kChunk;
+  Chunk8 c[CH];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ci = tl + i * T;
+    if (row < n_rows && ci < n_chunks) {
+      c[i] = load_chunk<F16>(x, row * n_cols + static_cast<int64_t>(ci) * kChunk);
+      a = fmaxf(a, chunk_absmax(c[i]));
+    }
+  }
+#pragma unroll
+  for (int off = T / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, T));
+  if (row >= n_rows) return;
+  const int64_t go = MAP ? (row / map.seg_in) * map.seg_out + map.off + row % map.seg_in : row;
+  const float r = a == 0.0f ? 0.0f : __fdiv_rn(7.0f, a);
+  if (tl == 0) scales[go] = a == 0.0f ? 0.0f : __fdiv_rn(a, 7.0f);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ci = tl + i * T;
+    if (ci >= n_chunks) continue;
+    int k[kChunk];
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) k[e] = code4(c[i].x[e], r);
+    if (codes) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        w[h] = (k[4 * h] & 0xff) | ((k[4 * h + 1] & 0xff) << 8) | ((k[4 * h + 2] & 0xff) << 16) |
+               (static_cast<uint32_t>(k[4 * h + 3] & 0xff) << 24);
+      *reinterpret_cast<uint2*>(codes + go * n_cols + static_cast<int64_t>(ci) * kChunk) = make_uint2(w[0], w[1]);
+    }
+    if (packed) {
+      uint32_t p = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p |= static_cast<uint32_t>((k[j] + 8) | ((k[j + 4] + 8) << 4)) << (8 * j);
+      *reinterpret_cast<uint32_t*>(packed + go * (n_cols / 2) + static_cast<int64_t>(ci) * 4) = p;
+    }
+  }
+}
+
+template <bool F16, int T, int CH>
+hipError_t run4(const void* x, int64_t n_rows, int n_cols, int8_t* codes, uint8_t* packed, float* s, hipStream_t st,
+                const RowMap* map) {
+  constexpr int kTeams = kThreads / T;
+  const int64_t blocks = (n_rows + kTeams - 1) / kTeams;
+  if (map)
+    hipLaunchKernelGGL((quantize_rows4<F16, T, CH, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
+                       x, n_rows, n_cols, codes, packed, s, *map);
+  else
+    hipLaunchKernelGGL((quantize_rows4<F16, T, CH, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       st, x, n_rows, n_cols, codes, packed, s, RowMap{1, 1, 0});
+  return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t run_int4(const void* x, int64_t n_rows, int n_cols, int8_t* codes, uint8_t* packed, float* s,
+                    hipStream_t st, const RowMap* map = nullptr) {
+  const int n_chunks = n_cols / kChunk;
+  if (n_chunks <= 8) return run4<F16, 8, 1>(x, n_rows, n_cols, codes, packed, s, st, map);
+  if (n_chunks <= 16) return run4<F16, 16, 1>(x, n_rows, n_cols, codes, packed, s, st, map);
+  if (n_chunks <= 32) return run4<F16, 32, 1>(x, n_rows, n_cols, codes, packed, s, st, map);
+  if (n_chunks <= 64) return run4<F16, 64, 1>(x, n_rows, n_cols, codes, packed, s, st, map);
+  return run4<F16, 64, 4>(x, n_rows, n_cols, codes, packed, s, st, map);
+}
+
+// packed 4-bit codes -> int8 codes, 8 per packed word: nibble n is code n - 8
+// (per byte: set bit 7, subtract 8, clear bit 7 again: no borrow crosses bytes)
+__global__ void unpack_int4(const uint32_t* __restrict__ packed, int64_t n_words, uint2* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += stride) {
+    const uint32_t w = packed[i];
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    out[i] = make_uint2(((lo | 0x80808080u) - 0x08080808u) ^ 0x80808080u,
+                        ((hi | 0x80808080u) - 0x08080808u) ^ 0x80808080u);
+  }
+}
+
 template <bool F16, int T, int CH, int G>
 hipError_t run_small(const void* x, int64_t n_groups, int64_t ge, int8_t* q, float* s, hipStream_t st,
                      const RowMap* map = nullptr) {
@@ -364,6 +460,28 @@ hipError_t launch_quantize_cols(const void* x, int x_f16, int64_t n_groups, int6
                                 int8_t* q, float* scales, hipStream_t st) {
   return x_f16 ? run_cols<true>(x, n_groups, rows_per_group, n_cols, q, scales, st)
                : run_cols<false>(x, n_groups, rows_per_group, n_cols, q, scales, st);
+}
+
+hipError_t launch_quantize_int4(const void* x, int x_f16, int64_t n_rows, int n_cols, int8_t* codes,
+                                uint8_t* packed, float* scales, hipStream_t st) {
+  return x_f16 ? run_int4<true>(x, n_rows, n_cols, codes, packed, scales, st)
+               : run_int4<false>(x, n_rows, n_cols, codes, packed, scales, st);
+}
+
+hipError_t launch_append_int4(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max, int pos,
+                              uint8_t* cache4, float* scales, hipStream_t st) {
+  const RowMap map{t_new, l_max, pos};
+  const int64_t n_rows = segments * t_new;
+  return x_f16 ? run_int4<true>(x, n_rows, n_cols, nullptr, cache4, scales, st, &map)
+               : run_int4<false>(x, n_rows, n_cols, nullptr, cache4, scales, st, &map);
+}
+
+hipError_t launch_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t st) {
+  const int64_t n_words = n_bytes / 4;
+  const int64_t blocks = std::min<int64_t>((n_words + 255) / 256, 8192);
+  hipLaunchKernelGGL(unpack_int4, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(packed), n_words, reinterpret_cast<uint2*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max,

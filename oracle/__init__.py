@@ -37,6 +37,7 @@ def _bind(L):
     L.oracle_float_to_half.argtypes = [P, P, I64]
     L.oracle_quantize_rows.argtypes = [P, F, I64, I32, I64, P, P]
     L.oracle_quantize_cols.argtypes = [P, F, I64, I64, I32, P, P]
+    L.oracle_quantize_rows_int4.argtypes = [P, F, I64, I32, P, P]
     L.oracle_logits_i32.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, F]
     FL = ctypes.c_float
     L.oracle_attn_int8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
@@ -46,7 +47,7 @@ def _bind(L):
                                          P, P]
     L.oracle_index_softmax_lut.argtypes = [I32, FL, P]
     L.oracle_attn_ref_f64.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P, F]
-    for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows", "oracle_quantize_cols",
+    for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows", "oracle_quantize_cols", "oracle_quantize_rows_int4",
                "oracle_logits_i32", "oracle_attn_int8", "oracle_attn_int8_trace",
                "oracle_attn_ref_f64", "oracle_index_softmax_lut"):
         getattr(L, fn).restype = ctypes.c_int
@@ -95,6 +96,23 @@ def quantize_rows(x, rows_per_scale=1, L=None):
                  np.float32)
     _check((L or lib()).oracle_quantize_rows(_p(x), int(is_half), n_rows, n_cols, rows_per_scale,
                                              _p(q), _p(s)), "quantize_rows")
+    return q, s
+
+
+def quantize_rows_int4(x, L=None):
+    """Per-token symmetric 4-bit quantization: codes in [-7, 7] (int8 array
+    like x) and scales absmax / 7 [n_rows]."""
+    x = np.ascontiguousarray(x)
+    n_cols = x.shape[-1]
+    n_rows = x.size // n_cols
+    if x.dtype == np.float16:
+        src, is_half = x.view(np.uint16), 1
+    else:
+        src, is_half = np.ascontiguousarray(x, np.float32), 0
+    q = np.empty(x.shape, np.int8)
+    s = np.empty(n_rows, np.float32)
+    _check((L or lib()).oracle_quantize_rows_int4(_p(src), is_half, n_rows, n_cols, _p(q), _p(s)),
+           "quantize_rows_int4")
     return q, s
 
 
@@ -201,5 +219,5 @@ def attn_ref_f64(q, k, v, B, H, Hkv, Lq, Lkv, d, causal, rows=None, nthreads=0, 
     return o
 
 
-__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "quantize_cols", "logits_i32", "index_softmax_lut", "attn_int8",
+__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "quantize_rows_int4", "quantize_cols", "logits_i32", "index_softmax_lut", "attn_int8",
            "attn_int8_trace", "attn_ref_f64"]

@@ -131,7 +131,10 @@ uint16_t float_to_half_bits(float x) {
 // Symmetric INT8 quantization of one group (IA §2.1, Eq. 3; IFA abstract for
 // the token-level granularity).
 // ---------------------------------------------------------------------------
-void quantize_group(const float* x, int64_t n, int8_t* q, float* s_out) {
+// qmax = 2^(bits - 1) - 1: 127 for INT8; 7 for the 4-bit codes of INT4 Q.K
+// (the same symmetric form with 7 levels on each side; INT-FlashAttention's
+// abstract names INT4 as a format the scheme carries over to).
+void quantize_group(const float* x, int64_t n, int8_t* q, float* s_out, float qmax = 127.0f) {
   float a = 0.0f;
   for (int64_t i = 0; i < n; ++i) a = std::max(a, std::fabs(x[i]));
   if (a == 0.0f) {
@@ -139,13 +142,13 @@ void quantize_group(const float* x, int64_t n, int8_t* q, float* s_out) {
     for (int64_t i = 0; i < n; ++i) q[i] = 0;
     return;
   }
-  const float s = a / 127.0f;   // stored scale: X ~ s * X_hat
-  const float r = 127.0f / a;   // multiplier applied to every element
+  const float s = a / qmax;     // stored scale: X ~ s * X_hat
+  const float r = qmax / a;     // multiplier applied to every element
   *s_out = s;
   for (int64_t i = 0; i < n; ++i) {
     const float y = x[i] * r;                  // one rounded fp32 multiply
     float t = PLANT("quant_round_away") ? std::round(y) : std::nearbyint(y);
-    t = std::min(127.0f, std::max(-127.0f, t));
+    t = std::min(qmax, std::max(-qmax, t));
     q[i] = static_cast<int8_t>(t);
   }
 }
@@ -532,6 +535,21 @@ int oracle_quantize_rows(const void* x, int x_is_half, int64_t n_rows, int32_t n
 int oracle_index_softmax_lut(int32_t bits, float c, int32_t* lut) {
   if (bits < 1 || bits > 8 || !(c > 0.0f) || !std::isfinite(c)) return 1;
   index_softmax_lut(bits, c, lut);
+  return 0;
+}
+
+// Per-token 4-bit codes (values in [-7, 7], one int8 each) and scales a / 7.
+int oracle_quantize_rows_int4(const void* x, int x_is_half, int64_t n_rows, int32_t n_cols, int8_t* q,
+                              float* scales) {
+  if (n_rows < 1 || n_cols < 1) return 1;
+  std::vector<float> buf(static_cast<size_t>(n_cols));
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int32_t c = 0; c < n_cols; ++c) {
+      const int64_t e = r * n_cols + c;
+      buf[c] = x_is_half ? half_bits_to_float(static_cast<const uint16_t*>(x)[e]) : static_cast<const float*>(x)[e];
+    }
+    quantize_group(buf.data(), n_cols, q + r * n_cols, scales + r, PLANT("q4_qmax_8") ? 8.0f : 7.0f);
+  }
   return 0;
 }
 

@@ -9,6 +9,10 @@
 //                     B H Hkv Lq Lkv d causal bits clip  o.out lse.out
 //   emu_driver lut    bits clip  table.out
 //   emu_driver qcols  x.bin dt n_groups rows n_cols  q.out s.out
+//   emu_driver q4     x.bin dt n_rows n_cols  codes.out packed.out s.out
+//   emu_driver app4   x.bin dt B Hkv T d L_max pos  cache4.out scales.out
+//   emu_driver fwd4   q.bin sq.bin k4.bin sk.bin v.bin sv.bin vmode odt
+//                     B H Hkv Lq Lkv d causal  o.out lse.out
 //   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out qhat.out sq.out
 //   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
@@ -101,6 +105,53 @@ int main(int argc, char** argv) {
     st = attn_quantize_cols(x, static_cast<attn_dtype>(dt), n_groups, rows, n_cols, q, sc, nullptr);
     write_file(argv[7], q, n);
     write_file(argv[8], sc, size_t(n_groups) * n_cols * 4);
+  } else if (mode == "q4" && argc == 9) {
+    const int dt = std::atoi(argv[3]);
+    const int64_t n_rows = std::atoll(argv[4]);
+    const int32_t n_cols = std::atoi(argv[5]);
+    const size_t n = size_t(n_rows) * n_cols;
+    void* x = read_file(argv[2], n * (dt == ATTN_F16 ? 2 : 4));
+    auto* c = static_cast<int8_t*>(alloc(n));
+    auto* pk = static_cast<uint8_t*>(alloc(n / 2));
+    auto* sc = static_cast<float*>(alloc(size_t(n_rows) * 4));
+    st = attn_quantize_rows_int4(x, static_cast<attn_dtype>(dt), n_rows, n_cols, c, pk, sc, nullptr);
+    write_file(argv[6], c, n);
+    write_file(argv[7], pk, n / 2);
+    write_file(argv[8], sc, size_t(n_rows) * 4);
+  } else if (mode == "app4" && argc == 12) {
+    const int dt = std::atoi(argv[3]);
+    const int B = std::atoi(argv[4]), Hkv = std::atoi(argv[5]), T = std::atoi(argv[6]);
+    const int d = std::atoi(argv[7]), L = std::atoi(argv[8]), pos = std::atoi(argv[9]);
+    void* x = read_file(argv[2], size_t(B) * Hkv * T * d * (dt == ATTN_F16 ? 2 : 4));
+    const size_t nc = size_t(B) * Hkv * L * d / 2, ns = size_t(B) * Hkv * L;
+    auto* c = static_cast<uint8_t*>(alloc(nc));
+    auto* sc = static_cast<float*>(alloc(ns * 4));
+    std::memset(c, 0x63, nc);
+    std::memset(sc, 0x63, ns * 4);
+    st = attn_kv_append_int4(x, static_cast<attn_dtype>(dt), B, Hkv, T, d, c, sc, L, pos, nullptr);
+    write_file(argv[10], c, nc);
+    write_file(argv[11], sc, ns * 4);
+  } else if (mode == "fwd4" && argc == 19) {
+    const int vmode = std::atoi(argv[8]), odt = std::atoi(argv[9]);
+    const int B = std::atoi(argv[10]), H = std::atoi(argv[11]), Hkv = std::atoi(argv[12]);
+    const int Lq = std::atoi(argv[13]), Lkv = std::atoi(argv[14]), d = std::atoi(argv[15]);
+    const int causal = std::atoi(argv[16]);
+    const size_t nq = size_t(B) * H * Lq, nk = size_t(B) * Hkv * Lkv;
+    auto* q = static_cast<int8_t*>(read_file(argv[2], nq * d));
+    auto* sq = static_cast<float*>(read_file(argv[3], nq * 4));
+    auto* k4 = static_cast<uint8_t*>(read_file(argv[4], nk * d / 2));
+    auto* sk = static_cast<float*>(read_file(argv[5], nk * 4));
+    auto* v = static_cast<int8_t*>(read_file(argv[6], nk * d));
+    auto* sv = static_cast<float*>(read_file(argv[7], (vmode == 1 ? nk : vmode == 2 ? size_t(B) * Hkv : vmode == 3 ? size_t(B) * Hkv * d : 1) * 4));
+    const size_t osz = nq * d * (odt == ATTN_F16 ? 2 : 4);
+    void* o = alloc(osz);
+    float* lse = static_cast<float*>(alloc(nq * 4));
+    const size_t ws_n = attn_int4qk_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
+    void* ws = ws_n ? std::aligned_alloc(256, (ws_n + 255) / 256 * 256) : nullptr;
+    st = attn_int4qk_fwd(q, sq, k4, sk, v, sv, static_cast<attn_vscale>(vmode), o, static_cast<attn_dtype>(odt), lse,
+                         B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n, nullptr);
+    write_file(argv[17], o, osz);
+    write_file(argv[18], lse, nq * 4);
   } else if (mode == "lut" && argc == 5) {
     const int bits = std::atoi(argv[2]);
     uint8_t tab[256];

@@ -299,6 +299,13 @@ inline emu_v2i ds_read_tr8_b64(const void* p) {
 // v_med3_f32 for b <= c: the middle value; a NaN first operand gives b
 inline float fmed3(float a, float b, float c) { return std::fmin(std::fmax(a, b), c); }
 
+// v_dot4_i32_i8: signed byte products of a and b, plus c
+inline int sdot4(int a, int b, int c) {
+  for (int i = 0; i < 4; ++i)
+    c += static_cast<int>(static_cast<int8_t>(a >> (8 * i))) * static_cast<int>(static_cast<int8_t>(b >> (8 * i)));
+  return c;
+}
+
 // v_dot4_u32_u8: sum of the four byte products of a and b, plus c
 inline uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) {
   for (int i = 0; i < 4; ++i) c += ((a >> (8 * i)) & 0xffu) * ((b >> (8 * i)) & 0xffu);
@@ -324,6 +331,7 @@ inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); ret
 #define __builtin_amdgcn_cvt_pk_u8_f32(f, b, old) emu::cvt_pk_u8_f32(f, b, old)
 #define __builtin_amdgcn_fmed3f(a, b, c) emu::fmed3(a, b, c)
 #define __builtin_amdgcn_udot4(a, b, c, clamp) emu::udot4(a, b, c)
+#define __builtin_amdgcn_sdot4(a, b, c, clamp) emu::sdot4(a, b, c)
 #define __any(p) emu::wave_any(p)
 #define __builtin_amdgcn_readfirstlane(x) (x)
 typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;

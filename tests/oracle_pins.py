@@ -522,6 +522,30 @@ def pin_attn_per_head_is_per_tensor_per_slice(L):
             assert np.array_equal(o[b, h], o1[0, 0]) and np.array_equal(l[b, h], l1[0, 0])
 
 
+def pin_quant_int4_closed_forms(L):
+    # 4-bit codes, qmax = 7: a hand-worked row with absmax 7 (s = 1, so codes
+    # are rne(x) with ties to even), integer rows (codes = x), a zero row, and
+    # the round-trip bound |x - s q| <= s / 2 on random rows
+    x = np.array([[7, 3.5, -3.5, 0.5, -0.5, 2.5, 1.49, -7.0],
+                  [0, 0, 0, 0, 0, 0, 0, 0],
+                  [-7, -6, -5, -4, 3, 2, 1, 0],
+                  [14, 7, -7, 1, 3, -5, 0, 13]], np.float32)
+    q, s = oracle.quantize_rows_int4(x, L=L)
+    assert q[0].tolist() == [7, 4, -4, 0, 0, 2, 1, -7] and s[0] == 1.0
+    assert not q[1].any() and s[1] == 0.0
+    assert q[2].tolist() == [-7, -6, -5, -4, 3, 2, 1, 0] and s[2] == 1.0
+    assert q[3].tolist() == [7, 4, -4, 0, 2, -2, 0, 6] and s[3] == 2.0     # 14 / 7; 3/2, -5/2 tie to even
+    r = _rng(57)
+    for dt in (np.float32, np.float16):
+        y = (r.standard_normal((300, 64)) * r.uniform(0.01, 50, size=(300, 1))).astype(dt)
+        qy, sy = oracle.quantize_rows_int4(y, L=L)
+        assert qy.min() >= -7 and qy.max() <= 7
+        assert np.all(np.abs(qy).max(axis=1) == 7)
+        err = np.abs(y.astype(np.float64) - sy[:, None].astype(np.float64) * qy)
+        assert np.all(err <= sy[:, None] * (0.5 + 1e-5))
+        assert np.array_equal(sy, (np.abs(y).max(axis=1).astype(np.float32) / np.float32(7)).astype(np.float32))
+
+
 def pin_quant_cols_are_rows_of_the_transpose(L):
     # per-column quantization of a [rows, cols] group is per-row quantization
     # of its transpose (the row quantizer is pinned above)

@@ -189,6 +189,39 @@ def test_quantize_cols_rejects_before_launch():
     assert q(s=A + 2) == INVALID
 
 
+def test_int4_entry_points_reject_before_launch():
+    p = ctypes.c_void_p
+    q4 = lambda **kw: L.attn_quantize_rows_int4(
+        p(kw.get("x", A)), kw.get("dt", 1), kw.get("n_rows", 16), kw.get("n_cols", 64), p(kw.get("c", A)),
+        p(kw.get("pk", A)), p(kw.get("s", A)), None)
+    assert q4(x=None) == INVALID and q4(s=None) == INVALID and q4(c=None, pk=None) == INVALID
+    assert q4(dt=5) == INVALID and q4(n_rows=0) == INVALID and q4(n_cols=0) == INVALID
+    assert q4(n_cols=60) == UNSUPPORTED and q4(n_cols=4096) == UNSUPPORTED
+    assert q4(x=A + 8) == INVALID and q4(c=A + 4) == INVALID and q4(pk=A + 2) == INVALID and q4(s=A + 2) == INVALID
+    ap = lambda **kw: L.attn_kv_append_int4(
+        p(kw.get("x", A)), kw.get("dt", 1), kw.get("B", 2), kw.get("Hkv", 2), kw.get("T", 1), kw.get("d", 128),
+        p(kw.get("c", A)), p(kw.get("s", A)), kw.get("L", 16), kw.get("pos", 15), None)
+    assert ap(x=None) == INVALID and ap(c=None) == INVALID and ap(pos=16) == INVALID and ap(T=0) == INVALID
+    assert ap(d=60) == UNSUPPORTED and ap(B=4096, Hkv=64, L=8192) == UNSUPPORTED
+    assert ap(c=A + 2) == INVALID and ap(x=A + 8) == INVALID
+    f = lambda **kw: L.attn_int4qk_fwd(
+        p(kw.get("q", A)), p(kw.get("sq", A)), p(kw.get("k", A)), p(kw.get("sk", A)), p(kw.get("v", A)),
+        p(kw.get("sv", A)), kw.get("vm", 0), p(kw.get("o", A)), kw.get("odt", 1), None, kw.get("B", 1),
+        kw.get("H", 2), kw.get("Hkv", 1), kw.get("Lq", 8), kw.get("Lkv", 8), kw.get("d", 64), kw.get("causal", 0),
+        p(kw.get("ws", None)), kw.get("wsb", 0), None)
+    for kw in (dict(q=None), dict(k=None), dict(sv=None), dict(o=None), dict(vm=4), dict(odt=3), dict(H=3, Hkv=2),
+               dict(causal=1, Lq=9, Lkv=8), dict(k=A + 8), dict(q=A + 4), dict(sk=A + 2)):
+        assert f(**kw) == INVALID, kw
+    assert f(d=96) == UNSUPPORTED
+    # decode shape without its workspace; prefill shape without room for the widened K
+    assert f(B=1, H=2, Hkv=1, Lq=1, Lkv=4096) == INVALID
+    assert f(B=1, H=1, Hkv=1, Lq=64, Lkv=64) == INVALID
+    assert f(B=1, H=1, Hkv=1, Lq=64, Lkv=64, ws=A, wsb=64 * 64 - 256) == INVALID
+    assert m.attn_int4qk_fwd_workspace_size(1, 1, 1, 64, 64, 64, 0) == 64 * 64
+    assert m.attn_int4qk_fwd_workspace_size(2, 8, 2, 1, 700, 128, 0) == \
+        m.attn_int8_fwd_workspace_size(2, 8, 2, 1, 700, 128, 0) > 0
+
+
 def test_debug_logits_rejects_before_launch():
     p = ctypes.c_void_p
     f = lambda **kw: L.attn_int8_debug_logits(

@@ -259,3 +259,67 @@ def test_emulated_attention_index_softmax(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, 
     assert np.abs(o - oo).max() <= tol * max(1.0, np.abs(oo).max())
     assert np.linalg.norm(o - oo) / np.linalg.norm(oo) <= (1e-3 if odt == F16 else 1e-5)
     assert np.abs(lse - lo).max() <= 1e-5 * max(1.0, np.abs(lo).max())
+
+
+@pytest.mark.parametrize("rows,cols,dt", [(7, 64, np.float16), (257, 128, np.float32), (3, 2048, np.float16),
+                                          (33, 24, np.float32), (100, 512, np.float16)])
+def test_emulated_quantize_int4(exe, tmp_path, rows, cols, dt):
+    import int4_format
+    r = np.random.Generator(np.random.PCG64(rows * 3 + cols))
+    x = (r.standard_normal((rows, cols)) * r.uniform(0.01, 40.0, size=(rows, 1))).astype(dt)
+    x[min(2, rows - 1)] = 0
+    out = [os.path.join(str(tmp_path), n) for n in ("c.out", "p.out", "s.out")]
+    run(exe, tmp_path, ["q4", put(tmp_path, "x.bin", x), F16 if dt == np.float16 else F32, rows, cols, *out])
+    qo, so = oracle.quantize_rows_int4(x)
+    assert np.array_equal(np.fromfile(out[0], np.int8).reshape(x.shape), qo)
+    assert np.array_equal(np.fromfile(out[1], np.uint8).reshape(rows, cols // 2), int4_format.pack(qo))
+    assert np.array_equal(np.fromfile(out[2], np.uint32), so.view(np.uint32))
+
+
+def test_emulated_kv_append_int4(exe, tmp_path):
+    import int4_format
+    B, Hkv, T, d, L, pos = 2, 3, 4, 128, 20, 9
+    r = np.random.Generator(np.random.PCG64(44))
+    x = r.standard_normal((B, Hkv, T, d)).astype(np.float16)
+    out = [os.path.join(str(tmp_path), n) for n in ("c.out", "s.out")]
+    run(exe, tmp_path, ["app4", put(tmp_path, "x.bin", x), F16, B, Hkv, T, d, L, pos, *out])
+    cache = np.fromfile(out[0], np.uint8).reshape(B, Hkv, L, d // 2)
+    sc = np.fromfile(out[1], np.float32).reshape(B, Hkv, L)
+    qo, so = oracle.quantize_rows_int4(x)
+    assert np.array_equal(cache[:, :, pos:pos + T], int4_format.pack(qo))
+    assert np.array_equal(sc[:, :, pos:pos + T].reshape(-1).view(np.uint32), so.view(np.uint32))
+    keep = np.ones(L, bool)
+    keep[pos:pos + T] = False
+    assert np.all(cache[:, :, keep] == 0x63) and np.all(sc[:, :, keep].view(np.uint32) == 0x63636363)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vmode,odt", [
+    (2, 8, 2, 1, 700, 128, 0, 0, F32), (1, 4, 1, 4, 520, 64, 1, 1, F16), (1, 16, 1, 1, 333, 128, 0, 3, F32),
+    (2, 4, 2, 77, 130, 128, 1, 0, F32), (1, 3, 3, 300, 300, 64, 1, 2, F16),
+])
+def test_emulated_attention_int4qk(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, vmode, odt):
+    # decode shapes read the packed codes in the kernel; prefill shapes widen
+    # them into the workspace first; both equal the oracle on the 4-bit codes
+    import int4_format
+    r = np.random.Generator(np.random.PCG64(B * 500 + Lq * 3 + Lkv))
+    q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
+    q[0, 0, 0] = 0
+    k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    qh, sq = oracle.quantize_rows_int4(q)
+    kh, sk = oracle.quantize_rows_int4(k)
+    if vmode == 3:
+        vh, sv = oracle.quantize_cols(v, Lkv)
+    else:
+        vh, sv = oracle.quantize_rows(v, {0: v.size // d, 1: 1, 2: Lkv}[vmode])
+    oo_p, lo_p = os.path.join(str(tmp_path), "o.out"), os.path.join(str(tmp_path), "l.out")
+    files = [put(tmp_path, n + ".bin", a) for n, a in
+             (("q", qh), ("sq", sq), ("k", int4_format.pack(kh)), ("sk", sk), ("v", vh), ("sv", sv))]
+    run(exe, tmp_path, ["fwd4", *files, vmode, odt, B, H, Hkv, Lq, Lkv, d, causal, oo_p, lo_p])
+    o = np.fromfile(oo_p, np.float16 if odt == F16 else np.float32).astype(np.float32).reshape(B, H, Lq, d)
+    lse = np.fromfile(lo_p, np.float32).reshape(B, H, Lq)
+    import int8_quantized_flashattention_amd as m
+    tile, split = m.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, vmode, B, H, Hkv, Lq, Lkv, d, causal, tile, split)
+    assert np.abs(o - oo).max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
+    assert np.abs(lse - lo).max() <= 1e-4 * max(1.0, np.abs(lo).max())
