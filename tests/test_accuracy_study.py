@@ -18,6 +18,8 @@ attention for
           (Q H)(K H)^T = Q K^T, which spreads outlier channels over all of d
   lut-b-c int8 with IndexSoftmax (IntAttention §3.1-3.2) in place of exp: a
           2^b-entry table over distances clipped at c (oracle)
+  q4k4    INT4 Q.K: Q and K in per-token 4-bit codes (absmax / 7), V INT8
+          per tensor (oracle); q4k4-had the same after the Hadamard rotation
 
 The comparison formats are written here in numpy; each is pinned before use:
 the e4m3 rounding against brute force over all codes, and the numpy INT8 loop
@@ -195,6 +197,14 @@ def errors(inputs):
         qh, sq = oracle.quantize_rows(q, 1)
         kh, sk = oracle.quantize_rows(k, 1)
         vh, sv = oracle.quantize_rows(v, v.size // D)
+        q4, s4 = oracle.quantize_rows_int4(q)
+        k4, t4 = oracle.quantize_rows_int4(k)
+        o, _ = oracle.attn_int8(q4, s4, k4, t4, vh, sv, 0, B, H, H, L, L, D, True, TILE, 0)
+        e["q4k4"] = rel(o.reshape(exact.shape), exact)
+        q4, s4 = oracle.quantize_rows_int4(np.ascontiguousarray((q @ hd).astype(np.float32)))
+        k4, t4 = oracle.quantize_rows_int4(np.ascontiguousarray((k @ hd).astype(np.float32)))
+        o, _ = oracle.attn_int8(q4, s4, k4, t4, vh, sv, 0, B, H, H, L, L, D, True, TILE, 0)
+        e["q4k4-had"] = rel(o.reshape(exact.shape), exact)
         for b, c in ((5, 6.6), (8, 6.6), (5, 5.5)):
             o, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 0, B, H, H, L, L, D, True, TILE, 0,
                                     index_softmax=(b, float(np.float32(c))))
@@ -246,3 +256,12 @@ def test_index_softmax_clip_must_zero_the_last_entry(errors):
     assert oracle.index_softmax_lut(5, np.float32(5.5))[-1] == 1
     assert oracle.index_softmax_lut(5, np.float32(6.6))[-1] == 0
     assert errors["outlier"]["lut-5-5.5"] > 5 * errors["outlier"]["lut-5-6.6"]
+
+
+def test_int4_qk_costs_accuracy_and_rotation_recovers_outliers(errors):
+    # 7 levels per side instead of 127: INT4 Q.K is several times the INT8
+    # path's error; the Hadamard rotation more than halves it with outlier
+    # channels (where the per-token scale is set by the outlier)
+    for name in ("gauss", "outlier"):
+        assert 3 * errors[name]["int8"] < errors[name]["q4k4"] < 0.5, name
+    assert errors["outlier"]["q4k4-had"] < 0.5 * errors["outlier"]["q4k4"]
