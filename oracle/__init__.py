@@ -38,6 +38,8 @@ def _bind(L):
     L.oracle_quantize_rows.argtypes = [P, F, I64, I32, I64, P, P]
     L.oracle_quantize_cols.argtypes = [P, F, I64, I64, I32, P, P]
     L.oracle_quantize_rows_int4.argtypes = [P, F, I64, I32, P, P]
+    L.oracle_quantize_rows_hadamard.argtypes = [P, F, I64, I32, I32, P, P]
+    L.oracle_hadamard_rows.argtypes = [P, I64, I32, P]
     L.oracle_logits_i32.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, F]
     FL = ctypes.c_float
     L.oracle_attn_int8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
@@ -47,7 +49,7 @@ def _bind(L):
                                          P, P]
     L.oracle_index_softmax_lut.argtypes = [I32, FL, P]
     L.oracle_attn_ref_f64.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, I32, P, I64, P, F]
-    for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows", "oracle_quantize_cols", "oracle_quantize_rows_int4",
+    for fn in ("oracle_half_to_float", "oracle_float_to_half", "oracle_quantize_rows", "oracle_quantize_cols", "oracle_quantize_rows_int4", "oracle_quantize_rows_hadamard", "oracle_hadamard_rows",
                "oracle_logits_i32", "oracle_attn_int8", "oracle_attn_int8_trace",
                "oracle_attn_ref_f64", "oracle_index_softmax_lut"):
         getattr(L, fn).restype = ctypes.c_int
@@ -113,6 +115,33 @@ def quantize_rows_int4(x, L=None):
     s = np.empty(n_rows, np.float32)
     _check((L or lib()).oracle_quantize_rows_int4(_p(src), is_half, n_rows, n_cols, _p(q), _p(s)),
            "quantize_rows_int4")
+    return q, s
+
+
+def hadamard_rows(x, L=None):
+    """Each row (last axis, a power of two) times the normalized Hadamard
+    matrix, by the fast transform in fp32."""
+    x = np.ascontiguousarray(x, np.float32)
+    y = np.empty_like(x)
+    n = x.shape[-1]
+    _check((L or lib()).oracle_hadamard_rows(_p(x), x.size // n, n, _p(y)), "hadamard_rows")
+    return y
+
+
+def quantize_rows_hadamard(x, bits=8, L=None):
+    """Rows rotated by the normalized Hadamard matrix, then per-token codes
+    (bits 8: [-127, 127]; bits 4: [-7, 7]) and scales."""
+    x = np.ascontiguousarray(x)
+    n_cols = x.shape[-1]
+    n_rows = x.size // n_cols
+    if x.dtype == np.float16:
+        src, is_half = x.view(np.uint16), 1
+    else:
+        src, is_half = np.ascontiguousarray(x, np.float32), 0
+    q = np.empty(x.shape, np.int8)
+    s = np.empty(n_rows, np.float32)
+    _check((L or lib()).oracle_quantize_rows_hadamard(_p(src), is_half, n_rows, n_cols, bits, _p(q), _p(s)),
+           "quantize_rows_hadamard")
     return q, s
 
 
@@ -219,5 +248,5 @@ def attn_ref_f64(q, k, v, B, H, Hkv, Lq, Lkv, d, causal, rows=None, nthreads=0, 
     return o
 
 
-__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "quantize_rows_int4", "quantize_cols", "logits_i32", "index_softmax_lut", "attn_int8",
+__all__ = ["lib", "half_to_float", "float_to_half", "quantize_rows", "quantize_rows_int4", "quantize_rows_hadamard", "hadamard_rows", "quantize_cols", "logits_i32", "index_softmax_lut", "attn_int8",
            "attn_int8_trace", "attn_ref_f64"]

@@ -24,6 +24,8 @@
 //  [FA3]  "FlashAttention-3: Fast and Accurate Attention with Asynchrony and
 //         Low-precision", abstract: tiled attention with the softmax fused
 //         block by block (online softmax).
+//  [FA3] also lists incoherent processing (a Hadamard rotation of Q and K
+//         before low-precision quantization, to spread outliers).
 //  [LLMI8] "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale",
 //         abstract: vector-wise quantization, i.e. one scale per row of the
 //         left operand times one scale per column of the right operand.
@@ -538,6 +540,26 @@ int oracle_index_softmax_lut(int32_t bits, float c, int32_t* lut) {
   return 0;
 }
 
+// Normalized Walsh-Hadamard rotation of one row of n = 2^k values (the
+// "incoherent processing" of the FlashAttention-3 page: an orthogonal
+// rotation of Q and K before quantization spreads outlier channels over the
+// whole row, and (Q H)(K H)^T = Q K^T). Sylvester ordering, H[i][j] =
+// (-1)^popcount(i & j). Computed as the fast transform in fp32: strides
+// h = 1, 2, 4, ..., n / 2; for each pair (a at index e with bit h clear, b at
+// e + h): a <- a + b, b <- a - b; then every value times fl32(1 / sqrt(n)).
+void hadamard_row(float* x, int n) {
+  for (int h = 1; h < n; h <<= 1)
+    for (int e = 0; e < n; ++e) {
+      if (e & h) continue;
+      const float a = x[e], b = x[e + h];
+      x[e] = a + b;
+      x[e + h] = PLANT("fwht_sign") ? b - a : a - b;
+    }
+  const float r = static_cast<float>(1.0 / std::sqrt(static_cast<double>(n)));
+  if (!PLANT("fwht_no_norm"))
+    for (int e = 0; e < n; ++e) x[e] = x[e] * r;
+}
+
 // Per-token 4-bit codes (values in [-7, 7], one int8 each) and scales a / 7.
 int oracle_quantize_rows_int4(const void* x, int x_is_half, int64_t n_rows, int32_t n_cols, int8_t* q,
                               float* scales) {
@@ -549,6 +571,33 @@ int oracle_quantize_rows_int4(const void* x, int x_is_half, int64_t n_rows, int3
       buf[c] = x_is_half ? half_bits_to_float(static_cast<const uint16_t*>(x)[e]) : static_cast<const float*>(x)[e];
     }
     quantize_group(buf.data(), n_cols, q + r * n_cols, scales + r, PLANT("q4_qmax_8") ? 8.0f : 7.0f);
+  }
+  return 0;
+}
+
+// Rows rotated by the normalized Hadamard matrix, then quantized per token
+// with qmax = 127 (bits 8) or 7 (bits 4). n_cols a power of two.
+int oracle_quantize_rows_hadamard(const void* x, int x_is_half, int64_t n_rows, int32_t n_cols, int32_t bits,
+                                  int8_t* q, float* scales) {
+  if (n_rows < 1 || n_cols < 1 || (n_cols & (n_cols - 1)) || (bits != 8 && bits != 4)) return 1;
+  std::vector<float> buf(static_cast<size_t>(n_cols));
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int32_t c = 0; c < n_cols; ++c) {
+      const int64_t e = r * n_cols + c;
+      buf[c] = x_is_half ? half_bits_to_float(static_cast<const uint16_t*>(x)[e]) : static_cast<const float*>(x)[e];
+    }
+    hadamard_row(buf.data(), n_cols);
+    quantize_group(buf.data(), n_cols, q + r * n_cols, scales + r, bits == 8 ? 127.0f : 7.0f);
+  }
+  return 0;
+}
+
+// The rotation alone (fp32 rows in, fp32 rows out), for the pins.
+int oracle_hadamard_rows(const float* x, int64_t n_rows, int32_t n_cols, float* y) {
+  if (n_rows < 1 || n_cols < 1 || (n_cols & (n_cols - 1))) return 1;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    std::copy(x + r * n_cols, x + (r + 1) * n_cols, y + r * n_cols);
+    hadamard_row(y + r * n_cols, n_cols);
   }
   return 0;
 }

@@ -546,6 +546,53 @@ def pin_quant_int4_closed_forms(L):
         assert np.array_equal(sy, (np.abs(y).max(axis=1).astype(np.float32) / np.float32(7)).astype(np.float32))
 
 
+def _sylvester(n):
+    i = np.arange(n)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def pin_hadamard_rotation(L):
+    for n in (8, 64, 128, 512):
+        # basis rows map to the Sylvester rows (-1)^popcount(i & j) / sqrt(n):
+        # each entry is exactly +-fl32(1 / sqrt(n))
+        r = np.float32(1.0 / np.sqrt(n))
+        y = oracle.hadamard_rows(np.eye(n, dtype=np.float32), L=L)
+        assert np.array_equal(y, (_sylvester(n) * r).astype(np.float32)), n
+        # against the dense product (a different algorithm), orthogonality
+        # (the normalized matrix is its own inverse) and norm preservation
+        g = _rng(58 + n)
+        x = (g.standard_normal((20, n)) * g.uniform(0.1, 30, size=(20, 1))).astype(np.float32)
+        yx = oracle.hadamard_rows(x, L=L)
+        ref = x.astype(np.float64) @ _sylvester(n) / np.sqrt(n)
+        assert np.allclose(yx, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+        back = oracle.hadamard_rows(yx, L=L)
+        assert np.allclose(back, x, rtol=1e-5, atol=1e-5 * np.abs(x).max())
+        assert np.allclose(np.linalg.norm(yx, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
+    # the rotated quantizer is the quantizer of the rotated rows, for 8 and 4 bits
+    g = _rng(59)
+    x = g.standard_normal((33, 128)).astype(np.float16)
+    x[0] = 0
+    for bits, quant in ((8, lambda z: oracle.quantize_rows(z, 1, L=L)), (4, lambda z: oracle.quantize_rows_int4(z, L=L))):
+        qh, sh = oracle.quantize_rows_hadamard(x, bits, L=L)
+        qr, sr = quant(oracle.hadamard_rows(x.astype(np.float32), L=L))
+        assert np.array_equal(qh, qr) and np.array_equal(sh.view(np.uint32), sr.view(np.uint32)), bits
+
+
+def pin_hadamard_keeps_attention(L):
+    # (Q H)(K H)^T = Q K^T: exact attention on the rotated Q and K equals the
+    # unrotated one (fp64 reference; the rotation's fp32 rounding only)
+    g = _rng(60)
+    B, H, Lq, Lkv, d = 1, 2, 9, 40, 64
+    q = g.standard_normal((B, H, Lq, d)).astype(np.float32)
+    k = g.standard_normal((B, H, Lkv, d)).astype(np.float32)
+    v = g.standard_normal((B, H, Lkv, d)).astype(np.float32)
+    o1 = oracle.attn_ref_f64(q, k, v, B, H, H, Lq, Lkv, d, True, L=L)
+    o2 = oracle.attn_ref_f64(oracle.hadamard_rows(q, L=L), oracle.hadamard_rows(k, L=L), v, B, H, H, Lq, Lkv, d,
+                             True, L=L)
+    assert np.allclose(o1, o2, rtol=1e-5, atol=1e-5)
+
+
 def pin_quant_cols_are_rows_of_the_transpose(L):
     # per-column quantization of a [rows, cols] group is per-row quantization
     # of its transpose (the row quantizer is pinned above)

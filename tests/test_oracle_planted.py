@@ -12,7 +12,7 @@ from oracle_pins import ALL_PINS
 PLANTS = ["quant_round_away", "drop_sk", "alpha_sign", "no_alpha", "l_no_rescale", "transpose_v",
           "causal_off_by_one", "gqa_wrong_head", "v_head_no_batch", "lut_half_step", "lut_round_index",
           "lut_no_clip", "lut_no_query_scale", "v_channel_no_head", "v_channel_transposed",
-          "cols_no_group", "q4_qmax_8"]
+          "cols_no_group", "q4_qmax_8", "fwht_sign", "fwht_no_norm"]
 
 
 @pytest.mark.parametrize("plant", PLANTS)
