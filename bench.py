@@ -25,7 +25,9 @@ Also reported on the same JSON line:
 
 `--qk int4` times the step with INT4 Q.K: Q and K in per-token 4-bit codes,
 K packed two codes per byte (the decode cache is then a packed K cache), Q
-quantized in its own pass. `--softmax index` times the same step with IndexSoftmax (a 2^b-entry
+quantized in its own pass. `--hadamard` rotates Q and K by the normalized Hadamard matrix as they are
+quantized (outlier handling; the attention is unchanged in exact arithmetic).
+`--softmax index` times the same step with IndexSoftmax (a 2^b-entry
 exponential table, `--lut-bits`, `--lut-clip`) in place of the exp softmax; that
 forward takes INT8 Q, so Q is then quantized in its own pass.
 
@@ -68,6 +70,8 @@ def parse():
                     help="exp softmax, or IndexSoftmax (table lookup; INT8 Q from its own pass)")
     ap.add_argument("--qk", choices=["int8", "int4"], default="int8",
                     help="INT8 Q.K, or INT4 Q.K: 4-bit codes, K packed two per byte (Q from its own pass)")
+    ap.add_argument("--hadamard", action="store_true",
+                    help="rotate Q and K by the normalized Hadamard matrix before quantizing them")
     ap.add_argument("--lut-bits", type=int, default=5, help="IndexSoftmax table bits b")
     ap.add_argument("--lut-clip", type=float, default=6.6, help="IndexSoftmax clipping threshold c")
     ap.add_argument("--attn-only", action="store_true",
@@ -206,7 +210,11 @@ def main():
     if lut and q4:
         print("IndexSoftmax and INT4 Q.K are separate forwards", file=sys.stderr)
         sys.exit(2)
-    fused_q = args.q_path == "fused" and not lut and not q4   # these forwards take INT8 codes of Q
+    rot = args.hadamard
+    if rot and w.kv_cache:
+        print("--hadamard rotates K as it is quantized; the decode cache appends unrotated tokens", file=sys.stderr)
+        sys.exit(2)
+    fused_q = args.q_path == "fused" and not lut and not q4 and not rot   # these take INT8 codes of Q
     if q4:
         kh = torch.empty(dk.shape[:-1] + (d // 2,), dtype=torch.uint8, device="cuda")   # packed 4-bit K
         ws_n = m.attn_int4qk_fwd_workspace_size(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
@@ -223,6 +231,12 @@ def main():
         k_new, v_new = dk[:, :, -1:].contiguous(), dv[:, :, -1:].contiguous()
 
     def quantize():
+        if rot:
+            bits = 4 if q4 else 8
+            m.attn_quantize_rows_hadamard(dq, bits, codes=qh, packed=False, scales=sq)
+            m.attn_quantize_rows_hadamard(dk, bits, codes=False if q4 else kh, packed=kh if q4 else False, scales=sk)
+            m.attn_quantize_rows(dv, rps_v, vh, sv)
+            return
         if q4:
             m.attn_quantize_rows_int4(dq, codes=qh, packed=False, scales=sq)
         elif not fused_q:
@@ -329,7 +343,7 @@ def main():
                    "o_dtype": w.o_dtype, "kv_tile": tile, "kv_split_len": split,
                    "kv_cache": bool(w.kv_cache),
                    "softmax": "index_softmax(b=%d, c=%g)" % lut_args if lut else "exp",
-                   "qk": args.qk,
+                   "qk": args.qk, "hadamard_qk": bool(rot),
                    "step": ("attention only" if args.attn_only else
                             ("append the new token's K,V to the %s cache" % ("INT4-K/INT8-V" if q4 else "INT8")
              if w.kv_cache else "quantize K,V")

@@ -133,6 +133,33 @@ attn_status attn_quantize_rows_int4(const void* x, attn_dtype x_dt, int64_t n_ro
                                     uint8_t* packed, float* scales, void* stream);
 
 /*
+ * attn_quantize_rows_hadamard — per-token quantization of rows first rotated
+ * by the normalized Hadamard matrix H / sqrt(n) (n = n_cols), the "incoherent
+ * processing" of the "FlashAttention-3" page: an orthogonal rotation of Q and
+ * K before low-precision quantization spreads outlier channels over the row,
+ * and (Q H)(K H)^T = Q K^T, so the attention is unchanged in exact
+ * arithmetic. Rotate Q and K (never V); the forwards then take the codes as
+ * usual.
+ *
+ * The rotation is the fast Walsh-Hadamard transform in fp32 with Sylvester
+ * ordering (H[i][j] = (-1)^popcount(i & j)): strides h = 1, 2, 4, ..., n / 2
+ * in that order, each pair (a at index e with bit h clear, b at e + h)
+ * becoming (a + b, a - b), then every value multiplied by fl32(1 / sqrt(n)).
+ * The codes follow attn_quantize_rows (bits = 8, codes in [-127, 127]) or
+ * attn_quantize_rows_int4 (bits = 4, codes and / or the packed layout) on
+ * the rotated values.
+ *
+ *   x       [n_rows, n_cols] of x_dt, device, 16-byte aligned.
+ *   n_cols  a power of two, 8 .. 2048 (else ATTN_ERR_UNSUPPORTED).
+ *   bits    8: codes required, packed must be NULL; 4: codes and / or packed
+ *           (else ATTN_ERR_INVALID_ARG).
+ *   codes   [n_rows, n_cols] int8 (8-byte aligned), packed [n_rows, n_cols / 2]
+ *           (4-byte aligned), scales [n_rows] fp32 (4-byte aligned).
+ */
+attn_status attn_quantize_rows_hadamard(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int32_t bits,
+                                        int8_t* codes, uint8_t* packed, float* scales, void* stream);
+
+/*
  * attn_kv_append_int4 — attn_kv_append for a packed 4-bit K cache (INT4
  * Q.K): the codes and scales of attn_quantize_rows_int4 for the T new tokens
  * x [B, Hkv, T, d] written into rows pos .. pos + T - 1 of every (b, kv head)

@@ -30,6 +30,7 @@ SIGNATURES = {
                                        _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
     "attn_int4qk_fwd_workspace_size": (_SZ, [_I32] * 7),
     "attn_kv_append_int4": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
+    "attn_quantize_rows_hadamard": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I32, _P, _P, _P, _P]),
     "attn_kv_append": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
@@ -168,6 +169,34 @@ def attn_quantize_rows_int4(x, codes=True, packed=True, scales=None, stream=None
     st = _lib.attn_quantize_rows_int4(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32, n_rows, n_cols,
                                       _ptr(c), _ptr(p), _ptr(scales), _stream(stream))
     _check("attn_quantize_rows_int4", st)
+    return c, p, scales
+
+
+def attn_quantize_rows_hadamard(x, bits=8, codes=True, packed=False, scales=None, stream=None):
+    """Rows of x (fp16/fp32, last axis a power of two) rotated by the
+    normalized Hadamard matrix, then per-token codes at 8 or 4 bits. codes /
+    packed: True (allocate), False (skip) or an output tensor (packed only
+    for bits 4). Returns (codes or None, packed or None, scales)."""
+    _dev(x, "x")
+    if x.dtype not in (torch.float16, torch.float32):
+        raise TypeError("x must be float16 or float32")
+    n_cols = x.shape[-1]
+    n_rows = x.numel() // n_cols
+    c = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is True else codes
+    p = torch.empty(tuple(x.shape[:-1]) + (n_cols // 2,), dtype=torch.uint8, device=x.device) \
+        if packed is True else packed
+    c = c if c is not False else None
+    p = p if p is not False else None
+    if c is not None:
+        _dev(c, "codes", torch.int8)
+    if p is not None:
+        _dev(p, "packed", torch.uint8)
+    if scales is None:
+        scales = torch.empty(n_rows, dtype=torch.float32, device=x.device)
+    _dev(scales, "scales", torch.float32)
+    st = _lib.attn_quantize_rows_hadamard(_ptr(x), ATTN_F16 if x.dtype == torch.float16 else ATTN_F32, n_rows,
+                                          n_cols, int(bits), _ptr(c), _ptr(p), _ptr(scales), _stream(stream))
+    _check("attn_quantize_rows_hadamard", st)
     return c, p, scales
 
 
@@ -418,7 +447,7 @@ def int8_attention(q, k, v, causal, v_per_token=False, o_dtype=torch.float16, re
 
 
 __all__ = ["attn_quantize_rows", "attn_quantize_cols", "attn_quantize_rows_int4", "attn_kv_append",
-           "attn_int4qk_fwd", "attn_int4qk_fwd_workspace_size", "attn_kv_append_int4", "attn_int8_fwd", "attn_int8_fwd_qfloat",
+           "attn_int4qk_fwd", "attn_int4qk_fwd_workspace_size", "attn_kv_append_int4", "attn_quantize_rows_hadamard", "attn_int8_fwd", "attn_int8_fwd_qfloat",
            "attn_int8_fwd_index_softmax", "attn_index_softmax_table", "attn_int8_fwd_workspace_size",
            "attn_int8_fwd_schedule", "attn_int8_debug_logits", "attn_status_str", "int8_attention",
            "AttnError", "LIB_PATH", "SIGNATURES"]

@@ -139,6 +139,23 @@ attn_status attn_quantize_rows_int4(const void* x, attn_dtype x_dt, int64_t n_ro
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_quantize_rows_hadamard(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int32_t bits,
+                                        int8_t* codes, uint8_t* packed, float* scales, void* stream) {
+  if (!x || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (bits == 8 ? (!codes || packed) : bits == 4 ? (!codes && !packed) : true) return ATTN_ERR_INVALID_ARG;
+  if (n_rows < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
+  if ((n_cols & (n_cols - 1)) || n_cols < 8 || n_cols > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if ((n_rows + 3) / 4 > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || (codes && !aligned(codes, 8)) || (packed && !aligned(packed, 4)) || !aligned(scales, 4))
+    return ATTN_ERR_INVALID_ARG;
+  const float rn = static_cast<float>(1.0 / std::sqrt(static_cast<double>(n_cols)));
+  const hipError_t e = attn::launch_quantize_rotated(x, x_dt == ATTN_F16, n_rows, n_cols, bits, rn, codes, packed,
+                                                     scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_kv_append_int4(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
                                 uint8_t* cache4, float* scales, int32_t L_max, int32_t pos, void* stream) {
   if (!x || !cache4 || !scales) return ATTN_ERR_INVALID_ARG;

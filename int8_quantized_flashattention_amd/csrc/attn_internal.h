@@ -72,6 +72,10 @@ hipError_t launch_quantize_int4(const void* x, int x_f16, int64_t n_rows, int n_
 // per-token packed 4-bit codes of new rows into their rows of a packed cache
 hipError_t launch_append_int4(const void* x, int x_f16, int64_t segments, int t_new, int n_cols, int l_max, int pos,
                               uint8_t* cache4, float* scales, hipStream_t st);
+// rows rotated by the normalized Hadamard matrix (n_cols = 2^k <= 2048,
+// rn = fl32(1 / sqrt(n_cols))), then per-token codes at 8 or 4 bits
+hipError_t launch_quantize_rotated(const void* x, int x_f16, int64_t n_rows, int n_cols, int bits, float rn,
+                                   int8_t* codes, uint8_t* packed, float* scales, hipStream_t st);
 // packed 4-bit codes (n_bytes, a multiple of 4) -> int8 codes (2 n_bytes)
 hipError_t launch_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t st);
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t st);

@@ -382,6 +382,140 @@ hipError_t run_int4(const void* x, int64_t n_rows, int n_cols, int8_t* codes, ui
   return run4<F16, 64, 4>(x, n_rows, n_cols, codes, packed, s, st, map);
 }
 
+// ---------------------------------------------------------------------------
+// Rows rotated by the normalized Hadamard matrix (n = 2^k columns), then
+// per-token codes at BITS = 8 or 4. A team of T lanes per row, lane tl holding
+// chunks tl + i T (i < CH) of 8 values. The fast transform runs its strides in
+// increasing order, h = 1, 2, 4 inside a chunk, then chunk offsets 1 .. T / 2
+// across lanes (shuffles) and T .. (CH / 2) T inside the lane; each pair
+// becomes (a + b, a - b) with a the lower index, the upper side formed as
+// fma(-1, own, partner) = partner - own, exactly the subtraction. Then every
+// value times rn = fl32(1 / sqrt(n)).
+// ---------------------------------------------------------------------------
+template <bool F16, int T, int CH, int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_rows_rot(const void* __restrict__ x, int64_t n_rows, int n_cols,
+                                                              float rn, int8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ packed, float* __restrict__ scales) {
+  constexpr int kTeams = kThreads / T;
+  const int tl = threadIdx.x % T;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kTeams + threadIdx.x / T;
+  const bool valid = row < n_rows;
+  Chunk8 c[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if (valid) {
+      c[i] = load_chunk<F16>(x, row * n_cols + static_cast<int64_t>(tl + i * T) * kChunk);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) c[i].x[e] = 0.0f;
+    }
+  }
+  // strides 1, 2, 4 inside each chunk
+#pragma unroll
+  for (int h = 1; h < kChunk; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e)
+        if (!(e & h)) {
+          const float a = c[i].x[e], b = c[i].x[e + h];
+          c[i].x[e] = a + b;
+          c[i].x[e + h] = a - b;
+        }
+  // chunk offsets 1 .. T / 2: the partner lane tl ^ m
+#pragma unroll
+  for (int m = 1; m < T; m <<= 1) {
+    const float sgn = (tl & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) {
+        const float p = __shfl_xor(c[i].x[e], m, T);
+        c[i].x[e] = __builtin_fmaf(sgn, c[i].x[e], p);
+      }
+  }
+  // chunk offsets T .. (CH / 2) T: chunks i and i ^ (m / T) of the lane
+#pragma unroll
+  for (int m = 1; m < CH; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (!(i & m)) {
+#pragma unroll
+        for (int e = 0; e < kChunk; ++e) {
+          const float a = c[i].x[e], b = c[i ^ m].x[e];
+          c[i].x[e] = a + b;
+          c[i ^ m].x[e] = a - b;
+        }
+      }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) c[i].x[e] = c[i].x[e] * rn;
+    a = fmaxf(a, chunk_absmax(c[i]));
+  }
+#pragma unroll
+  for (int off = T / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, T));
+  if (!valid) return;
+  if constexpr (BITS == 8) {
+    const float r = quant_recip(a);
+    if (tl == 0) scales[row] = quant_scale(a);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) store_codes(codes, row * n_cols + static_cast<int64_t>(tl + i * T) * kChunk, c[i], r,
+                                             a == 0.0f);
+  } else {
+    const float r = a == 0.0f ? 0.0f : __fdiv_rn(7.0f, a);
+    if (tl == 0) scales[row] = a == 0.0f ? 0.0f : __fdiv_rn(a, 7.0f);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t ci = tl + i * T;
+      int k[kChunk];
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) k[e] = code4(c[i].x[e], r);
+      if (codes) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          w[h] = (k[4 * h] & 0xff) | ((k[4 * h + 1] & 0xff) << 8) | ((k[4 * h + 2] & 0xff) << 16) |
+                 (static_cast<uint32_t>(k[4 * h + 3] & 0xff) << 24);
+        *reinterpret_cast<uint2*>(codes + row * n_cols + ci * kChunk) = make_uint2(w[0], w[1]);
+      }
+      if (packed) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p |= static_cast<uint32_t>((k[j] + 8) | ((k[j + 4] + 8) << 4)) << (8 * j);
+        *reinterpret_cast<uint32_t*>(packed + row * (n_cols / 2) + ci * 4) = p;
+      }
+    }
+  }
+}
+
+template <bool F16, int T, int CH, int BITS>
+hipError_t run_rot(const void* x, int64_t n_rows, int n_cols, float rn, int8_t* codes, uint8_t* packed, float* s,
+                   hipStream_t st) {
+  constexpr int kTeams = kThreads / T;
+  const int64_t blocks = (n_rows + kTeams - 1) / kTeams;
+  hipLaunchKernelGGL((quantize_rows_rot<F16, T, CH, BITS>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     st, x, n_rows, n_cols, rn, codes, packed, s);
+  return hipGetLastError();
+}
+
+template <bool F16, int BITS>
+hipError_t run_rot_n(const void* x, int64_t n_rows, int n_cols, float rn, int8_t* codes, uint8_t* packed, float* s,
+                     hipStream_t st) {
+  switch (n_cols / kChunk) {
+    case 1: return run_rot<F16, 1, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 2: return run_rot<F16, 2, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 4: return run_rot<F16, 4, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 8: return run_rot<F16, 8, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 16: return run_rot<F16, 16, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 32: return run_rot<F16, 32, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 64: return run_rot<F16, 64, 1, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    case 128: return run_rot<F16, 64, 2, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+    default: return run_rot<F16, 64, 4, BITS>(x, n_rows, n_cols, rn, codes, packed, s, st);
+  }
+}
+
 // packed 4-bit codes -> int8 codes, 8 per packed word: nibble n is code n - 8
 // (per byte: set bit 7, subtract 8, clear bit 7 again: no borrow crosses bytes)
 __global__ void unpack_int4(const uint32_t* __restrict__ packed, int64_t n_words, uint2* __restrict__ out) {
@@ -474,6 +608,15 @@ hipError_t launch_append_int4(const void* x, int x_f16, int64_t segments, int t_
   const int64_t n_rows = segments * t_new;
   return x_f16 ? run_int4<true>(x, n_rows, n_cols, nullptr, cache4, scales, st, &map)
                : run_int4<false>(x, n_rows, n_cols, nullptr, cache4, scales, st, &map);
+}
+
+hipError_t launch_quantize_rotated(const void* x, int x_f16, int64_t n_rows, int n_cols, int bits, float rn,
+                                   int8_t* codes, uint8_t* packed, float* scales, hipStream_t st) {
+  if (bits == 8)
+    return x_f16 ? run_rot_n<true, 8>(x, n_rows, n_cols, rn, codes, packed, scales, st)
+                 : run_rot_n<false, 8>(x, n_rows, n_cols, rn, codes, packed, scales, st);
+  return x_f16 ? run_rot_n<true, 4>(x, n_rows, n_cols, rn, codes, packed, scales, st)
+               : run_rot_n<false, 4>(x, n_rows, n_cols, rn, codes, packed, scales, st);
 }
 
 hipError_t launch_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t st) {

@@ -10,6 +10,7 @@
 //   emu_driver lut    bits clip  table.out
 //   emu_driver qcols  x.bin dt n_groups rows n_cols  q.out s.out
 //   emu_driver q4     x.bin dt n_rows n_cols  codes.out packed.out s.out
+//   emu_driver qrot   x.bin dt n_rows n_cols bits  codes.out packed.out s.out
 //   emu_driver app4   x.bin dt B Hkv T d L_max pos  cache4.out scales.out
 //   emu_driver fwd4   q.bin sq.bin k4.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out
@@ -152,6 +153,21 @@ int main(int argc, char** argv) {
                          B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n, nullptr);
     write_file(argv[17], o, osz);
     write_file(argv[18], lse, nq * 4);
+  } else if (mode == "qrot" && argc == 10) {
+    const int dt = std::atoi(argv[3]);
+    const int64_t n_rows = std::atoll(argv[4]);
+    const int32_t n_cols = std::atoi(argv[5]);
+    const int bits = std::atoi(argv[6]);
+    const size_t n = size_t(n_rows) * n_cols;
+    void* x = read_file(argv[2], n * (dt == ATTN_F16 ? 2 : 4));
+    auto* c = static_cast<int8_t*>(alloc(n));
+    auto* pk = static_cast<uint8_t*>(alloc(n / 2));
+    auto* sc = static_cast<float*>(alloc(size_t(n_rows) * 4));
+    st = attn_quantize_rows_hadamard(x, static_cast<attn_dtype>(dt), n_rows, n_cols, bits, c, bits == 4 ? pk : nullptr,
+                                     sc, nullptr);
+    write_file(argv[7], c, n);
+    write_file(argv[8], pk, n / 2);
+    write_file(argv[9], sc, size_t(n_rows) * 4);
   } else if (mode == "lut" && argc == 5) {
     const int bits = std::atoi(argv[2]);
     uint8_t tab[256];

@@ -222,6 +222,21 @@ def test_int4_entry_points_reject_before_launch():
         m.attn_int8_fwd_workspace_size(2, 8, 2, 1, 700, 128, 0) > 0
 
 
+def test_quantize_hadamard_rejects_before_launch():
+    p = ctypes.c_void_p
+    f = lambda **kw: L.attn_quantize_rows_hadamard(
+        p(kw.get("x", A)), kw.get("dt", 1), kw.get("n_rows", 16), kw.get("n_cols", 128), kw.get("bits", 8),
+        p(kw.get("c", A)), p(kw.get("pk", None)), p(kw.get("s", A)), None)
+    assert f(x=None) == INVALID and f(s=None) == INVALID and f(dt=4) == INVALID
+    assert f(c=None) == INVALID                      # bits 8 needs codes
+    assert f(pk=A) == INVALID                        # bits 8 has no packed form
+    assert f(bits=4, c=None) == INVALID              # bits 4 needs codes or packed
+    assert f(bits=5) == INVALID and f(n_rows=0) == INVALID and f(n_cols=0) == INVALID
+    assert f(n_cols=96) == UNSUPPORTED and f(n_cols=4) == UNSUPPORTED and f(n_cols=4096) == UNSUPPORTED
+    assert f(x=A + 8) == INVALID and f(c=A + 4) == INVALID and f(s=A + 2) == INVALID
+    assert f(bits=4, pk=A + 2) == INVALID
+
+
 def test_debug_logits_rejects_before_launch():
     p = ctypes.c_void_p
     f = lambda **kw: L.attn_int8_debug_logits(

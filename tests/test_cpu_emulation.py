@@ -323,3 +323,22 @@ def test_emulated_attention_int4qk(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal,
     oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, vmode, B, H, Hkv, Lq, Lkv, d, causal, tile, split)
     assert np.abs(o - oo).max() <= 2e-2 and np.linalg.norm(o - oo) / np.linalg.norm(oo) <= 1e-2
     assert np.abs(lse - lo).max() <= 1e-4 * max(1.0, np.abs(lo).max())
+
+
+@pytest.mark.parametrize("rows,cols,bits,dt", [(7, 64, 8, np.float16), (257, 128, 8, np.float32), (3, 2048, 8, np.float16),
+                                               (33, 8, 8, np.float32), (100, 1024, 4, np.float16), (65, 128, 4, np.float32),
+                                               (9, 16, 4, np.float16)])
+def test_emulated_quantize_hadamard(exe, tmp_path, rows, cols, bits, dt):
+    # the rotation's butterflies in the oracle's order: codes and scales bit-exact
+    import int4_format
+    r = np.random.Generator(np.random.PCG64(rows * 5 + cols + bits))
+    x = (r.standard_normal((rows, cols)) * r.uniform(0.01, 40.0, size=(rows, 1))).astype(dt)
+    x[:, cols // 3] *= dt(20)                         # an outlier channel
+    x[min(1, rows - 1)] = 0
+    out = [os.path.join(str(tmp_path), n) for n in ("c.out", "p.out", "s.out")]
+    run(exe, tmp_path, ["qrot", put(tmp_path, "x.bin", x), F16 if dt == np.float16 else F32, rows, cols, bits, *out])
+    qo, so = oracle.quantize_rows_hadamard(x, bits)
+    assert np.array_equal(np.fromfile(out[0], np.int8).reshape(x.shape), qo)
+    assert np.array_equal(np.fromfile(out[2], np.uint32), so.view(np.uint32))
+    if bits == 4:
+        assert np.array_equal(np.fromfile(out[1], np.uint8).reshape(rows, cols // 2), int4_format.pack(qo))
