@@ -26,7 +26,8 @@ Also reported on the same JSON line:
 `--qk int4` times the step with INT4 Q.K: Q and K in per-token 4-bit codes,
 K packed two codes per byte (the decode cache is then a packed K cache), Q
 quantized in its own pass. `--hadamard` rotates Q and K by the normalized Hadamard matrix as they are
-quantized (outlier handling; the attention is unchanged in exact arithmetic).
+quantized (outlier handling; the attention is unchanged in exact arithmetic);
+Q is then rotated inside the attention kernels' Q load.
 `--softmax index` times the same step with IndexSoftmax (a 2^b-entry
 exponential table, `--lut-bits`, `--lut-clip`) in place of the exp softmax; that
 forward takes INT8 Q, so Q is then quantized in its own pass.
@@ -214,7 +215,7 @@ def main():
     if rot and w.kv_cache:
         print("--hadamard rotates K as it is quantized; the decode cache appends unrotated tokens", file=sys.stderr)
         sys.exit(2)
-    fused_q = args.q_path == "fused" and not lut and not q4 and not rot   # these take INT8 codes of Q
+    fused_q = args.q_path == "fused" and not lut and not q4   # these take INT8 codes of Q
     if q4:
         kh = torch.empty(dk.shape[:-1] + (d // 2,), dtype=torch.uint8, device="cuda")   # packed 4-bit K
         ws_n = m.attn_int4qk_fwd_workspace_size(w.B, w.H, w.Hkv, w.Lq, w.Lkv, d, w.causal)
@@ -233,7 +234,8 @@ def main():
     def quantize():
         if rot:
             bits = 4 if q4 else 8
-            m.attn_quantize_rows_hadamard(dq, bits, codes=qh, packed=False, scales=sq)
+            if not fused_q:
+                m.attn_quantize_rows_hadamard(dq, bits, codes=qh, packed=False, scales=sq)
             m.attn_quantize_rows_hadamard(dk, bits, codes=False if q4 else kh, packed=kh if q4 else False, scales=sk)
             m.attn_quantize_rows(dv, rps_v, vh, sv)
             return
@@ -261,7 +263,8 @@ def main():
             m.attn_int8_fwd_index_softmax(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, lut_args[0],
                                           lut_args[1], out=o, workspace=ws)
         elif fused_q:
-            m.attn_int8_fwd_qfloat(dq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+            m.attn_int8_fwd_qfloat(dq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws,
+                                   hadamard=rot)
         else:
             m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
 
@@ -325,8 +328,10 @@ def main():
         roof["kernel"] += " (IndexSoftmax)"
     if q4:
         roof["kernel"] += " (INT4 Q.K, packed K)" if decode else " (INT4 Q.K: K widened, then the INT8 kernel)"
-    roof["traffic"] = measured_traffic(w.name + ("_index_softmax" if lut else "_int4qk" if q4 else ""
-                                                 if fused_q else "_separate_q"), kfiles)
+    if rot:
+        roof["kernel"] += " (Hadamard-rotated Q and K)"
+    roof["traffic"] = measured_traffic(w.name + ("_index_softmax" if lut else "_int4qk" if q4 else "_hadamard" if rot
+                                                 else "" if fused_q else "_separate_q"), kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
 

@@ -259,6 +259,22 @@ attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k
                                  void* stream);
 
 /*
+ * attn_int8_fwd_qfloat_hadamard — attn_int8_fwd_qfloat with each Q row first
+ * rotated by the normalized Hadamard matrix inside the kernels' Q load
+ * (incoherent processing, "FlashAttention-3" page), with exactly the
+ * arithmetic of attn_quantize_rows_hadamard (bits = 8): the codes, scales and
+ * O are bit-identical to attn_quantize_rows_hadamard on Q followed by
+ * attn_int8_fwd. K must be quantized with the same rotation
+ * (attn_quantize_rows_hadamard) for the logits to be Q K^T; V is not rotated.
+ * Arguments as attn_int8_fwd_qfloat (q_hat / s_q receive the rotated codes).
+ */
+attn_status attn_int8_fwd_qfloat_hadamard(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
+                                          const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                          attn_dtype o_dt, float* lse, int8_t* q_hat, float* s_q, int32_t B,
+                                          int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_int8_fwd_index_softmax — attn_int8_fwd with IndexSoftmax in place of
  * the exp softmax ("IntAttention: A Fully Integer Attention Pipeline for
  * Efficient Edge Inference", §3.1: the distance to the row max clipped at c

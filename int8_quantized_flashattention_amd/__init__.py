@@ -31,6 +31,9 @@ SIGNATURES = {
     "attn_int4qk_fwd_workspace_size": (_SZ, [_I32] * 7),
     "attn_kv_append_int4": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_quantize_rows_hadamard": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I32, _P, _P, _P, _P]),
+    "attn_int8_fwd_qfloat_hadamard": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P,
+                                                     ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                     _I32, _I32, _P, _SZ, _P]),
     "attn_kv_append": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
@@ -318,11 +321,13 @@ def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.flo
 
 def attn_int8_fwd_qfloat(q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
                          return_lse=False, q_hat=None, s_q=None, out=None, lse=None, workspace=None,
-                         stream=None):
+                         stream=None, hadamard=False):
     """The forward with Q given in fp16/fp32 [B,H,Lq,d]: the kernels quantize
     each Q row per token themselves (the same codes and scales as
     attn_quantize_rows). q_hat (int8 like q) and s_q ([B*H*Lq] fp32), when
-    given, receive them. Returns O (and lse when return_lse)."""
+    given, receive them. hadamard=True rotates each Q row by the normalized
+    Hadamard matrix first (attn_int8_fwd_qfloat_hadamard; K must carry the
+    same rotation). Returns O (and lse when return_lse)."""
     _dev(q, "q")
     if q.dtype not in (torch.float16, torch.float32):
         raise TypeError("q must be float16 or float32")
@@ -336,13 +341,11 @@ def attn_int8_fwd_qfloat(q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.f
         _dev(s_q, "s_q", torch.float32)
         if s_q.numel() != shape[0] * shape[1] * shape[3]:
             raise ValueError("s_q size does not match q")
-    st = _lib.attn_int8_fwd_qfloat(_ptr(q), ATTN_F16 if q.dtype == torch.float16 else ATTN_F32,
-                                   _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
-                                   _vmode(v_per_token),
-                                   _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32,
-                                   _ptr(lse), _ptr(q_hat), _ptr(s_q), *shape, int(causal),
-                                   _ptr(workspace), ws_bytes, _stream(stream))
-    _check("attn_int8_fwd_qfloat", st)
+    fn = _lib.attn_int8_fwd_qfloat_hadamard if hadamard else _lib.attn_int8_fwd_qfloat
+    st = fn(_ptr(q), ATTN_F16 if q.dtype == torch.float16 else ATTN_F32, _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
+            _vmode(v_per_token), _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32, _ptr(lse),
+            _ptr(q_hat), _ptr(s_q), *shape, int(causal), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("attn_int8_fwd_qfloat_hadamard" if hadamard else "attn_int8_fwd_qfloat", st)
     return (out, lse) if return_lse else out
 
 

@@ -223,7 +223,7 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
                        const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
                        attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq,
                        int32_t Lkv, int32_t d, int32_t causal, int32_t lut_bits, float clip,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream, int q_rotate = 0) {
   if (!k || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
   if (lut_bits != 0 && !lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
   if (q_float) {
@@ -257,6 +257,8 @@ attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, a
   a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.v_per_channel = (v_mode == ATTN_VSCALE_PER_CHANNEL);
   a.o_f16 = (o_dt == ATTN_F16);
   a.workspace = workspace;
+  a.q_rotate = q_rotate;
+  a.q_rot_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
   if (lut_bits != 0) {
     uint8_t tab[sizeof(a.lut_w)] = {};
     attn::index_softmax_table(lut_bits, clip, tab);
@@ -281,6 +283,16 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
   if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
   return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
                     B, H, Hkv, Lq, Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_int8_fwd_qfloat_hadamard(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
+                                          const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                          attn_dtype o_dt, float* lse, int8_t* q_hat, float* s_q, int32_t B,
+                                          int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                          int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q) return ATTN_ERR_INVALID_ARG;
+  return fwd_common(nullptr, nullptr, q, q_dt, q_hat, s_q, k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq,
+                    Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream, 1);
 }
 
 attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const int8_t* k,

@@ -190,7 +190,9 @@ __device__ __forceinline__ Partials partials(void* ws, int groups, int n_split, 
 // V scales constant along the keys (per tensor, head or channel) and INT8 Q.
 // K4: K packed at 4 bits (INT4 Q.K); the biased codes k + 8 enter the MFMA
 // and its accumulator starts at -8 sum_c q_c, so S_int is exact.
-template <int D, bool CAUSAL, bool VPT, bool QF, bool LUT, bool K4>
+// QF: 0 INT8 Q; 1 fp16/fp32 Q quantized here; 2 the same after the
+// normalized Hadamard rotation of each Q row.
+template <int D, bool CAUSAL, bool VPT, int QF, bool LUT, bool K4>
 // two wavefronts per SIMD (registers <= 256): the LDS ring allows six per CU
 __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(FwdArgs a, int split_len, int n_split) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
@@ -276,6 +278,47 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   request_k<D>(kr[0], rk, ln, k_first);
   request_vs<D, VPT>(sm[1], rv, rsk, rsv, ln, lane, k_second);
   request_k<D>(kr[1], rk, ln, k_second);
+  if constexpr (QF == 2) {
+    // Hadamard rotation of the row (the rotated quantizer's butterflies, strides
+    // in increasing order): 1 .. 8 inside the lane's 16 channels, 16 and 32
+    // across the row's lane groups (lanes l ^ 16, l ^ 32), 64 across the
+    // lane's 64-channel chunks; then times rn
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (!(e & h)) {
+            const float x0 = xq[c][e], x1 = xq[c][e + h];
+            xq[c][e] = x0 + x1;
+            xq[c][e + h] = x0 - x1;
+          }
+#pragma unroll
+    for (int lm = 16; lm < 64; lm <<= 1) {
+      const float sgn = (lane & lm) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xq[c][e] = __builtin_fmaf(sgn, xq[c][e], __shfl_xor(xq[c][e], lm, 64));
+    }
+#pragma unroll
+    for (int m = 1; m < NC; m <<= 1)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (!(c & m)) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float x0 = xq[c][e], x1 = xq[c ^ m][e];
+            xq[c][e] = x0 + x1;
+            xq[c ^ m][e] = x0 - x1;
+          }
+        }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xq[c][e] = xq[c][e] * a.q_rot_scale;
+  }
   if constexpr (QF) {
     float am = 0.0f;
 #pragma unroll
@@ -575,19 +618,21 @@ __global__ __launch_bounds__(256) void attn_decode_combine(FwdArgs a, int n_spli
 template <int D, bool CAUSAL, bool VPT>
 hipError_t launch_dec(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
-  if (a.q_float)
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, true, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+  if (a.q_float && a.q_rotate)
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, 2, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+  else if (a.q_float)
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, 1, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   else if (a.k_int4)
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false, false, true>), grid, dim3(64), 0, st, a, split_len, n_split);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, 0, false, true>), grid, dim3(64), 0, st, a, split_len, n_split);
   else
-    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, false, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+    hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, VPT, 0, false, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dec_lut(const FwdArgs& a, int split_len, int n_split, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.Hkv * n_split));
-  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, false, false, true, false>), grid, dim3(64), 0, st, a, split_len, n_split);
+  hipLaunchKernelGGL((attn_decode_kernel<D, CAUSAL, false, 0, true, false>), grid, dim3(64), 0, st, a, split_len, n_split);
   return hipGetLastError();
 }
 

@@ -340,7 +340,9 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
 // LUT: 0 exp2 softmax; 1 IndexSoftmax with the byte table; 2 IndexSoftmax
 // with the pair table (tables of at most 32 entries). IndexSoftmax only with
 // V scales constant along the keys (per tensor, head or channel) and INT8 Q.
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16, bool QF, int LUT>
+// QF: 0 INT8 Q; 1 fp16/fp32 Q quantized here; 2 the same after the
+// normalized Hadamard rotation of each Q row.
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16, int QF, int LUT>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
   constexpr int NC = D / 32;
@@ -420,6 +422,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   __syncthreads();
   request_tile<D, true, VPT>(sm[0], bf, ln, wave, lane, 0);
   if (n_tiles > 1) request_tile<D, true, VPT>(sm[1], bf, ln, wave, lane, BN);
+  if constexpr (QF == 2) {
+    // Hadamard rotation of the row (the rotated quantizer's butterflies, strides
+    // in increasing order): 1 .. 8 inside the lane's 16 channels, 16 across the
+    // lane pair, 32 and 64 across the lane's 32-channel chunks; then times rn
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (!(e & h)) {
+            const float x0 = xq[c][e], x1 = xq[c][e + h];
+            xq[c][e] = x0 + x1;
+            xq[c][e + h] = x0 - x1;
+          }
+    const float sgn = g ? -1.0f : 1.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xq[c][e] = __builtin_fmaf(sgn, xq[c][e], __shfl_xor(xq[c][e], 32, 64));
+#pragma unroll
+    for (int m = 1; m < NC; m <<= 1)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (!(c & m)) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float x0 = xq[c][e], x1 = xq[c ^ m][e];
+            xq[c][e] = x0 + x1;
+            xq[c ^ m][e] = x0 - x1;
+          }
+        }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xq[c][e] = xq[c][e] * a.q_rot_scale;
+  }
   if constexpr (QF) {
     float am = 0.0f;
 #pragma unroll
@@ -683,10 +722,12 @@ template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
 hipError_t launch_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
-  if (a.q_float)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, true, 0>), grid, dim3(kThreads), 0, st, a);
+  if (a.q_float && a.q_rotate)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, 2, 0>), grid, dim3(kThreads), 0, st, a);
+  else if (a.q_float)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, 1, 0>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, false, 0>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VPT, OUT_F16, 0, 0>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -695,9 +736,9 @@ hipError_t launch_lut(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
   if (a.lut_n < kLutPairRows - 1)      // n <= 31: entries and the zero slot fit
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, false, 2>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, 0, 2>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, false, 1>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, OUT_F16, 0, 1>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

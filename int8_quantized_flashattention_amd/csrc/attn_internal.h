@@ -23,6 +23,8 @@ struct FwdArgs {
   int v_per_head;      // s_v holds one scale per (batch, kv head)
   int v_per_channel;   // s_v holds one scale per (batch, kv head, channel)
   int k_int4;          // k holds packed 4-bit codes (d / 2 bytes per key)
+  int q_rotate;        // fused Q: rotate each row by the normalized Hadamard matrix first
+  float q_rot_scale;   // fl32(1 / sqrt(d)) for that rotation
   void* workspace;
   // IndexSoftmax: lut_n = 2^b - 1 (0: exp softmax), lut_k = (2^b - 1) / c in
   // fp32, lut_w = the table's bytes (entry i at byte i), zero from byte

@@ -14,7 +14,7 @@
 //   emu_driver app4   x.bin dt B Hkv T d L_max pos  cache4.out scales.out
 //   emu_driver fwd4   q.bin sq.bin k4.bin sk.bin v.bin sv.bin vmode odt
 //                     B H Hkv Lq Lkv d causal  o.out lse.out
-//   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt
+//   emu_driver fwdq   qf.bin qdt k.bin sk.bin v.bin sv.bin vmode odt   (fwdqh: Q rotated first)
 //                     B H Hkv Lq Lkv d causal  o.out lse.out qhat.out sq.out
 //   emu_driver logits q.bin k.bin B H Hkv Lq Lkv d causal  s.out
 //   emu_driver append x.bin dt B Hkv T d L_max pos  cache.out scales.out
@@ -173,7 +173,7 @@ int main(int argc, char** argv) {
     uint8_t tab[256];
     st = attn_index_softmax_table(bits, std::strtof(argv[3], nullptr), tab);
     write_file(argv[4], tab, bits >= 1 && bits <= 8 ? size_t(1) << bits : 0);
-  } else if (mode == "fwdq" && argc == 21) {
+  } else if ((mode == "fwdq" || mode == "fwdqh") && argc == 21) {
     const int qdt = std::atoi(argv[3]);
     const int vmode = std::atoi(argv[8]), odt = std::atoi(argv[9]);
     const int B = std::atoi(argv[10]), H = std::atoi(argv[11]), Hkv = std::atoi(argv[12]);
@@ -192,9 +192,9 @@ int main(int argc, char** argv) {
     float* sq = static_cast<float*>(alloc(nq * 4));
     const size_t ws_n = attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
     void* ws = ws_n ? std::aligned_alloc(256, (ws_n + 255) / 256 * 256) : nullptr;
-    st = attn_int8_fwd_qfloat(qf, static_cast<attn_dtype>(qdt), k, sk, v, sv,
-                              static_cast<attn_vscale>(vmode), o, static_cast<attn_dtype>(odt), lse,
-                              qh, sq, B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n, nullptr);
+    st = (mode == "fwdqh" ? attn_int8_fwd_qfloat_hadamard : attn_int8_fwd_qfloat)(
+        qf, static_cast<attn_dtype>(qdt), k, sk, v, sv, static_cast<attn_vscale>(vmode), o,
+        static_cast<attn_dtype>(odt), lse, qh, sq, B, H, Hkv, Lq, Lkv, d, causal, ws, ws_n, nullptr);
     write_file(argv[17], o, osz);
     write_file(argv[18], lse, nq * 4);
     write_file(argv[19], qh, nq * d);

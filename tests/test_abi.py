@@ -222,6 +222,16 @@ def test_int4_entry_points_reject_before_launch():
         m.attn_int8_fwd_workspace_size(2, 8, 2, 1, 700, 128, 0) > 0
 
 
+def test_fwd_qfloat_hadamard_rejects_before_launch():
+    p = ctypes.c_void_p
+    f = lambda **kw: L.attn_int8_fwd_qfloat_hadamard(
+        p(kw.get("q", A)), kw.get("qdt", 1), p(A), p(A), p(A), p(A), kw.get("vm", 0), p(kw.get("o", A)), 1, None,
+        None, None, 1, 2, 1, kw.get("Lq", 8), kw.get("Lkv", 8), kw.get("d", 64), 0, None, 0, None)
+    assert f(q=None) == INVALID and f(qdt=3) == INVALID and f(o=None) == INVALID and f(vm=4) == INVALID
+    assert f(d=96) == UNSUPPORTED and f(q=A + 8) == INVALID
+    assert f() == INVALID                            # decode shape without its workspace
+
+
 def test_quantize_hadamard_rejects_before_launch():
     p = ctypes.c_void_p
     f = lambda **kw: L.attn_quantize_rows_hadamard(

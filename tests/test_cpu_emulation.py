@@ -342,3 +342,32 @@ def test_emulated_quantize_hadamard(exe, tmp_path, rows, cols, bits, dt):
     assert np.array_equal(np.fromfile(out[2], np.uint32), so.view(np.uint32))
     if bits == 4:
         assert np.array_equal(np.fromfile(out[1], np.uint8).reshape(rows, cols // 2), int4_format.pack(qo))
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,qdt", [
+    (1, 2, 1, 130, 200, 128, 1, np.float16), (2, 3, 3, 65, 65, 64, 0, np.float32),
+    (1, 8, 2, 1, 700, 128, 0, np.float16), (1, 4, 1, 3, 300, 64, 1, np.float32),
+])
+def test_emulated_attention_rotated_float_q(exe, tmp_path, B, H, Hkv, Lq, Lkv, d, causal, qdt):
+    # Q rotated and quantized inside the kernels: the rotated quantizer's codes
+    # and scales, and the same O and lse as the forward fed with them
+    r = np.random.Generator(np.random.PCG64(B * 77 + Lq + Lkv))
+    q = (r.standard_normal((B, H, Lq, d)) * 3).astype(qdt)
+    q[..., 5] *= qdt(20)                               # an outlier channel
+    q[0, 0, min(1, Lq - 1)] = 0
+    k = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    v = r.standard_normal((B, Hkv, Lkv, d)).astype(np.float32)
+    qh, sq = oracle.quantize_rows_hadamard(q, 8)
+    kh, sk = oracle.quantize_rows_hadamard(k, 8)
+    vh, sv = oracle.quantize_rows(v, v.size // d)
+    out = {n: os.path.join(str(tmp_path), n) for n in ("o1", "l1", "o2", "l2", "qh", "sq")}
+    kv = [put(tmp_path, n + ".bin", a) for n, a in (("k", kh), ("sk", sk), ("v", vh), ("sv", sv))]
+    shape = [B, H, Hkv, Lq, Lkv, d, causal]
+    run(exe, tmp_path, ["fwdqh", put(tmp_path, "qf.bin", q), F16 if qdt == np.float16 else F32, *kv,
+                        0, F32, *shape, out["o1"], out["l1"], out["qh"], out["sq"]])
+    run(exe, tmp_path, ["fwd", put(tmp_path, "q.bin", qh), put(tmp_path, "sq.bin", sq), *kv,
+                        0, F32, *shape, out["o2"], out["l2"]])
+    assert np.array_equal(np.fromfile(out["qh"], np.int8).reshape(qh.shape), qh)
+    assert np.array_equal(np.fromfile(out["sq"], np.uint32), sq.view(np.uint32))
+    for a, b in (("o1", "o2"), ("l1", "l2")):
+        assert np.array_equal(np.fromfile(out[a], np.uint32), np.fromfile(out[b], np.uint32))

@@ -84,3 +84,31 @@ def test_rotation_reduces_error_with_outlier_channels(lib):
         errs[name] = float(np.linalg.norm(og - exact) / np.linalg.norm(exact))
     log("relative error vs exact: %s" % errs)
     assert errs["rotated"] < 0.6 * errs["plain"]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,qdt", [
+    (2, 4, 2, 77, 130, 128, 1, np.float16), (1, 3, 3, 300, 300, 64, 0, np.float32),
+    (2, 8, 2, 1, 1500, 128, 0, np.float16), (1, 8, 1, 2, 520, 64, 1, np.float32),
+])
+def test_fused_rotated_q_equals_separate(lib, B, H, Hkv, Lq, Lkv, d, causal, qdt):
+    # Q rotated and quantized in the kernels' Q load: the rotated quantizer's
+    # codes and scales, and O and lse bit for bit those of the forward fed with
+    # them (prefill and split-KV decode shapes)
+    seed = B * 313 + Lq + Lkv
+    q = gaussian((B, H, Lq, d), seed, qdt)
+    q[..., 3] *= qdt(20)
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    qh, sq, qd, _, sqd = rotated_both(lib, q)
+    kh, sk, kd, _, skd = rotated_both(lib, k)
+    vh, sv, vd, svd = quantize_both(lib, v, v.size // d)
+    o1, l1 = lib.attn_int8_fwd(qd, sqd, kd, skd, vd, svd, False, causal, torch.float32, return_lse=True)
+    qh2, sq2 = torch.empty_like(qd), torch.empty_like(sqd)
+    o2, l2 = lib.attn_int8_fwd_qfloat(dev(q), kd, skd, vd, svd, False, causal, torch.float32, return_lse=True,
+                                      q_hat=qh2, s_q=sq2, hadamard=True)
+    assert torch.equal(qh2, qd) and torch.equal(sq2.view(torch.int32), sqd.view(torch.int32))
+    assert torch.equal(o2.view(torch.int32), o1.view(torch.int32))
+    assert torch.equal(l2.view(torch.int32), l1.view(torch.int32))
+    tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
+    oo, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 0, B, H, Hkv, Lq, Lkv, d, causal, tile, split)
+    compare_o(host(o2), oo, "fused rotated Q")
