@@ -184,21 +184,123 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+namespace {
+
+// Workspace of the forward: the split-KV partials for decode shapes; for
+// packed 4-bit K on other shapes, room for K widened to INT8 codes.
+size_t workspace_need(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,
+                      bool k_int4) {
+  int tile, split, dec;
+  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
+  if (dec || !k_int4) return attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
+  const int64_t bytes = int64_t{B} * Hkv * Lkv * d;
+  return static_cast<size_t>((bytes + 255) / 256 * 256);
+}
+
+// One forward request, as the entry points fill it in.
+struct FwdRequest {
+  const int8_t* q = nullptr;           // INT8 Q codes and scales ...
+  const float* s_q = nullptr;
+  const void* q_float = nullptr;       // ... or fp16 / fp32 Q, quantized in the kernels
+  attn_dtype q_dt = ATTN_F32;
+  int8_t* q_hat = nullptr;             // optional outputs of the in-kernel quantization
+  float* s_q_out = nullptr;
+  int q_rotate = 0;                    // rotate the fp16 / fp32 Q rows first (Hadamard)
+  const int8_t* k = nullptr;           // INT8 codes, or packed 4-bit codes when k_int4
+  const float* s_k = nullptr;
+  int k_int4 = 0;
+  const int8_t* v = nullptr;
+  const float* s_v = nullptr;
+  attn_vscale v_mode = ATTN_VSCALE_PER_TENSOR;
+  void* o = nullptr;
+  attn_dtype o_dt = ATTN_F32;
+  float* lse = nullptr;
+  int32_t B = 0, H = 0, Hkv = 0, Lq = 0, Lkv = 0, d = 0, causal = 0;
+  int32_t lut_bits = 0;                // IndexSoftmax table bits (0: exp softmax)
+  float clip = 0.0f;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  void* stream = nullptr;
+};
+
+// Checks every argument, then launches. Nothing is launched on any error.
+attn_status run_fwd(const FwdRequest& r) {
+  if (!r.k || !r.s_k || !r.v || !r.s_v || !r.o) return ATTN_ERR_INVALID_ARG;
+  if (r.lut_bits != 0 && !lut_params_ok(r.lut_bits, r.clip)) return ATTN_ERR_INVALID_ARG;
+  if (r.q_float) {
+    if (r.q_dt != ATTN_F32 && r.q_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(r.q_float, 16) || (r.q_hat && !aligned(r.q_hat, 16)) || (r.s_q_out && !aligned(r.s_q_out, 4)))
+      return ATTN_ERR_INVALID_ARG;
+  } else {
+    if (!r.q || !r.s_q) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(r.q, 16) || !aligned(r.s_q, 4)) return ATTN_ERR_INVALID_ARG;
+  }
+  if (r.v_mode != ATTN_VSCALE_PER_TENSOR && r.v_mode != ATTN_VSCALE_PER_TOKEN &&
+      r.v_mode != ATTN_VSCALE_PER_HEAD && r.v_mode != ATTN_VSCALE_PER_CHANNEL)
+    return ATTN_ERR_INVALID_ARG;
+  if (r.o_dt != ATTN_F32 && r.o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  const attn_status s = check_shape(r.B, r.H, r.Hkv, r.Lq, r.Lkv, r.d, r.causal);
+  if (s != ATTN_OK) return s;
+  // IndexSoftmax kernels take INT8 Q and V scales constant along the keys
+  if (r.lut_bits != 0 && (r.q_float || r.v_mode == ATTN_VSCALE_PER_TOKEN)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(r.k, 16) || !aligned(r.v, 16) || !aligned(r.o, 16)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(r.s_k, 4) || !aligned(r.s_v, 4) || (r.lse && !aligned(r.lse, 4))) return ATTN_ERR_INVALID_ARG;
+  const size_t need = workspace_need(r.B, r.H, r.Hkv, r.Lq, r.Lkv, r.d, r.causal, r.k_int4);
+  if (need > 0 && (!r.workspace || r.workspace_bytes < need || !aligned(r.workspace, 256)))
+    return ATTN_ERR_INVALID_ARG;
+
+  attn::FwdArgs a{};
+  a.q = r.q; a.s_q = r.s_q; a.k = r.k; a.s_k = r.s_k; a.v = r.v; a.s_v = r.s_v;
+  a.q_float = r.q_float; a.q_float_f16 = (r.q_dt == ATTN_F16); a.q_hat_out = r.q_hat; a.s_q_out = r.s_q_out;
+  a.o = r.o; a.lse = r.lse; a.s_dump = nullptr;
+  a.B = r.B; a.H = r.H; a.Hkv = r.Hkv; a.Lq = r.Lq; a.Lkv = r.Lkv; a.d = r.d;
+  a.causal = r.causal; a.v_per_token = (r.v_mode == ATTN_VSCALE_PER_TOKEN);
+  a.v_per_head = (r.v_mode == ATTN_VSCALE_PER_HEAD); a.v_per_channel = (r.v_mode == ATTN_VSCALE_PER_CHANNEL);
+  a.o_f16 = (r.o_dt == ATTN_F16);
+  a.workspace = r.workspace;
+  a.q_rotate = r.q_rotate;
+  a.q_rot_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r.d)));
+  if (r.lut_bits != 0) {
+    uint8_t tab[sizeof(a.lut_w)] = {};
+    attn::index_softmax_table(r.lut_bits, r.clip, tab);
+    std::memcpy(a.lut_w, tab, sizeof(tab));
+    a.lut_n = (1 << r.lut_bits) - 1;
+    a.lut_k = static_cast<float>(static_cast<double>(a.lut_n) / static_cast<double>(r.clip));
+  }
+  int tile, split, dec;
+  attn::fwd_schedule(r.B, r.H, r.Hkv, r.Lq, r.Lkv, r.d, r.causal, &tile, &split, &dec);
+  const hipStream_t st = static_cast<hipStream_t>(r.stream);
+  hipError_t e;
+  if (dec) {
+    a.k_int4 = r.k_int4;               // the decode kernel reads packed codes itself
+    e = attn::launch_decode(a, split, st);
+  } else if (r.k_int4) {
+    // prefill shapes with packed K: widen K into the workspace, then the INT8 kernel
+    e = attn::launch_unpack_int4(reinterpret_cast<const uint8_t*>(r.k), int64_t{r.B} * r.Hkv * r.Lkv * r.d / 2,
+                                 static_cast<int8_t*>(r.workspace), st);
+    if (e == hipSuccess) {
+      a.k = static_cast<const int8_t*>(r.workspace);
+      a.workspace = nullptr;
+      e = attn::launch_prefill(a, st);
+    }
+  } else {
+    e = attn::launch_prefill(a, st);
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
 size_t attn_int4qk_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                                       int32_t causal) {
   if (check_shape(B, H, Hkv, Lq, Lkv, d, causal) != ATTN_OK) return 0;
-  int tile, split, dec;
-  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
-  if (dec) return attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
-  // prefill shapes: K unpacked to INT8 codes
-  const int64_t bytes = int64_t{B} * Hkv * Lkv * d;
-  return static_cast<size_t>((bytes + 255) / 256 * 256);
+  return workspace_need(B, H, Hkv, Lq, Lkv, d, causal, true);
 }
 
 size_t attn_int8_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
                                     int32_t d, int32_t causal) {
   if (check_shape(B, H, Hkv, Lq, Lkv, d, causal) != ATTN_OK) return 0;
-  return attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
+  return workspace_need(B, H, Hkv, Lq, Lkv, d, causal, false);
 }
 
 attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
@@ -216,61 +318,15 @@ attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq
 
 namespace {
 
-// Shared body of attn_int8_fwd and attn_int8_fwd_qfloat (q_float != NULL:
-// float Q, quantized in the kernels).
-attn_status fwd_common(const int8_t* q, const float* s_q, const void* q_float, attn_dtype q_dt,
-                       int8_t* q_hat, float* s_q_out, const int8_t* k, const float* s_k,
-                       const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
-                       attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq,
-                       int32_t Lkv, int32_t d, int32_t causal, int32_t lut_bits, float clip,
-                       void* workspace, size_t workspace_bytes, void* stream, int q_rotate = 0) {
-  if (!k || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
-  if (lut_bits != 0 && !lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
-  if (q_float) {
-    if (q_dt != ATTN_F32 && q_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-    if (!aligned(q_float, 16) || (q_hat && !aligned(q_hat, 16)) || (s_q_out && !aligned(s_q_out, 4)))
-      return ATTN_ERR_INVALID_ARG;
-  } else {
-    if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(s_q, 4)) return ATTN_ERR_INVALID_ARG;
-  }
-  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN && v_mode != ATTN_VSCALE_PER_HEAD &&
-      v_mode != ATTN_VSCALE_PER_CHANNEL)
-    return ATTN_ERR_INVALID_ARG;
-  if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
-  if (s != ATTN_OK) return s;
-  // IndexSoftmax kernels take INT8 Q and V scales constant along the keys
-  if (lut_bits != 0 && (q_float || v_mode == ATTN_VSCALE_PER_TOKEN)) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4))) return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
-    return ATTN_ERR_INVALID_ARG;
-
-  attn::FwdArgs a{};
-  a.q = q; a.s_q = s_q; a.k = k; a.s_k = s_k; a.v = v; a.s_v = s_v;
-  a.q_float = q_float; a.q_float_f16 = (q_dt == ATTN_F16); a.q_hat_out = q_hat; a.s_q_out = s_q_out;
-  a.o = o; a.lse = lse; a.s_dump = nullptr;
-  a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
-  a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN);
-  a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.v_per_channel = (v_mode == ATTN_VSCALE_PER_CHANNEL);
-  a.o_f16 = (o_dt == ATTN_F16);
-  a.workspace = workspace;
-  a.q_rotate = q_rotate;
-  a.q_rot_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
-  if (lut_bits != 0) {
-    uint8_t tab[sizeof(a.lut_w)] = {};
-    attn::index_softmax_table(lut_bits, clip, tab);
-    std::memcpy(a.lut_w, tab, sizeof(tab));
-    a.lut_n = (1 << lut_bits) - 1;
-    a.lut_k = static_cast<float>(static_cast<double>(a.lut_n) / static_cast<double>(clip));
-  }
-  int tile, split, dec;
-  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = dec ? attn::launch_decode(a, split, st) : attn::launch_prefill(a, st);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+// the arguments every forward shares
+FwdRequest request(const int8_t* k, const float* s_k, const int8_t* v, const float* s_v, attn_vscale v_mode,
+                   void* o, attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                   int32_t d, int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdRequest r;
+  r.k = k; r.s_k = s_k; r.v = v; r.s_v = s_v; r.v_mode = v_mode; r.o = o; r.o_dt = o_dt; r.lse = lse;
+  r.B = B; r.H = H; r.Hkv = Hkv; r.Lq = Lq; r.Lkv = Lkv; r.d = d; r.causal = causal;
+  r.workspace = workspace; r.workspace_bytes = workspace_bytes; r.stream = stream;
+  return r;
 }
 
 }  // namespace
@@ -281,8 +337,23 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
                           int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* workspace,
                           size_t workspace_bytes, void* stream) {
   if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
-  return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
-                    B, H, Hkv, Lq, Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream);
+  FwdRequest r = request(k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq, Lkv, d, causal, workspace,
+                         workspace_bytes, stream);
+  r.q = q; r.s_q = s_q;
+  return run_fwd(r);
+}
+
+attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
+                                 const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                 attn_dtype o_dt, float* lse, int8_t* q_hat, float* s_q, int32_t B,
+                                 int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
+                                 int32_t causal, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!q) return ATTN_ERR_INVALID_ARG;
+  FwdRequest r = request(k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq, Lkv, d, causal, workspace,
+                         workspace_bytes, stream);
+  r.q_float = q; r.q_dt = q_dt; r.q_hat = q_hat; r.s_q_out = s_q;
+  return run_fwd(r);
 }
 
 attn_status attn_int8_fwd_qfloat_hadamard(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
@@ -291,8 +362,10 @@ attn_status attn_int8_fwd_qfloat_hadamard(const void* q, attn_dtype q_dt, const 
                                           int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                                           int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q) return ATTN_ERR_INVALID_ARG;
-  return fwd_common(nullptr, nullptr, q, q_dt, q_hat, s_q, k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq,
-                    Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream, 1);
+  FwdRequest r = request(k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq, Lkv, d, causal, workspace,
+                         workspace_bytes, stream);
+  r.q_float = q; r.q_dt = q_dt; r.q_hat = q_hat; r.s_q_out = s_q; r.q_rotate = 1;
+  return run_fwd(r);
 }
 
 attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const int8_t* k,
@@ -303,69 +376,27 @@ attn_status attn_int8_fwd_index_softmax(const int8_t* q, const float* s_q, const
                                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
   if (!lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
-  return fwd_common(q, s_q, nullptr, ATTN_F32, nullptr, nullptr, k, s_k, v, s_v, v_mode, o, o_dt, lse,
-                    B, H, Hkv, Lq, Lkv, d, causal, lut_bits, clip, workspace, workspace_bytes, stream);
+  FwdRequest r = request(k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq, Lkv, d, causal, workspace,
+                         workspace_bytes, stream);
+  r.q = q; r.s_q = s_q; r.lut_bits = lut_bits; r.clip = clip;
+  return run_fwd(r);
 }
 
 attn_status attn_int4qk_fwd(const int8_t* q, const float* s_q, const uint8_t* k4, const float* s_k, const int8_t* v,
                             const float* s_v, attn_vscale v_mode, void* o, attn_dtype o_dt, float* lse, int32_t B,
                             int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !s_q || !k4 || !s_k || !v || !s_v || !o) return ATTN_ERR_INVALID_ARG;
-  if (v_mode != ATTN_VSCALE_PER_TENSOR && v_mode != ATTN_VSCALE_PER_TOKEN && v_mode != ATTN_VSCALE_PER_HEAD &&
-      v_mode != ATTN_VSCALE_PER_CHANNEL)
-    return ATTN_ERR_INVALID_ARG;
-  if (o_dt != ATTN_F32 && o_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  const attn_status s = check_shape(B, H, Hkv, Lq, Lkv, d, causal);
-  if (s != ATTN_OK) return s;
-  if (!aligned(q, 16) || !aligned(k4, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(s_q, 4) || !aligned(s_k, 4) || !aligned(s_v, 4) || (lse && !aligned(lse, 4)))
-    return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn_int4qk_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return ATTN_ERR_INVALID_ARG;
-
-  attn::FwdArgs a{};
-  a.q = q; a.s_q = s_q; a.k = reinterpret_cast<const int8_t*>(k4); a.s_k = s_k; a.v = v; a.s_v = s_v;
-  a.o = o; a.lse = lse; a.s_dump = nullptr;
-  a.B = B; a.H = H; a.Hkv = Hkv; a.Lq = Lq; a.Lkv = Lkv; a.d = d;
-  a.causal = causal; a.v_per_token = (v_mode == ATTN_VSCALE_PER_TOKEN);
-  a.v_per_head = (v_mode == ATTN_VSCALE_PER_HEAD); a.v_per_channel = (v_mode == ATTN_VSCALE_PER_CHANNEL);
-  a.o_f16 = (o_dt == ATTN_F16);
-  a.workspace = workspace;
-  int tile, split, dec;
-  attn::fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal, &tile, &split, &dec);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dec) {
-    a.k_int4 = 1;                      // the decode kernel reads the packed codes itself
-    e = attn::launch_decode(a, split, st);
-  } else {
-    // prefill shapes: unpack K into the workspace, then the INT8 kernel
-    e = attn::launch_unpack_int4(k4, int64_t{B} * Hkv * Lkv * d / 2, static_cast<int8_t*>(workspace), st);
-    if (e == hipSuccess) {
-      a.k = static_cast<const int8_t*>(workspace);
-      a.workspace = nullptr;
-      e = attn::launch_prefill(a, st);
-    }
-  }
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
+  FwdRequest r = request(reinterpret_cast<const int8_t*>(k4), s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq,
+                         Lkv, d, causal, workspace, workspace_bytes, stream);
+  r.q = q; r.s_q = s_q; r.k_int4 = 1;
+  return run_fwd(r);
 }
 
 attn_status attn_index_softmax_table(int32_t lut_bits, float clip, uint8_t* table) {
   if (!table || !lut_params_ok(lut_bits, clip)) return ATTN_ERR_INVALID_ARG;
   attn::index_softmax_table(lut_bits, clip, table);
   return ATTN_OK;
-}
-
-attn_status attn_int8_fwd_qfloat(const void* q, attn_dtype q_dt, const int8_t* k, const float* s_k,
-                                 const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
-                                 attn_dtype o_dt, float* lse, int8_t* q_hat, float* s_q, int32_t B,
-                                 int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
-                                 int32_t causal, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
-  if (!q) return ATTN_ERR_INVALID_ARG;
-  return fwd_common(nullptr, nullptr, q, q_dt, q_hat, s_q, k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H,
-                    Hkv, Lq, Lkv, d, causal, 0, 0.0f, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_int8_debug_logits(const int8_t* q, const int8_t* k, int32_t B, int32_t H,
