@@ -599,10 +599,11 @@ __global__ __launch_bounds__(256) void attn_decode_combine(FwdArgs a, int n_spli
     for (int c = 0; c < CPL; ++c) o[c] = __builtin_fmaf(f, pt.acc[pr * D + lane * CPL + c], o[c]);
   }
   const float scale = (a.v_per_token ? 1.0f : a.s_v[a.v_per_head ? gi : 0]) / L;
+  const float rl = 1.0f / L;
   float cs[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c)   // per-channel V: each channel its own scale
-    cs[c] = a.v_per_channel ? a.s_v[static_cast<int64_t>(gi) * D + lane * CPL + c] / L : scale;
+    cs[c] = a.v_per_channel ? a.s_v[static_cast<int64_t>(gi) * D + lane * CPL + c] * rl : scale;
   if constexpr (OUT_F16) {
     __half* out = static_cast<__half*>(a.o) + row * D + lane * CPL;
 #pragma unroll

@@ -642,6 +642,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const float scale = (VPT ? 1.0f : a.s_v[a.v_per_head ? b * a.Hkv + hk : 0]) / ltot;
   // per-channel V: channel c of the output takes its own scale
   const float* sch = a.s_v + (static_cast<int64_t>(b) * a.Hkv + hk) * D;
+  const float rl = 1.0f / ltot;
   const int64_t orow = (q_base + qi) * D;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       float cs[4] = {scale, scale, scale, scale};
       if (!VPT && a.v_per_channel) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cs[e] = sch[d0 + e] / ltot;
+        for (int e = 0; e < 4; ++e) cs[e] = sch[d0 + e] * rl;
       }
       const float o0 = acc[c][j4 * 4 + 0] * cs[0], o1 = acc[c][j4 * 4 + 1] * cs[1];
       const float o2 = acc[c][j4 * 4 + 2] * cs[2], o3 = acc[c][j4 * 4 + 3] * cs[3];
