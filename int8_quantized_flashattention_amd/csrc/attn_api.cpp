@@ -82,108 +82,6 @@ size_t fwd_workspace_bytes(int B, int H, int Hkv, int Lq, int Lkv, int d, int ca
 
 }  // namespace attn
 
-extern "C" {
-
-const char* attn_status_str(attn_status s) {
-  switch (s) {
-    case ATTN_OK: return "ok";
-    case ATTN_ERR_INVALID_ARG: return "invalid argument";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
-    case ATTN_ERR_HIP: return "HIP runtime error at launch";
-  }
-  return "unknown status";
-}
-
-attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols,
-                               int64_t rows_per_scale, int8_t* q, float* scales, void* stream) {
-  if (!x || !q || !scales) return ATTN_ERR_INVALID_ARG;
-  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (n_rows < 1 || n_cols < 1 || rows_per_scale < 1 || n_rows % rows_per_scale != 0)
-    return ATTN_ERR_INVALID_ARG;
-  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
-  if (n_cols % 8 != 0) return ATTN_ERR_UNSUPPORTED;
-  if (n_rows / rows_per_scale > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
-  const hipError_t e = attn::launch_quantize(x, x_dt == ATTN_F16, n_rows, n_cols, rows_per_scale, q,
-                                             scales, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-attn_status attn_quantize_cols(const void* x, attn_dtype x_dt, int64_t n_groups, int64_t rows_per_group,
-                               int32_t n_cols, int8_t* q, float* scales, void* stream) {
-  if (!x || !q || !scales) return ATTN_ERR_INVALID_ARG;
-  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (n_groups < 1 || rows_per_group < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
-  if (n_cols % 8 != 0 || n_cols > attn::kMaxQuantCols) return ATTN_ERR_UNSUPPORTED;
-  if (n_groups > INT64_MAX / rows_per_group || n_groups * rows_per_group > INT64_MAX / n_cols)
-    return ATTN_ERR_INVALID_ARG;
-  if (n_groups * n_cols > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
-  const hipError_t e = attn::launch_quantize_cols(x, x_dt == ATTN_F16, n_groups, rows_per_group, n_cols, q,
-                                                  scales, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-attn_status attn_quantize_rows_int4(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int8_t* codes,
-                                    uint8_t* packed, float* scales, void* stream) {
-  if (!x || !scales || (!codes && !packed)) return ATTN_ERR_INVALID_ARG;
-  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (n_rows < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
-  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
-  if (n_cols % 8 != 0 || n_cols > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
-  if ((n_rows + 3) / 4 > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || (codes && !aligned(codes, 8)) || (packed && !aligned(packed, 4)) || !aligned(scales, 4))
-    return ATTN_ERR_INVALID_ARG;
-  const hipError_t e = attn::launch_quantize_int4(x, x_dt == ATTN_F16, n_rows, n_cols, codes, packed, scales,
-                                                  static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-attn_status attn_quantize_rows_hadamard(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int32_t bits,
-                                        int8_t* codes, uint8_t* packed, float* scales, void* stream) {
-  if (!x || !scales) return ATTN_ERR_INVALID_ARG;
-  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (bits == 8 ? (!codes || packed) : bits == 4 ? (!codes && !packed) : true) return ATTN_ERR_INVALID_ARG;
-  if (n_rows < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
-  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
-  if ((n_cols & (n_cols - 1)) || n_cols < 8 || n_cols > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
-  if ((n_rows + 3) / 4 > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || (codes && !aligned(codes, 8)) || (packed && !aligned(packed, 4)) || !aligned(scales, 4))
-    return ATTN_ERR_INVALID_ARG;
-  const float rn = static_cast<float>(1.0 / std::sqrt(static_cast<double>(n_cols)));
-  const hipError_t e = attn::launch_quantize_rotated(x, x_dt == ATTN_F16, n_rows, n_cols, bits, rn, codes, packed,
-                                                     scales, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-attn_status attn_kv_append_int4(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
-                                uint8_t* cache4, float* scales, int32_t L_max, int32_t pos, void* stream) {
-  if (!x || !cache4 || !scales) return ATTN_ERR_INVALID_ARG;
-  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || L_max < 1 || pos < 0 || T > L_max - pos)
-    return ATTN_ERR_INVALID_ARG;
-  if (d % 8 != 0 || d > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
-  if (int64_t{B} * Hkv * L_max * d > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(cache4, 4) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
-  const hipError_t e = attn::launch_append_int4(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache4,
-                                                scales, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
-                           int8_t* cache, float* scales, int32_t L_max, int32_t pos, void* stream) {
-  if (!x || !cache || !scales) return ATTN_ERR_INVALID_ARG;
-  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || L_max < 1 || pos < 0 || T > L_max - pos)
-    return ATTN_ERR_INVALID_ARG;
-  if (d % 8 != 0 || d > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
-  if (int64_t{B} * Hkv * L_max * d > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(cache, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
-  const hipError_t e = attn::launch_append(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache,
-                                           scales, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
 namespace {
 
 // Workspace of the forward: the split-KV partials for decode shapes; for
@@ -291,6 +189,123 @@ attn_status run_fwd(const FwdRequest& r) {
 
 }  // namespace
 
+namespace {
+
+// the arguments every forward shares
+FwdRequest request(const int8_t* k, const float* s_k, const int8_t* v, const float* s_v, attn_vscale v_mode,
+                   void* o, attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
+                   int32_t d, int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdRequest r;
+  r.k = k; r.s_k = s_k; r.v = v; r.s_v = s_v; r.v_mode = v_mode; r.o = o; r.o_dt = o_dt; r.lse = lse;
+  r.B = B; r.H = H; r.Hkv = Hkv; r.Lq = Lq; r.Lkv = Lkv; r.d = d; r.causal = causal;
+  r.workspace = workspace; r.workspace_bytes = workspace_bytes; r.stream = stream;
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+attn_status attn_quantize_rows(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols,
+                               int64_t rows_per_scale, int8_t* q, float* scales, void* stream) {
+  if (!x || !q || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (n_rows < 1 || n_cols < 1 || rows_per_scale < 1 || n_rows % rows_per_scale != 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
+  if (n_cols % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (n_rows / rows_per_scale > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_quantize(x, x_dt == ATTN_F16, n_rows, n_cols, rows_per_scale, q,
+                                             scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_quantize_cols(const void* x, attn_dtype x_dt, int64_t n_groups, int64_t rows_per_group,
+                               int32_t n_cols, int8_t* q, float* scales, void* stream) {
+  if (!x || !q || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (n_groups < 1 || rows_per_group < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_cols % 8 != 0 || n_cols > attn::kMaxQuantCols) return ATTN_ERR_UNSUPPORTED;
+  if (n_groups > INT64_MAX / rows_per_group || n_groups * rows_per_group > INT64_MAX / n_cols)
+    return ATTN_ERR_INVALID_ARG;
+  if (n_groups * n_cols > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_quantize_cols(x, x_dt == ATTN_F16, n_groups, rows_per_group, n_cols, q,
+                                                  scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_quantize_rows_int4(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int8_t* codes,
+                                    uint8_t* packed, float* scales, void* stream) {
+  if (!x || !scales || (!codes && !packed)) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (n_rows < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
+  if (n_cols % 8 != 0 || n_cols > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if ((n_rows + 3) / 4 > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || (codes && !aligned(codes, 8)) || (packed && !aligned(packed, 4)) || !aligned(scales, 4))
+    return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_quantize_int4(x, x_dt == ATTN_F16, n_rows, n_cols, codes, packed, scales,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_quantize_rows_hadamard(const void* x, attn_dtype x_dt, int64_t n_rows, int32_t n_cols, int32_t bits,
+                                        int8_t* codes, uint8_t* packed, float* scales, void* stream) {
+  if (!x || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (bits == 8 ? (!codes || packed) : bits == 4 ? (!codes && !packed) : true) return ATTN_ERR_INVALID_ARG;
+  if (n_rows < 1 || n_cols < 1) return ATTN_ERR_INVALID_ARG;
+  if (n_rows > INT64_MAX / n_cols) return ATTN_ERR_INVALID_ARG;
+  if ((n_cols & (n_cols - 1)) || n_cols < 8 || n_cols > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if ((n_rows + 3) / 4 > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || (codes && !aligned(codes, 8)) || (packed && !aligned(packed, 4)) || !aligned(scales, 4))
+    return ATTN_ERR_INVALID_ARG;
+  const float rn = static_cast<float>(1.0 / std::sqrt(static_cast<double>(n_cols)));
+  const hipError_t e = attn::launch_quantize_rotated(x, x_dt == ATTN_F16, n_rows, n_cols, bits, rn, codes, packed,
+                                                     scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_kv_append_int4(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
+                                uint8_t* cache4, float* scales, int32_t L_max, int32_t pos, void* stream) {
+  if (!x || !cache4 || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || L_max < 1 || pos < 0 || T > L_max - pos)
+    return ATTN_ERR_INVALID_ARG;
+  if (d % 8 != 0 || d > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t{B} * Hkv * L_max * d > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(cache4, 4) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_append_int4(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache4,
+                                                scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hkv, int32_t T, int32_t d,
+                           int8_t* cache, float* scales, int32_t L_max, int32_t pos, void* stream) {
+  if (!x || !cache || !scales) return ATTN_ERR_INVALID_ARG;
+  if (x_dt != ATTN_F32 && x_dt != ATTN_F16) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || L_max < 1 || pos < 0 || T > L_max - pos)
+    return ATTN_ERR_INVALID_ARG;
+  if (d % 8 != 0 || d > attn::kMaxAppendCols) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t{B} * Hkv * L_max * d > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(cache, 8) || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  const hipError_t e = attn::launch_append(x, x_dt == ATTN_F16, int64_t{B} * Hkv, T, d, L_max, pos, cache,
+                                           scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 size_t attn_int4qk_fwd_workspace_size(int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                                       int32_t causal) {
   if (check_shape(B, H, Hkv, Lq, Lkv, d, causal) != ATTN_OK) return 0;
@@ -315,21 +330,6 @@ attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq
   *kv_split_len = split;
   return ATTN_OK;
 }
-
-namespace {
-
-// the arguments every forward shares
-FwdRequest request(const int8_t* k, const float* s_k, const int8_t* v, const float* s_v, attn_vscale v_mode,
-                   void* o, attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv,
-                   int32_t d, int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
-  FwdRequest r;
-  r.k = k; r.s_k = s_k; r.v = v; r.s_v = s_v; r.v_mode = v_mode; r.o = o; r.o_dt = o_dt; r.lse = lse;
-  r.B = B; r.H = H; r.Hkv = Hkv; r.Lq = Lq; r.Lkv = Lkv; r.d = d; r.causal = causal;
-  r.workspace = workspace; r.workspace_bytes = workspace_bytes; r.stream = stream;
-  return r;
-}
-
-}  // namespace
 
 attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
                           const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,

@@ -37,7 +37,6 @@ namespace {
 constexpr int BN = kDecodeBN;
 static_assert(BN == kPrefillBN, "one KV tile size for every schedule");
 constexpr int NB = BN / 16;                  // 16-key blocks per tile
-constexpr int QR = 16;                       // query rows per wavefront (MFMA tile)
 constexpr int kStages = 3;
 // the INT32 run of P_hat . V_hat is folded into fp32 at least every this many
 // tiles, keeping |sum| <= 127 * 127 * keys below 2^31
