@@ -172,7 +172,7 @@ def cpu_baseline(w, q, k, v, target_s, index_softmax=None, q4=False):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
