@@ -150,17 +150,23 @@ __device__ __forceinline__ void qk_tile(v16i (&s)[NKB], const int8_t* kst, const
 // O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T (FRESH: acc[c] =
 // V_hat^T . P_hat^T, the first product taking the inline constant 0 as its
 // accumulator, so a new INT32 run needs no zeroing instructions).
-template <int D, bool FRESH>
+// One V^T operand (channel chunk c, key block kb) read from a stage.
+template <int D>
+__device__ __forceinline__ v4i v_operand(const int8_t* vst, const Lanes<D>& ln, int c, int kb) {
+  const int8_t* p = vst + kb * 32 * D + ln.voff[c];
+  const v2i lo = lds_read_tr8(p);
+  const v2i hi = lds_read_tr8(p + 8 * D);
+  return v4i{lo.x, lo.y, hi.x, hi.y};
+}
+template <int D, bool FRESH, int PRE>
 __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, const Lanes<D>& ln,
-                                        const v4i (&pv)[NKB]) {
+                                        const v4i (&pv)[NKB], const v4i (&vpre)[PRE > 0 ? PRE : 1][NKB]) {
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int8_t* p = vst + kb * 32 * D + ln.voff[c];
-      const v2i lo = lds_read_tr8(p);
-      const v2i hi = lds_read_tr8(p + 8 * D);
-      acc[c] = mfma_i8(v4i{lo.x, lo.y, hi.x, hi.y}, pv[kb], (FRESH && kb == 0) ? zero16() : acc[c]);
+      const v4i vo = c < PRE ? vpre[c < PRE ? c : 0][kb] : v_operand<D>(vst, ln, c, kb);
+      acc[c] = mfma_i8(vo, pv[kb], (FRESH && kb == 0) ? zero16() : acc[c]);
     }
 }
 
@@ -347,7 +353,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
-  __shared__ Stage<D> sm[kStages];
+  // PAIR: a ring of four stages, two tiles requested together and one
+  // barrier per two tiles. PRE: V operands of this many channel chunks are
+  // read right after Q.K^T, ahead of the softmax. (The IndexSoftmax kernels
+  // keep one barrier per tile and no early reads: their table lookups leave
+  // no registers, and the pair table no LDS, for them.)
+  constexpr bool PAIR = LUT == 0;
+  constexpr int PRE = LUT ? 0 : 2;
+  constexpr int NST = PAIR ? 4 : kStages;
+  __shared__ Stage<D> sm[NST];
   __shared__ uint32_t lut_s[LUT ? 65 : 1];
   __shared__ uint16_t lut2_s[LUT == 2 ? kLutPairRows * 256 : 1];
 
@@ -378,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   // scale slots start at zero: a load past Lkv may leave a slot untouched
-  for (int i = tid; i < kStages * BN; i += kThreads) {
+  for (int i = tid; i < NST * BN; i += kThreads) {
     sm[i / BN].sk[i % BN] = 0.0f;
     sm[i / BN].sv[i % BN] = 0.0f;
   }
@@ -499,8 +513,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   int int_tiles = 0;                   // tiles in the current INT32 run
   bool fresh = true;                   // the next PV starts a new INT32 run
 
-  // tile 0 must have landed (tile 1 may still be in flight)
-  if (n_tiles > 1) wait_vm_lds<2 * LPW>();
+  // tile 0 must have landed (tile 1 may still be in flight; not with PAIR)
+  if (n_tiles > 1 && !PAIR) wait_vm_lds<2 * LPW>();
   else wait_vm_lds<0>();
   bare_barrier();
   // The wait above also covered the Q loads (issued before it). Passing the
@@ -526,13 +540,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   // stage being filled are distinct objects, passed as restrict pointers: the
   // compiler then knows that this tile's LDS reads do not depend on the loads
   // just issued and adds no wait for them.
-  auto step = [&](int t, const Stage<D>* __restrict__ st, Stage<D>* __restrict__ nx) __attribute__((always_inline)) {
+  auto step = [&](int t, const Stage<D>* __restrict__ st, Stage<D>* __restrict__ nx,
+                  Stage<D>* __restrict__ nx2) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    const bool req = t + 2 < n_tiles;
+    const bool req = t + 2 < n_tiles && (!PAIR || !(t & 1));
     if (req) request_tile<D, true, VPT>(*nx, bf, ln, wave, lane, k0 + 2 * BN);
+    if (PAIR && req && t + 3 < n_tiles) request_tile<D, true, VPT>(*nx2, bf, ln, wave, lane, k0 + 3 * BN);
 
     v16i s[NKB];
     qk_tile<D>(s, st->k, ln, qf);
+    v4i vpre[PRE > 0 ? PRE : 1][NKB];
+#pragma unroll
+    for (int c = 0; c < PRE; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) vpre[c][kb] = v_operand<D>(st->v, ln, c, kb);
+    if constexpr (PRE > 0) __builtin_amdgcn_sched_barrier(0);
     const bool mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
     float u[NKB][16];
     float mx;
@@ -601,8 +623,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     m = m_new;
 
     // per-token V converts every tile's product on its own: always a new run
-    if (VPT || fresh) pv_tile<D, true>(acc_i, st->v, ln, p);
-    else pv_tile<D, false>(acc_i, st->v, ln, p);
+    if (VPT || fresh) pv_tile<D, true, PRE>(acc_i, st->v, ln, p, vpre);
+    else pv_tile<D, false, PRE>(acc_i, st->v, ln, p, vpre);
     fresh = false;
     if constexpr (VPT) {
       // per-token V: tile scales differ, so each tile's INT32 product is
@@ -614,18 +636,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           acc[c][v] = __builtin_fmaf(alpha, acc[c][v], st_cur * static_cast<float>(acc_i[c][v]));
     }
 
-    // tile t+1 must have landed before anyone reads it; after the barrier
-    // every wavefront is done with stage t, which tile t+3 reuses
-    if (req) wait_vm_lds<2 * LPW>();
-    else wait_vm_lds<0>();
-    bare_barrier();
+    if constexpr (PAIR) {
+      // after an odd tile: tiles t+1, t+2 must have landed; after the barrier
+      // every wavefront is done with stages t-1 and t, which tiles t+3, t+4 reuse
+      if ((t & 1) && t + 1 < n_tiles) {
+        wait_vm_lds<0>();
+        bare_barrier();
+      }
+    } else {
+      // tile t+1 must have landed before anyone reads it; after the barrier
+      // every wavefront is done with stage t, which tile t+3 reuses
+      if (req) wait_vm_lds<2 * LPW>();
+      else wait_vm_lds<0>();
+      bare_barrier();
+    }
   };
 
-  int s_cur = 0;                       // stage of tile t; tile t+2 goes to the one before it
-  for (int t = 0; t < n_tiles; ++t) {
-    const int s_req = s_cur == 0 ? kStages - 1 : s_cur - 1;
-    step(t, &sm[s_cur], &sm[s_req]);
-    s_cur = s_cur == kStages - 1 ? 0 : s_cur + 1;
+  if constexpr (PAIR) {
+    for (int t = 0; t < n_tiles; ++t) step(t, &sm[t & 3], &sm[(t + 2) & 3], &sm[(t + 3) & 3]);
+  } else {
+    int s_cur = 0;                     // stage of tile t; tile t+2 goes to the one before it
+    for (int t = 0; t < n_tiles; ++t) {
+      const int s_req = s_cur == 0 ? kStages - 1 : s_cur - 1;
+      step(t, &sm[s_cur], &sm[s_req], &sm[s_req]);
+      s_cur = s_cur == kStages - 1 ? 0 : s_cur + 1;
+    }
   }
 
   if constexpr (!VPT) {
