@@ -30,9 +30,11 @@
 // the LDS destination: no registers, no LDS store instructions), in their
 // natural [key][channel] layout with the 16-byte chunks of each row XOR-
 // swizzled. The V^T operand is read with ds_read_b64_tr_b8, which hands each
-// lane 8 consecutive keys of one channel. Three stages form a ring: tile t+2
-// is requested while tile t is computed, and a stage is waited for one tile
-// after it was requested.
+// lane 8 consecutive keys of one channel. Four stages form a ring that
+// holds the pair of tiles being computed and the pair in flight: before an
+// even tile t the workgroup requests tiles t+2 and t+3, and after the odd
+// tile t+1 one wait and one barrier make them visible, so the four
+// wavefronts meet once per two tiles.
 //
 // Instruction budget. On gfx950 the issue time of the VALU work per
 // (query, key) pair is the first-order cost next to the pair's MFMA work, so
@@ -59,7 +61,7 @@ constexpr int BN = kPrefillBN;
 constexpr int NKB = BN / 32;                 // 32-key blocks per tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 // the INT32 run of P_hat . V_hat is folded into fp32 at least every this many
 // tiles, keeping |sum| <= 127 * 127 * keys below 2^31
 constexpr int kMaxIntTiles = 32768 / BN;
@@ -111,10 +113,10 @@ struct Lanes {
   }
 };
 
-// Request tile k0 into a stage: K (and V) rows plus the scales. Each
-// wavefront issues its scale load first, then LPW loads per operand, so
-// wait_vm_lds<N> with N = 2 LPW (K and V) leaves at most the newest tile's
-// K/V loads in flight.
+// Request tile k0 into a stage: K (and V) rows plus the scales. Wavefront 0
+// loads s_K (wavefront 1 s_V when it varies per key); every wavefront then
+// moves LPW 1 KB pieces of each operand, so a tile is complete once every
+// wavefront's loads have landed.
 template <int D, bool KV, bool VPT>
 __device__ __forceinline__ void request_tile(Stage<D>& st, const Bufs& bf, const Lanes<D>& ln, int wave, int lane,
                                              int k0) {
@@ -272,7 +274,7 @@ __device__ __forceinline__ float lut_tile(const float (&u)[NKB][16], float kap, 
 }
 
 // The same with a table of key pairs (tables of at most 32 entries): entry
-// ia + 256 ib of the pair table holds E[ia] | E[ib] << 8, index 32 being the
+// ia + 33 ib of the pair table holds E[ia] | E[ib] << 8, index 32 being the
 // zero slot, so one 16-bit LDS read serves two keys and two reads fill a
 // packed word of the PV operand.
 template <bool MASK>
@@ -291,8 +293,8 @@ __device__ __forceinline__ float lut2_tile(const float (&u)[NKB][16], float kap,
         idx[e] = static_cast<uint32_t>(x);
         if constexpr (MASK) idx[e] = (kb * 32 + j4 * 4 + e <= rel) ? idx[e] : 32u;
       }
-      const uint32_t lo = tab2[idx[0] + (idx[1] << 8)];
-      const uint32_t hi = tab2[idx[2] + (idx[3] << 8)];
+      const uint32_t lo = tab2[idx[0] + idx[1] * kLutPairRows];
+      const uint32_t hi = tab2[idx[2] + idx[3] * kLutPairRows];
       const uint32_t word = lo | (hi << 16);
       sum = __builtin_amdgcn_udot4(word, 0x01010101u, sum, false);
       pw[j4] = word;
@@ -353,17 +355,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
-  // PAIR: a ring of four stages, two tiles requested together and one
-  // barrier per two tiles. PRE: V operands of this many channel chunks are
-  // read right after Q.K^T, ahead of the softmax. (The IndexSoftmax kernels
-  // keep one barrier per tile and no early reads: their table lookups leave
-  // no registers, and the pair table no LDS, for them.)
-  constexpr bool PAIR = LUT == 0;
+  // PRE: V operands of this many channel chunks are read right after Q.K^T,
+  // ahead of the softmax (the IndexSoftmax kernels have no registers left
+  // for them)
   constexpr int PRE = LUT ? 0 : 2;
-  constexpr int NST = PAIR ? 4 : kStages;
-  __shared__ Stage<D> sm[NST];
+  __shared__ Stage<D> sm[kStages];
   __shared__ uint32_t lut_s[LUT ? 65 : 1];
-  __shared__ uint16_t lut2_s[LUT == 2 ? kLutPairRows * 256 : 1];
+  __shared__ uint16_t lut2_s[LUT == 2 ? kLutPairRows * kLutPairRows : 1];
 
   const int n_rb = (a.Lq + BM - 1) / BM;
   int bh, rb;
@@ -392,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   // scale slots start at zero: a load past Lkv may leave a slot untouched
-  for (int i = tid; i < NST * BN; i += kThreads) {
+  for (int i = tid; i < kStages * BN; i += kThreads) {
     sm[i / BN].sk[i % BN] = 0.0f;
     sm[i / BN].sv[i % BN] = 0.0f;
   }
@@ -404,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const uint8_t* tab = reinterpret_cast<const uint8_t*>(lut_s);   // zero from entry 32 on
     for (int e = tid; e < kLutPairRows * kLutPairRows; e += kThreads) {
       const int ia = e % kLutPairRows, ib = e / kLutPairRows;
-      lut2_s[ib * 256 + ia] = static_cast<uint16_t>(tab[ia] | (tab[ib] << 8));
+      lut2_s[e] = static_cast<uint16_t>(tab[ia] | (tab[ib] << 8));
     }
   }
 
@@ -513,9 +511,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   int int_tiles = 0;                   // tiles in the current INT32 run
   bool fresh = true;                   // the next PV starts a new INT32 run
 
-  // tile 0 must have landed (tile 1 may still be in flight; not with PAIR)
-  if (n_tiles > 1 && !PAIR) wait_vm_lds<2 * LPW>();
-  else wait_vm_lds<0>();
+  // tiles 0 and 1 must have landed
+  wait_vm_lds<0>();
   bare_barrier();
   // The wait above also covered the Q loads (issued before it). Passing the
   // fragment and s_Q through empty asm statements tells the compiler so; otherwise
@@ -535,17 +532,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const float nf = static_cast<float>(a.lut_n);
   float m_u = kNegInf;
 
-  // One tile: request t+2 | QK(t) [MFMA] | dequant, softmax(t) [VALU] | fold
-  // | PV(t) [MFMA] | wait for t+1 | barrier. The stage being read and the
-  // stage being filled are distinct objects, passed as restrict pointers: the
-  // compiler then knows that this tile's LDS reads do not depend on the loads
-  // just issued and adds no wait for them.
+  // One tile: (even t) request t+2, t+3 | QK(t) [MFMA] | dequant, softmax(t)
+  // [VALU] | fold | PV(t) [MFMA] | (odd t) wait for t+1, t+2 | barrier. The
+  // stage being read and the stages being filled are distinct objects, passed
+  // as restrict pointers: the compiler then knows that this tile's LDS reads
+  // do not depend on the loads just issued and adds no wait for them.
   auto step = [&](int t, const Stage<D>* __restrict__ st, Stage<D>* __restrict__ nx,
                   Stage<D>* __restrict__ nx2) __attribute__((always_inline)) {
     const int k0 = t * BN;
-    const bool req = t + 2 < n_tiles && (!PAIR || !(t & 1));
-    if (req) request_tile<D, true, VPT>(*nx, bf, ln, wave, lane, k0 + 2 * BN);
-    if (PAIR && req && t + 3 < n_tiles) request_tile<D, true, VPT>(*nx2, bf, ln, wave, lane, k0 + 3 * BN);
+    if (!(t & 1) && t + 2 < n_tiles) {
+      request_tile<D, true, VPT>(*nx, bf, ln, wave, lane, k0 + 2 * BN);
+      if (t + 3 < n_tiles) request_tile<D, true, VPT>(*nx2, bf, ln, wave, lane, k0 + 3 * BN);
+    }
 
     v16i s[NKB];
     qk_tile<D>(s, st->k, ln, qf);
@@ -636,32 +634,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           acc[c][v] = __builtin_fmaf(alpha, acc[c][v], st_cur * static_cast<float>(acc_i[c][v]));
     }
 
-    if constexpr (PAIR) {
-      // after an odd tile: tiles t+1, t+2 must have landed; after the barrier
-      // every wavefront is done with stages t-1 and t, which tiles t+3, t+4 reuse
-      if ((t & 1) && t + 1 < n_tiles) {
-        wait_vm_lds<0>();
-        bare_barrier();
-      }
-    } else {
-      // tile t+1 must have landed before anyone reads it; after the barrier
-      // every wavefront is done with stage t, which tile t+3 reuses
-      if (req) wait_vm_lds<2 * LPW>();
-      else wait_vm_lds<0>();
+    // after an odd tile: tiles t+1 and t+2 must have landed before anyone
+    // reads them; after the barrier every wavefront is done with stages t-1
+    // and t, which tiles t+3 and t+4 reuse
+    if ((t & 1) && t + 1 < n_tiles) {
+      wait_vm_lds<0>();
       bare_barrier();
     }
   };
 
-  if constexpr (PAIR) {
-    for (int t = 0; t < n_tiles; ++t) step(t, &sm[t & 3], &sm[(t + 2) & 3], &sm[(t + 3) & 3]);
-  } else {
-    int s_cur = 0;                     // stage of tile t; tile t+2 goes to the one before it
-    for (int t = 0; t < n_tiles; ++t) {
-      const int s_req = s_cur == 0 ? kStages - 1 : s_cur - 1;
-      step(t, &sm[s_cur], &sm[s_req], &sm[s_req]);
-      s_cur = s_cur == kStages - 1 ? 0 : s_cur + 1;
-    }
-  }
+  for (int t = 0; t < n_tiles; ++t) step(t, &sm[t & 3], &sm[(t + 2) & 3], &sm[(t + 3) & 3]);
 
   if constexpr (!VPT) {
     // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run

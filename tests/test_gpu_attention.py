@@ -80,6 +80,11 @@ SWEEP = [  # B, H, Hkv, Lq, Lkv, d, causal, v_per_token, o
     # V scales per (batch, kv head, channel)
     (2, 8, 2, 77, 130, 128, 1, "channel", "f16"), (2, 16, 4, 1, 700, 128, 0, "channel", "f32"),
     (1, 3, 3, 300, 300, 64, 1, "channel", "f32"), (1, 8, 1, 2, 520, 64, 1, "channel", "f16"),
+    # 1 .. 6 KV tiles of 64 keys around the two-tile steps of the prefill's stage ring
+    (1, 2, 1, 130, 127, 128, 0, 0, "f16"), (1, 2, 1, 130, 129, 128, 0, 0, "f16"),
+    (1, 2, 2, 64, 192, 64, 0, 0, "f32"), (1, 2, 2, 64, 193, 128, 0, 1, "f16"),
+    (1, 2, 2, 200, 256, 128, 1, 0, "f16"), (1, 2, 2, 100, 321, 128, 0, 0, "f32"),
+    (1, 2, 2, 40, 64, 128, 0, 0, "f16"), (1, 2, 2, 300, 384, 64, 1, "head", "f16"),
 ]
 
 
