@@ -124,11 +124,11 @@ constexpr int loads_per_tile() { return DLanes<D>::NLD + 1 + (VPT ? 1 : 0) + NB 
 template <int D, bool VPT>
 __device__ __forceinline__ void request_vs(DStage<D>& st, __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rsk,
                                            __amdgpu_buffer_rsrc_t rsv, const DLanes<D>& ln, int lane, int k0) {
-  lds_load4(rsk, st.sk, lane * 4, k0 * 4);
-  if (VPT) lds_load4(rsv, st.sv, lane * 4, k0 * 4);
+  lds_load4_nt(rsk, st.sk, lane * 4, k0 * 4);
+  if (VPT) lds_load4_nt(rsv, st.sv, lane * 4, k0 * 4);
   const uint32_t soff = static_cast<uint32_t>(k0) * D;
 #pragma unroll
-  for (int n = 0; n < DLanes<D>::NLD; ++n) lds_load16(rv, st.v + n * 1024, ln.ld[n], soff);
+  for (int n = 0; n < DLanes<D>::NLD; ++n) lds_load16_nt(rv, st.v + n * 1024, ln.ld[n], soff);
 }
 
 // K operands of the tile at key k0 into a register slot
@@ -139,7 +139,7 @@ __device__ __forceinline__ void request_k(KRegs<D>& kr, __amdgpu_buffer_rsrc_t r
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[kb * NC + c] = buf_load16(rk, ln.kg[kb & 1] + 8 * D * (kb >> 1) + 64 * c, soff);
+    for (int c = 0; c < NC; ++c) kr[kb * NC + c] = buf_load16_nt(rk, ln.kg[kb & 1] + 8 * D * (kb >> 1) + 64 * c, soff);
 }
 
 // packed K operands of the tile at key k0 into a register slot (d / 2 bytes per key)
@@ -151,7 +151,7 @@ __device__ __forceinline__ void request_k(KRegs4<D>& kr, __amdgpu_buffer_rsrc_t 
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      kr[kb * NC + c] = buf_load8(rk, ln.kg[kb & 1] / 2 + 4 * D * (kb >> 1) + 32 * c, soff);
+      kr[kb * NC + c] = buf_load8_nt(rk, ln.kg[kb & 1] / 2 + 4 * D * (kb >> 1) + 32 * c, soff);
 }
 
 // x of lane l ^ 16 (ds_swizzle bit mode: and 0x1f, or 0, xor 0x10 within 32

@@ -78,13 +78,29 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* dst, 
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, 0);
 }
-// 16 bytes per lane from a raw buffer into registers (zero where the offset
-// lies outside the buffer)
+// 8 or 16 bytes per lane from a raw buffer into registers (zero where the
+// offset lies outside the buffer)
 __device__ __forceinline__ v2i buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// The same loads with the non-temporal cache policy (the nt bit of the
+// instruction's cache-policy field), for data read exactly once: a split-KV
+// chunk streams its K and V rows past the caches instead of through them.
+constexpr int kCpolNT = 2;
+__device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, kCpolNT);
+}
+__device__ __forceinline__ void lds_load4_nt(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, soff, 0, kCpolNT);
+}
+__device__ __forceinline__ v2i buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCpolNT));
+}
+__device__ __forceinline__ v4i buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpolNT));
 }
 // ds_read_b64_tr_b8: in each group of 16 lanes, lane i receives byte i % 8 of
 // the 8-byte rows addressed by lanes 2 b + i / 8 (b = 0..7 gives byte b)
