@@ -356,9 +356,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   constexpr int NC = D / 32;
   constexpr int LPW = Lanes<D>::LPW;
   // PRE: V operands of this many channel chunks are read right after Q.K^T,
-  // ahead of the softmax (the IndexSoftmax kernels have no registers left
-  // for them)
-  constexpr int PRE = LUT ? 0 : 2;
+  // ahead of the softmax (the IndexSoftmax kernels have registers for one)
+  constexpr int PRE = LUT ? 1 : 2;
   __shared__ Stage<D> sm[kStages];
   __shared__ uint32_t lut_s[LUT ? 65 : 1];
   __shared__ uint16_t lut2_s[LUT == 2 ? kLutPairRows * kLutPairRows : 1];
