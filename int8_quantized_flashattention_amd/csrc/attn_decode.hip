@@ -20,7 +20,8 @@
 // QK of tile t has read it); V tiles and the scales go into a 3-stage LDS ring
 // (buffer loads with LDS destination, rows swizzled), since the V^T operands
 // need the transposing ds_read_b64_tr_b8. Keeping K out of LDS halves the ring,
-// so twice as many wavefronts (and loads in flight) fit on a CU.
+// so twice as many wavefronts (and loads in flight) fit on a CU. Every K, V
+// and scale byte is read exactly once, with the non-temporal cache policy.
 // Lane l holds query row l % 16 and, in each of the 4 key blocks of 16, keys
 // 4 b + 0..3 of its lane group, that is the 16 consecutive keys 16 (l / 16)
 // .. +15 of the tile, which are exactly its P operand for O^T = V^T P^T.

@@ -149,9 +149,6 @@ __device__ __forceinline__ void qk_tile(v16i (&s)[NKB], const int8_t* kst, const
     }
 }
 
-// O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T (FRESH: acc[c] =
-// V_hat^T . P_hat^T, the first product taking the inline constant 0 as its
-// accumulator, so a new INT32 run needs no zeroing instructions).
 // One V^T operand (channel chunk c, key block kb) read from a stage.
 template <int D>
 __device__ __forceinline__ v4i v_operand(const int8_t* vst, const Lanes<D>& ln, int c, int kb) {
@@ -160,6 +157,11 @@ __device__ __forceinline__ v4i v_operand(const int8_t* vst, const Lanes<D>& ln, 
   const v2i hi = lds_read_tr8(p + 8 * D);
   return v4i{lo.x, lo.y, hi.x, hi.y};
 }
+
+// O^T contribution of one tile: acc[c] += V_hat^T . P_hat^T (FRESH: acc[c] =
+// V_hat^T . P_hat^T, the first product taking the inline constant 0 as its
+// accumulator, so a new INT32 run needs no zeroing instructions). The
+// operands of the first PRE channel chunks were read earlier (vpre).
 template <int D, bool FRESH, int PRE>
 __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, const Lanes<D>& ln,
                                         const v4i (&pv)[NKB], const v4i (&vpre)[PRE > 0 ? PRE : 1][NKB]) {
@@ -354,7 +356,6 @@ template <int D, bool CAUSAL, bool VPT, bool OUT_F16, int QF, int LUT>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
   constexpr int NC = D / 32;
-  constexpr int LPW = Lanes<D>::LPW;
   // PRE: V operands of this many channel chunks are read right after Q.K^T,
   // ahead of the softmax (the IndexSoftmax kernels have registers for one)
   constexpr int PRE = LUT ? 1 : 2;
