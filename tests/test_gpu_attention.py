@@ -138,3 +138,31 @@ def test_per_block_v_via_per_token_scales(lib):
         assert tile == 64 and split % 64 == 0
         oo, _ = oracle.attn_int8(qa, sa, kh, sk, vh, sv, 1, B, H, Hkv, Lq, L, d, causal, tile, split)
         compare_o(host(o), oo, "per-block V Lq=%d causal=%d" % (Lq, causal))
+
+
+def _random_shapes(n, seed):
+    """Seeded random problems: GQA ratios 1, 2, 4; Lq up to 600 and Lkv up to
+    900 (Lq <= Lkv when causal); every V scale granularity; fp16 and fp32 O."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        d = rng.choice([64, 128])
+        causal = int(rng.random() < 0.6)
+        hkv = rng.choice([1, 2, 4])
+        h = hkv * rng.choice([1, 2, 4])
+        b = rng.choice([1, 2])
+        lq = rng.randint(1, 600)
+        lkv = rng.randint(lq if causal else 1, 900)
+        out.append((b, h, hkv, lq, lkv, d, causal, rng.choice([0, 1, "head", "channel"]), rng.choice(["f16", "f32"])))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(_random_shapes(48, 20261203))))
+def test_random_shapes(lib, i, shape):
+    B, H, Hkv, Lq, Lkv, d, causal, vpt, odt = shape
+    seed = 7000 + 3 * i
+    q = gaussian((B, H, Lq, d), seed, np.float16)
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    run_problem(lib, q, k, v, causal, vpt, odt, tag="random%d" % i)
