@@ -166,3 +166,29 @@ def test_random_shapes(lib, i, shape):
     k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
     v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
     run_problem(lib, q, k, v, causal, vpt, odt, tag="random%d" % i)
+
+
+def _random_decode_shapes(n, seed):
+    """Seeded random decode-shaped problems (at most 16 query rows per KV
+    head, so the split-KV kernel and the chunk merge run): Lkv up to 5000."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        g = rng.choice([1, 2, 4, 8])
+        lq = rng.randint(1, 16 // g)
+        causal = int(rng.random() < 0.5)
+        hkv = rng.choice([1, 2, 8])
+        out.append((rng.choice([1, 3]), hkv * g, hkv, lq, rng.randint(lq, 5000), rng.choice([64, 128]), causal,
+                    rng.choice([0, 1, "head", "channel"]), rng.choice(["f16", "f32"])))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(_random_decode_shapes(24, 20261204))))
+def test_random_decode_shapes(lib, i, shape):
+    B, H, Hkv, Lq, Lkv, d, causal, vpt, odt = shape
+    seed = 9000 + 3 * i
+    q = gaussian((B, H, Lq, d), seed, np.float16)
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    run_problem(lib, q, k, v, causal, vpt, odt, tag="random_decode%d" % i)
