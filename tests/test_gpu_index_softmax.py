@@ -110,3 +110,32 @@ def test_growing_logits(lib):
     v = r.standard_normal((B, H, L, d)).astype(np.float32)
     run_lut(lib, q, k, v, True, "tensor", "f32", 5, 6.6, tag="growing")
     run_lut(lib, q[:, :, -1:].copy(), k, v, False, "tensor", "f32", 5, 6.6, tag="growing-decode")
+
+
+def _random_shapes(n, seed):
+    """Seeded random problems for the table kernels: prefill and decode
+    shapes, table sizes b = 1 .. 8 (pair table up to b = 5, byte table above),
+    clips 0.5 .. 8, V per tensor, head or channel."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        d = rng.choice([64, 128])
+        causal = int(rng.random() < 0.6)
+        hkv = rng.choice([1, 2, 4])
+        h = hkv * rng.choice([1, 2, 4])
+        lq = rng.randint(1, 16 // (h // hkv)) if rng.random() < 0.3 else rng.randint(1, 500)
+        lkv = rng.randint(lq if causal else 1, 900)
+        out.append((rng.choice([1, 2]), h, hkv, lq, lkv, d, causal, rng.choice(["tensor", "head", "channel"]),
+                    rng.choice(["f16", "f32"]), rng.randint(1, 8), round(rng.uniform(0.5, 8.0), 2)))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(_random_shapes(32, 20261205))))
+def test_random_shapes(lib, i, shape):
+    B, H, Hkv, Lq, Lkv, d, causal, vmode, odt, bits, clip = shape
+    seed = 11000 + 3 * i
+    q = gaussian((B, H, Lq, d), seed, np.float16)
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    run_lut(lib, q, k, v, causal, vmode, odt, bits, clip, tag="random%d" % i)
