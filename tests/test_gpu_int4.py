@@ -108,3 +108,29 @@ def test_int4qk_decode_workload_sampled_rows(lib):
     rows = np.concatenate([b * w.H + np.arange(w.H) for b in (0, 21, 63)]).astype(np.int64)
     split = run_int4(lib, q, k, v, w.causal, "token", w.o_dtype, rows=rows, tag="int4 decode")
     assert split > 0
+
+
+def _random_shapes(n, seed):
+    """Seeded random INT4 Q.K problems: mostly decode shapes (the packed-K
+    kernel), some prefill shapes (K widened in the workspace)."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        g = rng.choice([1, 2, 4, 8])
+        hkv = rng.choice([1, 2, 4])
+        lq = rng.randint(1, 16 // g) if rng.random() < 0.7 else rng.randint(17, 300)
+        causal = int(rng.random() < 0.5)
+        out.append((rng.choice([1, 2]), hkv * g, hkv, lq, rng.randint(lq, 3000), rng.choice([64, 128]), causal,
+                    rng.choice(["tensor", "token", "head", "channel"]), rng.choice(["f16", "f32"])))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(_random_shapes(24, 20261206))))
+def test_random_shapes(lib, i, shape):
+    B, H, Hkv, Lq, Lkv, d, causal, vmode, odt = shape
+    seed = 13000 + 3 * i
+    q = gaussian((B, H, Lq, d), seed, np.float16)
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16)
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    run_int4(lib, q, k, v, causal, vmode, odt, tag="random%d" % i)
