@@ -451,7 +451,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       }
       lsum = static_cast<float>(isum);
     } else {
-      const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
+      const float bias = __builtin_fmaf(fabsf(m_use) >= kBiasGuardFrom ? fabsf(m_use) : 0.0f, kBiasGuard,
+                                        m_use - kLog2_127);
       if constexpr (VPT) {
         // s_t: largest s_V[j] over the tile's keys inside the chunk
         float x = (k0 + lane < s1) ? st->sv[lane] : 0.0f;

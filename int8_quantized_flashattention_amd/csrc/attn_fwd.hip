@@ -584,7 +584,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       }
     } else {
       // exp2(u c2 - bias) = 127 P_tilde, bias with the guard term |m| 2^-21
-      const float bias = __builtin_fmaf(fabsf(m_use), kBiasGuard, m_use - kLog2_127);
+      const float bias = __builtin_fmaf(fabsf(m_use) >= kBiasGuardFrom ? fabsf(m_use) : 0.0f, kBiasGuard,
+                                        m_use - kLog2_127);
       float rst = 0.0f;
       if constexpr (VPT) {
         st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);

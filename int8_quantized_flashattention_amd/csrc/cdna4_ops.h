@@ -37,6 +37,12 @@ constexpr float kRebase = 60.0f;
 // however large |m| is (the fp32 rounding of u c2 and of the bias grows with
 // |m|); P_hat and the row sum scale together, so the guard cancels in O
 constexpr float kBiasGuard = 4.76837158203125e-07f;   // 2^-21
+// The guard is applied only from |m| = 2^15 on: below, the two fp32 roundings
+// (of u c2 and of the bias, each at most |m| 2^-24) move the max key's
+// exponent by less than 2^-8, short of the log2(127.5 / 127) = 0.0057 that a
+// code of 128 needs, and an unneeded guard would shift every 127 P_tilde down
+// by |m| 2^-21 and flip codes that sit near a rounding tie.
+constexpr float kBiasGuardFrom = 32768.0f;
 
 __device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
