@@ -21,7 +21,19 @@ Also reported on the same JSON line:
                 sources still match the ones measured
   cpu_baseline  the oracle (plain C++, all host threads given to it) timed on
                 a bounded, seeded sample of the workload's query rows
-  kernels       per-kernel averages (quantize passes, attention) in the timed region
+  kernels       per-kernel times (quantize passes, attention) in the timed
+                region: mean, median and interquartile range of the HIP-event
+                durations
+  clocks        shader and memory clocks (MHz) read from the driver's sysfs
+                during the timed region
+  measured_peaks  second denominators measured on this GPU right after the
+                timed region: an INT8 MFMA loop (TOP/s) and a streaming HBM
+                read of 2 GiB (GB/s), from libattn_probes
+
+The GPU's clocks ramp up over the first ~100 ms of load, so before the W
+warm-up steps the forward runs back to back for --settle-ms of wall time
+(untimed, not counted as steps): with a handful of warm-up steps the timed
+steps would otherwise land in the ramp.
 
 `--qk int4` times the step with INT4 Q.K: Q and K in per-token 4-bit codes,
 K packed two codes per byte (the decode cache is then a packed K cache), Q
@@ -75,6 +87,9 @@ def parse():
                     help="rotate Q and K by the normalized Hadamard matrix before quantizing them")
     ap.add_argument("--lut-bits", type=int, default=5, help="IndexSoftmax table bits b")
     ap.add_argument("--lut-clip", type=float, default=6.6, help="IndexSoftmax clipping threshold c")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the forward back to back this long before the warm-up steps (clock ramp)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-loop and HBM-read probes")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the fused attention launches (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -121,6 +136,113 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def read_clocks():
+    """Current shader / memory clock levels (MHz) from the amdgpu sysfs files,
+    or {} where the driver does not expose them."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for key, name in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    for line in f:
+                        if "*" in line:
+                            out[key] = float(line.split(":")[1].strip().split("M")[0].split("m")[0])
+            except (OSError, ValueError, IndexError):
+                pass
+        if out:
+            break
+    return out
+
+
+class ClockSampler:
+    """Samples read_clocks() every few ms on a host thread while the timed
+    region runs; reports the median and range of each clock."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self.stop = threading.Event()
+        self.th = threading.Thread(target=self.run, daemon=True)
+
+    def run(self):
+        while not self.stop.is_set():
+            c = read_clocks()
+            if not c:
+                return
+            self.samples.append(c)
+            self.stop.wait(0.002)
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.th.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "sysfs pp_dpm_sclk / pp_dpm_mclk not readable"}
+        out = {"source": "amdgpu sysfs pp_dpm_sclk / pp_dpm_mclk during the timed region",
+               "samples": len(self.samples)}
+        for key in ("sclk_mhz", "mclk_mhz"):
+            v = [c[key] for c in self.samples if key in c]
+            if v:
+                out[key] = float(np.median(v))
+                out[key + "_range"] = [min(v), max(v)]
+        return out
+
+
+def measured_peaks(torch):
+    """INT8 MFMA-loop rate and streaming HBM read rate of this GPU (median of
+    five launches each, after one warm-up launch)."""
+    import ctypes
+    path = os.path.join(ROOT, "int8_quantized_flashattention_amd", "libattn_probes.so")
+    lib = ctypes.CDLL(path)
+    lib.attn_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    n_blocks, iters = 512, 2000                      # two 4-wavefront groups per CU
+    mout = torch.empty(n_blocks * 256 * 16, dtype=torch.int32, device="cuda")
+
+    def mfma():
+        assert lib.attn_probe_mfma_i8(n_blocks, iters, ctypes.c_void_p(mout.data_ptr()), sp) == 0
+
+    t_m = timed(mfma)
+    mfma_ops = n_blocks * 4 * iters * 4 * 65536
+    nbytes = 2 << 30                                 # 2 GiB: far past the 256 MB last-level cache
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    hb = 2048
+    hout = torch.empty(hb * 256, dtype=torch.int32, device="cuda")
+
+    def hbm():
+        assert lib.attn_probe_hbm_read(ctypes.c_void_p(src.data_ptr()), nbytes, hb,
+                                       ctypes.c_void_p(hout.data_ptr()), sp) == 0
+
+    t_h = timed(hbm)
+    del src
+    return {"mfma_i8_tops": round(mfma_ops / t_m / 1e12, 1),
+            "hbm_read_gbs": round(nbytes / t_h / 1e9, 1),
+            "probe": "libattn_probes: 512 groups x 4 wavefronts x 2000 rounds of 4 independent "
+                     "v_mfma_i32_32x32x32_i8; 2 GiB read with non-temporal 16-byte loads (median of 5)"}
 
 
 def host_threads():
@@ -268,6 +390,13 @@ def main():
         else:
             m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
 
+    quantize()
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            attend()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         if not args.attn_only:
             quantize()
@@ -277,19 +406,27 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        if not args.attn_only:
-            quantize()
-        e1.record(stream)
-        attend()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            e0.record(stream)
+            if not args.attn_only:
+                quantize()
+            e1.record(stream)
+            attend()
+            e2.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     step_ms = wall * 1e3 / args.steps
-    attn_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
-    quant_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    attn_t = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
+    quant_t = np.array([e0.elapsed_time(e1) for e0, e1, _ in ev])
+    attn_ms = float(np.mean(attn_t))
+    quant_ms = float(np.mean(quant_t))
+
+    def stats(t):
+        q1, med, q3 = np.percentile(t, [25, 50, 75])
+        return {"mean": round(float(np.mean(t)), 4), "median": round(float(med), 4),
+                "iqr": [round(float(q1), 4), round(float(q3), 4)]}
 
     ops = float(w.ops())
     value = ops / (step_ms * 1e-3) / 1e12
@@ -299,7 +436,9 @@ def main():
     q_bytes = q.nbytes if fused_q else q.size + 4 * w.B * w.H * w.Lq
     o_bytes = w.B * w.H * w.Lq * d * (2 if w.o_dtype == "f16" else 4)
     attn_bytes = q_bytes + kv_bytes + o_bytes      # compulsory HBM bytes
-    # quantize passes: read x (V twice when one scale covers the tensor), write codes and scales
+    # quantize passes, compulsory bytes: read x once, write codes and scales
+    # (one scale for a per-tensor V; its absmax pass re-reads V, mostly from
+    # the last-level cache, and that re-read is not counted)
     quantized = [k, v] if not w.kv_cache else [k[:, :, -1:], v[:, :, -1:]]
     if not fused_q:
         quantized.append(q)
@@ -307,7 +446,7 @@ def main():
     if q4:      # K's codes are half a byte each
         quant_bytes -= quantized[0].size // 2
     if not w.v_per_token:
-        quant_bytes += v.nbytes - 4 * (v.size // d) + 4
+        quant_bytes -= 4 * (v.size // d) - 4
 
     bound_mfma = ops / attn_bytes > PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if bound_mfma:
@@ -334,6 +473,11 @@ def main():
                                                  else "" if fused_q else "_separate_q"), kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
+    peaks = None if args.no_peaks else measured_peaks(torch)
+    if peaks:
+        mp = peaks["mfma_i8_tops"] if bound_mfma else peaks["hbm_read_gbs"]
+        roof["measured_peak"] = mp
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / mp, 4)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
@@ -356,10 +500,15 @@ def main():
                                " + quantize Q + fused attention"))},
         "roofline": roof,
         "kernels": {"attention_ms": round(attn_ms, 4), "quantize_ms": round(quant_ms, 4),
+                    "attention": stats(attn_t), "quantize": stats(quant_t),
                     "attention_tops": round(kernel_tops, 2),
                     "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1)
                     if quant_ms > 0 and not args.attn_only else None},
+        "clocks": clk.summary(),
+        "settle_ms": args.settle_ms,
     }
+    if peaks:
+        out["measured_peaks"] = peaks
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, lut_args, q4)
     print(json.dumps(out), flush=True)

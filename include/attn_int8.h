@@ -368,11 +368,13 @@ attn_status attn_int8_fwd_schedule(int32_t B, int32_t H, int32_t Hkv, int32_t Lq
                                    int32_t* kv_split_len);
 
 /*
- * attn_int8_debug_logits — test entry point: runs the INT8 Q.K^T tile code of
- * the fused prefill kernel (IntAttention §2.1: INT8 products with INT32
- * accumulation) and writes the exact INT32 logit of every visible pair to
- * s_out [B, H, Lq, Lkv] (int32, device, 16-byte aligned). Pairs masked by the
- * causal rule are not written. Same shape rules as attn_int8_fwd.
+ * attn_int8_debug_logits — test entry point: runs the fused prefill kernel
+ * itself, in an instance that keeps its grid, its K staging ring and barriers
+ * and its INT8 Q.K^T tile code (IntAttention §2.1: INT8 products with INT32
+ * accumulation) but writes the exact INT32 logit of every visible pair to
+ * s_out [B, H, Lq, Lkv] (int32, device, 16-byte aligned) in place of the
+ * softmax and P.V. Pairs masked by the causal rule are not written. Same
+ * shape rules as attn_int8_fwd; every shape runs the prefill kernel's tiles.
  */
 attn_status attn_int8_debug_logits(const int8_t* q, const int8_t* k, int32_t B, int32_t H,
                                    int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d, int32_t causal,

@@ -2,7 +2,8 @@
 
 Every source under csrc/ is compiled by hipcc for gfx950 only, then linked
 into one shared library next to this file. Packed-fp32 instruction selection
-is switched off for device code.
+is switched off for device code. The measurement kernels under probes/ (the
+benchmark's MFMA-loop and HBM-read peaks) go into libattn_probes.so.
 """
 import concurrent.futures as cf
 import glob
@@ -16,6 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn_int8.so")
+PROBES = os.path.join(HERE, "probes")
+PROBE_LIB = os.path.join(HERE, "libattn_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -46,19 +49,25 @@ def _compile(src):
     return obj, out
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs], check=True)
+    os.replace(tmp, lib)
+
+
 def build(verbose=False):
-    """Compile every csrc source for gfx950 and link libattn_int8.so."""
+    """Compile every csrc source for gfx950 and link libattn_int8.so; compile
+    the probes into libattn_probes.so."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
+    probes = sorted(glob.glob(os.path.join(PROBES, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        results = list(ex.map(_compile, srcs + probes))
     for _, out in results:
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp,
-                    *[o for o, _ in results]], check=True)
-    os.replace(tmp, LIB)
+    _link([o for o, _ in results[:len(srcs)]], LIB)
+    _link([o for o, _ in results[len(srcs):]], PROBE_LIB)
     return LIB
 
 

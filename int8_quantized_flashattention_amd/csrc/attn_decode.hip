@@ -32,6 +32,11 @@
 
 #include <type_traits>
 
+// fp32 products and sums are rounded as written (the logits and their
+// difference to the running max are the oracle's values bit for bit); fma
+// only where written.
+#pragma clang fp contract(off)
+
 namespace attn {
 namespace {
 
@@ -349,7 +354,13 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   asm volatile("" : "+v"(sq));
 
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
-  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);   // base-2 logit per S_int s_K
+  // Units of the running max m, as in the prefill kernel: exp softmax, the
+  // oracle's fp32 running max of the logits (times 8 for d = 64), fs = log2 e
+  // (/ 8) per unit; IndexSoftmax, base-2 logits (fs = 1), the max of u times
+  // c2 = s_Q log2 e / sqrt(d) (kept >= FLT_MIN: -inf * c2 stays -inf)
+  constexpr float kRs = 0.08838834764831845f;          // fl32(1 / sqrt(128))
+  const float fs = LUT ? 1.0f : (D == 64 ? kLog2e * 0.125f : kLog2e);
+  const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
   // packed K: the QK accumulator starts at -8 sum_c q_c (the codes' bias)
   int s_init = 0;
   if constexpr (K4) {
@@ -402,8 +413,11 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       }
     request_k<D>(kr[S], rk, ln, kq);
 
-    // u = S_int s_K[j], -inf past the chunk end or the causal limit; key
-    // 16 grp + 4 kb + e of the tile is visible iff 4 kb + e <= rel
+    // exp softmax: u = ((float(S_int) s_Q) s_K[j]) / sqrt(d), the oracle's
+    // three rounded fp32 products (for d = 64 the exact last factor 2^-3 is
+    // left out: u is 8 S); IndexSoftmax: u = S_int s_K[j]. -inf past the chunk
+    // end or the causal limit; key 16 grp + 4 kb + e of the tile is visible
+    // iff 4 kb + e <= rel
     const bool mask = (k0 + BN > s1) || (CAUSAL && k0 + BN - 1 > lim_first);
     const int rel = min(lim, s1 - 1) - k0 - 16 * grp;
     float u[NB][4];
@@ -414,18 +428,24 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = static_cast<float>(s[kb][e]) * skk[e];
+        float x = static_cast<float>(s[kb][e]);
+        if constexpr (!LUT) {
+          x = __fmul_rn(__fmul_rn(x, sq), skk[e]);
+          if constexpr (D != 64) x = __fmul_rn(x, kRs);
+        } else {
+          x = x * skk[e];
+        }
         u[kb][e] = (!mask || kb * 4 + e <= rel) ? x : kNegInf;
       }
       gm[kb] = fmaxf(fmaxf(u[kb][0], u[kb][1]), fmaxf(u[kb][2], u[kb][3]));
     }
     const float mx = row_max4(fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3])));
 
-    // online softmax in base 2 with 127 folded into the bias
-    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;
+    // online softmax (IndexSoftmax: c2 > 0, so max(u) c2 == max(u c2))
+    const float mx2 = !LUT ? mx : (mx == kNegInf) ? kNegInf : mx * c2;
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = exp2_hw(m - m_use);
+    const float alpha = exp2_hw((m - m_use) * fs);
     float st_cur = 0.0f, rst = 0.0f;
     uint32_t pw[NB];
     float lsum;
@@ -451,8 +471,6 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       }
       lsum = static_cast<float>(isum);
     } else {
-      const float bias = __builtin_fmaf(fabsf(m_use) >= kBiasGuardFrom ? fabsf(m_use) : 0.0f, kBiasGuard,
-                                        m_use - kLog2_127);
       if constexpr (VPT) {
         // s_t: largest s_V[j] over the tile's keys inside the chunk
         float x = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
@@ -473,7 +491,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          y[e] = exp2_hw(__builtin_fmaf(u[kb][e], c2, -bias));     // 127 P_tilde
+          // 127 P_tilde from the oracle's rounded difference u - m
+          y[e] = exp2_hw(__builtin_fmaf(__fsub_rn(u[kb][e], m_use), fs, kLog2_127));
           word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
         }
         gs[kb] = (y[0] + y[1]) + (y[2] + y[3]);
@@ -483,15 +502,15 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
     }
     const v4i p = v4i{static_cast<int>(pw[0]), static_cast<int>(pw[1]), static_cast<int>(pw[2]),
                       static_cast<int>(pw[3])};
-    l = alpha * l + lsum;
+    l = __builtin_fmaf(alpha, l, lsum);
 
     if constexpr (!VPT) {
       if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
         // fold the INT32 run (frame m) into acc (frame m_f)
         if (m_f == kNegInf) m_f = m_use;
-        float f = exp2_hw(m - m_f);
-        if (__any(m_use - m_f > kRebase)) {
-          const float rb = exp2_hw(m_f - m_use);
+        float f = exp2_hw((m - m_f) * fs);
+        if (__any((m_use - m_f) * fs > kRebase)) {
+          const float rb = exp2_hw((m_f - m_use) * fs);
           f *= rb;
           m_f = m_use;
 #pragma unroll
@@ -549,7 +568,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   wait_vm_lds<0>();                    // the last (empty) requests, before the LDS is released
 
   if constexpr (!VPT) {
-    const float back = (m == kNegInf) ? 0.0f : exp2_hw(m_f - m);
+    const float back = (m == kNegInf) ? 0.0f : exp2_hw((m_f - m) * fs);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -563,7 +582,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<float4*>(pt.acc + prow * D + cb * 16 + grp * 4) =
         make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-  if (grp == 0) *reinterpret_cast<float2*>(pt.ml + prow * 2) = make_float2(m, ltot);
+  // the partial's max in base 2 (-inf stays -inf): the merge weighs chunks by 2^(m_s - M)
+  if (grp == 0) *reinterpret_cast<float2*>(pt.ml + prow * 2) = make_float2(m * fs, ltot);
 }
 
 // Merge of the chunk partials of one query row per wavefront:

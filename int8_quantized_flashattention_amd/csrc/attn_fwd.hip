@@ -37,12 +37,16 @@
 // wavefronts meet once per two tiles.
 //
 // Instruction budget. On gfx950 the issue time of the VALU work per
-// (query, key) pair is the first-order cost next to the pair's MFMA work, so
-// per pair the kernel spends only: one INT32->fp32 convert, one multiply by
-// s_K[j], half a v_max3, one fma for the base-2 exponent (127 folded in), one
-// v_exp_f32, one add for the row sum and one v_cvt_pk_u8_f32 (round to
-// nearest even, saturating) that quantizes P and packs it into the MFMA
-// operand. Everything else is per tile or per workgroup:
+// (query, key) pair is the first-order cost next to the pair's MFMA work.
+// The logit and its distance to the running max are formed exactly as the
+// oracle rounds them (three fp32 products, one fp32 difference), so that only
+// the last-ulp behaviour of the exponential can move a quantized
+// probability; per pair the kernel spends one INT32->fp32 convert, two or
+// three multiplies, half a v_max3, one subtract, one fma for the base-2
+// exponent (127 folded in), one v_exp_f32, one add for the row sum and one
+// v_cvt_pk_u8_f32 (round to nearest even, saturating) that quantizes P and
+// packs it into the MFMA operand. Everything else is per tile or per
+// workgroup:
 //  - for per-tensor V the P_hat . V_hat products keep accumulating in the
 //    INT32 MFMA accumulator while no row of the wavefront raises its max and
 //    are folded into the fp32 accumulator (which keeps its own frame) only
@@ -52,6 +56,12 @@
 #include "cdna4_ops.h"
 
 #include <hip/hip_fp16.h>
+
+// Every fp32 product and sum below is rounded as written: the logits and
+// their difference to the running max must be the oracle's values bit for
+// bit, so no multiply may be fused into a following add (fma only where
+// written).
+#pragma clang fp contract(off)
 
 namespace attn {
 namespace {
@@ -174,14 +184,19 @@ __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, 
     }
 }
 
-// u = S_int * s_K[j] for this lane's keys (the query's factor c2 comes
-// later); masked keys get -inf. rel = (last visible key of the row) - k0 -
-// 16 g, so entry v of block kb is visible iff 32 kb + v <= rel, a compare of
-// a compile-time constant with one per-lane value. Returns the max over the
-// lane pair.
-template <bool MASK>
-__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float* sk, float (&u)[NKB][16], int rel,
-                                              int g) {
+// The dequantized logits of this lane's keys, masked keys -inf; returns the
+// max over the lane pair. EXP (exp softmax): x = ((float(S_int) * s_Q) *
+// s_K[j]) * (1/sqrt d), three rounded fp32 products in that order, the
+// oracle's logit bit for bit (for d = 64 the last factor is 2^-3, which is
+// exact, so it is left out and x is 8 S: the caller works in those units).
+// !EXP (IndexSoftmax): x = float(S_int) * s_K[j], the table path's u. rel =
+// (last visible key of the row) - k0 - 16 g, so entry v of block kb is
+// visible iff 32 kb + v <= rel, a compare of a compile-time constant with one
+// per-lane value.
+template <int D, bool MASK, bool EXP>
+__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float* sk, float sq, float (&x)[NKB][16],
+                                              int rel, int g) {
+  constexpr float kRs = 0.08838834764831845f;          // fl32(1 / sqrt(128))
   // the maximum is taken as a tree (independent partial maxima), so one
   // wavefront is not held up by a long dependency chain
   float gm[NKB * 4];
@@ -193,12 +208,18 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
       const float skk[4] = {skv.x, skv.y, skv.z, skv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = static_cast<float>(s[kb][j4 * 4 + e]) * skk[e];
-        if constexpr (MASK) x = (kb * 32 + j4 * 4 + e <= rel) ? x : kNegInf;
-        u[kb][j4 * 4 + e] = x;
+        float t = static_cast<float>(s[kb][j4 * 4 + e]);
+        if constexpr (EXP) {
+          t = __fmul_rn(__fmul_rn(t, sq), skk[e]);
+          if constexpr (D != 64) t = __fmul_rn(t, kRs);
+        } else {
+          t = t * skk[e];
+        }
+        if constexpr (MASK) t = (kb * 32 + j4 * 4 + e <= rel) ? t : kNegInf;
+        x[kb][j4 * 4 + e] = t;
       }
-      const float* x = &u[kb][j4 * 4];
-      gm[kb * 4 + j4] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float* y = &x[kb][j4 * 4];
+      gm[kb * 4 + j4] = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
     }
 #pragma unroll
   for (int w = NKB * 4; w > 1; w >>= 1)
@@ -209,11 +230,13 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// y = exp2(u c2 - bias) = 127 P_tilde; returns this lane's sum of y and packs
-// P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV operands.
-// Masked keys have u = -inf and c2 >= FLT_MIN, so their y is exactly 0.
+// y = exp2((x - m) ls + log2 127) = 127 P_tilde, with x - m the oracle's
+// rounded fp32 difference of the logit and the running max (ls = log2 e, or
+// log2 e / 8 when x carries the factor 8); returns this lane's sum of y and
+// packs P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV
+// operands. Masked keys have x = -inf, so their y is exactly 0.
 template <bool VPT>
-__device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2, float bias, const float* sv,
+__device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float m, float ls, const float* sv,
                                             float rst, v4i (&pv)[NKB], int g) {
   float gs[NKB * 4];                   // partial row sums, added as a tree
 #pragma unroll
@@ -230,7 +253,7 @@ __device__ __forceinline__ float probs_tile(const float (&u)[NKB][16], float c2,
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        y[e] = exp2_hw(__builtin_fmaf(u[kb][j4 * 4 + e], c2, -bias));
+        y[e] = exp2_hw(__builtin_fmaf(__fsub_rn(x[kb][j4 * 4 + e], m), ls, kLog2_127));
         word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
       }
       gs[kb * 4 + j4] = (y[0] + y[1]) + (y[2] + y[3]);
@@ -352,9 +375,13 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
 // V scales constant along the keys (per tensor, head or channel) and INT8 Q.
 // QF: 0 INT8 Q; 1 fp16/fp32 Q quantized here; 2 the same after the
 // normalized Hadamard rotation of each Q row.
-template <int D, bool CAUSAL, bool VPT, bool OUT_F16, int QF, int LUT>
+// DUMP: the logits-dump instance (test hook). It runs the same grid, the same
+// K staging ring, barriers and Q.K^T tile code, and writes the INT32 logit
+// of every visible pair instead of the softmax and P.V (INT8 Q, no scales).
+template <int D, bool CAUSAL, bool VPT, bool OUT_F16, int QF, int LUT, bool DUMP = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   static_assert(!LUT || (!VPT && !QF), "IndexSoftmax takes INT8 Q and V scales constant along the keys");
+  static_assert(!DUMP || (!VPT && !QF && !LUT), "the dump instance takes INT8 Q");
   constexpr int NC = D / 32;
   // PRE: V operands of this many channel chunks are read right after Q.K^T,
   // ahead of the softmax (the IndexSoftmax kernels have registers for one)
@@ -381,7 +408,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   const bool qvalid = qi < a.Lq;
   const int shift = a.Lkv - a.Lq;   // bottom-right causal alignment
 
-  const Bufs bf = make_bufs(a, kv_base, D, true, VPT);
+  // the dump instance has no V or scales: its V stages and scale slots are
+  // filled from K (and never read)
+  const Bufs bf = make_bufs(a, kv_base, D, !DUMP, VPT);
   Lanes<D> ln;
   ln.init(wave, lane);
 
@@ -429,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       qf[c] = v4i{0, 0, 0, 0};
       if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
     }
-    sq = qvalid ? a.s_q[q_base + qi] : 0.0f;
+    sq = (qvalid && !DUMP) ? a.s_q[q_base + qi] : 0.0f;
   }
   __syncthreads();
   request_tile<D, true, VPT>(sm[0], bf, ln, wave, lane, 0);
@@ -522,12 +551,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
   asm volatile("" : "+v"(sq));
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
-  // base-2 logit per unit of S_int * s_K. Kept >= FLT_MIN so that -inf * c2
-  // stays -inf for masked keys; a zero query (s_Q = 0) has S_int = 0 and all
-  // its logits stay exactly 0.
+  // Units of the running max m. Exp softmax: m is the oracle's fp32 running
+  // max of the logits (times 8 for d = 64), and fs = log2 e (/ 8) turns a
+  // difference of two such values into base 2. IndexSoftmax: m is in base-2
+  // logits (fs = 1), the max of u times c2 = s_Q log2 e / sqrt(d), kept >=
+  // FLT_MIN so that -inf * c2 stays -inf for masked keys.
+  const float fs = LUT ? 1.0f : (D == 64 ? kLog2e * 0.125f : kLog2e);
   const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
   // IndexSoftmax: table index per unit of u below the running max, and the
-  // running max of u itself (kept beside m, which is in base-2 logits)
+  // running max of u itself (kept beside m)
   const float kap = (sq * inv_sqrt_d) * a.lut_k;
   const float nf = static_cast<float>(a.lut_n);
   float m_u = kNegInf;
@@ -547,6 +579,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
     v16i s[NKB];
     qk_tile<D>(s, st->k, ln, qf);
+    if constexpr (DUMP) {
+      if (qvalid) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + kb * 32 + g * 16 + v;
+            if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
+          }
+      }
+    } else {
     v4i vpre[PRE > 0 ? PRE : 1][NKB];
 #pragma unroll
     for (int c = 0; c < PRE; ++c)
@@ -554,19 +597,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb) vpre[c][kb] = v_operand<D>(st->v, ln, c, kb);
     if constexpr (PRE > 0) __builtin_amdgcn_sched_barrier(0);
     const bool mask = (k0 + BN > a.Lkv) || (CAUSAL && k0 + BN - 1 > lim_first);
-    float u[NKB][16];
+    float u[NKB][16];                  // logits x (exp softmax) or u (IndexSoftmax)
     float mx;
     if (!mask) {
-      mx = dequant_tile<false>(s, st->sk, u, 0, g);
+      mx = dequant_tile<D, false, !LUT>(s, st->sk, sq, u, 0, g);
     } else {
-      mx = dequant_tile<true>(s, st->sk, u, min(lim, a.Lkv - 1) - k0 - 16 * g, g);
+      mx = dequant_tile<D, true, !LUT>(s, st->sk, sq, u, min(lim, a.Lkv - 1) - k0 - 16 * g, g);
     }
 
     // ---- softmax(t): running max, 127 P_tilde, row sum, P_hat ----
-    const float mx2 = (mx == kNegInf) ? kNegInf : mx * c2;   // c2 > 0: max(u) c2 == max(u c2)
+    // (IndexSoftmax: c2 > 0, so max(u) c2 == max(u c2))
+    const float mx2 = !LUT ? mx : (mx == kNegInf) ? kNegInf : mx * c2;
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = exp2_hw(m - m_use);            // 1 if unchanged, 0 on the first tile
+    const float alpha = exp2_hw((m - m_use) * fs);     // 1 if unchanged, 0 on the first tile
     v4i p[NKB];
     float lsum;
     float st_cur = 0.0f;
@@ -583,26 +627,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         else lsum = lut_tile<true>(u, kap, mu, nf, tab, rel, p);
       }
     } else {
-      // exp2(u c2 - bias) = 127 P_tilde, bias with the guard term |m| 2^-21
-      const float bias = __builtin_fmaf(fabsf(m_use) >= kBiasGuardFrom ? fabsf(m_use) : 0.0f, kBiasGuard,
-                                        m_use - kLog2_127);
       float rst = 0.0f;
       if constexpr (VPT) {
         st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);
         rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
       }
-      lsum = probs_tile<VPT>(u, c2, bias, st->sv, rst, p, g);
+      lsum = probs_tile<VPT>(u, m_use, fs, st->sv, rst, p, g);
     }
-    l = alpha * l + lsum;
+    l = __builtin_fmaf(alpha, l, lsum);
 
     if constexpr (!VPT) {
       if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
         // tile t raised some row's max: the INT32 run (tiles before t, frame
         // m) goes into acc (frame m_f) before PV(t) starts a new run
         if (m_f == kNegInf) m_f = m_use;
-        float f = exp2_hw(m - m_f);                   // 0 before the first tile
-        if (__any(m_use - m_f > kRebase)) {           // keep acc far from overflow
-          const float r = exp2_hw(m_f - m_use);
+        float f = exp2_hw((m - m_f) * fs);            // 0 before the first tile
+        if (__any((m_use - m_f) * fs > kRebase)) {    // keep acc far from overflow
+          const float r = exp2_hw((m_f - m_use) * fs);
           f *= r;
           m_f = m_use;
 #pragma unroll
@@ -634,6 +675,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         for (int v = 0; v < 16; ++v)
           acc[c][v] = __builtin_fmaf(alpha, acc[c][v], st_cur * static_cast<float>(acc_i[c][v]));
     }
+    }  // !DUMP
 
     // after an odd tile: tiles t+1 and t+2 must have landed before anyone
     // reads them; after the barrier every wavefront is done with stages t-1
@@ -645,10 +687,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   };
 
   for (int t = 0; t < n_tiles; ++t) step(t, &sm[t & 3], &sm[(t + 2) & 3], &sm[(t + 3) & 3]);
+  if constexpr (DUMP) return;
 
   if constexpr (!VPT) {
     // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run
-    const float back = exp2_hw(m_f - m);
+    const float back = exp2_hw((m_f - m) * fs);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -685,56 +728,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) = make_float4(o0, o1, o2, o3);
       }
     }
-  if (a.lse && g == 0) a.lse[q_base + qi] = (m + __builtin_log2f(ltot) - kLog2_127) * kLn2;
-}
-
-// Logits dump: the same K staging and Q.K^T tile code as the forward, writing
-// the exact INT32 logit of every visible pair.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_logits_kernel(FwdArgs a) {
-  __shared__ Stage<D> st;
-  const int bh = blockIdx.x;
-  const int rb = blockIdx.y;
-  const int b = bh / a.H, h = bh % a.H;
-  const int hk = h / (a.H / a.Hkv);
-  const int64_t kv_base = (static_cast<int64_t>(b) * a.Hkv + hk) * a.Lkv;
-  const int64_t q_base = static_cast<int64_t>(bh) * a.Lq;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int g = lane >> 5, lr = lane & 31;
-  const int qi = rb * BM + wave * 32 + lr;
-  const bool qvalid = qi < a.Lq;
-  const int lim = CAUSAL ? qi + (a.Lkv - a.Lq) : a.Lkv - 1;
-  const Bufs bf = make_bufs(a, kv_base, D, false, false);
-  Lanes<D> ln;
-  ln.init(wave, lane);
-  v4i qf[D / 32];
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    qf[c] = v4i{0, 0, 0, 0};
-    if (qvalid) qf[c] = *reinterpret_cast<const v4i*>(a.q + (q_base + qi) * D + c * 32 + g * 16);
-  }
-  const int last_q = min(rb * BM + BM - 1, a.Lq - 1);
-  const int kv_end = CAUSAL ? min(a.Lkv, last_q + (a.Lkv - a.Lq) + 1) : a.Lkv;
-  for (int k0 = 0; k0 < kv_end; k0 += BN) {
-    request_tile<D, false, false>(st, bf, ln, wave, lane, k0);
-    wait_vm_lds<0>();
-    bare_barrier();
-    v16i s[NKB];
-    qk_tile<D>(s, st.k, ln, qf);
-    if (qvalid) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + kb * 32 + g * 16 + v;
-          if (key < a.Lkv && key <= lim) a.s_dump[(q_base + qi) * a.Lkv + key] = s[kb][v];
-        }
-    }
-    wait_vm_lds<0>();
-    bare_barrier();              // every wavefront has read the stage before it is refilled
-  }
+  if (a.lse && g == 0) a.lse[q_base + qi] = (m * fs + __builtin_log2f(ltot) - kLog2_127) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16>
@@ -772,8 +766,8 @@ hipError_t launch_vo(const FwdArgs& a, hipStream_t st) {
 template <int D, bool CAUSAL>
 hipError_t launch_logits_t(const FwdArgs& a, hipStream_t st) {
   const int n_rb = (a.Lq + BM - 1) / BM;
-  const dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(n_rb));
-  hipLaunchKernelGGL((attn_logits_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, st, a);
+  const dim3 grid(static_cast<unsigned>(a.B * a.H * n_rb));
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, false, 0, 0, true>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -60,6 +60,20 @@ def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
 
+def default_threads():
+    """Worker threads when a call passes nthreads=0: the CPUs this process may
+    run on, at most 16 (a GPU host may show many more CPUs than its share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _nt(nthreads):
+    return nthreads if nthreads and nthreads > 0 else default_threads()
+
+
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle rejected the arguments of %s" % what)
@@ -170,7 +184,7 @@ def logits_i32(q, k, B, H, Hkv, Lq, Lkv, d, nthreads=0, L=None):
     q = np.ascontiguousarray(q, np.int8)
     k = np.ascontiguousarray(k, np.int8)
     out = np.empty((B, H, Lq, Lkv), np.int32)
-    _check((L or lib()).oracle_logits_i32(_p(q), _p(k), B, H, Hkv, Lq, Lkv, d, _p(out), nthreads),
+    _check((L or lib()).oracle_logits_i32(_p(q), _p(k), B, H, Hkv, Lq, Lkv, d, _p(out), _nt(nthreads)),
            "logits_i32")
     return out
 
@@ -210,7 +224,7 @@ def attn_int8(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal
         lse = np.empty((nr,), np.float32)
     rc = (L or lib()).oracle_attn_int8(*(_p(a) for a in args), int(v_per_token), B, H, Hkv, Lq, Lkv,
                                        d, int(causal), kv_tile, kv_split_len,
-                                       *_lut_args(index_softmax), _p(r), nr, _p(o), _p(lse), nthreads)
+                                       *_lut_args(index_softmax), _p(r), nr, _p(o), _p(lse), _nt(nthreads))
     _check(rc, "attn_int8")
     return o, lse
 
@@ -243,7 +257,7 @@ def attn_ref_f64(q, k, v, B, H, Hkv, Lq, Lkv, d, causal, rows=None, nthreads=0, 
         nr = r.size
         o = np.empty((nr, d), np.float64)
     rc = (L or lib()).oracle_attn_ref_f64(_p(q), _p(k), _p(v), B, H, Hkv, Lq, Lkv, d, int(causal),
-                                          _p(r), nr, _p(o), nthreads)
+                                          _p(r), nr, _p(o), _nt(nthreads))
     _check(rc, "attn_ref_f64")
     return o
 

@@ -14,10 +14,16 @@ LIB = os.path.join(HERE, "liboracle.so")
 FLAGS = ["-std=c++17", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-pthread"]
 
 
-def build(out=LIB, plant=None, extra=()):
+# AddressSanitizer + UBSan build (tests only; load it with the host's
+# libasan preloaded)
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out=LIB, plant=None, extra=(), sanitize=False):
     """Compile the oracle into `out`. `plant` names a deliberate mistake, used
-    only by the tests that show the pins catch such mistakes."""
-    cmd = ["g++", *FLAGS, *extra]
+    only by the tests that show the pins catch such mistakes; `sanitize`
+    builds it with AddressSanitizer and UBSan."""
+    cmd = ["g++", *FLAGS, *(SANITIZE if sanitize else ()), *extra]
     if plant is not None:
         cmd.append('-DORACLE_PLANT="%s"' % plant)
     cmd += [SRC, "-o", out + ".tmp"]

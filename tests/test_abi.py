@@ -268,3 +268,29 @@ def test_schedule_and_workspace_queries():
     with pytest.raises(m.AttnError):
         m.attn_int8_fwd_schedule(1, 1, 1, 8, 8, 48, 0)
     assert L.attn_int8_fwd_schedule(1, 1, 1, 8, 8, 64, 0, None, None) == INVALID
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probes.h")
+PROBE_LIB = os.path.join(ROOT, "int8_quantized_flashattention_amd", "libattn_probes.so")
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    # the benchmark's measurement kernels (include/attn_probes.h): every
+    # declared symbol is exported, and invalid arguments return 1 before any
+    # launch
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_probe_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["attn_probe_hbm_read", "attn_probe_mfma_i8"]
+    lib = ctypes.CDLL(PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.attn_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    assert lib.attn_probe_mfma_i8(0, 10, A, None) == 1
+    assert lib.attn_probe_mfma_i8(4, 0, A, None) == 1
+    assert lib.attn_probe_mfma_i8(4, 10, None, None) == 1
+    assert lib.attn_probe_hbm_read(A, 1 << 20, 8, None, None) == 1
+    assert lib.attn_probe_hbm_read(A, 100, 8, A, None) == 1          # not a multiple of 16
+    assert lib.attn_probe_hbm_read(A + 4, 1 << 20, 8, A, None) == 1  # misaligned source
+    assert lib.attn_probe_hbm_read(A, 1 << 20, 0, A, None) == 1

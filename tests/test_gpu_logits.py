@@ -1,5 +1,8 @@
-"""INT32 logits from the fused kernel's tile code == exact integer products.
-Visible pairs must match bit for bit; masked pairs must be left untouched."""
+"""INT32 logits from the fused prefill kernel (its dump instance: the same
+grid, K staging ring, barriers and Q.K^T tile code) == exact integer products.
+Visible pairs must match bit for bit; masked pairs must be left untouched.
+The cases include one head of the headline shape (L = 4096, d = 128, causal:
+64 KV tiles through the four-stage ring) and a ragged d = 128 problem."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +24,7 @@ CASES = [  # B, H, Hkv, Lq, Lkv, d, causal
     (1, 1, 1, 128, 128, 64, 0), (1, 8, 8, 1024, 1024, 64, 1), (1, 8, 8, 1024, 1024, 64, 0),
     (2, 4, 2, 77, 130, 128, 1), (1, 2, 1, 1, 200, 128, 0), (1, 1, 1, 300, 300, 128, 1),
     (1, 2, 2, 50, 190, 64, 1), (3, 8, 1, 129, 65, 128, 0), (1, 1, 1, 1, 1, 64, 1),
+    (1, 1, 1, 4096, 4096, 128, 1), (1, 2, 1, 2047, 3001, 128, 1), (2, 4, 4, 1000, 1000, 128, 0),
 ]
 
 
