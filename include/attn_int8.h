@@ -236,6 +236,37 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
                           size_t workspace_bytes, void* stream);
 
 /*
+ * attn_int8_fwd_noalloc — attn_int8_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, bit for bit, with no
+ * workspace argument. Decode-shaped problems keep their split-KV partials in
+ * a static device array of attn_int8_fwd_noalloc_max_scratch() bytes (32 MiB)
+ * that the library holds on each GPU it runs on until the process ends; the
+ * call allocates and frees nothing (no hipMalloc, no allocating library
+ * routine).
+ *
+ *   Arguments as for attn_int8_fwd, without workspace / workspace_bytes. The
+ *   calling thread's current device must be the device of `stream`.
+ *   Problems whose attn_int8_fwd_workspace_size(...) exceeds the scratch size
+ *   return ATTN_ERR_UNSUPPORTED (nothing launched); every other check and
+ *   status is as for attn_int8_fwd.
+ *   Every call on one GPU shares that GPU's scratch, and each call's kernels
+ *   write every scratch entry they read first (nothing needs clearing), so
+ *   calls in stream order are independent; calls that overlap on one GPU
+ *   (different streams, or different host threads without ordering) race on
+ *   the scratch and their results are undefined.
+ */
+attn_status attn_int8_fwd_noalloc(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                                  const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                  attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv,
+                                  int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* stream);
+
+/* attn_int8_fwd_noalloc_max_scratch — bytes of the per-GPU scratch of
+ * attn_int8_fwd_noalloc: the largest attn_int8_fwd_workspace_size(...) it
+ * accepts. */
+size_t attn_int8_fwd_noalloc_max_scratch(void);
+
+/*
  * attn_int8_fwd_qfloat — attn_int8_fwd with the per-token quantization of Q
  * fused into the kernels' Q load (IntAttention §2.1 Eq. 3, token-level as in
  * the INT-FlashAttention abstract): each query row is quantized in the kernel

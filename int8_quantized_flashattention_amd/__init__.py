@@ -37,6 +37,9 @@ SIGNATURES = {
     "attn_kv_append": (ctypes.c_int, [_P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P]),
     "attn_int8_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "attn_int8_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "attn_int8_fwd_noalloc_max_scratch": (_SZ, []),
     "attn_int8_fwd_qfloat": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_int, _P,
                                             ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _P, _SZ, _P]),
@@ -291,6 +294,8 @@ def _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
+    if workspace is False:           # the no-allocation forward takes none
+        return (B, H, Hkv, Lq, Lkv, d), out, lse, None, 0
     need = attn_int8_fwd_workspace_size(B, H, Hkv, Lq, Lkv, d, causal)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -317,6 +322,31 @@ def attn_int8_fwd(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.flo
                             *shape, int(causal), _ptr(workspace), ws_bytes, _stream(stream))
     _check("attn_int8_fwd", st)
     return (out, lse) if return_lse else out
+
+
+def attn_int8_fwd_noalloc(q, s_q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,
+                          return_lse=False, out=None, lse=None, stream=None):
+    """attn_int8_fwd without a workspace: decode-shaped problems keep their
+    split-KV partials in the library's static per-GPU scratch, and the call
+    allocates nothing in the library (pass `out` (and `lse`) to allocate
+    nothing here either). Calls that overlap on one GPU race on that scratch.
+    Returns O (and lse when return_lse)."""
+    _dev(q, "q", torch.int8)
+    _dev(s_q, "s_q", torch.float32)
+    shape, out, lse, _, _ = _fwd_common(q, k, s_k, v, s_v, v_per_token, causal, o_dtype, return_lse, out, lse,
+                                        workspace=False)
+    if s_q.numel() != shape[0] * shape[1] * shape[3]:
+        raise ValueError("s_q size does not match q")
+    st = _lib.attn_int8_fwd_noalloc(_ptr(q), _ptr(s_q), _ptr(k), _ptr(s_k), _ptr(v), _ptr(s_v),
+                                    _vmode(v_per_token), _ptr(out), ATTN_F16 if o_dtype == torch.float16 else ATTN_F32,
+                                    _ptr(lse), *shape, int(causal), _stream(stream))
+    _check("attn_int8_fwd_noalloc", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_int8_fwd_noalloc_max_scratch():
+    """Bytes of the per-GPU scratch of attn_int8_fwd_noalloc."""
+    return int(_lib.attn_int8_fwd_noalloc_max_scratch())
 
 
 def attn_int8_fwd_qfloat(q, k, s_k, v, s_v, v_per_token, causal, o_dtype=torch.float16,

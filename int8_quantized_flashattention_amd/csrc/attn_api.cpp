@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "attn_internal.h"
 
@@ -121,8 +122,8 @@ struct FwdRequest {
   void* stream = nullptr;
 };
 
-// Checks every argument, then launches. Nothing is launched on any error.
-attn_status run_fwd(const FwdRequest& r) {
+// Checks every argument (the workspace only when check_ws).
+attn_status check_fwd(const FwdRequest& r, bool check_ws) {
   if (!r.k || !r.s_k || !r.v || !r.s_v || !r.o) return ATTN_ERR_INVALID_ARG;
   if (r.lut_bits != 0 && !lut_params_ok(r.lut_bits, r.clip)) return ATTN_ERR_INVALID_ARG;
   if (r.q_float) {
@@ -144,8 +145,15 @@ attn_status run_fwd(const FwdRequest& r) {
   if (!aligned(r.k, 16) || !aligned(r.v, 16) || !aligned(r.o, 16)) return ATTN_ERR_INVALID_ARG;
   if (!aligned(r.s_k, 4) || !aligned(r.s_v, 4) || (r.lse && !aligned(r.lse, 4))) return ATTN_ERR_INVALID_ARG;
   const size_t need = workspace_need(r.B, r.H, r.Hkv, r.Lq, r.Lkv, r.d, r.causal, r.k_int4);
-  if (need > 0 && (!r.workspace || r.workspace_bytes < need || !aligned(r.workspace, 256)))
+  if (check_ws && need > 0 && (!r.workspace || r.workspace_bytes < need || !aligned(r.workspace, 256)))
     return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// Checks every argument, then launches. Nothing is launched on any error.
+attn_status run_fwd(const FwdRequest& r) {
+  const attn_status chk = check_fwd(r, true);
+  if (chk != ATTN_OK) return chk;
 
   attn::FwdArgs a{};
   a.q = r.q; a.s_q = r.s_q; a.k = r.k; a.s_k = r.s_k; a.v = r.v; a.s_v = r.s_v;
@@ -190,6 +198,33 @@ attn_status run_fwd(const FwdRequest& r) {
 }  // namespace
 
 namespace {
+
+// ---------------------------------------------------------------------------
+// Scratch of attn_int8_fwd_noalloc: the split-KV partials live in a static
+// device array (one copy per GPU, held until the process ends) instead of a
+// caller-provided workspace. In host code `scratch` names a host-side stand-in,
+// not a device address: the device address of each GPU's copy is looked up
+// once per device, with that device current, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;   // 32 MiB
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This thread's current device's copy of scratch (looked up on first use).
+attn_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_HIP;
+  if (dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
 
 // the arguments every forward shares
 FwdRequest request(const int8_t* k, const float* s_k, const int8_t* v, const float* s_v, attn_vscale v_mode,
@@ -340,6 +375,31 @@ attn_status attn_int8_fwd(const int8_t* q, const float* s_q, const int8_t* k, co
   FwdRequest r = request(k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq, Lkv, d, causal, workspace,
                          workspace_bytes, stream);
   r.q = q; r.s_q = s_q;
+  return run_fwd(r);
+}
+
+size_t attn_int8_fwd_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+attn_status attn_int8_fwd_noalloc(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
+                                  const int8_t* v, const float* s_v, attn_vscale v_mode, void* o,
+                                  attn_dtype o_dt, float* lse, int32_t B, int32_t H, int32_t Hkv,
+                                  int32_t Lq, int32_t Lkv, int32_t d, int32_t causal, void* stream) {
+  if (!q || !s_q) return ATTN_ERR_INVALID_ARG;
+  FwdRequest r = request(k, s_k, v, s_v, v_mode, o, o_dt, lse, B, H, Hkv, Lq, Lkv, d, causal, nullptr, 0, stream);
+  r.q = q; r.s_q = s_q;
+  const attn_status chk = check_fwd(r, false);       // every argument but the workspace
+  if (chk != ATTN_OK) return chk;
+  const size_t need = attn::fwd_workspace_bytes(B, H, Hkv, Lq, Lkv, d, causal);
+  if (need > kNoAllocScratchBytes) return ATTN_ERR_UNSUPPORTED;
+  if (need > 0) {
+    // every partial the merge reads is written by the split-KV kernel first,
+    // so the scratch needs no clearing between calls
+    void* ws = nullptr;
+    const attn_status e = current_scratch(&ws);
+    if (e != ATTN_OK) return e;
+    r.workspace = ws;
+    r.workspace_bytes = kNoAllocScratchBytes;
+  }
   return run_fwd(r);
 }
 

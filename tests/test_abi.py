@@ -294,3 +294,24 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.attn_probe_hbm_read(A, 100, 8, A, None) == 1          # not a multiple of 16
     assert lib.attn_probe_hbm_read(A + 4, 1 << 20, 8, A, None) == 1  # misaligned source
     assert lib.attn_probe_hbm_read(A, 1 << 20, 0, A, None) == 1
+
+
+def test_noalloc_forward_rejects_before_any_hip_call():
+    # arguments are checked before the per-GPU scratch is looked up, so these
+    # return their status with no HIP call at all (this host has no GPU)
+    f = L.attn_int8_fwd_noalloc
+    args = [A, A, A, A, A, A, 0, A, 1, None, 1, 2, 1, 8, 8, 64, 0, None]
+    bad = list(args)
+    bad[0] = None                                   # q
+    assert f(*bad) == INVALID
+    bad = list(args)
+    bad[15] = 96                                    # d
+    assert f(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[9] = A + 2                                  # misaligned lse
+    assert f(*bad) == INVALID
+    # a decode shape whose split-KV partials exceed the scratch
+    big = [A, A, A, A, A, A, 1, A, 1, None, 4096, 16, 16, 1, 8, 128, 0, None]
+    assert m.attn_int8_fwd_workspace_size(4096, 16, 16, 1, 8, 128, 0) > L.attn_int8_fwd_noalloc_max_scratch()
+    assert f(*big) == UNSUPPORTED
+    assert L.attn_int8_fwd_noalloc_max_scratch() == 32 << 20
