@@ -358,14 +358,27 @@ __device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int
 }
 
 // Workgroup -> (b*h, row block). Workgroups are dealt to the 8 XCDs round
-// robin, so consecutive ids land on different XCDs (each with its own L2);
-// the id is re-numbered so that each XCD walks whole heads, row blocks of a
-// head back to back (longest causal block first). The workgroups resident on
-// one XCD then share the K/V of two or three heads.
+// robin, so consecutive ids land on different XCDs (each with its own L2),
+// and each XCD takes a contiguous range of heads. When every XCD holds whole
+// heads, its heads are taken in groups of up to 8 and each group row block by
+// row block, longest (causal) first: every head's longest blocks start early,
+// so the launch does not end waiting on a long block that started late, while
+// the workgroups in flight on an XCD still share the K/V of at most 8 heads.
+// Otherwise heads are walked one after the other, longest block first.
 __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
   const int n = gridDim.x, id = blockIdx.x;
   const int xcd = id & 7, slot = id >> 3;
-  const int w = xcd * (n >> 3) + min(xcd, n & 7) + slot;
+  const int per = n >> 3;
+  if ((n & 7) == 0 && per % n_rb == 0) {
+    const int nh = per / n_rb;                 // heads of this XCD
+    int G = nh < 8 ? nh : 8;
+    while (nh % G) --G;                        // groups of G heads
+    const int grp = slot / (G * n_rb), s = slot - grp * G * n_rb;
+    rb = n_rb - 1 - s / G;
+    bh = xcd * nh + grp * G + s % G;
+    return;
+  }
+  const int w = xcd * per + min(xcd, n & 7) + slot;
   bh = w / n_rb;
   rb = n_rb - 1 - (w - bh * n_rb);
 }
