@@ -28,10 +28,12 @@ extern "C" {
 int attn_probe_mfma_i8(int32_t n_blocks, int32_t iters, int32_t* out, void* stream);
 
 /* attn_probe_hbm_read — reads n_bytes (a multiple of 16, src 16-byte aligned)
- * once with non-temporal 16-byte loads, n_blocks workgroups of 256 lanes in a
- * grid-stride loop. out: uint32 [n_blocks * 256], device, receives one XOR
- * fold per lane. Bytes per launch = n_bytes. */
-int attn_probe_hbm_read(const void* src, int64_t n_bytes, int32_t n_blocks, uint32_t* out, void* stream);
+ * once with 16-byte loads (non-temporal when `nontemporal` is nonzero):
+ * n_blocks workgroups of 256 lanes, each streaming one contiguous slice with
+ * four loads per lane in flight. out: uint32 [n_blocks * 256], device,
+ * receives one XOR fold per lane. Bytes per launch = n_bytes. */
+int attn_probe_hbm_read(const void* src, int64_t n_bytes, int32_t n_blocks, int32_t nontemporal, uint32_t* out,
+                        void* stream);
 
 #ifdef __cplusplus
 }

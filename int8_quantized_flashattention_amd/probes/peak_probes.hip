@@ -40,22 +40,25 @@ __global__ __launch_bounds__(256) void mfma_i8_loop(int iters, int32_t* out) {
   }
 }
 
-// Grid-stride read of n16 16-byte words (four loads in flight per lane),
-// folded into one word per thread.
-__global__ __launch_bounds__(256) void hbm_read(const v4u* src, int64_t n16, uint32_t* out) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+// Each workgroup streams one contiguous slice of n16 16-byte words (a
+// multiple of 1024 words per slice; the tail slice may be shorter): every lane
+// keeps four 16-byte loads in flight, 16 KB per workgroup per round, and folds
+// the words into one value per thread. NT: non-temporal loads.
+template <bool NT>
+__global__ __launch_bounds__(256) void hbm_read(const v4u* src, int64_t n16, int64_t per_block, uint32_t* out) {
+  const int64_t beg = static_cast<int64_t>(blockIdx.x) * per_block;
+  const int64_t end = beg + per_block < n16 ? beg + per_block : n16;
   uint32_t x = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const v4u w0 = __builtin_nontemporal_load(src + i);
-    const v4u w1 = __builtin_nontemporal_load(src + i + stride);
-    const v4u w2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const v4u w3 = __builtin_nontemporal_load(src + i + 3 * stride);
-    x ^= w0.x ^ w0.y ^ w0.z ^ w0.w ^ w1.x ^ w1.y ^ w1.z ^ w1.w;
-    x ^= w2.x ^ w2.y ^ w2.z ^ w2.w ^ w3.x ^ w3.y ^ w3.z ^ w3.w;
+  int64_t i = beg + threadIdx.x;
+  for (; i + 3 * 256 < end; i += 4 * 256) {
+    v4u w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = NT ? __builtin_nontemporal_load(src + i + u * 256) : src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
   }
-  for (; i < n16; i += stride) {
-    const v4u w = __builtin_nontemporal_load(src + i);
+  for (; i < end; i += 256) {
+    const v4u w = NT ? __builtin_nontemporal_load(src + i) : src[i];
     x ^= w.x ^ w.y ^ w.z ^ w.w;
   }
   out[static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = x;
@@ -71,11 +74,19 @@ int attn_probe_mfma_i8(int32_t n_blocks, int32_t iters, int32_t* out, void* stre
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
-int attn_probe_hbm_read(const void* src, int64_t n_bytes, int32_t n_blocks, uint32_t* out, void* stream) {
+int attn_probe_hbm_read(const void* src, int64_t n_bytes, int32_t n_blocks, int32_t nontemporal, uint32_t* out,
+                        void* stream) {
   if (!src || !out || n_blocks < 1 || n_bytes < 16 || (n_bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
     return 1;
-  hipLaunchKernelGGL(hbm_read, dim3(n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const v4u*>(src), n_bytes / 16, out);
+  const int64_t n16 = n_bytes / 16;
+  const int64_t per_block = (n16 + n_blocks - 1) / n_blocks;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    hipLaunchKernelGGL(hbm_read<true>, dim3(n_blocks), dim3(256), 0, st, static_cast<const v4u*>(src), n16, per_block,
+                       out);
+  else
+    hipLaunchKernelGGL(hbm_read<false>, dim3(n_blocks), dim3(256), 0, st, static_cast<const v4u*>(src), n16, per_block,
+                       out);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

@@ -285,15 +285,15 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     for n in names:
         assert hasattr(lib, n), n
     lib.attn_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    lib.attn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                                        ctypes.c_void_p]
+    lib.attn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p]
     assert lib.attn_probe_mfma_i8(0, 10, A, None) == 1
     assert lib.attn_probe_mfma_i8(4, 0, A, None) == 1
     assert lib.attn_probe_mfma_i8(4, 10, None, None) == 1
-    assert lib.attn_probe_hbm_read(A, 1 << 20, 8, None, None) == 1
-    assert lib.attn_probe_hbm_read(A, 100, 8, A, None) == 1          # not a multiple of 16
-    assert lib.attn_probe_hbm_read(A + 4, 1 << 20, 8, A, None) == 1  # misaligned source
-    assert lib.attn_probe_hbm_read(A, 1 << 20, 0, A, None) == 1
+    assert lib.attn_probe_hbm_read(A, 1 << 20, 8, 0, None, None) == 1
+    assert lib.attn_probe_hbm_read(A, 100, 8, 0, A, None) == 1          # not a multiple of 16
+    assert lib.attn_probe_hbm_read(A + 4, 1 << 20, 8, 1, A, None) == 1  # misaligned source
+    assert lib.attn_probe_hbm_read(A, 1 << 20, 0, 0, A, None) == 1
 
 
 def test_noalloc_forward_rejects_before_any_hip_call():
