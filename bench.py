@@ -48,6 +48,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--q-path fused|separate] [--softmax exp|index]
        python bench.py --copy-calibration     (1 GiB device copies, for the
                                                HBM counter scale)
+       python bench.py --lds-patterns         (the prefill tile's four LDS access
+                                               patterns, one launch each, for the
+                                               LDS counters of each pattern)
 """
 import hashlib
 import argparse
@@ -92,6 +95,8 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-loop and HBM-read probes")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the fused attention launches (for profiling runs)")
+    ap.add_argument("--lds-patterns", action="store_true",
+                    help="run the prefill tile's LDS access patterns (libattn_probes) once each and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run five 1 GiB device-to-device copies and exit")
     return ap.parse_args()
@@ -251,6 +256,26 @@ def measured_peaks(torch):
                      "medians of 5 launches" % best[1]}
 
 
+def lds_patterns():
+    """One launch per LDS access pattern of the prefill tile (K operand reads,
+    transposing V reads, scale reads, LDS-destination loads): 512 workgroups x
+    200 rounds each, so a counter run sees each pattern alone."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "int8_quantized_flashattention_amd", "libattn_probes.so"))
+    lib.attn_probe_lds_patterns.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    src = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    out = torch.empty(512 * 256, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    names = ["k_operand_ds_read_b128", "v_operand_ds_read_b64_tr_b8", "scale_ds_read_b128", "stage_buffer_load_lds"]
+    for mode, name in enumerate(names):
+        assert lib.attn_probe_lds_patterns(mode, ctypes.c_void_p(src.data_ptr()), 512, 200,
+                                           ctypes.c_void_p(out.data_ptr()), sp) == 0
+    torch.cuda.synchronize()
+    print(json.dumps({"lds_patterns": names, "workgroups": 512, "rounds": 200}), flush=True)
+
+
 def host_threads():
     try:
         n = len(os.sched_getaffinity(0))
@@ -310,6 +335,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.lds_patterns:
+        lds_patterns()
         return
     w = WORKLOADS[args.workload]
     q, k, v = w.inputs()

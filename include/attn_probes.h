@@ -35,6 +35,19 @@ int attn_probe_mfma_i8(int32_t n_blocks, int32_t iters, int32_t* out, void* stre
 int attn_probe_hbm_read(const void* src, int64_t n_bytes, int32_t n_blocks, int32_t nontemporal, uint32_t* out,
                         void* stream);
 
+/* attn_probe_lds_patterns — one LDS access pattern of the prefill kernel's
+ * tile (d = 128, 64 keys) in a loop of `iters` rounds on a resident K/V
+ * stage, n_blocks workgroups of 256 lanes, so that LDS counters (bank
+ * conflicts per instruction) can be read for that pattern alone. mode: 0 the
+ * K operand reads (8 ds_read_b128 per round), 1 the transposing V operand
+ * reads (16 ds_read_b64_tr_b8), 2 the per-key scale reads (8 ds_read_b128,
+ * each half-wave on one address), 3 the LDS-destination buffer loads of one
+ * stage request from src (8 KB read, 16-byte aligned, device; four 1 KB loads
+ * per wavefront) with a wait and two barriers per round. out: uint32
+ * [n_blocks * 256], device. */
+int attn_probe_lds_patterns(int32_t mode, const void* src, int32_t n_blocks, int32_t iters, uint32_t* out,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

