@@ -197,9 +197,6 @@ template <int D, bool MASK, bool EXP>
 __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float* sk, float sq, float (&x)[NKB][16],
                                               int rel, int g) {
   constexpr float kRs = 0.08838834764831845f;          // fl32(1 / sqrt(128))
-  // the maximum is taken as a tree (independent partial maxima), so one
-  // wavefront is not held up by a long dependency chain
-  float gm[NKB * 4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -218,14 +215,17 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
         if constexpr (MASK) t = (kb * 32 + j4 * 4 + e <= rel) ? t : kNegInf;
         x[kb][j4 * 4 + e] = t;
       }
-      const float* y = &x[kb][j4 * 4];
-      gm[kb * 4 + j4] = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
     }
+  // the maximum: per 32-key block a chain of three-input maxima (v_max3),
+  // the blocks' chains independent of each other
+  float mx = kNegInf;
 #pragma unroll
-  for (int w = NKB * 4; w > 1; w >>= 1)
+  for (int kb = 0; kb < NKB; ++kb) {
+    float pm = fmaxf(fmaxf(x[kb][0], x[kb][1]), x[kb][2]);
 #pragma unroll
-    for (int i = 0; i < w / 2; ++i) gm[i] = fmaxf(gm[i], gm[i + w / 2]);
-  const float mx = gm[0];
+    for (int e = 3; e < 15; e += 2) pm = fmaxf(fmaxf(pm, x[kb][e]), x[kb][e + 1]);
+    mx = fmaxf(mx, fmaxf(pm, x[kb][15]));
+  }
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -360,10 +360,13 @@ __device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int
 // Workgroup -> (b*h, row block). Workgroups are dealt to the 8 XCDs round
 // robin, so consecutive ids land on different XCDs (each with its own L2),
 // and each XCD takes a contiguous range of heads. When every XCD holds whole
-// heads, its heads are taken in groups of up to 8 and each group row block by
+// heads, its heads are taken in groups of up to 4 and each group row block by
 // row block, longest (causal) first: every head's longest blocks start early,
 // so the launch does not end waiting on a long block that started late, while
-// the workgroups in flight on an XCD still share the K/V of at most 8 heads.
+// the workgroups in flight on an XCD share the K/V of at most 4 heads (4 MB at
+// L = 4096, d = 128, the size of an XCD's L2). Measured at B4 H32 L4096 d128
+// causal: groups of 1, 2, 4 and 8 heads take 0.556, 0.525, 0.507 and 0.507 ms
+// and miss the L2 for 271, 273, 358 and 666 MB per launch.
 // Otherwise heads are walked one after the other, longest block first.
 __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
   const int n = gridDim.x, id = blockIdx.x;
@@ -371,7 +374,7 @@ __device__ __forceinline__ void tile_of_block(int n_rb, int& bh, int& rb) {
   const int per = n >> 3;
   if ((n & 7) == 0 && per % n_rb == 0) {
     const int nh = per / n_rb;                 // heads of this XCD
-    int G = nh < 8 ? nh : 8;
+    int G = nh < 4 ? nh : 4;
     while (nh % G) --G;                        // groups of G heads
     const int grp = slot / (G * n_rb), s = slot - grp * G * n_rb;
     rb = n_rb - 1 - s / G;
@@ -623,7 +626,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const float mx2 = !LUT ? mx : (mx == kNegInf) ? kNegInf : mx * c2;
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = exp2_hw((m - m_use) * fs);     // 1 if unchanged, 0 on the first tile
+    // alpha = 2^((m - m_use) fs): 1 when no row of the wavefront raised its
+    // max (then it is not computed), 0 on a row's first visible tile
+    float alpha = 1.0f;
+    if constexpr (VPT) alpha = exp2_hw((m - m_use) * fs);
     v4i p[NKB];
     float lsum;
     float st_cur = 0.0f;
@@ -647,10 +653,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       }
       lsum = probs_tile<VPT>(u, m_use, fs, st->sv, rst, p, g);
     }
-    l = __builtin_fmaf(alpha, l, lsum);
 
     if constexpr (!VPT) {
       if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
+        alpha = exp2_hw((m - m_use) * fs);
         // tile t raised some row's max: the INT32 run (tiles before t, frame
         // m) goes into acc (frame m_f) before PV(t) starts a new run
         if (m_f == kNegInf) m_f = m_use;
@@ -673,6 +679,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         int_tiles = 1;
       }
     }
+    l = __builtin_fmaf(alpha, l, lsum);
     m = m_new;
 
     // per-token V converts every tile's product on its own: always a new run
