@@ -430,8 +430,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       for (int e = 0; e < 4; ++e) {
         float x = static_cast<float>(s[kb][e]);
         if constexpr (!LUT) {
-          x = __fmul_rn(__fmul_rn(x, sq), skk[e]);
-          if constexpr (D != 64) x = __fmul_rn(x, kRs);
+          x = (x * sq) * skk[e];
+          if constexpr (D != 64) x = x * kRs;
         } else {
           x = x * skk[e];
         }
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // 127 P_tilde from the oracle's rounded difference u - m
-          y[e] = exp2_hw(__builtin_fmaf(__fsub_rn(u[kb][e], m_use), fs, kLog2_127));
+          y[e] = exp2_hw(__builtin_fmaf((u[kb][e] - m_use), fs, kLog2_127));
           word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
         }
         gs[kb] = (y[0] + y[1]) + (y[2] + y[3]);

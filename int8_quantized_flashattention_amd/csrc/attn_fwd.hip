@@ -207,8 +207,8 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
       for (int e = 0; e < 4; ++e) {
         float t = static_cast<float>(s[kb][j4 * 4 + e]);
         if constexpr (EXP) {
-          t = __fmul_rn(__fmul_rn(t, sq), skk[e]);
-          if constexpr (D != 64) t = __fmul_rn(t, kRs);
+          t = (t * sq) * skk[e];
+          if constexpr (D != 64) t = t * kRs;
         } else {
           t = t * skk[e];
         }
@@ -253,7 +253,7 @@ __device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float m, 
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        y[e] = exp2_hw(__builtin_fmaf(__fsub_rn(x[kb][j4 * 4 + e], m), ls, kLog2_127));
+        y[e] = exp2_hw(__builtin_fmaf((x[kb][j4 * 4 + e] - m), ls, kLog2_127));
         word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
       }
       gs[kb * 4 + j4] = (y[0] + y[1]) + (y[2] + y[3]);

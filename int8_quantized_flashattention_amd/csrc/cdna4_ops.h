@@ -114,9 +114,26 @@ __device__ __forceinline__ uint32_t quant_code(float x, float r) {
   t = fminf(127.0f, fmaxf(-127.0f, t));
   return static_cast<uint32_t>(static_cast<int>(t)) & 0xffu;
 }
-// codes of 4 values, byte i from x[i]
+// codes of 4 values, byte i from x[i], for r = 127 / absmax of a group that
+// holds the x: then |x * r| <= 127 (1 + 2^-24) and rne(x * r) lies in
+// [-127, 127], so the clamp never acts. Adding 1.5 * 2^23 to the rounded
+// product rounds it to an integer (ties to even: the sum's ulp is 1) and
+// leaves that integer's two's-complement low byte in the low byte of the
+// sum's bits; three byte permutes pack the four low bytes. The product must
+// be rounded on its own (a fused x * r + 1.5 * 2^23 would round the exact
+// product instead, and differ at ties): both operations are written here,
+// where contraction is off (the _rn helpers of the HIP headers carry the
+// headers' own contraction setting).
 __device__ __forceinline__ uint32_t quant_word(const float* x, float r) {
-  return quant_code(x[0], r) | (quant_code(x[1], r) << 8) | (quant_code(x[2], r) << 16) | (quant_code(x[3], r) << 24);
+#pragma clang fp contract(off)
+  uint32_t b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(x[i] * r + 12582912.0f);
+  // v_perm_b32 (s0, s1, sel): byte k of the result is byte sel_k of s1:s0
+  // (s1 = bytes 0-3, s0 = bytes 4-7), selector 12 gives 0
+  const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // 16 consecutive Q values of one row as fp32 (fp16 or fp32 storage)

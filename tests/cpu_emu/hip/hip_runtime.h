@@ -365,6 +365,7 @@ using std::max;
 using std::min;
 
 inline float __fmul_rn(float a, float b) { return a * b; }   // built with -ffp-contract=off
+inline float __fadd_rn(float a, float b) { return a + b; }   // built with -ffp-contract=off
 inline float __fsub_rn(float a, float b) { return a - b; }   // built with -ffp-contract=off
 inline float __fdiv_rn(float a, float b) { return a / b; }
 inline float __uint_as_float(uint32_t u) { return emu::bits_to_float(u); }
