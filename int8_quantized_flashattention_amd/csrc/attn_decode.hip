@@ -245,16 +245,9 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   v4i qf[NC];
   float sq = 0.0f;
   float xq[QF ? NC : 1][16];
+  v4i q16[QF ? NC : 1][2];
   if constexpr (QF) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (rvalid) {
-        load16_as_f32(a.q_float, qrow * D + c * 64 + grp * 16, a.q_float_f16, xq[c]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xq[c][e] = 0.0f;
-      }
-    }
+    if (rvalid && a.q_float_f16) q16_load<NC>(a.q_float, qrow * D + grp * 16, 64, q16);
   } else {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -283,6 +276,18 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   request_k<D>(kr[0], rk, ln, k_first);
   request_vs<D, VPT>(sm[1], rv, rsk, rsv, ln, lane, k_second);
   request_k<D>(kr[1], rk, ln, k_second);
+  if constexpr (QF) {
+    // the Q row, converted once the first tiles are requested
+    if (rvalid) {
+      if (a.q_float_f16) q16_f32<NC>(q16, xq);
+      else q32_f32<NC>(a.q_float, qrow * D + grp * 16, 64, xq);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xq[c][e] = 0.0f;
+    }
+  }
   if constexpr (QF == 2) {
     // Hadamard rotation of the row (the rotated quantizer's butterflies, strides
     // in increasing order): 1 .. 8 inside the lane's 16 channels, 16 and 32

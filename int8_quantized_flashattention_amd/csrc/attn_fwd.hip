@@ -458,16 +458,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   v4i qf[NC];
   float sq = 0.0f;
   float xq[QF ? NC : 1][16];
+  v4i q16[QF ? NC : 1][2];
   if constexpr (QF) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (qvalid) {
-        load16_as_f32(a.q_float, (q_base + qi) * D + c * 32 + g * 16, a.q_float_f16, xq[c]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xq[c][e] = 0.0f;
-      }
-    }
+    if (qvalid && a.q_float_f16) q16_load<NC>(a.q_float, (q_base + qi) * D + g * 16, 32, q16);
   } else {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -479,6 +472,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   __syncthreads();
   request_tile<D, true, VPT>(sm[0], bf, ln, wave, lane, 0);
   if (n_tiles > 1) request_tile<D, true, VPT>(sm[1], bf, ln, wave, lane, BN);
+  if constexpr (QF) {
+    // the Q row, converted once the first tiles are requested
+    if (qvalid) {
+      if (a.q_float_f16) q16_f32<NC>(q16, xq);
+      else q32_f32<NC>(a.q_float, (q_base + qi) * D + g * 16, 32, xq);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xq[c][e] = 0.0f;
+    }
+  }
   if constexpr (QF == 2) {
     // Hadamard rotation of the row (the rotated quantizer's butterflies, strides
     // in increasing order): 1 .. 8 inside the lane's 16 channels, 16 across the

@@ -136,30 +136,42 @@ __device__ __forceinline__ uint32_t quant_word(const float* x, float r) {
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// 16 consecutive Q values of one row as fp32 (fp16 or fp32 storage)
-__device__ __forceinline__ void load16_as_f32(const void* base, int64_t elem, bool f16, float (&x)[16]) {
-  if (f16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+// N runs of 16 consecutive Q values of one row, run c at element elem0 + c *
+// stride. fp16 rows: q16_load issues every load of the row (raw halves in
+// registers) and q16_f32 converts them once they are needed, so the row
+// costs one memory latency and work placed between the two calls overlaps
+// it. fp32 rows (q32_f32) are loaded and converted in one go.
+template <int N>
+__device__ __forceinline__ void q16_load(const void* base, int64_t elem0, int stride, v4i (&raw)[N][2]) {
+  const uint16_t* p = static_cast<const uint16_t*>(base) + elem0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 raw = p[h];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int c = 0; c < N; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) raw[c][h] = reinterpret_cast<const v4i*>(p + c * stride)[h];
+}
+template <int N>
+__device__ __forceinline__ void q16_f32(const v4i (&raw)[N][2], float (&x)[N][16]) {
+#pragma unroll
+  for (int c = 0; c < N; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __half2 hv = *reinterpret_cast<const __half2*>(&w[i]);
-        const float2 f = __half22float2(hv);
-        x[h * 8 + 2 * i] = f.x;
-        x[h * 8 + 2 * i + 1] = f.y;
+        const uint32_t w = static_cast<uint32_t>(raw[c][h][i]);
+        x[c][h * 8 + 2 * i] = __half2float(__ushort_as_half(static_cast<unsigned short>(w & 0xffffu)));
+        x[c][h * 8 + 2 * i + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16)));
       }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+}
+template <int N>
+__device__ __forceinline__ void q32_f32(const void* base, int64_t elem0, int stride, float (&x)[N][16]) {
+  const float* p = static_cast<const float*>(base) + elem0;
+#pragma unroll
+  for (int c = 0; c < N; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 f = p[i];
-      x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+      const float4 f = reinterpret_cast<const float4*>(p + c * stride)[i];
+      x[c][4 * i] = f.x; x[c][4 * i + 1] = f.y; x[c][4 * i + 2] = f.z; x[c][4 * i + 3] = f.w;
     }
-  }
 }
 
 // Raw buffer resource over nbytes bytes (loads at or past the end read 0)

@@ -378,6 +378,8 @@ struct __half { _Float16 v; };
 struct alignas(4) __half2 { _Float16 x, y; };
 inline float2 __half22float2(__half2 h) { return {static_cast<float>(h.x), static_cast<float>(h.y)}; }
 inline __half __float2half_rn(float a) { return {static_cast<_Float16>(a)}; }
+inline __half __ushort_as_half(unsigned short u) { __half h; std::memcpy(&h.v, &u, 2); return h; }
+inline float __half2float(__half h) { return static_cast<float>(h.v); }
 inline __half2 __floats2half2_rn(float a, float b) {
   return {static_cast<_Float16>(a), static_cast<_Float16>(b)};
 }
