@@ -57,6 +57,26 @@ def test_quantize_all_zero_tensor(lib):
     assert np.all(q == 0) and np.all(s == 0)
 
 
+# One fp16 group of 2-3 M values (the two-pass path with hundreds of
+# workgroups per group): a ragged last workgroup, the largest magnitude at the
+# last element, negative zeros, ties at scale 1, and an all-zero tensor of that
+# size.
+def test_quantize_large_tensor_group(lib):
+    r = _rng(77)
+    x = (r.standard_normal((23457, 128)) * 3).astype(np.float16)
+    x[-1, -1] = -1000.0
+    x[5, :7] = -0.0
+    quantize_both(lib, x, x.shape[0])
+    y = r.integers(-127, 128, size=(16411, 128)).astype(np.float16)
+    y[::3, ::5] += np.float16(0.5)
+    y[0, 0] = 127.0
+    q, s, _, _ = quantize_both(lib, np.clip(y, -127, 127).astype(np.float16), y.shape[0])
+    assert s[0] == 1.0
+    z = np.zeros((20000, 128), np.float16)
+    q, s, _, _ = quantize_both(lib, z, z.shape[0])
+    assert np.all(q == 0) and np.all(s == 0)
+
+
 # quantize-on-append into an INT8 cache: (B, Hkv, T, d, L_max, pos, dtype)
 APPEND = [
     (2, 3, 1, 128, 40, 39, np.float16), (1, 8, 5, 64, 16, 0, np.float32),
