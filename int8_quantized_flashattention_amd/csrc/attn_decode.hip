@@ -241,7 +241,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
 
   // Q fragment (B operand of S^T): 16 bytes per 64-channel chunk; s_Q. QF:
   // the row arrives in fp16/fp32 and is quantized here (the quantizer's
-  // arithmetic; the row's 4 lanes share its absmax).
+  // arithmetic; the row's 4 lanes share its absmax); an fp16 row is requested
+  // whole here and converted after the first tile requests.
   v4i qf[NC];
   float sq = 0.0f;
   float xq[QF ? NC : 1][16];

@@ -451,10 +451,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   }
 
-  // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk. Loaded
+  // Q fragment (B operand of S^T): 16 bytes per 32-channel chunk. Requested
   // before the first stage requests, so that the prologue's wait covers it.
   // QF: the row arrives in fp16/fp32 and is quantized here, per token with
-  // the quantizer's arithmetic; the lane pair (l, l ^ 32) holds the row.
+  // the quantizer's arithmetic; the lane pair (l, l ^ 32) holds the row. An
+  // fp16 row is requested whole here and converted after the stage requests.
   v4i qf[NC];
   float sq = 0.0f;
   float xq[QF ? NC : 1][16];
