@@ -231,19 +231,20 @@ def attn_int8(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal
 
 def attn_int8_trace(q, s_q, k, s_k, v, s_v, v_per_token, B, H, Hkv, Lq, Lkv, d, causal,
                     kv_tile, kv_split_len, b, h, i, L=None, index_softmax=None):
-    """One row with its per-key trace: dict of O, lse, S, m_tile, p_tilde, p_hat, w, split_m."""
+    """One row with its per-key trace: dict of o, lse, t (base-2 logit), m_tile, y (127 P_tilde),
+    p_hat, w (multiplier of y), split_m."""
     args = [np.ascontiguousarray(a) for a in (q, s_q, k, s_k, v, s_v)]
     o = np.empty(d, np.float32)
     lse = np.empty(1, np.float32)
-    S, mt, pt, w, sm = (np.empty(Lkv, np.float32) for _ in range(5))
+    t, mt, y, w, sm = (np.empty(Lkv, np.float32) for _ in range(5))
     ph = np.empty(Lkv, np.int32)
     rc = (L or lib()).oracle_attn_int8_trace(*(_p(a) for a in args), int(v_per_token), B, H, Hkv,
                                              Lq, Lkv, d, int(causal), kv_tile, kv_split_len,
                                              *_lut_args(index_softmax), b, h, i,
-                                             _p(o), _p(lse), _p(S), _p(mt), _p(pt), _p(ph), _p(w),
+                                             _p(o), _p(lse), _p(t), _p(mt), _p(y), _p(ph), _p(w),
                                              _p(sm))
     _check(rc, "attn_int8_trace")
-    return dict(o=o, lse=float(lse[0]), S=S, m_tile=mt, p_tilde=pt, p_hat=ph, w=w, split_m=sm)
+    return dict(o=o, lse=float(lse[0]), t=t, m_tile=mt, y=y, p_hat=ph, w=w, split_m=sm)
 
 
 def attn_ref_f64(q, k, v, B, H, Hkv, Lq, Lkv, d, causal, rows=None, nthreads=0, L=None):

@@ -35,25 +35,34 @@
 //  * quantizer: q = clamp(rne(x * r), -127, 127) with r = 127/a and s = a/127,
 //    a = absmax of the group; x*r is one rounded fp32 multiply; an all-zero
 //    group gets s = 0 and q = 0.
+//  * logits in base 2: t = (S_int * (s_Q * c)) * s_K[j] in fp32, with
+//    c = fl32(log2(e) / sqrt(d)); e^(S - m) is then 2^(t - m') (the
+//    rescale factor alpha = s_Q s_K / sqrt(d) of IA §3.1, Eq. 4, times
+//    log2(e), its row part formed once per row).
+//  * 127 P_tilde = y = 2^(t - b(m')), b(m') = m' - log2(127) in fp32 (moved
+//    up one float when m' - b still exceeds log2(127), see exp_bias), with
+//    fp32 exp2 of the fp32 difference.
 //  * per-token V inside the INT8 P.V product: the scale of tile t is
 //    s_t = max of s_V over the tile's in-range keys; key j's probability is
-//    quantized with multiplier w_j = (127 * s_V[j]) / s_t.
-//  * P_hat = rne(P_tilde * w) of the exact product (at most 48 significant
-//    bits, so exact in double); w = 127 for per-tensor V.
+//    quantized with multiplier w_j = s_V[j] / s_t (fp32) on y.
+//  * P_hat = rne(y * w) of the exact product (at most 48 significant bits,
+//    so exact in double); w = 1 for per-tensor V.
 //  * per-head V (one scale per (batch, kv head), a block granularity that
 //    IA §3.3 lists as compatible): the tile scale is that head's s_V and
-//    w = 127, i.e. the per-tensor arithmetic with the head's own scale.
+//    w = 1, i.e. the per-tensor arithmetic with the head's own scale.
 //  * per-channel V (one scale per (batch, kv head, channel), the per-channel
 //    granularity of IA §3.3): the scale is constant along the keys, so the
-//    tile sums carry no V scale (s_t = 1, w = 127) and channel c of the
+//    tile sums carry no V scale (s_t = 1, w = 1) and channel c of the
 //    output is multiplied by its scale at the end.
 //  * the running max used to quantize a tile is the max after that tile (m').
-//  * rowsum l accumulates the fp32 P_tilde before quantization.
+//  * rowsum l accumulates the fp32 y = 127 P_tilde before quantization, and
+//    O = acc / l.
 //  * INT32 accumulation inside a tile, fp32 across tiles.
 //  * causal mask is bottom-right aligned: query i sees key j iff
 //    j <= i + (Lkv - Lq).
 //  * GQA: query head h reads kv head h / (H / Hkv).
-//  * 1/sqrt(d) is the fp32 rounding of the double value.
+//  * 1/sqrt(d) (IndexSoftmax) and log2(e)/sqrt(d) (exp softmax) are the fp32
+//    roundings of the double values.
 //  * IndexSoftmax: see index_softmax_lut and attend_row_lut below (table
 //    sampled at the left end of each index bucket with multiplier 127; the
 //    distance taken on the dequantized logit; online rescale by exp; the
@@ -177,13 +186,27 @@ struct Problem {
 
 // Per-key trace of one row, for the invariant tests.
 struct RowTrace {
-  float* S;        // [Lkv] dequantized logit (-inf if masked)
-  float* m_tile;   // [Lkv] running max m' used for the key's tile
-  float* p_tilde;  // [Lkv] exp(S - m')
-  int32_t* p_hat;  // [Lkv] quantized probability
-  float* w;        // [Lkv] quantization multiplier of the key
+  float* t;        // [Lkv] dequantized logit in base 2, S log2(e) (-inf if masked)
+  float* m_tile;   // [Lkv] running max m' of t used for the key's tile
+  float* y;        // [Lkv] 127 P_tilde as computed: 2^(t - b(m'))
+  int32_t* p_hat;  // [Lkv] quantized probability rne(y w)
+  float* w;        // [Lkv] multiplier of y (1, or s_V[j] / s_t for per-token V)
   float* split_m;  // [Lkv] final running max of the key's split
 };
+
+// log2(127) as an fp32 value.
+const float kLog2_127 = static_cast<float>(std::log2(127.0));
+
+// The exponent bias of a running max m (base-2 units): b = m - log2(127) in
+// fp32, moved up to the next float when m - b still exceeds log2(127) after
+// rounding. Then every visible key has t - b <= log2(127) in fp32, so
+// 2^(t - b) stays at or below 127 (plus the exponential's own rounding) and
+// the probability code never exceeds 127, whatever the size of m.
+float exp_bias(float m) {
+  float b = m - kLog2_127;
+  if (!PLANT("no_bias_nudge") && m - b > kLog2_127) b = std::nextafter(b, std::numeric_limits<float>::infinity());
+  return b;
+}
 
 // One query row, step by step. Returns O[d] (fp32) and lse.
 void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, RowTrace* tr) {
@@ -208,14 +231,21 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
     last = static_cast<int64_t>(i) + (P.Lkv - P.Lq);
     if (PLANT("causal_off_by_one")) last -= 1;
   }
-  const float inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+  // Base-2 logit factor of the row: the rescale factor alpha = s_Q s_K / sqrt(d)
+  // (IA §3.1, Eq. 4) times log2(e), so that e^(S - m) = 2^(t - m') with
+  // t = S log2(e). The row's part a = s_Q c is formed once, with c = log2(e) /
+  // sqrt(d) rounded to fp32; each key's scale multiplies after it.
+  const double c_d = PLANT("no_log2e") ? 1.0 / std::sqrt(static_cast<double>(d))
+                                       : 1.0 / (std::log(2.0) * std::sqrt(static_cast<double>(d)));
+  const float c = static_cast<float>(c_d);
+  const float a = sq * c;
   const float NEG_INF = -std::numeric_limits<float>::infinity();
 
   const int Bc = P.kv_tile;
   const int split_len = P.kv_split_len > 0 ? P.kv_split_len : P.Lkv;
   const int n_splits = (P.Lkv + split_len - 1) / split_len;
 
-  std::vector<float> acc(d), S(Bc), pt(Bc), w(Bc);
+  std::vector<float> acc(d), S(Bc), yv(Bc), w(Bc);
   std::vector<int32_t> ph(Bc), T(d);
   std::vector<float> sm(n_splits), sl(n_splits), sacc(static_cast<size_t>(n_splits) * d);
 
@@ -223,32 +253,32 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
     const int s0 = sp * split_len;
     const int s1 = std::min(P.Lkv, s0 + split_len);
     // Online softmax state of this split (FA3 abstract: softmax fused tile by
-    // tile; IA §2.2: max-subtracted stable softmax).
+    // tile; IA §2.2: max-subtracted stable softmax), in base-2 logit units.
     float m = NEG_INF, l = 0.0f;
     std::fill(acc.begin(), acc.end(), 0.0f);
     for (int t0 = s0; t0 < s1; t0 += Bc) {         // ascending tile order
       const int t1 = std::min(s1, t0 + Bc);
       const int n = t1 - t0;
-      // Dequantized logits: S = S_int * s_Q[i] * s_K[j] / sqrt(d)
-      // (IA §2.1 integer logits; IA §3.1 Eq. 4 for the rescale factor; the
-      // per-row x per-column scale product is LLM.int8()'s vector-wise form).
+      // Dequantized logits in base 2: t = (S_int * a) * s_K[j], two rounded
+      // fp32 products (IA §2.1 integer logits; the per-row x per-column scale
+      // product is LLM.int8()'s vector-wise form).
       float mt = NEG_INF;
       for (int jj = 0; jj < n; ++jj) {
         const int j = t0 + jj;
         if (j > last) { S[jj] = NEG_INF; continue; }
         const int32_t s_int = dot_i8(qv, kmat + static_cast<int64_t>(j) * d, d);
-        float x = static_cast<float>(s_int) * sq;
+        float x = static_cast<float>(s_int) * a;
         if (!PLANT("drop_sk")) x = x * sk[j];
-        x = x * inv_sqrt_d;
         S[jj] = x;
         mt = std::max(mt, x);
       }
       const float m_new = std::max(m, mt);
       if (m_new == NEG_INF) continue;                // nothing visible yet
-      float alpha = (m == NEG_INF) ? 0.0f : std::exp(m - m_new);
-      if (PLANT("alpha_sign")) alpha = (m == NEG_INF) ? 0.0f : std::exp(m_new - m);
+      float alpha = (m == NEG_INF) ? 0.0f : std::exp2(m - m_new);
+      if (PLANT("alpha_sign")) alpha = (m == NEG_INF) ? 0.0f : std::exp2(m_new - m);
       if (PLANT("no_alpha")) alpha = (m == NEG_INF) ? 0.0f : 1.0f;
-      // Scale of this tile's V contribution and per-key P multipliers.
+      const float eb = PLANT("bias_sign") ? m_new + kLog2_127 : exp_bias(m_new);
+      // Scale of this tile's V contribution and per-key multipliers of y.
       float st;
       if (P.v_mode == 1) {
         st = 0.0f;
@@ -260,36 +290,39 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
       }
       float lsum = 0.0f;
       for (int jj = 0; jj < n; ++jj) {
-        const float p = (S[jj] == NEG_INF) ? 0.0f : std::exp(S[jj] - m_new);
-        pt[jj] = p;
-        lsum += p;
+        // y = 127 P_tilde = 2^(t - b(m')): the C library's fp32 exp2 of the
+        // fp32 difference
+        const float y = (S[jj] == NEG_INF) ? 0.0f : std::exp2(S[jj] - eb);
+        yv[jj] = y;
+        lsum += y;
         float wj;
-        if (P.v_mode == 1) wj = (st > 0.0f) ? (127.0f * sv[t0 + jj]) / st : 0.0f;
-        else wj = 127.0f;
+        if (P.v_mode == 1) wj = (st > 0.0f) ? sv[t0 + jj] / st : 0.0f;
+        else wj = 1.0f;
         w[jj] = wj;
-        // P_hat = rne(P_tilde * w): signed INT8 probabilities with multiplier
-        // 127 (IA §3.2 describes this as the prior methods' choice).
-        ph[jj] = static_cast<int32_t>(std::nearbyint(static_cast<double>(p) * static_cast<double>(wj)));
+        // P_hat = rne(127 P_tilde w): signed INT8 probabilities with
+        // multiplier 127 (IA §3.2 describes this as the prior methods'
+        // choice); the product y w is exact in double.
+        ph[jj] = static_cast<int32_t>(std::nearbyint(static_cast<double>(y) * static_cast<double>(wj)));
       }
       l = PLANT("l_no_rescale") ? (l + lsum) : (alpha * l + lsum);
       // T = P_hat . V_hat over this tile, exact in INT32.
-      for (int c = 0; c < d; ++c) T[c] = 0;
+      for (int c2 = 0; c2 < d; ++c2) T[c2] = 0;
       for (int jj = 0; jj < n; ++jj) {
         if (ph[jj] == 0) continue;
         const int8_t* vr = vmat + static_cast<int64_t>(t0 + jj) * d;
-        for (int c = 0; c < d; ++c) {
-          const int8_t vv = PLANT("transpose_v") ? vmat[static_cast<int64_t>(c % P.Lkv) * d + ((t0 + jj) % d)] : vr[c];
-          T[c] += ph[jj] * static_cast<int32_t>(vv);
+        for (int c2 = 0; c2 < d; ++c2) {
+          const int8_t vv = PLANT("transpose_v") ? vmat[static_cast<int64_t>(c2 % P.Lkv) * d + ((t0 + jj) % d)] : vr[c2];
+          T[c2] += ph[jj] * static_cast<int32_t>(vv);
         }
       }
       // fp32 accumulation across tiles: acc = alpha * acc + s_t * T
       // (IA §2.1: O ~ s_V * P * V_hat).
-      for (int c = 0; c < d; ++c) acc[c] = alpha * acc[c] + st * static_cast<float>(T[c]);
+      for (int c2 = 0; c2 < d; ++c2) acc[c2] = alpha * acc[c2] + st * static_cast<float>(T[c2]);
       m = m_new;
       if (tr) {
         for (int jj = 0; jj < n; ++jj) {
           const int j = t0 + jj;
-          tr->S[j] = S[jj]; tr->m_tile[j] = m_new; tr->p_tilde[j] = pt[jj];
+          tr->t[j] = S[jj]; tr->m_tile[j] = m_new; tr->y[j] = yv[jj];
           tr->p_hat[j] = ph[jj]; tr->w[j] = w[jj];
         }
       }
@@ -306,17 +339,19 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
   std::fill(acc.begin(), acc.end(), 0.0f);
   for (int sp = 0; sp < n_splits; ++sp) {
     if (sm[sp] == NEG_INF) continue;
-    const float f = std::exp(sm[sp] - M);
+    const float f = std::exp2(sm[sp] - M);
     L += f * sl[sp];
-    for (int c = 0; c < d; ++c) acc[c] += f * sacc[static_cast<size_t>(sp) * d + c];
+    for (int c2 = 0; c2 < d; ++c2) acc[c2] += f * sacc[static_cast<size_t>(sp) * d + c2];
   }
-  // Output: O = acc / (127 * l); s_V is already inside acc, except per-channel
-  // scales, which multiply their channel here.
-  for (int c = 0; c < d; ++c) {
-    const float sc = P.v_mode == 3 ? sv[PLANT("v_channel_transposed") ? (c * 7) % d : c] : 1.0f;
-    o[c] = (acc[c] * sc) / (127.0f * L);
+  // Output: O = acc / l, l = sum of 127 P_tilde; s_V is already inside acc,
+  // except per-channel scales, which multiply their channel here.
+  for (int c2 = 0; c2 < d; ++c2) {
+    const float sc = P.v_mode == 3 ? sv[PLANT("v_channel_transposed") ? (c2 * 7) % d : c2] : 1.0f;
+    o[c2] = (acc[c2] * sc) / L;
   }
-  if (lse) *lse = M + std::log(L);
+  // natural log of sum_j e^(S_j) = ln 2 * (M - log2(127) + log2(l))
+  if (lse) *lse = static_cast<float>((static_cast<double>(M) - std::log2(127.0) + std::log2(static_cast<double>(L))) *
+                                     std::log(2.0));
 }
 
 // ---------------------------------------------------------------------------
@@ -383,6 +418,7 @@ void attend_row_lut(const Problem& P, int b, int h, int i, float* o, float* lse,
   std::vector<int32_t> lut(static_cast<size_t>(n_idx) + 1);
   index_softmax_lut(P.lut_bits, P.clip, lut.data());
   const float g = sq * inv_sqrt_d;               // natural-log logit per unit of u
+  const float g2 = static_cast<float>(static_cast<double>(g) / std::log(2.0));   // base-2 (trace only)
   const float k_b = static_cast<float>(static_cast<double>(n_idx) / static_cast<double>(P.clip));
   const float kappa = PLANT("lut_no_query_scale") ? inv_sqrt_d * k_b : g * k_b;
 
@@ -435,17 +471,17 @@ void attend_row_lut(const Problem& P, int b, int h, int i, float* o, float* lse,
       if (tr) {
         for (int jj = 0; jj < n; ++jj) {
           const int j = t0 + jj;
-          tr->S[j] = u[jj] == NEG_INF ? NEG_INF : u[jj] * g;
-          tr->m_tile[j] = m_new * g;
-          tr->p_tilde[j] = static_cast<float>(e[jj]) / 127.0f;
+          tr->t[j] = u[jj] == NEG_INF ? NEG_INF : u[jj] * g2;
+          tr->m_tile[j] = m_new * g2;
+          tr->y[j] = static_cast<float>(e[jj]);
           tr->p_hat[j] = e[jj];
-          tr->w[j] = 127.0f;
+          tr->w[j] = 1.0f;
         }
       }
     }
     sm[sp] = m; sl[sp] = l;
     std::copy(acc.begin(), acc.end(), sacc.begin() + static_cast<size_t>(sp) * d);
-    if (tr) for (int j = s0; j < s1; ++j) tr->split_m[j] = m == NEG_INF ? NEG_INF : m * g;
+    if (tr) for (int j = s0; j < s1; ++j) tr->split_m[j] = m == NEG_INF ? NEG_INF : m * g2;
   }
 
   // merge the splits by their maxima
@@ -665,23 +701,23 @@ int oracle_attn_int8(const int8_t* q, const float* s_q, const int8_t* k, const f
 }
 
 // Same as oracle_attn_int8 for one row, also returning the per-key trace
-// (each array has Lkv entries; masked keys keep S = -inf and P = 0).
+// (each array has Lkv entries; masked keys keep t = -inf and y = 0).
 int oracle_attn_int8_trace(const int8_t* q, const float* s_q, const int8_t* k, const float* s_k,
                            const int8_t* v, const float* s_v, int32_t v_mode,
                            int32_t B, int32_t H, int32_t Hkv, int32_t Lq, int32_t Lkv, int32_t d,
                            int32_t causal, int32_t kv_tile, int32_t kv_split_len,
                            int32_t lut_bits, float clip,
                            int32_t b, int32_t h, int32_t i, float* o, float* lse,
-                           float* S, float* m_tile, float* p_tilde, int32_t* p_hat, float* w,
+                           float* t, float* m_tile, float* y, int32_t* p_hat, float* w,
                            float* split_m) {
   Problem P{q, s_q, k, s_k, v, s_v, v_mode, B, H, Hkv, Lq, Lkv, d, causal, kv_tile, kv_split_len,
             lut_bits, clip};
   if (!problem_ok(P) || b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Lq) return 1;
   const float NEG_INF = -std::numeric_limits<float>::infinity();
   for (int j = 0; j < Lkv; ++j) {
-    S[j] = NEG_INF; m_tile[j] = NEG_INF; p_tilde[j] = 0.0f; p_hat[j] = 0; w[j] = 0.0f; split_m[j] = NEG_INF;
+    t[j] = NEG_INF; m_tile[j] = NEG_INF; y[j] = 0.0f; p_hat[j] = 0; w[j] = 0.0f; split_m[j] = NEG_INF;
   }
-  RowTrace tr{S, m_tile, p_tilde, p_hat, w, split_m};
+  RowTrace tr{t, m_tile, y, p_hat, w, split_m};
   (P.lut_bits ? attend_row_lut : attend_row)(P, b, h, i, o, lse, &tr);
   return 0;
 }

@@ -349,11 +349,12 @@ def pin_attn_tile_ramp(L):
 
 
 def pin_attn_trace_identity(L):
-    # For every row: the output equals sum_j P_hat_j e^{m_t(j) - m} s_t V_hat_j / (127 l)
-    # with l = sum_j P_tilde_j e^{m_t(j) - m}, where m_t(j) is the running max used
-    # for j's tile and m the final max; each trace entry is checked against its
-    # definition (S from exact integer logits; m_t a running max over tiles;
-    # P_tilde = exp(S - m_t); P_hat = rne(P_tilde w)).
+    # For every row: the output equals sum_j P_hat_j 2^{m_t(j) - m} s_t V_hat_j / l
+    # with l = sum_j y_j 2^{m_t(j) - m}, where m_t(j) is the running max (base-2
+    # logits) used for j's tile and m the final max; each trace entry is checked
+    # against its definition (t = S log2 e from exact integer logits; m_t a
+    # running max over tiles; y = 127 P_tilde = 127 e^{S - m_t} up to the fp32
+    # rounding of the logit scale and of the exponent bias; P_hat = rne(y w)).
     r = _rng(47)
     B, H, Hkv, Lq, Lkv, d = 1, 2, 1, 9, 150, 64
     q = r.standard_normal((B, H, Lq, d)).astype(np.float32)
@@ -374,8 +375,8 @@ def pin_attn_trace_identity(L):
                 vis = np.arange(Lkv) <= last
                 sint = kh[0, 0].astype(np.int64) @ qh[0, h, i].astype(np.int64)
                 S = sint * np.float64(sq[h * Lq_ + i]) * sk.astype(np.float64) / math.sqrt(d)
-                assert np.all(np.isneginf(t["S"][~vis]))
-                assert np.allclose(t["S"][vis], S[vis], rtol=1e-5, atol=1e-5)
+                assert np.all(np.isneginf(t["t"][~vis]))
+                assert np.allclose(t["t"][vis], S[vis] / math.log(2.0), rtol=1e-5, atol=1e-5)
                 # running max over tiles inside each split
                 splen = split if split else Lkv
                 for j in range(Lkv):
@@ -383,11 +384,11 @@ def pin_attn_trace_identity(L):
                         continue
                     s0 = (j // splen) * splen
                     tend = min(Lkv, (j // Bc + 1) * Bc, last + 1)
-                    assert t["m_tile"][j] == np.max(t["S"][s0:tend])
-                pt = np.where(vis, np.exp(t["S"].astype(np.float64) - t["m_tile"]), 0.0)
-                assert np.allclose(t["p_tilde"], pt, rtol=1e-6, atol=1e-7)
-                assert np.array_equal(t["p_hat"],
-                                      np.rint(t["p_tilde"].astype(np.float64) * t["w"]).astype(np.int32))
+                    assert t["m_tile"][j] == np.max(t["t"][s0:tend])
+                # y = 127 e^{S - m_t}: base-2 logits, natural-log check
+                yy = np.where(vis, 127.0 * np.exp((t["t"].astype(np.float64) - t["m_tile"]) * math.log(2.0)), 0.0)
+                assert np.allclose(t["y"], yy, rtol=2e-6, atol=1e-6)
+                assert np.array_equal(t["p_hat"], np.rint(t["y"].astype(np.float64) * t["w"]).astype(np.int32))
                 assert t["p_hat"].min() >= 0 and t["p_hat"].max() <= 127
                 # tile scales of V
                 svv = sv[:Lkv].astype(np.float64) if vpt else np.full(Lkv, np.float64(sv[0]))
@@ -396,22 +397,49 @@ def pin_attn_trace_identity(L):
                     t0 = (j // Bc) * Bc
                     st[j] = svv[t0:min(Lkv, t0 + Bc)].max()
                 if vpt:
-                    assert np.allclose(t["w"], 127 * svv / st, rtol=1e-6)
+                    assert np.allclose(t["w"], svv / st, rtol=1e-6)
                 else:
-                    assert np.all(t["w"] == 127)
+                    assert np.all(t["w"] == 1)
                 M = t["m_tile"][vis].max()
-                f = np.where(vis, np.exp(t["m_tile"].astype(np.float64) - M), 0.0)
-                lsum = np.sum(t["p_tilde"] * f)
-                o_id = (t["p_hat"] * f * st) @ vh[0, 0].astype(np.float64) / (127 * lsum)
+                f = np.where(vis, np.exp2(t["m_tile"].astype(np.float64) - M), 0.0)
+                lsum = np.sum(t["y"] * f)
+                o_id = (t["p_hat"] * f * st) @ vh[0, 0].astype(np.float64) / lsum
                 assert np.allclose(t["o"], o_id, rtol=1e-4, atol=1e-5), np.abs(t["o"] - o_id).max()
-                assert abs(t["lse"] - (M + math.log(lsum))) < 1e-4 * max(1.0, abs(M))
+                # lse = ln sum_j e^{S_j}, with y = 127 e^{S - m_t} and M in base 2
+                lse_id = M * math.log(2.0) + math.log(lsum / 127.0)
+                assert abs(t["lse"] - lse_id) < 1e-4 * max(1.0, abs(lse_id))
+
+
+def pin_attn_huge_logits_keep_codes_in_range(L):
+    # Logits of 2^17..2^19 (base 2), where fp32 spacing is 2^-6..2^-4: the
+    # dominant key's probability code must stay a signed 8-bit value (at most
+    # 127, and within the rounding of the logit of 127), and the row's output
+    # is that key's V row (the other key's weight is 2^-(2^17) = 0).
+    d, Lq = 64, 256
+    r = _rng(53)
+    c = np.float32(1.0 / (math.log(2.0) * math.sqrt(d)))
+    s_int = 64 * 127 * 127
+    sq = (r.uniform(2.0 ** 17, 2.0 ** 19, Lq) / (s_int * np.float64(c))).astype(np.float32)
+    qh = np.full((1, 1, Lq, d), 127, np.int8)
+    kh = np.zeros((1, 1, 2, d), np.int8)
+    kh[0, 0, 0] = 127
+    sk = np.ones(2, np.float32)
+    vh = r.integers(-127, 128, (1, 1, 2, d)).astype(np.int8)
+    sv = np.array([0.01], np.float32)
+    o, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sv, False, 1, 1, 1, Lq, 2, d, False, 64, L=L)
+    ref = vh[0, 0, 0].astype(np.float64) * np.float64(sv[0])
+    assert np.allclose(o[0, 0], ref[None, :], rtol=0.5 / 120, atol=1e-6)
+    for i in range(Lq):
+        t = oracle.attn_int8_trace(qh, sq, kh, sk, vh, sv, False, 1, 1, 1, Lq, 2, d, False, 64, 0,
+                                   0, 0, i, L=L)
+        assert 120 <= t["p_hat"][0] <= 127 and t["p_hat"][1] == 0, (i, t["p_hat"], t["y"])
 
 
 def pin_attn_bound_vs_dequant_softmax(L):
     # Proven bound: with exact softmax weights p_ij of the dequantized logits and
-    # the method's effective weights w_ij = P_hat e^{m_t(j)-m_i} / (127 l_i),
-    # |w_ij - p_ij| <= e^{m_t(j)-m_i} / (254 l_i) (P_hat is within 1/2 of
-    # 127 P_tilde), so |O_ic - O*_ic| <= sum_j e^{m_t(j)-m_i}/(254 l_i) |s_V V_hat_jc|
+    # the method's effective weights w_ij = P_hat 2^{m_t(j)-m_i} / l_i (l_i the sum
+    # of y = 127 P_tilde), |w_ij - p_ij| <= 2^{m_t(j)-m_i} / (2 l_i) (P_hat is within
+    # 1/2 of y), so |O_ic - O*_ic| <= sum_j 2^{m_t(j)-m_i}/(2 l_i) |s_V V_hat_jc|
     # (per-tensor V), plus fp32 slack.
     r = _rng(48)
     B, H, Lq, Lkv, d = 1, 2, 64, 300, 64
@@ -424,11 +452,11 @@ def pin_attn_bound_vs_dequant_softmax(L):
             for i in range(0, Lq, 7):
                 t = oracle.attn_int8_trace(qh, sq, kh, sk, vh, sv, False, B, H, H, Lq, Lkv, d, causal,
                                            Bc, 0, 0, h, i, L=L)
-                vis = ~np.isneginf(t["S"])
+                vis = ~np.isneginf(t["t"])
                 M = t["m_tile"][vis].max()
-                f = np.where(vis, np.exp(t["m_tile"].astype(np.float64) - M), 0.0)
-                lsum = np.sum(t["p_tilde"] * f)
-                bound = (f / (254 * lsum)) @ np.abs(vh[0, h].astype(np.float64) * sv[0])
+                f = np.where(vis, np.exp2(t["m_tile"].astype(np.float64) - M), 0.0)
+                lsum = np.sum(t["y"] * f)
+                bound = (f / (2 * lsum)) @ np.abs(vh[0, h].astype(np.float64) * sv[0])
                 err = np.abs(o[0, h, i].astype(np.float64) - ref[0, h, i])
                 assert np.all(err <= bound * (1 + 1e-3) + 1e-5), (err - bound).max()
 

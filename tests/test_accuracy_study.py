@@ -96,22 +96,23 @@ def int8_online(q, k, v, causal, mult):
     qh, kh, vh = (x.astype(np.float64) for x in (qh, kh, vh))
     sq, sk = sq.reshape(B, H, L), sk.reshape(B, H, L)
     s_int = np.matmul(qh, np.swapaxes(kh, -1, -2)).astype(np.float32)   # exact, |S| < 2^24
-    inv_sqrt_d = np.float32(1.0 / np.sqrt(D))
+    # base-2 logits: the row factor s_Q log2(e) / sqrt(d) in fp32
+    aq = (sq * np.float32(1.0 / (np.log(2.0) * np.sqrt(D)))).astype(np.float32)
     m = np.full((B, H, L, 1), -np.inf)
     ell = np.zeros((B, H, L, 1))
     acc = np.zeros((B, H, L, D))
     rows = np.arange(L)[:, None]
     for t0 in range(0, L, TILE):
         keys = np.arange(t0, min(L, t0 + TILE))
-        # the dequantized logit in fp32, in the oracle's order (S_int s_Q, then s_K, then 1/sqrt(d))
-        s = ((s_int[..., keys] * sq[..., :, None]) * sk[..., None, keys] * inv_sqrt_d).astype(np.float64)
+        # the base-2 logit in fp32, in the oracle's order (S_int (s_Q c), then s_K)
+        s = ((s_int[..., keys] * aq[..., :, None]) * sk[..., None, keys]).astype(np.float64)
         if causal:
             s = np.where(keys[None, :] <= rows, s, -np.inf)
         m_new = np.maximum(m, s.max(-1, keepdims=True))
         alive = np.isfinite(m_new)
         mu = np.where(alive, m_new, 0.0)
-        alpha = np.where(np.isfinite(m), np.exp(m - mu), 0.0)
-        pt = np.exp(s - mu)
+        alpha = np.where(np.isfinite(m), np.exp2(m - mu), 0.0)
+        pt = np.exp2(s - mu)
         ell = alpha * ell + pt.sum(-1, keepdims=True)
         ph = np.round(mult * pt)
         acc = alpha * acc + float(sv[0]) * np.matmul(ph, vh[..., keys, :])
