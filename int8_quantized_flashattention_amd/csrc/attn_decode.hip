@@ -360,12 +360,11 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   asm volatile("" : "+v"(sq));
 
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
-  // Units of the running max m, as in the prefill kernel: exp softmax, the
-  // oracle's fp32 running max of the logits (times 8 for d = 64), fs = log2 e
-  // (/ 8) per unit; IndexSoftmax, base-2 logits (fs = 1), the max of u times
-  // c2 = s_Q log2 e / sqrt(d) (kept >= FLT_MIN: -inf * c2 stays -inf)
-  constexpr float kRs = 0.08838834764831845f;          // fl32(1 / sqrt(128))
-  const float fs = LUT ? 1.0f : (D == 64 ? kLog2e * 0.125f : kLog2e);
+  // The running max m is in base-2 logits, as in the prefill kernel: exp
+  // softmax, the oracle's fp32 running max of u = (S_int aq) s_K[j] with aq =
+  // s_Q log2(e) / sqrt(d); IndexSoftmax, the max of u times c2 = s_Q log2 e /
+  // sqrt(d) (kept >= FLT_MIN: -inf * c2 stays -inf)
+  const float aq = sq * kLogitScale<D>;
   const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
   // packed K: the QK accumulator starts at -8 sum_c q_c (the codes' bias)
   int s_init = 0;
@@ -419,9 +418,9 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       }
     request_k<D>(kr[S], rk, ln, kq);
 
-    // exp softmax: u = ((float(S_int) s_Q) s_K[j]) / sqrt(d), the oracle's
-    // three rounded fp32 products (for d = 64 the exact last factor 2^-3 is
-    // left out: u is 8 S); IndexSoftmax: u = S_int s_K[j]. -inf past the chunk
+    // exp softmax: the base-2 logit u = (float(S_int) aq) s_K[j], the
+    // oracle's two rounded fp32 products; IndexSoftmax: u = S_int s_K[j].
+    // -inf past the chunk
     // end or the causal limit; key 16 grp + 4 kb + e of the tile is visible
     // iff 4 kb + e <= rel
     const bool mask = (k0 + BN > s1) || (CAUSAL && k0 + BN - 1 > lim_first);
@@ -436,8 +435,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       for (int e = 0; e < 4; ++e) {
         float x = static_cast<float>(s[kb][e]);
         if constexpr (!LUT) {
-          x = (x * sq) * skk[e];
-          if constexpr (D != 64) x = x * kRs;
+          x = (x * aq) * skk[e];
         } else {
           x = x * skk[e];
         }
@@ -451,7 +449,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
     const float mx2 = !LUT ? mx : (mx == kNegInf) ? kNegInf : mx * c2;
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = exp2_hw((m - m_use) * fs);
+    const float alpha = exp2_hw(m - m_use);
     float st_cur = 0.0f, rst = 0.0f;
     uint32_t pw[NB];
     float lsum;
@@ -485,6 +483,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
         st_cur = x;
         rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
       }
+      const float eb = exp_bias(m_use);
       float gs[NB];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
@@ -497,8 +496,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // 127 P_tilde from the oracle's rounded difference u - m
-          y[e] = exp2_hw(__builtin_fmaf((u[kb][e] - m_use), fs, kLog2_127));
+          // 127 P_tilde = 2^(u - eb), the oracle's rounded difference
+          y[e] = exp2_hw(u[kb][e] - eb);
           word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
         }
         gs[kb] = (y[0] + y[1]) + (y[2] + y[3]);
@@ -514,9 +513,9 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
         // fold the INT32 run (frame m) into acc (frame m_f)
         if (m_f == kNegInf) m_f = m_use;
-        float f = exp2_hw((m - m_f) * fs);
-        if (__any((m_use - m_f) * fs > kRebase)) {
-          const float rb = exp2_hw((m_f - m_use) * fs);
+        float f = exp2_hw(m - m_f);
+        if (__any(m_use - m_f > kRebase)) {
+          const float rb = exp2_hw(m_f - m_use);
           f *= rb;
           m_f = m_use;
 #pragma unroll
@@ -574,7 +573,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   wait_vm_lds<0>();                    // the last (empty) requests, before the LDS is released
 
   if constexpr (!VPT) {
-    const float back = (m == kNegInf) ? 0.0f : exp2_hw((m_f - m) * fs);
+    const float back = (m == kNegInf) ? 0.0f : exp2_hw(m_f - m);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -588,8 +587,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<float4*>(pt.acc + prow * D + cb * 16 + grp * 4) =
         make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-  // the partial's max in base 2 (-inf stays -inf): the merge weighs chunks by 2^(m_s - M)
-  if (grp == 0) *reinterpret_cast<float2*>(pt.ml + prow * 2) = make_float2(m * fs, ltot);
+  // the partial's max (base 2, -inf stays -inf): the merge weighs chunks by 2^(m_s - M)
+  if (grp == 0) *reinterpret_cast<float2*>(pt.ml + prow * 2) = make_float2(m, ltot);
 }
 
 // Merge of the chunk partials of one query row per wavefront:

@@ -185,18 +185,17 @@ __device__ __forceinline__ void pv_tile(v16i (&acc)[D / 32], const int8_t* vst, 
 }
 
 // The dequantized logits of this lane's keys, masked keys -inf; returns the
-// max over the lane pair. EXP (exp softmax): x = ((float(S_int) * s_Q) *
-// s_K[j]) * (1/sqrt d), three rounded fp32 products in that order, the
-// oracle's logit bit for bit (for d = 64 the last factor is 2^-3, which is
-// exact, so it is left out and x is 8 S: the caller works in those units).
-// !EXP (IndexSoftmax): x = float(S_int) * s_K[j], the table path's u. rel =
+// max over the lane pair. EXP (exp softmax): the base-2 logit x =
+// (float(S_int) * aq) * s_K[j], two rounded fp32 products in that order with
+// aq = s_Q log2(e) / sqrt(d) formed once per row, the oracle's logit bit for
+// bit. !EXP (IndexSoftmax): x = float(S_int) * s_K[j] (aq unused), the table
+// path's u. rel =
 // (last visible key of the row) - k0 - 16 g, so entry v of block kb is
 // visible iff 32 kb + v <= rel, a compare of a compile-time constant with one
 // per-lane value.
 template <int D, bool MASK, bool EXP>
-__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float* sk, float sq, float (&x)[NKB][16],
+__device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float* sk, float aq, float (&x)[NKB][16],
                                               int rel, int g) {
-  constexpr float kRs = 0.08838834764831845f;          // fl32(1 / sqrt(128))
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -207,8 +206,7 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
       for (int e = 0; e < 4; ++e) {
         float t = static_cast<float>(s[kb][j4 * 4 + e]);
         if constexpr (EXP) {
-          t = (t * sq) * skk[e];
-          if constexpr (D != 64) t = t * kRs;
+          t = (t * aq) * skk[e];
         } else {
           t = t * skk[e];
         }
@@ -230,13 +228,12 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// y = exp2((x - m) ls + log2 127) = 127 P_tilde, with x - m the oracle's
-// rounded fp32 difference of the logit and the running max (ls = log2 e, or
-// log2 e / 8 when x carries the factor 8); returns this lane's sum of y and
-// packs P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t)) into the PV
-// operands. Masked keys have x = -inf, so their y is exactly 0.
+// y = 2^(x - eb) = 127 P_tilde, with eb the exponent bias of the running max
+// (exp_bias) and x - eb the oracle's rounded fp32 difference; returns this
+// lane's sum of y and packs P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t))
+// into the PV operands. Masked keys have x = -inf, so their y is exactly 0.
 template <bool VPT>
-__device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float m, float ls, const float* sv,
+__device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float eb, const float* sv,
                                             float rst, v4i (&pv)[NKB], int g) {
   float gs[NKB * 4];                   // partial row sums, added as a tree
 #pragma unroll
@@ -253,7 +250,7 @@ __device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float m, 
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        y[e] = exp2_hw(__builtin_fmaf((x[kb][j4 * 4 + e] - m), ls, kLog2_127));
+        y[e] = exp2_hw(x[kb][j4 * 4 + e] - eb);
         word = __builtin_amdgcn_cvt_pk_u8_f32(VPT ? y[e] * wr[e] : y[e], e, word);
       }
       gs[kb * 4 + j4] = (y[0] + y[1]) + (y[2] + y[3]);
@@ -573,12 +570,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
   asm volatile("" : "+v"(sq));
   const float inv_sqrt_d = (D == 64) ? 0.125f : static_cast<float>(0.08838834764831845);
-  // Units of the running max m. Exp softmax: m is the oracle's fp32 running
-  // max of the logits (times 8 for d = 64), and fs = log2 e (/ 8) turns a
-  // difference of two such values into base 2. IndexSoftmax: m is in base-2
-  // logits (fs = 1), the max of u times c2 = s_Q log2 e / sqrt(d), kept >=
+  // The running max m is in base-2 logits. Exp softmax: the oracle's fp32
+  // running max of x = (S_int aq) s_K[j], aq = s_Q log2(e) / sqrt(d).
+  // IndexSoftmax: the max of u times c2 = s_Q log2 e / sqrt(d), kept >=
   // FLT_MIN so that -inf * c2 stays -inf for masked keys.
-  const float fs = LUT ? 1.0f : (D == 64 ? kLog2e * 0.125f : kLog2e);
+  const float aq = sq * kLogitScale<D>;
   const float c2 = fmaxf(sq * inv_sqrt_d * kLog2e, kFltMin);
   // IndexSoftmax: table index per unit of u below the running max, and the
   // running max of u itself (kept beside m)
@@ -622,9 +618,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     float u[NKB][16];                  // logits x (exp softmax) or u (IndexSoftmax)
     float mx;
     if (!mask) {
-      mx = dequant_tile<D, false, !LUT>(s, st->sk, sq, u, 0, g);
+      mx = dequant_tile<D, false, !LUT>(s, st->sk, aq, u, 0, g);
     } else {
-      mx = dequant_tile<D, true, !LUT>(s, st->sk, sq, u, min(lim, a.Lkv - 1) - k0 - 16 * g, g);
+      mx = dequant_tile<D, true, !LUT>(s, st->sk, aq, u, min(lim, a.Lkv - 1) - k0 - 16 * g, g);
     }
 
     // ---- softmax(t): running max, 127 P_tilde, row sum, P_hat ----
@@ -632,10 +628,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     const float mx2 = !LUT ? mx : (mx == kNegInf) ? kNegInf : mx * c2;
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    // alpha = 2^((m - m_use) fs): 1 when no row of the wavefront raised its
-    // max (then it is not computed), 0 on a row's first visible tile
+    // alpha = 2^(m - m_use): 1 when no row of the wavefront raised its max
+    // (then it is not computed), 0 on a row's first visible tile
     float alpha = 1.0f;
-    if constexpr (VPT) alpha = exp2_hw((m - m_use) * fs);
+    if constexpr (VPT) alpha = exp2_hw(m - m_use);
     v4i p[NKB];
     float lsum;
     float st_cur = 0.0f;
@@ -657,18 +653,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);
         rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
       }
-      lsum = probs_tile<VPT>(u, m_use, fs, st->sv, rst, p, g);
+      lsum = probs_tile<VPT>(u, exp_bias(m_use), st->sv, rst, p, g);
     }
 
     if constexpr (!VPT) {
       if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
-        alpha = exp2_hw((m - m_use) * fs);
+        alpha = exp2_hw(m - m_use);
         // tile t raised some row's max: the INT32 run (tiles before t, frame
         // m) goes into acc (frame m_f) before PV(t) starts a new run
         if (m_f == kNegInf) m_f = m_use;
-        float f = exp2_hw((m - m_f) * fs);            // 0 before the first tile
-        if (__any((m_use - m_f) * fs > kRebase)) {    // keep acc far from overflow
-          const float r = exp2_hw((m_f - m_use) * fs);
+        float f = exp2_hw(m - m_f);                   // 0 before the first tile
+        if (__any(m_use - m_f > kRebase)) {           // keep acc far from overflow
+          const float r = exp2_hw(m_f - m_use);
           f *= r;
           m_f = m_use;
 #pragma unroll
@@ -717,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
 
   if constexpr (!VPT) {
     // total in the frame of the final max m: 2^(m_f - m) acc + INT32 run
-    const float back = exp2_hw((m_f - m) * fs);
+    const float back = exp2_hw(m_f - m);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -754,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         *reinterpret_cast<float4*>(static_cast<float*>(a.o) + orow + d0) = make_float4(o0, o1, o2, o3);
       }
     }
-  if (a.lse && g == 0) a.lse[q_base + qi] = (m * fs + __builtin_log2f(ltot) - kLog2_127) * kLn2;
+  if (a.lse && g == 0) a.lse[q_base + qi] = (m + __builtin_log2f(ltot) - kLog2_127) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool VPT, bool OUT_F16>

@@ -37,6 +37,22 @@ __device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log2(e) / sqrt(d) rounded to fp32 (d = 64, 128): a row's base-2 logit is
+// (S_int (s_Q c)) s_K[j] with c this factor
+template <int D>
+constexpr float kLogitScale = D == 64 ? 0.18033687770366669f : 0.12751743197441101f;
+
+// Exponent bias of a running max m (base 2): m - log2(127) in fp32, moved up
+// one float when m minus it still exceeds log2(127) after rounding. Every
+// logit x <= m then has x - b <= log2(127) in fp32, so 2^(x - b) stays within
+// 127 (up to the exponential's own rounding) and its code fits a signed byte
+// whatever the magnitude of m. The nudged value is never +-0.
+__device__ __forceinline__ float exp_bias(float m) {
+  const float b = m - kLog2_127;
+  const uint32_t u = __float_as_uint(b);
+  return (m - b > kLog2_127) ? __uint_as_float(b > 0.0f ? u + 1u : u - 1u) : b;
+}
+
 // 32x32x32 and 16x16x64 INT8 products with INT32 accumulation
 __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
