@@ -631,7 +631,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     // alpha = 2^(m - m_use): 1 when no row of the wavefront raised its max
     // (then it is not computed), 0 on a row's first visible tile
     float alpha = 1.0f;
-    if constexpr (VPT) alpha = exp2_hw(m - m_use);
+    const bool rose = __any(m_new > m);
+    if (VPT && rose) alpha = exp2_hw(m - m_use);
     v4i p[NKB];
     float lsum;
     float st_cur = 0.0f;
@@ -657,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     }
 
     if constexpr (!VPT) {
-      if (__any(m_new > m) || ++int_tiles > kMaxIntTiles) {
+      if (rose || ++int_tiles > kMaxIntTiles) {
         alpha = exp2_hw(m - m_use);
         // tile t raised some row's max: the INT32 run (tiles before t, frame
         // m) goes into acc (frame m_f) before PV(t) starts a new run
@@ -690,12 +691,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     fresh = false;
     if constexpr (VPT) {
       // per-token V: tile scales differ, so each tile's INT32 product is
-      // converted on its own: acc = alpha acc + s_t PV(t)
+      // converted on its own: acc = alpha acc + s_t PV(t), the product by
+      // alpha only on tiles that raised a max, both in place (written as one
+      // fma, the compiler accumulates into the product's register and the
+      // loop then copies all of acc back every tile)
+      if (rose) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[c][v] *= alpha;
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          acc[c][v] = __builtin_fmaf(alpha, acc[c][v], st_cur * static_cast<float>(acc_i[c][v]));
+          acc[c][v] = __builtin_fmaf(st_cur, static_cast<float>(acc_i[c][v]), acc[c][v]);
     }
     }  // !DUMP
 
