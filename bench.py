@@ -106,11 +106,37 @@ CSRC = os.path.join(ROOT, "int8_quantized_flashattention_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def code_of(text):
+    """C/C++ source without its comments and with runs of whitespace folded,
+    so that a change to comments alone leaves the hash below unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":                  # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_sources_hash(names):
+    """Hash of the kernel sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(CSRC, n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, n), encoding="utf-8") as f:
+            h.update(code_of(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,8 +17,9 @@
  *      IntAttention §2.2; tile-wise fusion as in "FlashAttention-3",
  *      abstract), probabilities quantized to INT8 with multiplier 127
  *      (IntAttention §3.2, the prior-methods scheme), INT8 P.V into INT32 per
- *      tile, and the final rescale O = acc / (127 l) (IntAttention §2.1,
- *      O ~ s_V P V_hat).
+ *      tile, and the final rescale O = acc / l with l the row sum of 127 P
+ *      (IntAttention §2.1, O ~ s_V P V_hat). The logits are taken in base 2
+ *      (the same softmax: e^(S - m) = 2^((S - m) log2 e)).
  *
  * Conventions shared by every entry point:
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except the
@@ -219,13 +220,17 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
  *   tensor must have fewer than 2^31 elements.
  *
  * Per row the kernel visits the KV tiles reported by attn_int8_fwd_schedule
- * in ascending order. For tile t with running max m' (after the tile):
- * P_tilde = exp(S - m'), l = alpha l + sum P_tilde, P_hat = rne(P_tilde w_j)
- * with w_j = 127 (per-tensor and per-head V) or 127 s_V[j] / s_t (per-token V,
- * s_t = the largest s_V of the tile's keys), acc = alpha acc + s_t *
- * (P_hat . V_hat) (s_t = s_V for per-tensor V, the (batch, kv head)'s s_V for
- * per-head V, 1 for per-channel V), and finally O = acc / (127 l), channel c
- * multiplied by its scale for per-channel V. Because P_hat
+ * in ascending order. Each key's logit is taken in base 2,
+ * t = (S_int * (s_Q * c)) * s_K[j] in fp32 with c = fl32(log2(e) / sqrt(d)).
+ * For tile t with running max m' of t (after the tile) and the exponent bias
+ * b = m' - log2(127) in fp32 (moved up one float when m' - b still exceeds
+ * log2(127), so that no code passes 127): y = 2^(t - b) = 127 P_tilde,
+ * l = alpha l + sum y with alpha = 2^(m_old - m'), P_hat = rne(y w_j) with
+ * w_j = 1 (per-tensor and per-head V) or s_V[j] / s_t (per-token V, s_t = the
+ * largest s_V of the tile's keys), acc = alpha acc + s_t * (P_hat . V_hat)
+ * (s_t = s_V for per-tensor V, the (batch, kv head)'s s_V for per-head V, 1
+ * for per-channel V), and finally O = acc / l, channel c multiplied by its
+ * scale for per-channel V; lse = ln 2 (m' - log2(127) + log2 l). Because P_hat
  * follows the running max, O depends on the tile size and split points; they
  * are part of the result's definition and are reported by the schedule query.
  */

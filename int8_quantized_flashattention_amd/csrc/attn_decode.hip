@@ -32,9 +32,9 @@
 
 #include <type_traits>
 
-// fp32 products and sums are rounded as written (the logits and their
-// difference to the running max are the oracle's values bit for bit); fma
-// only where written.
+// fp32 products and sums are rounded as written (the logits and the exponent
+// argument, a logit minus the bias of the running max, are the oracle's values
+// bit for bit); fma only where written.
 #pragma clang fp contract(off)
 
 namespace attn {

@@ -38,15 +38,15 @@
 //
 // Instruction budget. On gfx950 the issue time of the VALU work per
 // (query, key) pair is the first-order cost next to the pair's MFMA work.
-// The logit and its distance to the running max are formed exactly as the
-// oracle rounds them (three fp32 products, one fp32 difference), so that only
-// the last-ulp behaviour of the exponential can move a quantized
-// probability; per pair the kernel spends one INT32->fp32 convert, two or
-// three multiplies, half a v_max3, one subtract, one fma for the base-2
-// exponent (127 folded in), one v_exp_f32, one add for the row sum and one
-// v_cvt_pk_u8_f32 (round to nearest even, saturating) that quantizes P and
-// packs it into the MFMA operand. Everything else is per tile or per
-// workgroup:
+// The logit is taken in base 2 with the row's factor s_Q log2(e) / sqrt(d)
+// formed once, and it and the exponent argument x - b (b: the exponent bias
+// of the running max, 127 folded in) are formed exactly as the oracle rounds
+// them (two fp32 products, one fp32 difference), so that only the last-ulp
+// behaviour of the exponential can move a quantized probability; per pair the
+// kernel spends one INT32->fp32 convert, two multiplies, half a v_max3, one
+// subtract, one v_exp_f32, one add for the row sum and one v_cvt_pk_u8_f32
+// (round to nearest even, saturating) that quantizes P and packs it into the
+// MFMA operand. Everything else is per tile or per workgroup:
 //  - for per-tensor V the P_hat . V_hat products keep accumulating in the
 //    INT32 MFMA accumulator while no row of the wavefront raises its max and
 //    are folded into the fp32 accumulator (which keeps its own frame) only
@@ -57,10 +57,10 @@
 
 #include <hip/hip_fp16.h>
 
-// Every fp32 product and sum below is rounded as written: the logits and
-// their difference to the running max must be the oracle's values bit for
-// bit, so no multiply may be fused into a following add (fma only where
-// written).
+// Every fp32 product and sum below is rounded as written: the logits and the
+// exponent argument (a logit minus the bias of the running max) must be the
+// oracle's values bit for bit, so no multiply may be fused into a following
+// add (fma only where written).
 #pragma clang fp contract(off)
 
 namespace attn {
