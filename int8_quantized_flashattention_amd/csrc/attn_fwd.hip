@@ -230,11 +230,12 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
 
 // y = 2^(x - eb) = 127 P_tilde, with eb the exponent bias of the running max
 // (exp_bias) and x - eb the oracle's rounded fp32 difference; returns this
-// lane's sum of y and packs P_hat = rne(y) (per-token V: rne(y s_V[j] / s_t))
-// into the PV operands. Masked keys have x = -inf, so their y is exactly 0.
+// lane's sum of y and packs P_hat = rne(y) (per-token V: rne(y w_j) with the
+// key multipliers w_j = s_V[j] (1 / s_t) read from wr) into the PV operands.
+// Masked keys have x = -inf, so their y is exactly 0.
 template <bool VPT>
-__device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float eb, const float* sv,
-                                            float rst, v4i (&pv)[NKB], int g) {
+__device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float eb, const float* wr_s,
+                                            v4i (&pv)[NKB], int g) {
   float gs[NKB * 4];                   // partial row sums, added as a tree
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -243,8 +244,8 @@ __device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float eb,
     for (int j4 = 0; j4 < 4; ++j4) {
       float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
       if constexpr (VPT) {
-        const float4 s4 = *reinterpret_cast<const float4*>(sv + kb * 32 + g * 16 + j4 * 4);
-        wr[0] = s4.x * rst; wr[1] = s4.y * rst; wr[2] = s4.z * rst; wr[3] = s4.w * rst;
+        const float4 w4 = *reinterpret_cast<const float4*>(wr_s + kb * 32 + g * 16 + j4 * 4);
+        wr[0] = w4.x; wr[1] = w4.y; wr[2] = w4.z; wr[3] = w4.w;
       }
       uint32_t word = 0;
       float y[4];
@@ -333,8 +334,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // s_t of a tile for per-token V: the largest s_V[j] over the tile's keys
 // below Lkv (a stage may hold stale entries past the end).
-__device__ __forceinline__ float tile_vscale(const float* sv, int lane, int k0, int Lkv) {
-  float x = (k0 + lane < Lkv) ? sv[lane] : 0.0f;
+__device__ __forceinline__ float tile_vscale(float svl) {
+  float x = svl;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
   return x;
@@ -402,6 +403,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
   __shared__ Stage<D> sm[kStages];
   __shared__ uint32_t lut_s[LUT ? 65 : 1];
   __shared__ uint16_t lut2_s[LUT == 2 ? kLutPairRows * kLutPairRows : 1];
+  // per-token V: each wavefront's key multipliers s_V[j] / s_t of the tile
+  __shared__ float wr_s[VPT ? kWaves : 1][VPT ? BN : 1];
 
   const int n_rb = (a.Lq + BM - 1) / BM;
   int bh, rb;
@@ -649,12 +652,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         else lsum = lut_tile<true>(u, kap, mu, nf, tab, rel, p);
       }
     } else {
-      float rst = 0.0f;
       if constexpr (VPT) {
-        st_cur = tile_vscale(st->sv, lane, k0, a.Lkv);
-        rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
+        // s_t and the multiplier of this lane's key (lane = key of the tile),
+        // formed once per key and shared through the wavefront's LDS row: the
+        // LDS executes a wavefront's accesses in order, and the wave barrier
+        // keeps the compiler from moving the reads above the write
+        const float svl = (k0 + lane < a.Lkv) ? st->sv[lane] : 0.0f;
+        st_cur = tile_vscale(svl);
+        const float rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
+        wr_s[wave][lane] = svl * rst;
+        __builtin_amdgcn_wave_barrier();
       }
-      lsum = probs_tile<VPT>(u, exp_bias(m_use), st->sv, rst, p, g);
+      lsum = probs_tile<VPT>(u, exp_bias(m_use), wr_s[VPT ? wave : 0], p, g);
     }
 
     if constexpr (!VPT) {

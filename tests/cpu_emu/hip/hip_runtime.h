@@ -354,6 +354,7 @@ typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;
 // loads every lane issued before the wait (LDS-destination loads included)
 // are complete for all of them after it; the emulated lanes meet here
 #define __builtin_amdgcn_s_waitcnt(x) emu::wave_sync()
+#define __builtin_amdgcn_wave_barrier() emu::wave_sync()
 #define __builtin_amdgcn_ds_swizzle(x, off) emu::ds_swizzle(x, off)
 #define __builtin_amdgcn_s_barrier() emu::syncthreads()
 #define __builtin_amdgcn_sched_group_barrier(m, n, id) ((void)0)
