@@ -435,6 +435,31 @@ def pin_attn_huge_logits_keep_codes_in_range(L):
         assert 120 <= t["p_hat"][0] <= 127 and t["p_hat"][1] == 0, (i, t["p_hat"], t["y"])
 
 
+def pin_attn_huge_negative_logits_keep_codes_in_range(L):
+    # Every logit negative, the row max between -2^19 and -2^17 (base 2): the
+    # exponent bias is then negative and steps toward zero; the least negative
+    # key still gets a code in [120, 127] and the row's output is its V row.
+    d, Lq = 64, 256
+    r = _rng(54)
+    c = np.float32(1.0 / (math.log(2.0) * math.sqrt(d)))
+    s_int = -64 * 127                          # Q codes 127, key 0 codes -1
+    sq = (r.uniform(2.0 ** 17, 2.0 ** 19, Lq) / (-s_int * np.float64(c))).astype(np.float32)
+    qh = np.full((1, 1, Lq, d), 127, np.int8)
+    kh = np.full((1, 1, 2, d), -127, np.int8)
+    kh[0, 0, 0] = -1
+    sk = np.ones(2, np.float32)
+    vh = r.integers(-127, 128, (1, 1, 2, d)).astype(np.int8)
+    sv = np.array([0.01], np.float32)
+    o, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sv, False, 1, 1, 1, Lq, 2, d, False, 64, L=L)
+    ref = vh[0, 0, 0].astype(np.float64) * np.float64(sv[0])
+    assert np.allclose(o[0, 0], ref[None, :], rtol=0.5 / 120, atol=1e-6)
+    for i in range(Lq):
+        t = oracle.attn_int8_trace(qh, sq, kh, sk, vh, sv, False, 1, 1, 1, Lq, 2, d, False, 64, 0,
+                                   0, 0, i, L=L)
+        assert t["m_tile"][0] < -2.0 ** 16
+        assert 120 <= t["p_hat"][0] <= 127 and t["p_hat"][1] == 0, (i, t["p_hat"], t["y"])
+
+
 def pin_attn_bound_vs_dequant_softmax(L):
     # Proven bound: with exact softmax weights p_ij of the dequantized logits and
     # the method's effective weights w_ij = P_hat 2^{m_t(j)-m_i} / l_i (l_i the sum

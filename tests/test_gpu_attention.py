@@ -59,19 +59,24 @@ def test_wide_outlier_problem(lib):
     run_problem(lib, q, k, v, True, False, "f32", tag="wide_outlier")
 
 
+@pytest.mark.parametrize("neg", [False, True])
 @pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt", [
     (1, 4, 2, 300, 333, 128, 1, 0, "f32"), (1, 4, 2, 300, 333, 64, 0, 1, "f16"),
     (2, 8, 2, 1, 700, 128, 0, 0, "f32"), (1, 8, 1, 2, 520, 64, 1, 1, "f16")])
-def test_huge_logits(lib, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt):
+def test_huge_logits(lib, B, H, Hkv, Lq, Lkv, d, causal, vpt, odt, neg):
     # Q and K x200: row maxima of ~10^5 (base 2 about 2^17), where the fp32
     # spacing of the running max is 2^-7..2^-6 and the exponent bias has to
     # keep the dominant key's code within a signed byte (a code of 128 would
-    # read as -128 and flip that key's V row). V x1/4: a code that rounds the
-    # other way at a tie moves O by at most |V|/127 < 1e-2.
+    # read as -128 and flip that key's V row). neg: |Q| against -|K|, so every
+    # logit and every row max is negative (about -2^18; the bias steps toward
+    # zero). V x1/4: a code that rounds the other way at a tie moves O by at
+    # most |V|/127 < 1e-2.
     q = gaussian((B, H, Lq, d), 50200 + d, np.float32) * np.float32(200.0)
     k = gaussian((B, Hkv, Lkv, d), 50201 + d, np.float32) * np.float32(200.0)
     v = gaussian((B, Hkv, Lkv, d), 50202 + d, np.float32) * np.float32(0.25)
-    run_problem(lib, q, k, v, bool(causal), bool(vpt), odt, tag="huge_logits")
+    if neg:
+        q, k = np.abs(q), -np.abs(k)
+    run_problem(lib, q, k, v, bool(causal), bool(vpt), odt, tag="huge_logits_neg" if neg else "huge_logits")
 
 
 # ragged and degenerate shapes: Lq/Lkv not multiples of the tiles, Lq != Lkv,
