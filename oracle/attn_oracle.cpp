@@ -44,9 +44,10 @@
 //    fp32 exp2 of the fp32 difference.
 //  * per-token V inside the INT8 P.V product: the scale of tile t is
 //    s_t = max of s_V over the tile's in-range keys; key j's probability is
-//    quantized with multiplier w_j = s_V[j] / s_t (fp32) on y.
-//  * P_hat = rne(y * w) of the exact product (at most 48 significant bits,
-//    so exact in double); w = 1 for per-tensor V.
+//    quantized with multiplier w_j = s_V[j] / s_t (one rounded fp32
+//    division) on y.
+//  * P_hat = rne(fl32(y * w)): the product rounded to fp32 first, the
+//    precision of the code decision; w = 1 for per-tensor V.
 //  * per-head V (one scale per (batch, kv head), a block granularity that
 //    IA §3.3 lists as compatible): the tile scale is that head's s_V and
 //    w = 1, i.e. the per-tensor arithmetic with the head's own scale.
@@ -301,8 +302,10 @@ void attend_row(const Problem& P, int b, int h, int i, float* o, float* lse, Row
         w[jj] = wj;
         // P_hat = rne(127 P_tilde w): signed INT8 probabilities with
         // multiplier 127 (IA §3.2 describes this as the prior methods'
-        // choice); the product y w is exact in double.
-        ph[jj] = static_cast<int32_t>(std::nearbyint(static_cast<double>(y) * static_cast<double>(wj)));
+        // choice); y w is one rounded fp32 product (exact when w = 1), the
+        // precision in which the kernels take the same decision.
+        const float yw = y * wj;
+        ph[jj] = static_cast<int32_t>(std::nearbyint(yw));
       }
       l = PLANT("l_no_rescale") ? (l + lsum) : (alpha * l + lsum);
       // T = P_hat . V_hat over this tile, exact in INT32.
