@@ -207,6 +207,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
   constexpr int NL = loads_per_tile<D, VPT>();
   __shared__ DStage<D> sm[kStages];
   __shared__ uint32_t lut_s[LUT ? 65 : 1];
+  // per-token V: the key multipliers s_V[j] / s_t of the current tile
+  __shared__ float wr_s[VPT ? BN : 1];
 
   const int G = a.H / a.Hkv;                 // query heads per KV head
   const int R = G * a.Lq;                    // query rows of the group (<= 16)
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
     const float m_new = fmaxf(m, mx2);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = exp2_hw(m - m_use);
-    float st_cur = 0.0f, rst = 0.0f;
+    float st_cur = 0.0f;
     uint32_t pw[NB];
     float lsum;
     if constexpr (LUT) {
@@ -476,12 +478,17 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       lsum = static_cast<float>(isum);
     } else {
       if constexpr (VPT) {
-        // s_t: largest s_V[j] over the tile's keys inside the chunk
-        float x = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
+        // s_t: largest s_V[j] over the tile's keys inside the chunk; then the
+        // multiplier of this lane's key, s_V[j] / s_t as the oracle's one
+        // rounded division, shared through LDS (a wavefront's LDS accesses
+        // execute in order; the wave barrier keeps the reads after the write)
+        const float svl = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
+        float x = svl;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
         st_cur = x;
-        rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
+        wr_s[VPT ? lane : 0] = st_cur > 0.0f ? __fdiv_rn(svl, st_cur) : 0.0f;
+        __builtin_amdgcn_wave_barrier();
       }
       const float eb = exp_bias(m_use);
       float gs[NB];
@@ -489,8 +496,8 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
       for (int kb = 0; kb < NB; ++kb) {
         float wr[4] = {1.0f, 1.0f, 1.0f, 1.0f};
         if constexpr (VPT) {
-          const float4 s4 = *reinterpret_cast<const float4*>(st->sv + grp * 16 + kb * 4);
-          wr[0] = s4.x * rst; wr[1] = s4.y * rst; wr[2] = s4.z * rst; wr[3] = s4.w * rst;
+          const float4 w4 = *reinterpret_cast<const float4*>(wr_s + grp * 16 + kb * 4);
+          wr[0] = w4.x; wr[1] = w4.y; wr[2] = w4.z; wr[3] = w4.w;
         }
         uint32_t word = 0;
         float y[4];

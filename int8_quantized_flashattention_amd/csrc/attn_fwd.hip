@@ -230,9 +230,9 @@ __device__ __forceinline__ float dequant_tile(const v16i (&s)[NKB], const float*
 
 // y = 2^(x - eb) = 127 P_tilde, with eb the exponent bias of the running max
 // (exp_bias) and x - eb the oracle's rounded fp32 difference; returns this
-// lane's sum of y and packs P_hat = rne(y) (per-token V: rne(y w_j) with the
-// key multipliers w_j = s_V[j] (1 / s_t) read from wr) into the PV operands.
-// Masked keys have x = -inf, so their y is exactly 0.
+// lane's sum of y and packs P_hat = rne(y) (per-token V: rne(y w_j), the fp32
+// product, with the key multipliers w_j = s_V[j] / s_t read from wr) into the
+// PV operands. Masked keys have x = -inf, so their y is exactly 0.
 template <bool VPT>
 __device__ __forceinline__ float probs_tile(const float (&x)[NKB][16], float eb, const float* wr_s,
                                             v4i (&pv)[NKB], int g) {
@@ -654,13 +654,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     } else {
       if constexpr (VPT) {
         // s_t and the multiplier of this lane's key (lane = key of the tile),
-        // formed once per key and shared through the wavefront's LDS row: the
-        // LDS executes a wavefront's accesses in order, and the wave barrier
-        // keeps the compiler from moving the reads above the write
+        // s_V[j] / s_t as the oracle's one rounded division, formed once per
+        // key and shared through the wavefront's LDS row: the LDS executes a
+        // wavefront's accesses in order, and the wave barrier keeps the
+        // compiler from moving the reads above the write
         const float svl = (k0 + lane < a.Lkv) ? st->sv[lane] : 0.0f;
         st_cur = tile_vscale(svl);
-        const float rst = st_cur > 0.0f ? 1.0f / st_cur : 0.0f;
-        wr_s[wave][lane] = svl * rst;
+        wr_s[wave][lane] = st_cur > 0.0f ? __fdiv_rn(svl, st_cur) : 0.0f;
         __builtin_amdgcn_wave_barrier();
       }
       lsum = probs_tile<VPT>(u, exp_bias(m_use), wr_s[VPT ? wave : 0], p, g);

@@ -59,6 +59,19 @@ def test_wide_outlier_problem(lib):
     run_problem(lib, q, k, v, True, False, "f32", tag="wide_outlier")
 
 
+def test_per_token_v_tie_problem(lib):
+    # B2 H11 Hkv11 Lq296 Lkv1127 d64 causal, per-token V, fp16 in and out,
+    # channel 37 of Q and K x20 (problem 446 of the random sweep). In rows
+    # peaked on key 881 that key's y is 127 and 127 s_V[j] / s_t lies within
+    # 5e-6 of 102.5: a multiplier formed as s_V[j] * (1 / s_t), one ulp above
+    # the quotient, rounds the code to 103 instead of 102 and moves O by 0.02
+    B, H, Hkv, Lq, Lkv, d = 2, 11, 11, 296, 1127, 64
+    q = gaussian((B, H, Lq, d), 104460, outlier_channels=[37])
+    k = gaussian((B, Hkv, Lkv, d), 104461, outlier_channels=[37])
+    v = gaussian((B, Hkv, Lkv, d), 104462)
+    run_problem(lib, q, k, v, True, True, "f16", tag="per_token_v_tie")
+
+
 @pytest.mark.parametrize("neg", [False, True])
 @pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt", [
     (1, 4, 2, 300, 333, 128, 1, 0, "f32"), (1, 4, 2, 300, 333, 64, 0, 1, "f16"),
