@@ -225,9 +225,9 @@ attn_status attn_kv_append(const void* x, attn_dtype x_dt, int32_t B, int32_t Hk
  * For tile t with running max m' of t (after the tile) and the exponent bias
  * b = m' - log2(127) in fp32 (moved up one float when m' - b still exceeds
  * log2(127), so that no code passes 127): y = 2^(t - b) = 127 P_tilde,
- * l = alpha l + sum y with alpha = 2^(m_old - m'), P_hat = rne(y w_j) with
- * w_j = 1 (per-tensor and per-head V) or s_V[j] / s_t (per-token V, s_t = the
- * largest s_V of the tile's keys), acc = alpha acc + s_t * (P_hat . V_hat)
+ * l = alpha l + sum y with alpha = 2^(m_old - m'), P_hat = rne(fl32(y w_j))
+ * with w_j = 1 (per-tensor and per-head V) or the fp32 quotient s_V[j] / s_t
+ * (per-token V, s_t = the largest s_V of the tile's keys), acc = alpha acc + s_t * (P_hat . V_hat)
  * (s_t = s_V for per-tensor V, the (batch, kv head)'s s_V for per-head V, 1
  * for per-channel V), and finally O = acc / l, channel c multiplied by its
  * scale for per-channel V; lse = ln 2 (m' - log2(127) + log2 l). Because P_hat
