@@ -483,10 +483,7 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
         // rounded division, shared through LDS (a wavefront's LDS accesses
         // execute in order; the wave barrier keeps the reads after the write)
         const float svl = (k0 + lane < s1) ? st->sv[lane] : 0.0f;
-        float x = svl;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-        st_cur = x;
+        st_cur = wave_max_nonneg(svl);
         wr_s[VPT ? lane : 0] = st_cur > 0.0f ? __fdiv_rn(svl, st_cur) : 0.0f;
         __builtin_amdgcn_wave_barrier();
       }

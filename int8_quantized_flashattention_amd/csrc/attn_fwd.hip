@@ -334,12 +334,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // s_t of a tile for per-token V: the largest s_V[j] over the tile's keys
 // below Lkv (a stage may hold stale entries past the end).
-__device__ __forceinline__ float tile_vscale(float svl) {
-  float x = svl;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
+__device__ __forceinline__ float tile_vscale(float svl) { return wave_max_nonneg(svl); }
 
 __device__ __forceinline__ Bufs make_bufs(const FwdArgs& a, int64_t kv_base, int D, bool scales, bool vpt) {
   Bufs bf;

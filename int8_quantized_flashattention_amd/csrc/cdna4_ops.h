@@ -37,6 +37,24 @@ __device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Largest of the 64 lanes' non-negative fp32 values, in every lane: the bit
+// patterns of non-negative floats order as the floats do, so unsigned maxima
+// on them are exact. Inside rows of 16 lanes by DPP moves (quad exchanges, then
+// the half-row and row mirrors), then across the four rows by reading one lane
+// of each: VALU work only, no LDS round trip.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0xB1, 0xf, 0xf, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x4E, 0xf, 0xf, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x141, 0xf, 0xf, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x140, 0xf, 0xf, false)));
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 16));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 32));
+  const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 48));
+  return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 // log2(e) / sqrt(d) rounded to fp32 (d = 64, 128): a row's base-2 logit is
 // (S_int (s_Q c)) s_K[j] with c this factor
 template <int D>

@@ -221,6 +221,40 @@ inline int ds_swizzle(int x, int offset) {
 
 inline void wave_sync() { ctx.wave->bar.arrive_and_wait(); }
 
+// DPP move inside rows of 16 lanes, for the controls the kernels use:
+// quad_perm (0x00-0xff: lane 4q + i reads lane 4q + sel_i), row_mirror
+// (0x140: lane i of a row reads lane 15 - i) and row_half_mirror (0x141:
+// lane i of each half row reads lane 7 - i). All rows and banks enabled.
+inline int update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl) {
+  (void)old; (void)bound_ctrl;
+  if (row_mask != 0xf || bank_mask != 0xf) std::abort();
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  std::memcpy(w.slot[self], &src, 4);
+  w.bar.arrive_and_wait();
+  const int row = self & ~15, i = self & 15;
+  int from;
+  if (ctrl >= 0 && ctrl < 0x100) from = row + (i & ~3) + ((ctrl >> (2 * (i & 3))) & 3);
+  else if (ctrl == 0x140) from = row + 15 - i;
+  else if (ctrl == 0x141) from = row + (i & 8) + 7 - (i & 7);
+  else std::abort();
+  int r;
+  std::memcpy(&r, w.slot[from], 4);
+  w.bar.arrive_and_wait();
+  return r;
+}
+
+inline int readlane(int x, int lane) {
+  Wave& w = *ctx.wave;
+  const int self = ctx.lane;
+  std::memcpy(w.slot[self], &x, 4);
+  w.bar.arrive_and_wait();
+  int r;
+  std::memcpy(&r, w.slot[lane & 63], 4);
+  w.bar.arrive_and_wait();
+  return r;
+}
+
 inline int wave_any(int p) {
   Wave& w = *ctx.wave;
   const int self = ctx.lane;
@@ -340,6 +374,8 @@ inline uint32_t float_to_bits(float f) { uint32_t u; std::memcpy(&u, &f, 4); ret
 #define __builtin_amdgcn_sdot4(a, b, c, clamp) emu::sdot4(a, b, c)
 #define __any(p) emu::wave_any(p)
 #define __builtin_amdgcn_readfirstlane(x) (x)
+#define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emu::update_dpp(old, src, ctrl, rm, bm, bc)
+#define __builtin_amdgcn_readlane(x, l) emu::readlane(x, l)
 typedef emu::BufRsrc __amdgpu_buffer_rsrc_t;
 // no register-allocation hints on the host
 #define ATTN_WAVES_PER_EU(n)
