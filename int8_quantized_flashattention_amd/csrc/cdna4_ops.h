@@ -37,17 +37,26 @@ __device__ __forceinline__ v16i zero16() { return v16i{0, 0, 0, 0, 0, 0, 0, 0, 0
 __device__ __forceinline__ v4i zero4() { return v4i{0, 0, 0, 0}; }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Largest of the 64 lanes' non-negative fp32 values, in every lane: the bit
-// patterns of non-negative floats order as the floats do, so unsigned maxima
-// on them are exact. Inside rows of 16 lanes by DPP moves (quad exchanges, then
-// the half-row and row mirrors), then across the four rows by reading one lane
-// of each: VALU work only, no LDS round trip.
-__device__ __forceinline__ float wave_max_nonneg(float x) {
+// Largest of the non-negative fp32 values of each aligned group of T lanes
+// (T = 8 or 16), in every lane of the group: the bit patterns of non-negative
+// floats order as the floats do, so unsigned maxima on them are exact. DPP
+// moves inside the 16-lane rows (quad exchanges, then the half-row mirror, for
+// T = 16 also the row mirror): VALU work only, no LDS round trip.
+template <int T>
+__device__ __forceinline__ float group_max_nonneg(float x) {
+  static_assert(T == 8 || T == 16, "DPP groups of 8 or 16 lanes");
   uint32_t u = __float_as_uint(x);
   u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0xB1, 0xf, 0xf, false)));
   u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x4E, 0xf, 0xf, false)));
   u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x141, 0xf, 0xf, false)));
-  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x140, 0xf, 0xf, false)));
+  if constexpr (T == 16)
+    u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x140, 0xf, 0xf, false)));
+  return __uint_as_float(u);
+}
+
+// The same over all 64 lanes: each row's maximum, then one lane of each row.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  const uint32_t u = __float_as_uint(group_max_nonneg<16>(x));
   const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 0));
   const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 16));
   const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 32));

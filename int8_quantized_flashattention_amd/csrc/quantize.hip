@@ -119,9 +119,14 @@ __global__ __launch_bounds__(kThreads) void quantize_small_groups(
       const int ci = tl + i * T;
       if (g0 + j < n_groups && ci < n_chunks) a[j] = fmaxf(a[j], chunk_absmax(c[j][i]));
     }
-    // team-wide maximum (exact: max is order-free)
+    // team-wide maximum (exact: max is order-free); teams of 8 or 16 lanes
+    // by DPP moves inside the 16-lane rows, wider ones by lane shuffles
+    if constexpr (T == 8 || T == 16) {
+      a[j] = group_max_nonneg<T>(a[j]);
+    } else {
 #pragma unroll
-    for (int off = T / 2; off > 0; off >>= 1) a[j] = fmaxf(a[j], __shfl_xor(a[j], off, T));
+      for (int off = T / 2; off > 0; off >>= 1) a[j] = fmaxf(a[j], __shfl_xor(a[j], off, T));
+    }
   }
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -333,8 +338,12 @@ __global__ __launch_bounds__(kThreads) void quantize_rows4(const void* __restric
       a = fmaxf(a, chunk_absmax(c[i]));
     }
   }
+  if constexpr (T == 8 || T == 16) {
+    a = group_max_nonneg<T>(a);
+  } else {
 #pragma unroll
-  for (int off = T / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, T));
+    for (int off = T / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, T));
+  }
   if (row >= n_rows) return;
   const int64_t go = MAP ? (row / map.seg_in) * map.seg_out + map.off + row % map.seg_in : row;
   const float r = a == 0.0f ? 0.0f : __fdiv_rn(7.0f, a);
