@@ -307,13 +307,22 @@ __global__ __launch_bounds__(64) ATTN_WAVES_PER_EU(2) void attn_decode_kernel(Fw
             xq[c][e] = x0 + x1;
             xq[c][e + h] = x0 - x1;
           }
-#pragma unroll
-    for (int lm = 16; lm < 64; lm <<= 1) {
-      const float sgn = (lane & lm) ? -1.0f : 1.0f;
+    {
+      // stride 16 by a lane shuffle; stride 32 by v_permlane32_swap, which
+      // hands lanes 0-31 (own, partner) and lanes 32-63 (partner, own), so one
+      // fma gives own + partner below and partner - own above
+      const float sgn16 = (lane & 16) ? -1.0f : 1.0f, sgn32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xq[c][e] = __builtin_fmaf(sgn, xq[c][e], __shfl_xor(xq[c][e], lm, 64));
+        for (int e = 0; e < 16; ++e) xq[c][e] = __builtin_fmaf(sgn16, xq[c][e], __shfl_xor(xq[c][e], 16, 64));
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(xq[c][e]), __float_as_uint(xq[c][e]), false, false);
+          xq[c][e] = __builtin_fmaf(sgn32, __uint_as_float(r[1]), __uint_as_float(r[0]));
+        }
     }
 #pragma unroll
     for (int m = 1; m < NC; m <<= 1)

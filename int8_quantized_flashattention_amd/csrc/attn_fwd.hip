@@ -495,11 +495,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
             xq[c][e] = x0 + x1;
             xq[c][e + h] = x0 - x1;
           }
+    // stride 32 across the lane pair: v_permlane32_swap hands lanes 0-31
+    // (own, partner) and lanes 32-63 (partner, own), so one fma gives own +
+    // partner below and partner - own above (VALU only, no LDS round trip)
     const float sgn = g ? -1.0f : 1.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xq[c][e] = __builtin_fmaf(sgn, xq[c][e], __shfl_xor(xq[c][e], 32, 64));
+      for (int e = 0; e < 16; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(xq[c][e]), __float_as_uint(xq[c][e]), false, false);
+        xq[c][e] = __builtin_fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+      }
 #pragma unroll
     for (int m = 1; m < NC; m <<= 1)
 #pragma unroll
