@@ -612,6 +612,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           }
       }
     } else {
+    // Issue priority (s_setprio) rises through the tile's VALU work: 1 from
+    // here, 2 for the probabilities, 3 for the P.V issue, back to 0 once it
+    // is issued. Of the two wavefronts that share a SIMD, the one further
+    // along its softmax wins the VALU arbitration and reaches its products
+    // first, so the pair drifts out of step instead of running both
+    // softmaxes together and then both waiting on the matrix core (which
+    // leaves the VALU idle). The arithmetic is unchanged.
+    __builtin_amdgcn_s_setprio(1);
     v4i vpre[PRE > 0 ? PRE : 1][NKB];
 #pragma unroll
     for (int c = 0; c < PRE; ++c)
@@ -664,6 +672,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
         wr_s[wave][lane] = st_cur > 0.0f ? __fdiv_rn(svl, st_cur) : 0.0f;
         __builtin_amdgcn_wave_barrier();
       }
+      __builtin_amdgcn_s_setprio(2);
       lsum = probs_tile<VPT>(u, exp_bias(m_use), wr_s[VPT ? wave : 0], p, g);
     }
 
@@ -695,9 +704,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     l = __builtin_fmaf(alpha, l, lsum);
     m = m_new;
 
+    __builtin_amdgcn_s_setprio(3);
     // per-token V converts every tile's product on its own: always a new run
     if (VPT || fresh) pv_tile<D, true, PRE>(acc_i, st->v, ln, p, vpre);
     else pv_tile<D, false, PRE>(acc_i, st->v, ln, p, vpre);
+    __builtin_amdgcn_s_setprio(0);
     fresh = false;
     if constexpr (VPT) {
       // per-token V: tile scales differ, so each tile's INT32 product is
