@@ -613,8 +613,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       }
     } else {
     // Issue priority (s_setprio) rises through the tile's VALU work: 1 from
-    // here, 2 for the probabilities, 3 for the P.V issue, back to 0 once it
-    // is issued. Of the two wavefronts that share a SIMD, the one further
+    // here, 2 for the probabilities (exp or table), 3 for the P.V issue, back
+    // to 0 once it is issued. Of the two wavefronts that share a SIMD, the one further
     // along its softmax wins the VALU arbitration and reaches its products
     // first, so the pair drifts out of step instead of running both
     // softmaxes together and then both waiting on the matrix core (which
@@ -650,6 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
     float st_cur = 0.0f;
     if constexpr (LUT) {
       m_u = fmaxf(m_u, mx);
+      __builtin_amdgcn_s_setprio(2);
       const float mu = m_u * kap;
       const int rel = min(lim, a.Lkv - 1) - k0 - 16 * g;
       if constexpr (LUT == 2) {

@@ -72,6 +72,20 @@ def test_per_token_v_tie_problem(lib):
     run_problem(lib, q, k, v, True, True, "f16", tag="per_token_v_tie")
 
 
+def test_exact_rounding_tie_problem(lib):
+    # B2 H12 Hkv3 Lq1177 Lkv2608 d64, not causal, per-token V, fp32 inputs,
+    # fp16 O, channel 11 of Q and K x20 (problem 1958 of the random sweep). In
+    # the peaked row (b 0, h 1, query 711) key 882's fp32 product y * w is
+    # exactly 40.5: the oracle rounds it to the even code 40, and an exponential
+    # one ulp higher gives 41, which moves that row by ~0.018, inside the
+    # tolerance (the one way the exact logits leave for a code to differ)
+    B, H, Hkv, Lq, Lkv, d = 2, 12, 3, 1177, 2608, 64
+    q = gaussian((B, H, Lq, d), 119580, np.float32, [11])
+    k = gaussian((B, Hkv, Lkv, d), 119581, np.float32, [11])
+    v = gaussian((B, Hkv, Lkv, d), 119582, np.float32)
+    run_problem(lib, q, k, v, False, True, "f16", tag="exact_tie")
+
+
 @pytest.mark.parametrize("neg", [False, True])
 @pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,vpt,odt", [
     (1, 4, 2, 300, 333, 128, 1, 0, "f32"), (1, 4, 2, 300, 333, 64, 0, 1, "f16"),
