@@ -599,6 +599,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
       if (t + 3 < n_tiles) request_tile<D, true, VPT>(*nx2, bf, ln, wave, lane, k0 + 3 * BN);
     }
 
+    // causal: a tile past the last row of this wavefront changes nothing (a
+    // fully masked tile is a no-op), so its arithmetic is skipped; the
+    // wavefront still issues its share of the stage loads and meets the
+    // barrier. (The last tile of a row block lies past the first two
+    // wavefronts' rows.)
+    const bool dead = CAUSAL && k0 > min(qw0 + 31, a.Lq - 1) + shift;
+    if (DUMP || !dead) {
     v16i s[NKB];
     qk_tile<D>(s, st->k, ln, qf);
     if constexpr (DUMP) {
@@ -730,6 +737,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(FwdArgs a) {
           acc[c][v] = __builtin_fmaf(st_cur, static_cast<float>(acc_i[c][v]), acc[c][v]);
     }
     }  // !DUMP
+    }  // live tile
 
     // after an odd tile: tiles t+1 and t+2 must have landed before anyone
     // reads them; after the barrier every wavefront is done with stages t-1
