@@ -26,6 +26,11 @@ Also reported on the same JSON line:
                 durations
   clocks        shader and memory clocks (MHz) read from the driver's sysfs
                 during the timed region
+  roofline_int8_q  (prefill, Q quantized in the kernel) the same forward on
+                INT8 codes of Q (attn_int8_fwd), timed right after the timed
+                region in steps of the separate-Q path: the attention kernel
+                without the Q quantization that the fused step moves into its
+                prologue
   measured_peaks  second denominators measured on this GPU right after the
                 timed region: an INT8 MFMA loop (TOP/s) and a streaming HBM
                 read of 2 GiB (GB/s), from libattn_probes
@@ -533,11 +538,42 @@ def main():
                                                  else "" if fused_q else "_separate_q"), kfiles)
     roof["kernel_ms"] = round(attn_ms, 4)
     roof["algorithmic_per_launch"] = ops if bound_mfma else attn_bytes
+    # the same forward on INT8 codes of Q: steps of the separate-Q path (K, V
+    # and Q quantized in their own passes, then attn_int8_fwd), run right after
+    # the timed region with events around the forward alone. This is the
+    # attention kernel without the Q quantization in its prologue. (Launched
+    # back to back with no quantize passes between them, the forwards run
+    # slower: the clock drops under the sustained matrix-core load.)
+    int8_q = None
+    if fused_q and bound_mfma and not rot and not args.attn_only:
+        def step8():
+            quantize()
+            m.attn_quantize_rows(dq, 1, qh, sq)
+        ev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for _ in range(max(args.warmup, 10)):
+            step8()
+            m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+        for e1, e2 in ev8:
+            step8()
+            e1.record(stream)
+            m.attn_int8_fwd(qh, sq, kh, sk, vh, sv, w.v_per_token, w.causal, odt, out=o, workspace=ws)
+            e2.record(stream)
+        torch.cuda.synchronize()
+        t8 = np.array([e1.elapsed_time(e2) for e1, e2 in ev8])
+        tops8 = ops / (float(np.mean(t8)) * 1e-3) / 1e12
+        int8_q = {"kernel": "attn_fwd_kernel on INT8 Q (attn_int8_fwd), timed in steps of the separate-Q "
+                            "path (quantize K, V and Q, then the forward); not the step timed above",
+                  "kernel_ms": round(float(np.mean(t8)), 4), "times_ms": stats(t8),
+                  "achieved": round(tops8, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                  "frac": round(tops8 / PEAK_INT8_TOPS, 4)}
     peaks = None if args.no_peaks else measured_peaks(torch)
     if peaks:
         mp = peaks["mfma_i8_tops"] if bound_mfma else peaks["hbm_read_gbs"]
         roof["measured_peak"] = mp
         roof["frac_of_measured_peak"] = round(roof["achieved"] / mp, 4)
+        if int8_q:
+            int8_q["frac_of_measured_peak"] = round(int8_q["achieved"] / mp, 4)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
@@ -559,6 +595,7 @@ def main():
                             + (" + fused attention (Q quantized in the kernel)" if fused_q else
                                " + quantize Q + fused attention"))},
         "roofline": roof,
+        "roofline_int8_q": int8_q,
         "kernels": {"attention_ms": round(attn_ms, 4), "quantize_ms": round(quant_ms, 4),
                     "attention": stats(attn_t), "quantize": stats(quant_t),
                     "attention_tops": round(kernel_tops, 2),
