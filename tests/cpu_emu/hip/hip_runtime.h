@@ -19,13 +19,14 @@
 #pragma once
 
 #include <algorithm>
-#include <barrier>
 #include <cmath>
+#include <condition_variable>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <thread>
 #include <type_traits>
 #include <vector>
@@ -64,9 +65,45 @@ inline uint2 make_uint2(unsigned a, unsigned b) { return {a, b}; }
 
 namespace emu {
 
+// A reusable barrier with its own mutex and condition variable (generation
+// count; arrive_and_drop leaves it for good). The C++ library's barrier parks
+// its waiters in a process-wide pool of mutexes keyed by address, which
+// ThreadSanitizer sees as ordering threads of unrelated barriers (other
+// wavefronts) and so hides the races this emulation is also run to find.
+class Barrier {
+ public:
+  explicit Barrier(int n) : expected_(n) {}
+  void arrive_and_wait() {
+    std::unique_lock<std::mutex> lk(mu_);
+    const unsigned long gen = gen_;
+    if (++arrived_ == expected_) {
+      next_phase();
+    } else {
+      cv_.wait(lk, [&] { return gen_ != gen; });
+    }
+  }
+  void arrive_and_drop() {
+    std::lock_guard<std::mutex> lk(mu_);
+    --expected_;
+    if (arrived_ == expected_ && expected_ > 0) next_phase();
+  }
+
+ private:
+  void next_phase() {
+    arrived_ = 0;
+    ++gen_;
+    cv_.notify_all();
+  }
+  std::mutex mu_;
+  std::condition_variable cv_;
+  int expected_;
+  int arrived_ = 0;
+  unsigned long gen_ = 0;
+};
+
 struct Wave {
   explicit Wave(int n) : bar(n) {}
-  std::barrier<> bar;
+  Barrier bar;
   alignas(16) unsigned char slot[64][64];
 };
 
@@ -77,7 +114,7 @@ struct Ctx {
 };
 inline thread_local Ctx ctx;
 inline dim3 g_grid, g_block;
-inline std::barrier<>* g_block_bar = nullptr;
+inline Barrier* g_block_bar = nullptr;
 
 template <class F>
 void launch(dim3 grid, dim3 block, F&& body) {
@@ -88,7 +125,7 @@ void launch(dim3 grid, dim3 block, F&& body) {
   for (unsigned bz = 0; bz < grid.z; ++bz)
     for (unsigned by = 0; by < grid.y; ++by)
       for (unsigned bx = 0; bx < grid.x; ++bx) {
-        std::barrier<> bbar(nthreads);
+        Barrier bbar(nthreads);
         g_block_bar = &bbar;
         std::vector<std::unique_ptr<Wave>> waves;
         for (int w = 0; w < nwaves; ++w)
