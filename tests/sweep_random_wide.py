@@ -3,6 +3,7 @@
 Run by hand on a GPU host (not collected by pytest):
 
     python tests/sweep_random_wide.py --n 300 --log sweep.log
+    python tests/sweep_random_wide.py --decode --n 1000 --log sweep_decode.log
 
 Problem i draws its shape and options from PCG64(70000 + i): B 1-3, query
 heads 1-16 with 1, 2, 4 or 8 query heads per KV head, Lq up to 2000 and Lkv
@@ -56,10 +57,39 @@ def problem(i):
                 outliers=outliers, seeds=(base, base + 1, base + 2))
 
 
+def decode_problem(i):
+    """Problem i of the decode-shaped sweep, from PCG64(90000 + i): at most 16
+    query rows per KV head (the split-KV path): B 1-8, 1-8 KV heads with 1, 2,
+    4 or 8 query heads each, Lq 1-4 (causal or not when Lq > 1), Lkv 1-20000,
+    d 64 or 128, each V granularity, fp16 or fp32 inputs and O, half of the
+    problems with 1-2 % of the channels of Q and K x20."""
+    r = np.random.Generator(np.random.PCG64(90000 + i))
+    d = int(r.choice([64, 128]))
+    g = int(r.choice([1, 2, 4, 8]))
+    Lq = int(r.integers(1, 16 // g + 1)) if g < 16 else 1
+    Lq = min(Lq, 4)
+    Hkv = int(r.integers(1, 9))
+    B = int(r.integers(1, 9))
+    Lkv = int(r.integers(max(Lq, 1), 20001))
+    causal = bool(r.integers(0, 2)) and Lq > 1
+    vmode = [False, True, "head", "channel"][int(r.integers(0, 4))]
+    o = ["f16", "f32"][int(r.integers(0, 2))]
+    dt = ["f16", "f32"][int(r.integers(0, 2))]
+    outliers = None
+    if r.integers(0, 2):
+        n = int(r.integers(1, max(1, round(0.02 * d)) + 1))
+        outliers = sorted(int(c) for c in r.choice(d, size=n, replace=False))
+    base = 200000 + 10 * i
+    return dict(B=B, H=Hkv * g, Hkv=Hkv, Lq=Lq, Lkv=Lkv, d=d, causal=causal, vmode=vmode, o=o, dt=dt,
+                outliers=outliers, seeds=(base, base + 1, base + 2))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--n", type=int, default=300, help="random problems after the fixed one")
     ap.add_argument("--log", default=None, help="also append the lines to this file")
+    ap.add_argument("--decode", action="store_true",
+                    help="decode-shaped problems (at most 16 query rows per KV head: split-KV path)")
     args = ap.parse_args()
     import int8_quantized_flashattention_amd as lib
 
@@ -75,7 +105,7 @@ def main():
     worst = None
     t0 = time.time()
     for i in range(args.n + 1):
-        p = problem(i)
+        p = decode_problem(i) if args.decode else problem(i)
         dt = np.float16 if p["dt"] == "f16" else np.float32
         sq_, sk_, sv_ = p["seeds"]
         q = gaussian((p["B"], p["H"], p["Lq"], p["d"]), sq_, dt, p["outliers"])
