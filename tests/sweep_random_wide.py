@@ -4,6 +4,7 @@ Run by hand on a GPU host (not collected by pytest):
 
     python tests/sweep_random_wide.py --n 300 --log sweep.log
     python tests/sweep_random_wide.py --decode --n 1000 --log sweep_decode.log
+    python tests/sweep_random_wide.py --lut --n 1000 --log sweep_lut.log
 
 Problem i draws its shape and options from PCG64(70000 + i): B 1-3, query
 heads 1-16 with 1, 2, 4 or 8 query heads per KV head, Lq up to 2000 and Lkv
@@ -30,6 +31,7 @@ sys.path.insert(0, os.path.dirname(HERE))
 
 from gpu_parity import O_MAX_ABS, O_REL_FRO, run_problem  # noqa: E402
 from workloads import gaussian  # noqa: E402
+from test_gpu_index_softmax import run_lut  # noqa: E402
 
 
 def problem(i):
@@ -84,12 +86,47 @@ def decode_problem(i):
                 outliers=outliers, seeds=(base, base + 1, base + 2))
 
 
+def lut_problem(i):
+    """Problem i of the IndexSoftmax sweep, from PCG64(110000 + i): prefill
+    shapes (Lq up to 2000, Lkv up to 3000) and, for 30 % of the problems,
+    decode shapes (at most 16 query rows per KV head); B 1-3, 1-8 KV heads with
+    GQA 1-8, d 64 or 128, causal or not, table bits 1-8 and clip 0.5-8, V per
+    tensor, head or channel, fp16 or fp32 inputs and O, half of the problems
+    with 1-2 % of the channels of Q and K x20."""
+    r = np.random.Generator(np.random.PCG64(110000 + i))
+    d = int(r.choice([64, 128]))
+    g = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.integers(1, 9))
+    B = int(r.integers(1, 4))
+    causal = bool(r.integers(0, 2))
+    if r.random() < 0.3:
+        Lq = int(r.integers(1, 16 // g + 1))
+        Lkv = int(r.integers(Lq, 12001))
+    else:
+        Lkv = int(r.integers(1, 3001))
+        Lq = int(r.integers(1, min(2000, Lkv) + 1)) if causal else int(r.integers(1, 2001))
+    vmode = ["tensor", "head", "channel"][int(r.integers(0, 3))]
+    o = ["f16", "f32"][int(r.integers(0, 2))]
+    dt = ["f16", "f32"][int(r.integers(0, 2))]
+    bits = int(r.integers(1, 9))
+    clip = round(float(r.uniform(0.5, 8.0)), 2)
+    outliers = None
+    if r.integers(0, 2):
+        n = int(r.integers(1, max(1, round(0.02 * d)) + 1))
+        outliers = sorted(int(c) for c in r.choice(d, size=n, replace=False))
+    base = 300000 + 10 * i
+    return dict(B=B, H=Hkv * g, Hkv=Hkv, Lq=Lq, Lkv=Lkv, d=d, causal=causal, vmode=vmode, o=o, dt=dt,
+                bits=bits, clip=clip, outliers=outliers, seeds=(base, base + 1, base + 2))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--n", type=int, default=300, help="random problems after the fixed one")
     ap.add_argument("--log", default=None, help="also append the lines to this file")
     ap.add_argument("--decode", action="store_true",
                     help="decode-shaped problems (at most 16 query rows per KV head: split-KV path)")
+    ap.add_argument("--lut", action="store_true",
+                    help="IndexSoftmax problems (attn_int8_fwd_index_softmax against the oracle's table path)")
     args = ap.parse_args()
     import int8_quantized_flashattention_amd as lib
 
@@ -105,7 +142,7 @@ def main():
     worst = None
     t0 = time.time()
     for i in range(args.n + 1):
-        p = decode_problem(i) if args.decode else problem(i)
+        p = lut_problem(i) if args.lut else decode_problem(i) if args.decode else problem(i)
         dt = np.float16 if p["dt"] == "f16" else np.float32
         sq_, sk_, sv_ = p["seeds"]
         q = gaussian((p["B"], p["H"], p["Lq"], p["d"]), sq_, dt, p["outliers"])
@@ -114,11 +151,15 @@ def main():
         m = {}
         err = None
         try:
-            run_problem(lib, q, k, v, p["causal"], p["vmode"], p["o"], tag="sweep%d" % i, measure=m)
+            if args.lut:
+                run_lut(lib, q, k, v, p["causal"], p["vmode"], p["o"], p["bits"], p["clip"], tag="lut%d" % i,
+                        measure=m)
+            else:
+                run_problem(lib, q, k, v, p["causal"], p["vmode"], p["o"], tag="sweep%d" % i, measure=m)
         except AssertionError as e:          # a bit-exact check failed
             err = "bit-exact: %r" % (e.args,)
         ok = (err is None and m["finite"] and m["max_abs"] <= O_MAX_ABS and m["rel_fro"] <= O_REL_FRO
-              and m["lse_err"] <= 1e-4)
+              and m["lse_err"] <= (1e-5 if args.lut else 1e-4) and m.get("strict", True))
         n_ok += ok
         rec = dict(i=i, ok=bool(ok), err=err, **{k_: v_ for k_, v_ in p.items() if k_ != "seeds"}, **m)
         if m and (worst is None or m["max_abs"] > worst["max_abs"]):
