@@ -6,6 +6,7 @@ Run by hand on a GPU host (not collected by pytest):
     python tests/sweep_random_wide.py --decode --n 1000 --log sweep_decode.log
     python tests/sweep_random_wide.py --lut --n 1000 --log sweep_lut.log
     python tests/sweep_random_wide.py --int4 --n 1000 --log sweep_int4.log
+    python tests/sweep_random_wide.py --hadamard --n 1000 --log sweep_hadamard.log
 
 Problem i draws its shape and options from PCG64(70000 + i): B 1-3, query
 heads 1-16 with 1, 2, 4 or 8 query heads per KV head, Lq up to 2000 and Lkv
@@ -34,6 +35,7 @@ from gpu_parity import O_MAX_ABS, O_REL_FRO, run_problem  # noqa: E402
 from workloads import gaussian  # noqa: E402
 from test_gpu_index_softmax import run_lut  # noqa: E402
 from test_gpu_int4 import run_int4  # noqa: E402
+from test_gpu_hadamard import run_rotated  # noqa: E402
 
 
 def problem(i):
@@ -151,12 +153,34 @@ def int4_problem(i):
                 outliers=outliers, seeds=(base, base + 1, base + 2))
 
 
+def hadamard_problem(i):
+    """Problem i of the Hadamard sweep, from PCG64(150000 + i): Q and K rotated
+    before quantization; 30 % decode shapes (Lkv up to 12000), 70 % prefill
+    shapes (Lq up to 2000, Lkv up to 3000); B 1-3, 1-8 KV heads with GQA 1-8,
+    d 64 or 128, causal or not, V per tensor, token, head or channel, fp16 or
+    fp32 inputs and O, half with outlier channels."""
+    p = int4_problem(i)
+    r = np.random.Generator(np.random.PCG64(150000 + i))
+    g = p["H"] // p["Hkv"]
+    causal = bool(r.integers(0, 2))
+    if r.random() < 0.3:
+        Lq = int(r.integers(1, 16 // g + 1))
+        Lkv = int(r.integers(Lq, 12001))
+    else:
+        Lkv = int(r.integers(1, 3001))
+        Lq = int(r.integers(1, min(2000, Lkv) + 1)) if causal else int(r.integers(1, 2001))
+    base = 500000 + 10 * i
+    return dict(p, Lq=Lq, Lkv=Lkv, causal=causal, seeds=(base, base + 1, base + 2))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--n", type=int, default=300, help="random problems after the fixed one")
     ap.add_argument("--log", default=None, help="also append the lines to this file")
     ap.add_argument("--decode", action="store_true",
                     help="decode-shaped problems (at most 16 query rows per KV head: split-KV path)")
+    ap.add_argument("--hadamard", action="store_true",
+                    help="Q and K rotated by the normalized Hadamard matrix (quantizer and fused-Q forward)")
     ap.add_argument("--int4", action="store_true",
                     help="INT4 Q.K problems (attn_int4qk_fwd against the oracle on the same 4-bit codes)")
     ap.add_argument("--lut", action="store_true",
@@ -176,8 +200,8 @@ def main():
     worst = None
     t0 = time.time()
     for i in range(args.n + 1):
-        p = (lut_problem(i) if args.lut else int4_problem(i) if args.int4 else decode_problem(i) if args.decode
-             else problem(i))
+        p = (lut_problem(i) if args.lut else int4_problem(i) if args.int4 else hadamard_problem(i) if args.hadamard
+             else decode_problem(i) if args.decode else problem(i))
         dt = np.float16 if p["dt"] == "f16" else np.float32
         sq_, sk_, sv_ = p["seeds"]
         q = gaussian((p["B"], p["H"], p["Lq"], p["d"]), sq_, dt, p["outliers"])
@@ -191,6 +215,8 @@ def main():
                         measure=m)
             elif args.int4:
                 run_int4(lib, q, k, v, p["causal"], p["vmode"], p["o"], tag="int4_%d" % i, measure=m)
+            elif args.hadamard:
+                run_rotated(lib, q, k, v, p["causal"], p["vmode"], p["o"], tag="rot%d" % i, measure=m)
             else:
                 run_problem(lib, q, k, v, p["causal"], p["vmode"], p["o"], tag="sweep%d" % i, measure=m)
         except AssertionError as e:          # a bit-exact check failed

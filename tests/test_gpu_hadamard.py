@@ -10,7 +10,7 @@ import torch
 
 import int4_format
 import oracle
-from gpu_parity import compare_o, dev, host, log, quantize_both
+from gpu_parity import compare_o, dev, host, log, o_errors, quantize_both, quantize_cols_both
 from workloads import WORKLOADS, gaussian
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +31,47 @@ def rotated_both(lib, x, bits=8):
     if bits == 4:
         assert np.array_equal(host(p), int4_format.pack(qo))
     return qo, so, c, p, s
+
+
+def run_rotated(lib, q, k, v, causal, vmode, odt, tag="", measure=None):
+    """The rotated path on the GPU against the oracle: Q and K rotated and
+    quantized (codes and scales bit-exact), V per tensor, token, head or
+    channel; the forward on the rotated codes, and the forward that rotates
+    and quantizes fp16/fp32 Q in its Q load, which must return the same codes,
+    scales, O and lse bit for bit. measure: if a dict, the O and lse errors
+    are stored in it instead of being asserted (the bit-exact checks still
+    assert)."""
+    B, H, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    log("[%s] B=%d H=%d Hkv=%d Lq=%d Lkv=%d d=%d causal=%d v=%s o=%s" % (tag, B, H, Hkv, Lq, Lkv, d, causal, vmode, odt))
+    qh, sq, qd, _, sqd = rotated_both(lib, q)
+    kh, sk, kd, _, skd = rotated_both(lib, k)
+    if vmode == "channel":
+        vh, sv, vd, svd = quantize_cols_both(lib, v, Lkv)
+    else:
+        vh, sv, vd, svd = quantize_both(lib, v, {"tensor": v.size // d, "token": 1, "head": Lkv}[vmode])
+    vp = {"tensor": False, "token": True, "head": "head", "channel": "channel"}[vmode]
+    tdt = torch.float16 if odt == "f16" else torch.float32
+    o1, l1 = lib.attn_int8_fwd(qd, sqd, kd, skd, vd, svd, vp, causal, tdt, return_lse=True)
+    qh2, sq2 = torch.empty_like(qd), torch.empty_like(sqd)
+    o2, l2 = lib.attn_int8_fwd_qfloat(dev(q), kd, skd, vd, svd, vp, causal, tdt, return_lse=True,
+                                      q_hat=qh2, s_q=sq2, hadamard=True)
+    assert torch.equal(qh2, qd) and torch.equal(sq2.view(torch.int32), sqd.view(torch.int32)), "fused rotated Q codes"
+    iv = torch.int16 if tdt == torch.float16 else torch.int32
+    assert torch.equal(o2.view(iv), o1.view(iv)) and torch.equal(l2.view(torch.int32), l1.view(torch.int32)), \
+        "fused rotated-Q forward differs"
+    tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
+    mode = {"tensor": 0, "token": 1, "head": 2, "channel": 3}[vmode]
+    oo, lo = oracle.attn_int8(qh, sq, kh, sk, vh, sv, mode, B, H, Hkv, Lq, Lkv, d, causal, tile, split)
+    og, lg = host(o1).astype(np.float32).reshape(-1, d), host(l1).reshape(-1)
+    lo = lo.reshape(-1)
+    lse_err = float(np.max(np.abs(lg - lo) / np.maximum(1.0, np.abs(lo)))) if lo.size else 0.0
+    if measure is not None:
+        measure["max_abs"], measure["rel_fro"], measure["finite"] = o_errors(og, oo.reshape(-1, d))
+        measure["lse_err"] = lse_err
+        return
+    compare_o(og, oo.reshape(-1, d), tag)
+    assert lse_err <= 1e-4
 
 
 @pytest.mark.parametrize("rows,cols,bits,dt", [(7, 64, 8, np.float16), (4096, 128, 8, np.float16),
@@ -112,3 +153,17 @@ def test_fused_rotated_q_equals_separate(lib, B, H, Hkv, Lq, Lkv, d, causal, qdt
     tile, split = lib.attn_int8_fwd_schedule(B, H, Hkv, Lq, Lkv, d, causal)
     oo, _ = oracle.attn_int8(qh, sq, kh, sk, vh, sv, 0, B, H, Hkv, Lq, Lkv, d, causal, tile, split)
     compare_o(host(o2), oo, "fused rotated Q")
+
+
+@pytest.mark.parametrize("vmode", ["tensor", "token", "head", "channel"])
+@pytest.mark.parametrize("B,H,Hkv,Lq,Lkv,d,causal,odt", [
+    (2, 4, 2, 150, 333, 128, 1, "f16"), (2, 8, 2, 1, 2100, 64, 0, "f32")])
+def test_rotated_path_every_v_mode(lib, B, H, Hkv, Lq, Lkv, d, causal, odt, vmode):
+    # rotated Q and K with each V granularity, prefill and split-KV decode
+    # shapes, one outlier channel in Q and K: codes bit-exact, the fused
+    # rotated-Q forward bit-identical, O against the oracle
+    seed = 17000 + Lq + Lkv
+    q = gaussian((B, H, Lq, d), seed, np.float16, [5])
+    k = gaussian((B, Hkv, Lkv, d), seed + 1, np.float16, [5])
+    v = gaussian((B, Hkv, Lkv, d), seed + 2, np.float16)
+    run_rotated(lib, q, k, v, causal, vmode, odt, tag="rot_%s" % vmode)
